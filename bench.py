@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Bench of the small-T groupwise-int projection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+
+A step is one projection Y = X . dequant(Wq) of the headline workload: the
+GDN-QK-like int4 projection, T=8, K=5120, N=8192, group 64, fp16 scales, with
+inputs resident in HBM.  Consecutive steps rotate through distinct weight
+replicas totalling > 1 GiB, so every step streams its weights from HBM rather
+than from the 256 MB Infinity Cache.  Steps are timed with HIP events on the
+stream the kernels run on.  The line printed also carries the sweep the metric
+asks for (T = 1, 2, 4, 8 for the int4 QK and int5 gate/value projections, and
+the SwiGLU pair), the roofline of the dominant kernel, a parity check of the
+timed configuration against the oracle and the oracle's own CPU time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/projection + effective HBM GB/s (% of peak) at T=1,2,4,8, K=5120 int4/int5"
+PEAK_GBS = 8000.0  # MI355X HBM3E peak
+COLD_BYTES = 1 << 30
+KERNEL_SRC = os.path.join(ROOT, "groupwise_int_weight_amd", "csrc", "ngq_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qk", choices=["qk", "gv"])
+    p.add_argument("--T", type=int, default=8)
+    p.add_argument("--no-sweep", action="store_true", help="time only the headline configuration")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-calibration", action="store_true")
+    p.add_argument("--sweep-steps", type=int, default=100)
+    return p.parse_args()
+
+
+def packed_bytes(ngq, w):
+    return ngq.ngq_packed_bytes(w.K, w.N, w.bits)
+
+
+def algorithmic_bytes(ngq, w, T, n_out=None):
+    """Packed weights + scales read once, X read once, Y written once."""
+    n_out = w.N if n_out is None else n_out
+    return packed_bytes(ngq, w) + ngq.ngq_scale_bytes(w.K, w.N, w.bits) + 2 * T * w.K + 2 * T * n_out
+
+
+class Rotation:
+    """Distinct replicas of one workload's weights, enough to exceed the caches."""
+
+    def __init__(self, ngq, w, T, seed=0):
+        import synthetic
+
+        self.w = w
+        self.T = T
+        nb = packed_bytes(ngq, w)
+        per = nb + ngq.ngq_scale_bytes(w.K, w.N, w.bits)
+        self.replicas = max(2, math.ceil(COLD_BYTES / per))
+        self.wq, self.s, self.x = synthetic.device_replicas(w, T, self.replicas, nb, seed=seed)
+        self.cold_bytes = self.replicas * per
+
+
+def time_steps(launch, replicas, steps, warmup):
+    import torch
+
+    for i in range(warmup):
+        launch(i % replicas)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        launch(i % replicas)
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per step
+
+
+def calibrate(ngq):
+    """Attainable HBM read rate (own streaming-read kernel) and a torch copy of
+    known size (the reference point for the traffic counters)."""
+    import torch
+
+    out = {}
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    ms = time_steps(lambda i: ngq.ngq_stream_read(buf, sink), 1, 10, 3)
+    out["stream_read_GBps"] = nbytes / ms / 1e6
+    del buf
+    cb = 1 << 30
+    src = torch.zeros(cb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_steps(lambda i: dst.copy_(src), 1, 10, 3)
+    out["torch_copy_bytes"] = cb
+    out["torch_copy_GBps"] = 2 * cb / ms / 1e6  # read + write
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_projection(ngq, w, T, steps, warmup):
+    import torch
+
+    rot = Rotation(ngq, w, T)
+    y = torch.empty((T, w.N), dtype=torch.bfloat16, device="cuda")
+
+    def launch(i):
+        ngq.ngq_gemm(rot.x, rot.wq[i], rot.s[i], w.bits, w.N, y=y)
+
+    ms = time_steps(launch, rot.replicas, steps, warmup)
+    return ms, rot, y
+
+
+def run_swiglu(ngq, T, steps, warmup):
+    import torch
+
+    import synthetic
+
+    wgu, wdn = synthetic.WORKLOADS["gate_up"], synthetic.WORKLOADS["down"]
+    n_ff = synthetic.N_FF
+    rg = Rotation(ngq, wgu, T)
+    rd = Rotation(ngq, wdn, T)
+    h = torch.empty((T, n_ff), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, wdn.N), dtype=torch.bfloat16, device="cuda")
+    ms_gu = time_steps(lambda i: ngq.ngq_swiglu_gemm(rg.x, rg.wq[i], rg.s[i], 4, n_ff, h=h), rg.replicas, steps,
+                       warmup)
+    ms_dn = time_steps(lambda i: ngq.ngq_gemm(h, rd.wq[i], rd.s[i], 4, wdn.N, y=y), rd.replicas, steps, warmup)
+    b_gu = algorithmic_bytes(ngq, wgu, T, n_out=n_ff)
+    b_dn = algorithmic_bytes(ngq, wdn, T)
+    del rg, rd
+    torch.cuda.empty_cache()
+    return [
+        {"workload": "gate_up+SwiGLU int4 K=5120 N=2x17408", "T": T, "us": ms_gu * 1e3,
+         "GBps": b_gu / ms_gu / 1e6, "pct_peak": 100 * b_gu / ms_gu / 1e6 / PEAK_GBS},
+        {"workload": "down int4 K=17408 N=5120", "T": T, "us": ms_dn * 1e3,
+         "GBps": b_dn / ms_dn / 1e6, "pct_peak": 100 * b_dn / ms_dn / 1e6 / PEAK_GBS},
+    ]
+
+
+def parity_check(ngq, rot, y_dev):
+    """Recompute replica 0 and compare sampled columns with the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from tests.parity import compare
+
+    w, T = rot.w, rot.T
+    ngq.ngq_gemm(rot.x, rot.wq[0], rot.s[0], w.bits, w.N, y=y_dev)
+    torch.cuda.synchronize()
+    yb = y_dev.view(torch.int16).cpu().numpy().view(np.uint16)
+    packed = rot.wq[0].cpu().numpy()
+    scales = rot.s[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    x = rot.x.view(torch.int16).cpu().numpy().view(np.uint16)
+    g = np.random.default_rng(7)
+    cols = np.unique(np.concatenate([np.arange(32), np.arange(w.N - 32, w.N), g.integers(0, w.N, 192)]))
+    y64, axw, axs = oracle.gemm(x, packed, scales, w.K, w.N, w.bits, w.scale_bf16, cols=cols.astype(np.int32),
+                                nthreads=8, with_bounds=True)
+    rep = compare(yb[:, cols], y64, axw, axs, w.K, w.bits)
+    rep["columns_checked"] = int(cols.size)
+    return rep, (x, packed, scales)
+
+
+def cpu_baseline(w, T, host_inputs, bytes_full):
+    """The oracle as it stands, on the host cores, over a column sample of the
+    same projection; scaled to the full projection's bytes."""
+    import numpy as np
+
+    import oracle
+
+    x, packed, scales = host_inputs
+    threads = max(1, min(16, os.cpu_count() or 1))
+    ncols = w.N  # the whole projection: ~8 s of single-core work at T=8
+    cols = np.arange(ncols, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.gemm(x, packed, scales, w.K, w.N, w.bits, w.scale_bf16, cols=cols, nthreads=threads)
+    dt = time.perf_counter() - t0
+    frac = ncols / w.N
+    return {
+        "value": bytes_full * frac / dt / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"one full T={T} projection ({ncols} of {w.N} columns, fp64 scalar oracle, "
+                  f"{threads} threads), {dt:.2f} s wall; value = its algorithmic bytes / wall time",
+        "us_per_projection_equiv": dt / frac * 1e6,
+    }
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(name, T):
+    """HBM bytes per launch from committed counter runs, if the kernel source is
+    the one they were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sha") != kernel_sha():
+        return None
+    entry = d.get("workloads", {}).get(f"{name}_T{T}")
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path is not sharded "
+              f"across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import groupwise_int_weight_amd as ngq
+    import synthetic
+
+    assert torch.cuda.is_available(), "bench needs a HIP device"
+    torch.cuda.set_device(0)
+    ngq.lib()
+
+    calib = {} if args.no_calibration else calibrate(ngq)
+
+    w = synthetic.WORKLOADS[args.workload]
+    T = args.T
+    ms, rot, y = run_projection(ngq, w, T, args.steps, args.warmup)
+    nbytes = algorithmic_bytes(ngq, w, T)
+    gbps = nbytes / ms / 1e6
+    parity, host_inputs = parity_check(ngq, rot, y)
+    cold = rot.cold_bytes
+    replicas = rot.replicas
+    del rot
+    torch.cuda.empty_cache()
+
+    sweep = []
+    if not args.no_sweep:
+        for name in ("qk", "gv"):
+            wl = synthetic.WORKLOADS[name]
+            for t in (1, 2, 4, 8):
+                ms_t, r, _ = run_projection(ngq, wl, t, args.sweep_steps, 10)
+                b = algorithmic_bytes(ngq, wl, t)
+                sweep.append({"workload": f"{name} int{wl.bits} K={wl.K} N={wl.N}", "T": t, "us": ms_t * 1e3,
+                              "GBps": b / ms_t / 1e6, "pct_peak": 100 * b / ms_t / 1e6 / PEAK_GBS})
+                del r
+                torch.cuda.empty_cache()
+        for t in (1, 8):
+            sweep.extend(run_swiglu(ngq, t, args.sweep_steps, 10))
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, T, host_inputs, nbytes)
+
+    traffic = traffic_for(args.workload, T)
+    names = {"qk": "GDN-QK-like Q4 projection", "gv": "attention gate/value-like Q5 projection"}
+    line = {
+        "metric": METRIC,
+        "value": gbps,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": names[args.workload], "T": T, "K": w.K, "N": w.N, "bits": w.bits, "group": 64,
+            "scales": "bf16" if w.scale_bf16 else "fp16", "accumulate": "fp32", "out": "bf16",
+            "cache": f"cold: {replicas} replicas rotated ({cold / 2**30:.2f} GiB)",
+            "parallelism": "single GPU",
+        },
+        "us_per_projection": ms * 1e3,
+        "pct_of_peak": 100 * gbps / PEAK_GBS,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": gbps,
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gbps / PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+        "cpu_baseline": cpu,
+        "calibration": calib,
+        "parity": parity,
+        "sweep": sweep,
+        "context": {"rtx4090_single_op_us": {"attention_q5_gate_value_t8": 39.936, "gdn_qk_q4_t8": 31.744},
+                    "note": "the pages' own timings on another GPU with unstated shapes; not a target"},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+"""Python binding of libngq: small-T groupwise-int projections on MI355X.
+
+Thin ctypes marshalling over the C ABI declared in ``include/ngq.h``; every
+step of the projection runs in the library's HIP kernels.  PyTorch is used
+only for device memory and the current stream.  The names match the C entry
+points: ``ngq_pack``, ``ngq_gemm``, ``ngq_swiglu_gemm`` and the debug exports.
+
+The library must be built first (``python -m groupwise_int_weight_amd.build``);
+importing a GPU entry point without it raises ``NgqLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libngq.so")
+
+NGQ_OK = 0
+NGQ_ERR_ARG = -1
+NGQ_ERR_SHAPE = -2
+NGQ_ERR_UNSUPPORTED = -3
+NGQ_ERR_ALIGN = -4
+NGQ_ERR_HIP = -5
+NGQ_INT4, NGQ_INT5, NGQ_INT8 = 4, 5, 8
+NGQ_SCALE_BF16 = 0x100
+NGQ_GROUP = 64
+NGQ_MAX_T = 8
+
+# Every function the header declares, with its ctypes signature.
+_SIZE = ctypes.c_size_t
+_INT = ctypes.c_int
+_PTR = ctypes.c_void_p
+SIGNATURES = {
+    "ngq_packed_bytes": (_SIZE, [_INT, _INT, _INT, _INT]),
+    "ngq_scale_bytes": (_SIZE, [_INT, _INT, _INT, _INT]),
+    "ngq_pack": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR]),
+    "ngq_gemm": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR]),
+    "ngq_swiglu_gemm": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR]),
+    "ngq_unpack_codes": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR]),
+    "ngq_dequant_f32": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR]),
+    "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
+    "ngq_strerror": (ctypes.c_char_p, [_INT]),
+    "ngq_version": (_INT, []),
+}
+
+
+class NgqLibraryMissing(ImportError):
+    pass
+
+
+class NgqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {ngq_strerror(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libngq.so (raises NgqLibraryMissing when it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise NgqLibraryMissing(
+                f"{LIB_PATH} is not built; run `python -m groupwise_int_weight_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != NGQ_OK:
+        raise NgqError(status, where)
+
+
+def ngq_strerror(status: int) -> str:
+    return lib().ngq_strerror(int(status)).decode()
+
+
+def ngq_version() -> int:
+    return int(lib().ngq_version())
+
+
+def ngq_packed_bytes(K: int, N: int, bits: int, group: int = NGQ_GROUP) -> int:
+    return int(lib().ngq_packed_bytes(K, N, bits, group))
+
+
+def ngq_scale_bytes(K: int, N: int, bits: int, group: int = NGQ_GROUP) -> int:
+    return int(lib().ngq_scale_bytes(K, N, bits, group))
+
+
+def ngq_pack(codes: np.ndarray, bits: int, group: int = NGQ_GROUP) -> np.ndarray:
+    """Pack int8 codes [K][N] (host) into the library's layout (host uint8 array)."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    K, N = codes.shape
+    nbytes = ngq_packed_bytes(K, N, bits, group)
+    out = np.zeros(max(nbytes, 16), dtype=np.uint8)
+    _check(lib().ngq_pack(K, N, bits, group, codes.ctypes.data, out.ctypes.data), "ngq_pack")
+    return out[:nbytes]
+
+
+# ---- device entry points (torch tensors on the current HIP device) ----------
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dev_ptr(t, what):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def _format_bits(bits: int, scales) -> int:
+    import torch
+
+    b = int(bits) & 0xFF
+    if scales is not None and scales.dtype == torch.bfloat16:
+        b |= NGQ_SCALE_BF16
+    elif scales is not None and scales.dtype != torch.float16:
+        raise TypeError("scales must be float16 or bfloat16")
+    return b
+
+
+def ngq_gemm(x, wq, scales, bits: int, N: int, y=None, group: int = NGQ_GROUP, stream=None):
+    """y[T][N] (bf16) = x[T][K] (bf16) . dequant(wq) with scales [K/64][N]."""
+    import torch
+
+    T, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    st = lib().ngq_gemm(T, K, N, _format_bits(bits, scales), group, _dev_ptr(x, "x"), _dev_ptr(wq, "wq"),
+                        _dev_ptr(scales, "scales"), _dev_ptr(y, "y"), _stream(stream))
+    _check(st, "ngq_gemm")
+    return y
+
+
+def ngq_swiglu_gemm(x, wq_gate_up, scales_gate_up, bits: int, N_ff: int, h=None, group: int = NGQ_GROUP,
+                    stream=None):
+    """h[T][N_ff] (bf16) = SiLU(x . W_gate) * (x . W_up), W = [gate | up] packed as K x 2N_ff."""
+    import torch
+
+    T, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if h is None:
+        h = torch.empty((T, N_ff), dtype=torch.bfloat16, device=x.device)
+    st = lib().ngq_swiglu_gemm(T, K, N_ff, _format_bits(bits, scales_gate_up), group, _dev_ptr(x, "x"),
+                               _dev_ptr(wq_gate_up, "wq_gate_up"), _dev_ptr(scales_gate_up, "scales_gate_up"),
+                               _dev_ptr(h, "h"), _stream(stream))
+    _check(st, "ngq_swiglu_gemm")
+    return h
+
+
+def ngq_unpack_codes(wq, K: int, N: int, bits: int, group: int = NGQ_GROUP, stream=None):
+    import torch
+
+    codes = torch.empty((K, N), dtype=torch.int8, device=wq.device)
+    _check(lib().ngq_unpack_codes(K, N, int(bits) & 0xFF, group, _dev_ptr(wq, "wq"), _dev_ptr(codes, "codes"),
+                                  _stream(stream)), "ngq_unpack_codes")
+    return codes
+
+
+def ngq_dequant_f32(wq, scales, K: int, N: int, bits: int, group: int = NGQ_GROUP, stream=None):
+    import torch
+
+    w = torch.empty((K, N), dtype=torch.float32, device=wq.device)
+    _check(lib().ngq_dequant_f32(K, N, _format_bits(bits, scales), group, _dev_ptr(wq, "wq"),
+                                 _dev_ptr(scales, "scales"), _dev_ptr(w, "w"), _stream(stream)),
+           "ngq_dequant_f32")
+    return w
+
+
+def ngq_stream_read(buf, sink, stream=None):
+    _check(lib().ngq_stream_read(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _dev_ptr(sink, "sink"),
+                                 _stream(stream)), "ngq_stream_read")
+
+
+__all__ = [
+    "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
+    "ngq_packed_bytes", "ngq_scale_bytes", "ngq_strerror", "ngq_version", "NgqError", "NgqLibraryMissing",
+    "lib", "SIGNATURES",
+]

@@ -1,0 +1,624 @@
+// ngq_gemm.hip -- gfx950 kernels of libngq and their C entry points.
+//
+// The projection Y[T x N] = X[T x K] . dequant(Wq[K x N]) for T <= 8 tokens
+// (the small-batch Q4/Q5 projections whose T=8 routing the NInfer-4090 V3
+// topic, section "What V3 did", tunes for the GDN projection, the attention
+// Q5 projection and the SwiGLU path).  The pages give the operation and its
+// single-operator timings on an RTX 4090 ("Measured data"), not a kernel; the
+// design below is written for CDNA4.
+//
+// Work decomposition.  One workgroup (8 waves) owns a tile of 16*V output
+// columns over the whole K, so no partial sum ever leaves the workgroup and the
+// result is deterministic.  The waves of a workgroup split K into contiguous
+// ranges of group pairs and meet once, at the end, in LDS.  V (1..4 columns per
+// lane) is picked per shape so that the number of tiles fills the 256 CUs in
+// whole rounds; consecutive tiles go to the same XCD (workgroup b runs on XCD
+// b % 8), so neighbouring columns that share a cache line share an L2.
+//
+// Inner step.  The path streams packed weights once from HBM and is bandwidth
+// bound, but at T=8 a VALU-only dot product would need ~4.5 VALU lane-ops per
+// weight against ~3.7 available at 70 % of HBM peak, so the multiply-add runs
+// on the matrix cores: v_mfma_f32_16x16x32_bf16 with A = 16 weight columns x
+// 32 k, B = 32 k x 16 "slots".  T <= 8 fills only half of the 16 slots, so
+// slot j = t + 8h carries token t restricted to the first (h = 0) or second
+// (h = 1) group of a pair of 64-k groups: one MFMA chain then yields separate
+// per-group partial sums for two groups at once, which is what the per-group
+// scale needs, at no cost in MFMA issue.
+//
+// Unpack without subtraction.  A code field u (0..31) becomes the bf16 value
+// 128 + u by placing u in the low mantissa bits under the exponent byte 0x43.
+// The wanted code is c = u - bias, so sum_k x (128 + u) over-counts by
+// (128 + bias) sum_k x; that term comes from one extra MFMA per step with a
+// constant A = -(128 + bias), which seeds each group's partial sum.  int8
+// fields are converted exactly with v_cvt_f32_ubyte and their bias (128) is
+// removed the same way.  Each group partial is then scaled in fp32:
+// acc += s[g][n] * partial, so no rounded weight*scale product is ever formed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "ngq_internal.h"
+
+namespace ngq {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+// A buffer offset that is out of range for every buffer (all are < 2 GiB, and
+// adding an in-range offset cannot wrap 32 bits).  Out-of-range buffer loads
+// return zero without touching memory.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // raw buffer (stride 0), 32-bit data format: bounds-checked against `bytes`
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int NW>
+__device__ __forceinline__ void load_words(uint32_t* d, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (NW == 1) {
+    d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (NW == 2) {
+    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    d[0] = v[0]; d[1] = v[1];
+  } else if constexpr (NW == 3) {
+    u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    d[0] = v[0]; d[1] = v[1]; d[2] = v[2];
+  } else if constexpr (NW == 4) {
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+  } else {
+    load_words<4>(d, r, off);
+    load_words<NW - 4>(d + 4, r, off + 16u);
+  }
+}
+
+// ---- unpack: one 8-k block of one column -> eight bf16 (128 + u), k order ----
+
+// High bits of int5 for one 8-k block: byte `byte_idx` of the P1 word holds
+// them for k = 8*block + 0..7.  Returns them at bit 4 of each byte, split into
+// k 0..3 (hi_e) and k 4..7 (hi_f).  x * 0x204081 copies 4 bits to offsets 0,
+// 7, 14, 21 without overlap; the mask keeps bit i of the nibble at 8 i + 4.
+__device__ __forceinline__ void int5_high_bits(uint32_t p1word, uint32_t byte_idx, uint32_t& hi_e,
+                                               uint32_t& hi_f) {
+  const uint32_t sh = 8u * byte_idx;
+  const uint32_t lo4 = __builtin_amdgcn_ubfe(p1word, sh, 4u) << 4;
+  const uint32_t hi4 = __builtin_amdgcn_ubfe(p1word, sh + 4u, 4u) << 4;
+  hi_e = (lo4 * 0x00204081u) & 0x10101010u;
+  hi_f = (hi4 * 0x00204081u) & 0x10101010u;
+}
+
+// Eight 4-bit fields of a P0 word (field i = k i) plus optional 5th bits to
+// eight bf16 values 128 + u in k order: two byte permutes spread the nibbles to
+// one byte each, two more permutes put the exponent byte 0x43 above each.
+__device__ __forceinline__ u32x4 nibbles_to_bf16(uint32_t w, uint32_t hi_e, uint32_t hi_f) {
+  const uint32_t w4 = w >> 4;
+  const uint32_t e = (__builtin_amdgcn_perm(w4, w, 0x05010400u) & 0x0F0F0F0Fu) | hi_e;  // k0 k1 k2 k3
+  const uint32_t f = (__builtin_amdgcn_perm(w4, w, 0x07030602u) & 0x0F0F0F0Fu) | hi_f;  // k4 k5 k6 k7
+  const uint32_t ex = 0x43434343u;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(ex, e, 0x04010400u);
+  r[1] = __builtin_amdgcn_perm(ex, e, 0x04030402u);
+  r[2] = __builtin_amdgcn_perm(ex, f, 0x04010400u);
+  r[3] = __builtin_amdgcn_perm(ex, f, 0x04030402u);
+  return r;
+}
+
+// Two int8 words (k 0..3, k 4..7) to eight bf16 values u (exact: u <= 255 has
+// at most 8 significant bits, so the upper half of its fp32 is its bf16).
+__device__ __forceinline__ u32x4 bytes_to_bf16(uint32_t w0, uint32_t w1) {
+  const uint32_t a0 = __float_as_uint((float)(w0 & 0xFFu));
+  const uint32_t a1 = __float_as_uint((float)((w0 >> 8) & 0xFFu));
+  const uint32_t a2 = __float_as_uint((float)((w0 >> 16) & 0xFFu));
+  const uint32_t a3 = __float_as_uint((float)(w0 >> 24));
+  const uint32_t b0 = __float_as_uint((float)(w1 & 0xFFu));
+  const uint32_t b1 = __float_as_uint((float)((w1 >> 8) & 0xFFu));
+  const uint32_t b2 = __float_as_uint((float)((w1 >> 16) & 0xFFu));
+  const uint32_t b3 = __float_as_uint((float)(w1 >> 24));
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+  r[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+  r[3] = __builtin_amdgcn_perm(b3, b2, 0x07060302u);
+  return r;
+}
+
+template <int BITS>
+struct Code {
+  static constexpr int bias = 1 << (BITS - 1);
+  // value of the unpacked bf16 minus the code: 128 + bias for the nibble
+  // formats (value 128 + u), bias for int8 (value u)
+  static constexpr int offset = BITS == 8 ? bias : 128 + bias;
+  // bf16 bit pattern of -offset (exact: 136, 144 and 128 need <= 5 bits)
+  static constexpr uint16_t neg_offset_bf16 = BITS == 4 ? 0xC308 : (BITS == 5 ? 0xC310 : 0xC300);
+};
+
+__device__ __forceinline__ float scale_to_f32(uint32_t dw, int half, bool bf16) {
+  const uint32_t bits = half ? (dw >> 16) : (dw & 0xFFFFu);
+  if (bf16) return __uint_as_float(bits << 16);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct GemmArgs {
+  const void* x;
+  const void* wq;
+  const void* scales;
+  void* y;
+  int T, K;
+  int Nout;    // output columns
+  int Ncols;   // columns of the packed matrix and of the scales
+  int up_off;  // SwiGLU: column offset of the up half (N_ff); 0 otherwise
+  int G;       // K / 64
+  int pairs;   // ceil(G / 2)
+  int ppw;     // pairs per wave
+  int ntiles;  // workgroups
+  uint32_t p0_bytes, p1_bytes, s_bytes, x_bytes;
+};
+
+template <int BITS, int V, int NSETS>
+struct PairBuf {
+  static constexpr int WPK = BITS == 8 ? 2 : 1;  // P0 words per 8-k block and column
+  uint32_t a[NSETS][4][V * WPK];                 // [set][step][word]; int8: V words of row 2kb, then 2kb+1
+  uint32_t p1[NSETS][2][BITS == 5 ? V : 1];      // int5 high-bit words, one per half pair
+  uint32_t b[4][4];                              // X fragment per step
+  uint32_t sc[NSETS][2 * V];                     // 4V scales (16-bit) per set
+};
+
+// Registers per pair buffer -> how many pairs to keep in flight.
+template <int BITS, int V, int NSETS>
+constexpr int pipeline_depth() {
+  constexpr int wpk = BITS == 8 ? 2 : 1;
+  constexpr int regs = NSETS * (4 * V * wpk + (BITS == 5 ? 2 * V : 0) + 2 * V) + 16;
+  constexpr int d = 168 / regs;
+  return d < 2 ? 2 : (d > 6 ? 6 : d);
+}
+
+template <int BITS, bool SBF16, int V, int NSETS>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+  constexpr int NB = pipeline_depth<BITS, V, NSETS>();
+  constexpr int WPK = BITS == 8 ? 2 : 1;
+  constexpr int TILE = 16 * V;
+  __shared__ float red[kWaves * NSETS * TILE * 8];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;  // operand row / slot index
+  const int q = lane >> 4;  // operand k-slot / result row group
+
+  // XCD-aware tile order: XCD x receives workgroups x, x+8, ...; give them
+  // consecutive tiles.
+  const int b = blockIdx.x;
+  const int xcd = b & 7, per = a.ntiles >> 3, rem = a.ntiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
+  const int c0 = tile * TILE;
+
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+
+  const uint32_t rowb = (uint32_t)a.Ncols * 4u;  // bytes of one packed row
+  // Within a pair (16 k-blocks of 8 k), k-slot q of step s reads k-block
+  // 2s + (q & 1) of group (q >> 1): lanes q = 0, 1 serve the first group,
+  // q = 2, 3 the second.
+  const uint32_t lane_kb = 8u * (uint32_t)(q >> 1) + (uint32_t)(q & 1);
+  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];
+  // B slot j = m carries token t = m & 7 for group half h = m >> 3; only the
+  // k-slots of that half are non-zero.
+  const int t = m & 7, h = m >> 3;
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s) {
+    const uint32_t col = (uint32_t)(c0 + s * a.up_off + V * m);
+    offA[s] = lane_kb * WPK * rowb + col * 4u;
+    offP1[s] = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
+    // result rows 4q..4q+3 of every MFMA -> columns c0 + 4Vq + [0, 4V)
+    offS[s] = (uint32_t)h * (uint32_t)a.Ncols * 2u + (uint32_t)(c0 + s * a.up_off + 4 * V * q) * 2u;
+  }
+  const bool b_active = ((q >> 1) == h) && (t < a.T);
+  const uint32_t offB = (uint32_t)t * (uint32_t)a.K * 2u + lane_kb * 16u;
+
+  const int pbase = wave * a.ppw;
+
+  auto issue = [&](PairBuf<BITS, V, NSETS>& buf, int pi) {
+    const int p = pbase + pi;
+    // Wave-uniform flags (bitwise, so that no lane-divergent branch appears).
+    const bool valid = (pi < a.ppw) & (p < a.pairs);
+    // last pair of an odd group count: its second group does not exist
+    const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
+    const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb : kOOB;
+    const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb : kOOB;
+    const bool bload = valid & b_active & !(half & ((q >> 1) != 0));
+    const uint32_t pb = bload ? (uint32_t)p * 256u + offB : kOOB;
+    const uint32_t ps = valid ? (uint32_t)p * rowb : kOOB;  // two scale rows of 2-byte entries
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const uint32_t o = offA[s] + pa + (uint32_t)st * 2u * WPK * rowb;
+        load_words<V>(&buf.a[s][st][0], rW, o);
+        if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
+      }
+      load_words<4>(&buf.b[st][0], rX, pb + (uint32_t)st * 32u);
+    }
+    if constexpr (BITS == 5) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        load_words<V>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
+        load_words<V>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) load_words<2 * V>(&buf.sc[s][0], rS, offS[s] + ps);
+  };
+
+  f32x4 acc[NSETS][V];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+
+  auto compute = [&](const PairBuf<BITS, V, NSETS>& buf) {
+    bf16x8 bfrag[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      u32x4 bv = {buf.b[st][0], buf.b[st][1], buf.b[st][2], buf.b[st][3]};
+      bfrag[st] = __builtin_bit_cast(bf16x8, bv);
+    }
+    // -(128 + bias) * sum_k x over each group half: seeds every partial sum
+    f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfrag[st], dx, 0, 0, 0);
+    f32x4 dp[NSETS][V];
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) dp[s][i] = dx;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          u32x4 av;
+          if constexpr (BITS == 4) {
+            av = nibbles_to_bf16(buf.a[s][st][i], 0u, 0u);
+          } else if constexpr (BITS == 5) {
+            uint32_t he, hf;
+            // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
+            int5_high_bits(buf.p1[s][st >> 1][i], 2u * (uint32_t)(st & 1) + (uint32_t)(q & 1), he, hf);
+            av = nibbles_to_bf16(buf.a[s][st][i], he, hf);
+          } else {
+            av = bytes_to_bf16(buf.a[s][st][i], buf.a[s][st][V + i]);
+          }
+          dp[s][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag[st],
+                                                             dp[s][i], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = V * r + i;
+          const float sc = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
+          acc[s][i][r] = __builtin_fmaf(sc, dp[s][i][r], acc[s][i][r]);
+        }
+  };
+
+  // NB pairs in flight per wave.  Loads are issued unconditionally (pairs past
+  // the wave's range get out-of-range offsets: no memory traffic, zeros) so
+  // that no branch separates a load from its use; only the compute is skipped.
+  // The scheduling barriers keep the pairs' loads in issue order, so the
+  // counter wait before each compute covers exactly that pair's loads.
+  PairBuf<BITS, V, NSETS> buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    issue(buf[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int it = 0; it < a.ppw; it += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (it + u < a.ppw) compute(buf[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[u], it + u + NB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Slots j and j + 8 hold the two group halves of token j: add them.
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[s][i][r]), 0x128 /* row_ror:8 */, 0xF,
+                                                   0xF, false);
+        acc[s][i][r] += __int_as_float(other);
+      }
+  if (h == 0) {
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int col = V * (4 * q + r) + i;
+          red[((wave * NSETS + s) * TILE + col) * 8 + t] = acc[s][i][r];
+        }
+  }
+  __syncthreads();
+
+  // Sum the waves in a fixed order, round, store (consecutive threads write
+  // consecutive columns of one token row).
+  uint16_t* y = static_cast<uint16_t*>(a.y);
+  for (int idx = threadIdx.x; idx < 8 * TILE; idx += kThreads) {
+    const int tt = idx / TILE, col = idx % TILE;
+    if (tt >= a.T || c0 + col >= a.Nout) continue;
+    float v[NSETS];
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) {
+      float sum = 0.f;
+      for (int w = 0; w < kWaves; ++w) sum += red[((w * NSETS + s) * TILE + col) * 8 + tt];
+      v[s] = sum;
+    }
+    float out;
+    if constexpr (NSETS == 2) {
+      out = v[0] * v[1] / (1.0f + expf(-v[0]));  // SiLU(gate) * up
+    } else {
+      out = v[0];
+    }
+    y[(size_t)tt * a.Nout + c0 + col] = f32_to_bf16_rne(out);
+  }
+}
+
+// ---- debug kernels: the GEMM's unpack and scale decoding, materialised ----
+
+template <int BITS, bool SBF16, bool DEQUANT>
+__global__ __launch_bounds__(256) void unpack_kernel(const void* wq, uint32_t p0_bytes, const void* scales,
+                                                     int K, int N, void* out) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int kb = blockIdx.y;  // 8-k block
+  if (n >= N) return;
+  const uint32_t* p0 = static_cast<const uint32_t*>(wq);
+  u32x4 v;
+  if constexpr (BITS == 4) {
+    v = nibbles_to_bf16(p0[(size_t)kb * N + n], 0u, 0u);
+  } else if constexpr (BITS == 5) {
+    const uint32_t* p1 = reinterpret_cast<const uint32_t*>(static_cast<const char*>(wq) + p0_bytes);
+    uint32_t he, hf;
+    int5_high_bits(p1[(size_t)(kb >> 2) * N + n], (uint32_t)(kb & 3), he, hf);
+    v = nibbles_to_bf16(p0[(size_t)kb * N + n], he, hf);
+  } else {
+    v = bytes_to_bf16(p0[(size_t)(2 * kb) * N + n], p0[(size_t)(2 * kb + 1) * N + n]);
+  }
+  float sc = 1.0f;
+  if constexpr (DEQUANT) {
+    const uint32_t* s32 = static_cast<const uint32_t*>(scales);
+    const size_t si = (size_t)(kb / 8) * N + n;
+    sc = scale_to_f32(s32[si >> 1], (int)(si & 1), SBF16);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t bits16 = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    const float val = __uint_as_float(bits16 << 16) - (float)Code<BITS>::offset;  // the code, exact
+    const size_t o = (size_t)(8 * kb + e) * N + n;
+    if constexpr (DEQUANT)
+      static_cast<float*>(out)[o] = val * sc;
+    else
+      static_cast<int8_t*>(out)[o] = (int8_t)(int)val;
+  }
+}
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t n16,
+                                                          uint32_t* sink) {
+  uint32_t x = 0;
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a0 = __builtin_nontemporal_load(&buf[i]);
+    const u32x4 a1 = __builtin_nontemporal_load(&buf[i + stride]);
+    const u32x4 a2 = __builtin_nontemporal_load(&buf[i + 2 * stride]);
+    const u32x4 a3 = __builtin_nontemporal_load(&buf[i + 3 * stride]);
+    x ^= a0[0] ^ a0[1] ^ a0[2] ^ a0[3] ^ a1[0] ^ a1[1] ^ a1[2] ^ a1[3];
+    x ^= a2[0] ^ a2[1] ^ a2[2] ^ a2[3] ^ a3[0] ^ a3[1] ^ a3[2] ^ a3[3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a0 = buf[i];
+    x ^= a0[0] ^ a0[1] ^ a0[2] ^ a0[3];
+  }
+  // one word per workgroup: xor-reduce through LDS
+  __shared__ uint32_t part[256];
+  part[threadIdx.x] = x;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) part[threadIdx.x] ^= part[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0];
+}
+
+}  // namespace dev
+
+// ---- host side: configuration and launch ------------------------------------
+
+namespace {
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static int cache[64] = {0};
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev >= 0 && dev < 64) cache[dev] = cus;
+  return cus;
+}
+
+// Columns per lane V: the tile count should fill the CUs in whole rounds
+// (one 8-wave workgroup per CU at a time).  Efficiency = tiles / (rounds * CUs);
+// on a tie prefer the larger V when the rounds are full (fewer, longer tiles
+// read X fewer times), else the smaller V (more CUs busy in the last round).
+int choose_v(int N, int cus, int vmax) {
+  int best_v = 1;
+  double best_eff = -1.0;
+  for (int v = vmax; v >= 1; --v) {
+    const long tiles = (N + 16L * v - 1) / (16L * v);
+    const long rounds = (tiles + cus - 1) / cus;
+    const double eff = (double)tiles / (double)(rounds * cus);
+    const bool full = eff > 0.999;
+    if (eff > best_eff + 1e-9 || (!full && eff > best_eff - 1e-9)) {
+      best_eff = eff;
+      best_v = v;
+    }
+  }
+  return best_v;
+}
+
+template <int BITS, bool SBF16, int NSETS>
+hipError_t launch_v(int v, const dev::GemmArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.ntiles), block(dev::kThreads);
+  if constexpr (NSETS == 1) {
+    switch (v) {
+      case 1: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 1, 1>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 2, 1>), grid, block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 3, 1>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 4, 1>), grid, block, 0, st, a); break;
+    }
+  } else {
+    switch (v) {
+      case 1: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 1, 2>), grid, block, 0, st, a); break;
+      default: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 2, 2>), grid, block, 0, st, a); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int NSETS>
+hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, hipStream_t st) {
+  if (f.bits == 4) return f.scale_bf16 ? launch_v<4, true, NSETS>(v, a, st) : launch_v<4, false, NSETS>(v, a, st);
+  if (f.bits == 5) return f.scale_bf16 ? launch_v<5, true, NSETS>(v, a, st) : launch_v<5, false, NSETS>(v, a, st);
+  return f.scale_bf16 ? launch_v<8, true, NSETS>(v, a, st) : launch_v<8, false, NSETS>(v, a, st);
+}
+
+// Shared validation and launch of ngq_gemm (nsets 1) and ngq_swiglu_gemm (2).
+int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void* x, const void* wq,
+             const void* scales, void* y, void* stream) {
+  Format f;
+  int rc = parse_format(bits, group, &f);
+  if (rc != NGQ_OK) return rc;
+  if (T < 0 || T > NGQ_MAX_T) return NGQ_ERR_SHAPE;
+  if ((rc = check_kn(K, Nout)) != NGQ_OK) return rc;
+  const long ncols_l = (long)Nout * nsets;
+  if (ncols_l > (1L << 30)) return NGQ_ERR_SHAPE;
+  const int Ncols = (int)ncols_l;
+  if (T == 0 || Nout == 0) return NGQ_OK;
+  const size_t xb = (size_t)T * K * 2, yb = (size_t)T * Nout * 2;
+  const size_t wb0 = p0_bytes(K, Ncols, f.bits), wb1 = p1_bytes(K, Ncols, f.bits);
+  const size_t sb = (size_t)(K / kGroup) * Ncols * 2;
+  if ((rc = check_ptr(y)) != NGQ_OK) return rc;
+  if (K > 0) {
+    if ((rc = check_ptr(x)) != NGQ_OK) return rc;
+    if ((rc = check_ptr(wq)) != NGQ_OK) return rc;
+    if ((rc = check_ptr(scales)) != NGQ_OK) return rc;
+  }
+  if (xb >= kMaxBuffer || yb >= kMaxBuffer || wb0 + wb1 >= kMaxBuffer || sb >= kMaxBuffer)
+    return NGQ_ERR_UNSUPPORTED;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, wq, wb0 + wb1) || overlaps(y, yb, scales, sb)) return NGQ_ERR_ARG;
+
+  const int vmax = nsets == 1 ? 4 : 2;
+  const int v = choose_v(Nout, cu_count(), vmax);
+  dev::GemmArgs a;
+  a.x = x; a.wq = wq; a.scales = scales; a.y = y;
+  a.T = T; a.K = K; a.Nout = Nout; a.Ncols = Ncols; a.up_off = nsets == 2 ? Nout : 0;
+  a.G = K / kGroup;
+  a.pairs = (a.G + 1) / 2;
+  a.ppw = (a.pairs + dev::kWaves - 1) / dev::kWaves;
+  a.ntiles = (Nout + 16 * v - 1) / (16 * v);
+  a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
+  hipError_t e = nsets == 1 ? launch_fmt<1>(f, v, a, (hipStream_t)stream) : launch_fmt<2>(f, v, a, (hipStream_t)stream);
+  return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
+template <bool DEQUANT>
+int run_unpack(int K, int N, int bits, int group, const void* wq, const void* scales, void* out, void* stream) {
+  Format f;
+  int rc = parse_format(bits, group, &f);
+  if (rc != NGQ_OK) return rc;
+  if ((rc = check_kn(K, N)) != NGQ_OK) return rc;
+  if (K == 0 || N == 0) return NGQ_OK;
+  if ((rc = check_ptr(wq)) != NGQ_OK) return rc;
+  if ((rc = check_ptr(out)) != NGQ_OK) return rc;
+  if (DEQUANT && (rc = check_ptr(scales)) != NGQ_OK) return rc;
+  const size_t wb = p0_bytes(K, N, f.bits) + p1_bytes(K, N, f.bits);
+  const size_t ob = (size_t)K * N * (DEQUANT ? 4 : 1);
+  if (wb >= kMaxBuffer) return NGQ_ERR_UNSUPPORTED;
+  if (overlaps(out, ob, wq, wb)) return NGQ_ERR_ARG;
+  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / 8)), block(256);
+  const uint32_t p0b = (uint32_t)p0_bytes(K, N, f.bits);
+  hipStream_t st = (hipStream_t)stream;
+#define NGQ_UNPACK(B, S) hipLaunchKernelGGL((dev::unpack_kernel<B, S, DEQUANT>), grid, block, 0, st, wq, p0b, scales, K, N, out)
+  if (f.bits == 4) { if (f.scale_bf16) NGQ_UNPACK(4, true); else NGQ_UNPACK(4, false); }
+  else if (f.bits == 5) { if (f.scale_bf16) NGQ_UNPACK(5, true); else NGQ_UNPACK(5, false); }
+  else { if (f.scale_bf16) NGQ_UNPACK(8, true); else NGQ_UNPACK(8, false); }
+#undef NGQ_UNPACK
+  return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace ngq
+
+using namespace ngq;
+
+extern "C" int ngq_gemm(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                        const void* scales, void* y, void* stream) {
+  return run_gemm(1, T, K, N, bits, group, x, wq, scales, y, stream);
+}
+
+extern "C" int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
+                               const void* wq_gate_up, const void* scales_gate_up, void* h, void* stream) {
+  return run_gemm(2, T, K, N_ff, bits, group, x, wq_gate_up, scales_gate_up, h, stream);
+}
+
+extern "C" int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream) {
+  return run_unpack<false>(K, N, bits, group, wq, nullptr, codes, stream);
+}
+
+extern "C" int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const void* scales, float* w,
+                               void* stream) {
+  return run_unpack<true>(K, N, bits, group, wq, scales, w, stream);
+}
+
+extern "C" int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (bytes % 16) return NGQ_ERR_SHAPE;
+  if (bytes == 0) return NGQ_OK;
+  int rc;
+  if ((rc = check_ptr(buf)) != NGQ_OK) return rc;
+  if ((rc = check_ptr(sink)) != NGQ_OK) return rc;
+  const size_t n16 = bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  blocks = std::min<size_t>(blocks, 4096);
+  hipLaunchKernelGGL(dev::stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const dev::u32x4*>(buf), n16, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}

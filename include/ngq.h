@@ -1,0 +1,137 @@
+/*
+ * ngq.h -- C ABI of libngq: small-T groupwise-int projections on MI355X (gfx950).
+ *
+ * The operation.  A decode or speculative-verify step of a groupwise-int
+ * quantised model multiplies T <= 8 token activations by each quantised
+ * projection matrix:
+ *
+ *     Y[T x N] = X[T x K] . dequant(Wq[K x N]),   dequant: w[k][n] = c[k][n] * s[k/64][n]
+ *
+ * The NInfer-4090 V3 topic (lcz.me/topic/2047), section "What V3 did", tunes
+ * the T=8 routing of small-batch Q4/Q5 projections for the GDN projection, the
+ * attention Q5 projection and the SwiGLU path, and its "Measured data"
+ * section times the T=8 attention Q5 gate/value and GDN QK Q4 projections as
+ * single operators.  The ninfer-ext README, "Comparison with upstream NInfer",
+ * credits a Q5 K-split path aimed at the verify rounds of speculative decoding
+ * (T = drafts + 1).  The pages fix neither the layout nor the arithmetic;
+ * this library takes symmetric codes with one scale per 64 consecutive k and
+ * column, fp32 accumulation and bf16 output.
+ *
+ * Conventions (all entry points):
+ *  - Every buffer is allocated by the caller.  Device pointers are HIP device
+ *    memory on the current device; host pointers are ordinary host memory.
+ *    The library keeps no pointer after a call returns and allocates nothing.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  GPU
+ *    entry points enqueue work and return without synchronising; a device
+ *    fault surfaces at the caller's next synchronisation.
+ *  - Arguments are validated before any HIP call; on error nothing is
+ *    enqueued and a negative NGQ_ERR_* status is returned.  No C++ exception
+ *    crosses this boundary.  Entry points are reentrant and thread-safe.
+ *  - Results are deterministic: the same inputs on the same device give
+ *    bit-identical outputs (no atomics, fixed reduction order).
+ *  - Every buffer must be 16-byte aligned and smaller than 2 GiB.
+ *
+ * Packed weight layout (little-endian 32-bit words, row-major, column fastest;
+ * u is the offset-binary field, c the signed code):
+ *   int4 (bits 4): P0 = u32[K/8][N]; bits 4i..4i+3 of word (kb, n) hold
+ *                  u = c + 8 for k = 8 kb + i.  c in [-8, 7].
+ *   int5 (bits 5): P0 as int4 holding u & 15 with u = c + 16, then directly
+ *                  after it P1 = u32[K/32][N]; bit i of word (kb, n) holds
+ *                  u >> 4 for k = 32 kb + i.  c in [-16, 15].
+ *   int8 (bits 8): P0 = u32[K/4][N]; byte i of word (kb, n) holds u = c + 128
+ *                  for k = 4 kb + i.  c in [-128, 127].
+ *   scales:        [K/64][N] fp16 (default) or bf16 (bits | NGQ_SCALE_BF16).
+ *   x:             [T][K] bf16, row-major.   y: [T][N] bf16, row-major.
+ */
+#ifndef NGQ_H
+#define NGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NGQ_OK 0
+#define NGQ_ERR_ARG (-1)         /* null pointer, aliasing output, code out of range */
+#define NGQ_ERR_SHAPE (-2)       /* T, K or N outside the supported shapes */
+#define NGQ_ERR_UNSUPPORTED (-3) /* bit width, scale flag, group size or buffer size */
+#define NGQ_ERR_ALIGN (-4)       /* a buffer is not 16-byte aligned */
+#define NGQ_ERR_HIP (-5)         /* the HIP runtime reported an error */
+
+/* Bit widths, and the flag selecting bf16 scales (OR it into `bits`). */
+#define NGQ_INT4 4
+#define NGQ_INT5 5
+#define NGQ_INT8 8
+#define NGQ_SCALE_BF16 0x100
+#define NGQ_GROUP 64 /* the only supported group size */
+#define NGQ_MAX_T 8  /* tokens per call: plain decode (1) up to 7 drafts + 1 */
+
+/* Bytes of the packed weight buffer (P0, plus P1 for int5) for a K x N
+ * matrix; 0 when the arguments are invalid.  Host only, no HIP call. */
+size_t ngq_packed_bytes(int K, int N, int bits, int group);
+
+/* Bytes of the scale buffer, (K/64) * N * 2; 0 when invalid.  Host only. */
+size_t ngq_scale_bytes(int K, int N, int bits, int group);
+
+/* Pack signed codes into the layout above.  Host only, no HIP call.
+ *   codes  : host int8 [K][N], row-major, each within the range of `bits`
+ *   wq_out : host buffer of ngq_packed_bytes(K, N, bits, group) bytes
+ * K % 64 == 0, N % 4 == 0.  Returns NGQ_ERR_ARG for a code out of range (the
+ * output is then unspecified), NGQ_ERR_SHAPE / NGQ_ERR_UNSUPPORTED as above.
+ * The NGQ_SCALE_BF16 flag is ignored here. */
+int ngq_pack(int K, int N, int bits, int group, const int8_t* codes, void* wq_out);
+
+/* Y = X . dequant(Wq) for 0 <= T <= 8 tokens (the projection of the "What V3
+ * did" T-routing, NInfer-4090 V3 topic).
+ *   x      : device bf16 [T][K]
+ *   wq     : device, ngq_pack layout for K x N
+ *   scales : device fp16|bf16 [K/64][N]
+ *   y      : device bf16 [T][N], overwritten; must not overlap the inputs
+ * K % 64 == 0 (K = 0 writes zeros), N % 4 == 0; T == 0 or N == 0 is a no-op.
+ * Accumulates in fp32 and rounds to bf16 to nearest even. */
+int ngq_gemm(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+             const void* scales, void* y, void* stream);
+
+/* Fused gate/up projection with the SiLU-times-up epilogue of a SwiGLU MLP
+ * (the "SwiGLU path" of the NInfer-4090 V3 topic, section "What V3 did"):
+ *   h[t][j] = bf16( SiLU(g) * u ),  g = (X . W)[t][j],  u = (X . W)[t][N_ff + j]
+ * with SiLU(g) = g / (1 + e^-g), g and u kept in fp32.
+ *   x              : device bf16 [T][K]
+ *   wq_gate_up     : device, ngq_pack layout of the K x (2 N_ff) matrix whose
+ *                    columns [0, N_ff) are the gate and [N_ff, 2 N_ff) the up
+ *                    projection
+ *   scales_gate_up : device fp16|bf16 [K/64][2 N_ff]
+ *   h              : device bf16 [T][N_ff], overwritten; must not overlap inputs
+ * The down projection is a plain ngq_gemm with K = N_ff and x = h. */
+int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
+                    const void* wq_gate_up, const void* scales_gate_up, void* h, void* stream);
+
+/* Debug export: the signed codes as the GEMM kernels unpack them.
+ *   wq : device, ngq_pack layout;  codes : device int8 [K][N], overwritten. */
+int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream);
+
+/* Debug export: w[k][n] = c[k][n] * s[k/64][n] in fp32 (exact), with the
+ * GEMM kernels' unpack and scale decoding.  w : device float [K][N]. */
+int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const void* scales, float* w,
+                    void* stream);
+
+/* Bandwidth calibration: stream `bytes` (a multiple of 16) from device memory
+ * `buf` with 128-bit loads and write one word per workgroup to `sink`
+ * (device, at least 16384 bytes) so the reads cannot be elided.  Used by the
+ * bench to measure the attainable HBM read rate of the device. */
+int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
+
+/* Static description of a status code. */
+const char* ngq_strerror(int status);
+
+/* Layout/ABI version of this library (increments when either changes). */
+int ngq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NGQ_H */

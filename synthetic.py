@@ -100,3 +100,19 @@ def random_words(nbytes: int, g: np.random.Generator) -> np.ndarray:
     """Uniformly random packed bytes.  Every field of every packed layout is
     then uniform over its range, i.e. codes uniform over the full signed range."""
     return g.integers(0, 256, size=nbytes, dtype=np.uint8)
+
+
+def device_replicas(w: Workload, T: int, replicas: int, packed_bytes: int, seed: int = 0, device: str = "cuda"):
+    """`replicas` distinct copies of a packed weight matrix and its scales, drawn
+    on the device (uniform random bytes = uniform codes over the full range),
+    plus one bf16 activation block [T][K].  Used to rotate through more memory
+    than the caches hold when timing."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + w.config_id)
+    wq = torch.randint(0, 256, (replicas, packed_bytes), dtype=torch.uint8, device=device, generator=g)
+    s = torch.rand((replicas, w.K // GROUP, w.N), device=device, generator=g) * (w.scale_hi - w.scale_lo) + w.scale_lo
+    s = s.to(torch.bfloat16 if w.scale_bf16 else torch.float16)
+    x = torch.randn((T, w.K), device=device, generator=g).to(torch.bfloat16)
+    return wq, s, x

@@ -1,0 +1,168 @@
+"""Host-side checks of libngq that need no GPU: the library loads, exports
+every symbol the header declares, packs byte-identically to the oracle, and
+rejects bad arguments with the documented status before any HIP call."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ngq.h")
+
+
+@pytest.fixture(scope="module")
+def ngq():
+    import groupwise_int_weight_amd as g
+
+    if not os.path.exists(g.LIB_PATH):
+        from groupwise_int_weight_amd import build
+
+        build.build()
+    g.lib()
+    return g
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ngq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_packed_bytes", "ngq_scale_bytes",
+                     "ngq_unpack_codes", "ngq_dequant_f32", "ngq_strerror"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(ngq):
+    names = header_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", ngq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(ngq_\w+)$", out, flags=re.M))
+    assert set(names) <= exported, set(names) - exported
+    # the binding knows the signature of every declared function, and nothing more
+    assert set(ngq.SIGNATURES) == set(names)
+    for n in names:
+        assert getattr(ngq.lib(), n) is not None
+
+
+def test_version_and_strerror(ngq):
+    assert ngq.ngq_version() >= 1
+    msgs = {s: ngq.ngq_strerror(s) for s in [0, -1, -2, -3, -4, -5]}
+    assert len(set(msgs.values())) == 6
+    assert ngq.ngq_strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("bits", [4, 5, 8])
+@pytest.mark.parametrize("K,N", [(64, 4), (192, 12), (320, 100), (1024, 36)])
+def test_pack_matches_oracle_bytes(ngq, oracle_lib, bits, K, N):
+    g = np.random.default_rng(K * 7 + N + bits)
+    codes = synthetic.draw_codes(K, N, bits, g)
+    mine = ngq.ngq_pack(codes, bits)
+    ref = oracle_lib.pack(codes, bits)
+    assert mine.size == ref.size == ngq.ngq_packed_bytes(K, N, bits)
+    assert np.array_equal(mine, ref)
+
+
+def test_pack_extreme_codes_match_oracle(ngq, oracle_lib):
+    for bits in (4, 5, 8):
+        lo, hi = synthetic.code_range(bits)
+        codes = np.tile(np.array([lo, hi, 0, -1], np.int8), (128, 2))
+        assert np.array_equal(ngq.ngq_pack(codes, bits), oracle_lib.pack(codes, bits))
+
+
+def test_sizes(ngq):
+    assert ngq.ngq_packed_bytes(5120, 8192, 4) == 5120 * 8192 // 2
+    assert ngq.ngq_packed_bytes(5120, 12288, 5) == 5120 * 12288 // 2 + 5120 * 12288 // 8
+    assert ngq.ngq_packed_bytes(5120, 8192, 8) == 5120 * 8192
+    assert ngq.ngq_packed_bytes(5120, 12288, 5 | ngq.NGQ_SCALE_BF16) == ngq.ngq_packed_bytes(5120, 12288, 5)
+    assert ngq.ngq_scale_bytes(5120, 8192, 4) == 80 * 8192 * 2
+    assert ngq.ngq_packed_bytes(100, 8, 4) == 0     # K % 64
+    assert ngq.ngq_packed_bytes(64, 6, 4) == 0      # N % 4
+    assert ngq.ngq_packed_bytes(64, 8, 6) == 0      # bits
+    assert ngq.ngq_packed_bytes(64, 8, 4, 32) == 0  # group
+    assert ngq.ngq_packed_bytes(0, 8, 4) == 0
+
+
+def test_pack_errors(ngq):
+    L = ngq.lib()
+    codes = np.zeros((64, 4), np.int8)
+    out = np.zeros(1024, np.uint8)
+    assert L.ngq_pack(64, 4, 6, 64, codes.ctypes.data, out.ctypes.data) == ngq.NGQ_ERR_UNSUPPORTED
+    assert L.ngq_pack(64, 4, 4, 128, codes.ctypes.data, out.ctypes.data) == ngq.NGQ_ERR_UNSUPPORTED
+    assert L.ngq_pack(32, 4, 4, 64, codes.ctypes.data, out.ctypes.data) == ngq.NGQ_ERR_SHAPE
+    assert L.ngq_pack(64, 4, 4, 64, None, out.ctypes.data) == ngq.NGQ_ERR_ARG
+    bad = codes.copy()
+    bad[3, 2] = 8
+    assert L.ngq_pack(64, 4, 4, 64, bad.ctypes.data, out.ctypes.data) == ngq.NGQ_ERR_ARG
+    bad[3, 2] = -17
+    assert L.ngq_pack(64, 4, 5, 64, bad.ctypes.data, out.ctypes.data) == ngq.NGQ_ERR_ARG
+
+
+# Fake, never-dereferenced device addresses: every call below fails validation,
+# which happens before any HIP call, so no GPU is needed.
+X, W, S, Y = 0x100000, 0x200000, 0x300000, 0x400000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((9, 64, 4, 4, 64, X, W, S, Y), -2),        # T > 8
+    ((-1, 64, 4, 4, 64, X, W, S, Y), -2),       # T < 0
+    ((1, 100, 4, 4, 64, X, W, S, Y), -2),       # K % 64
+    ((1, 64, 6, 4, 64, X, W, S, Y), -2),        # N % 4
+    ((1, 64, 4, 7, 64, X, W, S, Y), -3),        # bits
+    ((1, 64, 4, 4 | 0x200, 64, X, W, S, Y), -3),  # unknown flag
+    ((1, 64, 4, 4, 128, X, W, S, Y), -3),       # group
+    ((1, 64, 4, 4, 64, X, W, S, None), -1),     # null y
+    ((1, 64, 4, 4, 64, None, W, S, Y), -1),     # null x
+    ((1, 64, 4, 4, 64, X, None, S, Y), -1),     # null wq
+    ((1, 64, 4, 4, 64, X, W, None, Y), -1),     # null scales
+    ((1, 64, 4, 4, 64, X + 8, W, S, Y), -4),    # misaligned x
+    ((1, 64, 4, 5, 64, X, W + 4, S, Y), -4),    # misaligned wq
+    ((1, 64, 4, 4, 64, X, W, S, Y + 2), -4),    # misaligned y
+    ((1, 64, 4, 4, 64, X, W, S, X), -1),        # y overlaps x
+    ((2, 64, 64, 4, 64, X, W, S, W + 16), -1),  # y overlaps wq
+    ((1, 1 << 24, 512, 4, 64, X, W, S, Y), -3),  # packed weights >= 2 GiB
+])
+def test_gemm_rejects_bad_arguments(ngq, args, status):
+    assert ngq.lib().ngq_gemm(*args, None) == status
+
+
+def test_swiglu_rejects_bad_arguments(ngq):
+    L = ngq.lib()
+    assert L.ngq_swiglu_gemm(9, 64, 4, 4, 64, X, W, S, Y, None) == -2
+    assert L.ngq_swiglu_gemm(1, 64, 6, 4, 64, X, W, S, Y, None) == -2
+    assert L.ngq_swiglu_gemm(1, 64, 4, 4, 64, X, W, S, None, None) == -1
+    # the up half makes wq 2 N_ff columns wide: h must not overlap it either
+    assert L.ngq_swiglu_gemm(1, 64, 8, 4, 64, X, W, S, W + 400, None) == -1
+
+
+def test_empty_calls_are_no_ops(ngq):
+    """T == 0 or N == 0 returns OK without touching any pointer or the GPU."""
+    L = ngq.lib()
+    assert L.ngq_gemm(0, 64, 4, 4, 64, None, None, None, None, None) == 0
+    assert L.ngq_gemm(3, 64, 0, 4, 64, None, None, None, None, None) == 0
+    assert L.ngq_swiglu_gemm(0, 64, 4, 4, 64, None, None, None, None, None) == 0
+    assert L.ngq_unpack_codes(0, 4, 4, 64, None, None, None) == 0
+    assert L.ngq_dequant_f32(64, 0, 4, 64, None, None, None, None) == 0
+    assert L.ngq_stream_read(None, 0, None, None) == 0
+
+
+def test_debug_exports_reject_bad_arguments(ngq):
+    L = ngq.lib()
+    assert L.ngq_unpack_codes(100, 4, 4, 64, W, Y, None) == -2
+    assert L.ngq_unpack_codes(64, 4, 4, 64, W, None, None) == -1
+    assert L.ngq_unpack_codes(64, 4, 4, 64, W + 4, Y, None) == -4
+    assert L.ngq_dequant_f32(64, 4, 4, 64, W, None, Y, None) == -1
+    assert L.ngq_stream_read(X, 24, Y, None) == -2
+
+
+def test_binding_refuses_host_tensors(ngq):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        ngq.ngq_gemm(x, torch.zeros(32, dtype=torch.uint8), torch.zeros((1, 4), dtype=torch.float16), 4, 4)
