@@ -73,20 +73,32 @@ class Rotation:
 
 
 def time_steps(launch, replicas, steps, warmup):
+    """Average GPU time of one launch: `warmup` eager launches, then exactly
+    `steps` launches (rotating through the replicas) captured in one HIP graph
+    and replayed once between two events on the capturing stream.  The graph
+    removes the host's per-launch cost (~10 us through Python), so the events
+    bracket back-to-back kernels, as a serving loop would replay them."""
     import torch
 
     for i in range(warmup):
         launch(i % replicas)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            launch(i % replicas)
+    g.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        launch(i % replicas)
+    g.replay()
     end.record()
     end.synchronize()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps  # ms per step
+    ms = start.elapsed_time(end) / steps
+    del g
+    return ms
 
 
 def calibrate(ngq):
@@ -117,9 +129,16 @@ def run_projection(ngq, w, T, steps, warmup):
 
     rot = Rotation(ngq, w, T)
     y = torch.empty((T, w.N), dtype=torch.bfloat16, device="cuda")
+    lib = ngq.lib()
+    wp = [rot.wq[i].data_ptr() for i in range(rot.replicas)]
+    sp = [rot.s[i].data_ptr() for i in range(rot.replicas)]
+    xp, yp = rot.x.data_ptr(), y.data_ptr()
+    bits = w.bits | (ngq.NGQ_SCALE_BF16 if w.scale_bf16 else 0)
 
     def launch(i):
-        ngq.ngq_gemm(rot.x, rot.wq[i], rot.s[i], w.bits, w.N, y=y)
+        st = lib.ngq_gemm(T, w.K, w.N, bits, 64, xp, wp[i], sp[i], yp, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise ngq.NgqError(st, "ngq_gemm")
 
     ms = time_steps(launch, rot.replicas, steps, warmup)
     return ms, rot, y
@@ -242,7 +261,14 @@ def main():
     ms, rot, y = run_projection(ngq, w, T, args.steps, args.warmup)
     nbytes = algorithmic_bytes(ngq, w, T)
     gbps = nbytes / ms / 1e6
+    # the graph's last launch must equal an eager launch on the same replica
+    last = (args.steps - 1) % rot.replicas
+    y_graph = y.clone()
+    ngq.ngq_gemm(rot.x, rot.wq[last], rot.s[last], w.bits, w.N, y=y)
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(y_graph, y))
     parity, host_inputs = parity_check(ngq, rot, y)
+    parity["graph_replay_matches_eager"] = graph_ok
     cold = rot.cold_bytes
     replicas = rot.replicas
     del rot

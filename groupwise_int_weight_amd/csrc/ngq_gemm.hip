@@ -173,7 +173,7 @@ struct PairBuf {
   static constexpr int WPK = BITS == 8 ? 2 : 1;  // P0 words per 8-k block and column
   uint32_t a[NSETS][4][V * WPK];                 // [set][step][word]; int8: V words of row 2kb, then 2kb+1
   uint32_t p1[NSETS][2][BITS == 5 ? V : 1];      // int5 high-bit words, one per half pair
-  uint32_t b[4][4];                              // X fragment per step
+  uint32_t x[2][4];                              // X rows of the pair: 2 loads x 16 B per lane
   uint32_t sc[NSETS][2 * V];                     // 4V scales (16-bit) per set
 };
 
@@ -181,8 +181,8 @@ struct PairBuf {
 template <int BITS, int V, int NSETS>
 constexpr int pipeline_depth() {
   constexpr int wpk = BITS == 8 ? 2 : 1;
-  constexpr int regs = NSETS * (4 * V * wpk + (BITS == 5 ? 2 * V : 0) + 2 * V) + 16;
-  constexpr int d = 168 / regs;
+  constexpr int regs = NSETS * (4 * V * wpk + (BITS == 5 ? 2 * V : 0) + 2 * V) + 8;
+  constexpr int d = 140 / regs;  // leaves ~110 registers for the compute
   return d < 2 ? 2 : (d > 6 ? 6 : d);
 }
 
@@ -192,6 +192,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   constexpr int WPK = BITS == 8 ? 2 : 1;
   constexpr int TILE = 16 * V;
   __shared__ float red[kWaves * NSETS * TILE * 8];
+  // Per-wave staging of the X block of one pair: 8 token rows of 128 k (bf16),
+  // rows padded to 272 B against bank conflicts, then a 16-byte zero block.
+  constexpr uint32_t XROW = 272, XSLOT = 8 * XROW + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kWaves * XSLOT];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -219,6 +223,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   // B slot j = m carries token t = m & 7 for group half h = m >> 3; only the
   // k-slots of that half are non-zero.
   const int t = m & 7, h = m >> 3;
+  uint8_t* const xslot = xs + wave * XSLOT;
 #pragma unroll
   for (int s = 0; s < NSETS; ++s) {
     const uint32_t col = (uint32_t)(c0 + s * a.up_off + V * m);
@@ -227,8 +232,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     // result rows 4q..4q+3 of every MFMA -> columns c0 + 4Vq + [0, 4V)
     offS[s] = (uint32_t)h * (uint32_t)a.Ncols * 2u + (uint32_t)(c0 + s * a.up_off + 4 * V * q) * 2u;
   }
-  const bool b_active = ((q >> 1) == h) && (t < a.T);
-  const uint32_t offB = (uint32_t)t * (uint32_t)a.K * 2u + lane_kb * 16u;
+  // X block of a pair, read coalesced: load L, lane l -> token 4L + (l >> 4),
+  // 8 k at k-block (l & 15) of the pair.  Rows t >= T load nothing (zeros).
+  const int xrow = lane >> 4, xkb = lane & 15;
+  const uint32_t offX = (uint32_t)xrow * (uint32_t)a.K * 2u + (uint32_t)xkb * 16u;
+  const uint32_t rowX4 = 4u * (uint32_t)a.K * 2u;
+  const bool x0_on = xrow < a.T, x1_on = xrow + 4 < a.T;
+  // B fragment source in the staging slot (the zero block for the other half)
+  const bool b_on = (q >> 1) == h;
+  const uint32_t bsrc = b_on ? (uint32_t)t * XROW + lane_kb * 16u : 8u * XROW;
+  if (lane == 0) *reinterpret_cast<u32x4*>(xslot + 8 * XROW) = u32x4{0u, 0u, 0u, 0u};
 
   const int pbase = wave * a.ppw;
 
@@ -240,8 +253,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
     const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb : kOOB;
     const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb : kOOB;
-    const bool bload = valid & b_active & !(half & ((q >> 1) != 0));
-    const uint32_t pb = bload ? (uint32_t)p * 256u + offB : kOOB;
+    const bool xin = valid & !(half & (xkb >= 8));
+    const uint32_t px0 = (xin & x0_on) ? (uint32_t)p * 256u + offX : kOOB;
+    const uint32_t px1 = (xin & x1_on) ? (uint32_t)p * 256u + offX + rowX4 : kOOB;
     const uint32_t ps = valid ? (uint32_t)p * rowb : kOOB;  // two scale rows of 2-byte entries
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -251,8 +265,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         load_words<V>(&buf.a[s][st][0], rW, o);
         if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
       }
-      load_words<4>(&buf.b[st][0], rX, pb + (uint32_t)st * 32u);
     }
+    load_words<4>(&buf.x[0][0], rX, px0);
+    load_words<4>(&buf.x[1][0], rX, px1);
     if constexpr (BITS == 5) {
 #pragma unroll
       for (int s = 0; s < NSETS; ++s) {
@@ -274,11 +289,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
                         Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
 
   auto compute = [&](const PairBuf<BITS, V, NSETS>& buf) {
+    // stage the pair's X rows, then read the four B fragments back (LDS is in
+    // order within a wave, so no barrier is needed)
+    *reinterpret_cast<u32x4*>(xslot + (uint32_t)xrow * XROW + (uint32_t)xkb * 16u) =
+        u32x4{buf.x[0][0], buf.x[0][1], buf.x[0][2], buf.x[0][3]};
+    *reinterpret_cast<u32x4*>(xslot + (uint32_t)(xrow + 4) * XROW + (uint32_t)xkb * 16u) =
+        u32x4{buf.x[1][0], buf.x[1][1], buf.x[1][2], buf.x[1][3]};
     bf16x8 bfrag[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      u32x4 bv = {buf.b[st][0], buf.b[st][1], buf.b[st][2], buf.b[st][3]};
-      bfrag[st] = __builtin_bit_cast(bf16x8, bv);
+      const uint32_t o = b_on ? bsrc + (uint32_t)st * 32u : bsrc;
+      bfrag[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xslot + o));
     }
     // -(128 + bias) * sum_k x over each group half: seeds every partial sum
     f32x4 dx = {0.f, 0.f, 0.f, 0.f};
@@ -324,26 +345,31 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         }
   };
 
-  // NB pairs in flight per wave.  Loads are issued unconditionally (pairs past
-  // the wave's range get out-of-range offsets: no memory traffic, zeros) so
-  // that no branch separates a load from its use; only the compute is skipped.
-  // The scheduling barriers keep the pairs' loads in issue order, so the
-  // counter wait before each compute covers exactly that pair's loads.
+  // NB pairs in flight per wave.  Inside the main loop loads are issued without
+  // a branch (a pair past the wave's range gets out-of-range offsets: no
+  // memory traffic, zeros), so no branch separates a load from its use and the
+  // counter wait before each compute covers exactly that pair's loads; the
+  // scheduling barriers keep the pairs' loads in issue order.
   PairBuf<BITS, V, NSETS> buf[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     issue(buf[u], u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int it = 0; it < a.ppw; it += NB) {
+  int it = 0;
+  for (; it + NB < a.ppw; it += NB) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      if (it + u < a.ppw) compute(buf[u]);
+      compute(buf[u]);
       __builtin_amdgcn_sched_barrier(0);
       issue(buf[u], it + u + NB);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the last (up to NB) pairs are already in flight: no more loads
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    if (it + u < a.ppw) compute(buf[u]);
 
   // Slots j and j + 8 hold the two group halves of token j: add them.
 #pragma unroll

@@ -3,7 +3,10 @@ the smoke check and the bench).
 
 Gates, for bf16 outputs y_gpu against the oracle's exact fp64 result y64 and
 its correctly rounded bf16 value y16:
-  E1  ||y_gpu - y64||_2 / ||y64||_2 <= 2e-3
+  E1  ||y_gpu - y64||_2 / ||y64||_2 <= max(2e-3, 1.05 * floor), where floor
+      is the same ratio for the correctly rounded y16: on a small sample the
+      bf16 output rounding alone can exceed 2e-3, and no bf16 answer can beat
+      the correctly rounded one
   E2  max_i |y_gpu,i - y16,i| <= 1e-2 * rms(y64), except elements where
       y_gpu,i is the other bf16 neighbour of y64,i and y64,i lies within eps_i
       of the midpoint of the two neighbours (an fp32 evaluation may round
@@ -32,6 +35,7 @@ def compare(y_gpu_bits: np.ndarray, y64: np.ndarray, abs_xw: np.ndarray, abs_xs:
     y16 = bf16_bits_to_f64(y16_bits)
     norm = float(np.linalg.norm(y64))
     rel_l2 = float(np.linalg.norm(yg - y64)) / norm if norm > 0 else float(np.linalg.norm(yg))
+    floor = float(np.linalg.norm(y16 - y64)) / norm if norm > 0 else 0.0
     rms = float(np.sqrt(np.mean(y64 ** 2))) if y64.size else 0.0
     tol = 1e-2 * rms
     err = np.abs(yg - y16)
@@ -43,6 +47,8 @@ def compare(y_gpu_bits: np.ndarray, y64: np.ndarray, abs_xw: np.ndarray, abs_xs:
     over = err > tol
     return {
         "rel_l2": rel_l2,
+        "rel_l2_rne_floor": floor,
+        "rel_l2_gate": max(2e-3, 1.05 * floor),
         "max_err_over_rms": float(err.max() / rms) if err.size and rms > 0 else 0.0,
         "max_err_vs_y64_over_rms": float(np.abs(yg - y64).max() / rms) if err.size and rms > 0 else 0.0,
         "n": int(y64.size),
@@ -56,5 +62,18 @@ def compare(y_gpu_bits: np.ndarray, y64: np.ndarray, abs_xw: np.ndarray, abs_xs:
 
 def assert_parity(rep: dict, what: str = ""):
     assert rep["nonfinite"] == 0, (what, rep)
-    assert rep["rel_l2"] <= 2e-3, (what, rep)
+    assert rep["rel_l2"] <= rep["rel_l2_gate"], (what, rep)
     assert rep["n_fail"] == 0, (what, rep)
+
+
+def rel_l2_gate(y_bits_or_f64, exact: np.ndarray) -> tuple:
+    """(relative L2 error, gate) of a bf16 result against exact values, with the
+    same floor rule as E1."""
+    import oracle
+
+    yg = y_bits_or_f64 if y_bits_or_f64.dtype == np.float64 else bf16_bits_to_f64(y_bits_or_f64)
+    y16 = bf16_bits_to_f64(oracle.round_bf16_array(exact))
+    norm = float(np.linalg.norm(exact))
+    rel = float(np.linalg.norm(yg - exact)) / norm
+    floor = float(np.linalg.norm(y16 - exact)) / norm
+    return rel, max(2e-3, 1.05 * floor)
