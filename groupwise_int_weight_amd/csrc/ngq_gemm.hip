@@ -193,8 +193,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   constexpr int TILE = 16 * V;
   __shared__ float red[kWaves * NSETS * TILE * 8];
   // Per-wave staging of the X block of one pair: 8 token rows of 128 k (bf16),
-  // rows padded to 272 B against bank conflicts, then a 16-byte zero block.
-  constexpr uint32_t XROW = 272, XSLOT = 8 * XROW + 16;
+  // rows padded to 272 B against bank conflicts, then a zero block that the
+  // lanes of the other group half read at the same step offsets (16 B each at
+  // 0, 32, 64, 96), so every lane reads one address without a select.
+  constexpr uint32_t XROW = 272, XZERO = 112, XSLOT = 8 * XROW + XZERO;
   __shared__ __attribute__((aligned(16))) uint8_t xs[kWaves * XSLOT];
 
   const int lane = threadIdx.x & 63;
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   // B fragment source in the staging slot (the zero block for the other half)
   const bool b_on = (q >> 1) == h;
   const uint32_t bsrc = b_on ? (uint32_t)t * XROW + lane_kb * 16u : 8u * XROW;
-  if (lane == 0) *reinterpret_cast<u32x4*>(xslot + 8 * XROW) = u32x4{0u, 0u, 0u, 0u};
+  if (lane < XZERO / 16) *reinterpret_cast<u32x4*>(xslot + 8 * XROW + 16u * (uint32_t)lane) = u32x4{0u, 0u, 0u, 0u};
 
   const int pbase = wave * a.ppw;
 
@@ -298,8 +300,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     bf16x8 bfrag[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const uint32_t o = b_on ? bsrc + (uint32_t)st * 32u : bsrc;
-      bfrag[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xslot + o));
+      bfrag[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xslot + bsrc + (uint32_t)st * 32u));
     }
     // -(128 + bias) * sum_k x over each group half: seeds every partial sum
     f32x4 dx = {0.f, 0.f, 0.f, 0.f};
