@@ -48,7 +48,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
+// 12 waves (3 per SIMD) with one pair each in flight: measured on MI355X, 12 to
+// 16 pairs in flight per CU stream fastest; deeper per-wave pipelines or fewer
+// waves congest the memory pipeline or leave it short.
+constexpr int kWaves = 12;
 constexpr int kThreads = kWaves * 64;
 // A buffer offset that is out of range for every buffer (all are < 2 GiB, and
 // adding an in-range offset cannot wrap 32 bits).  Out-of-range buffer loads
@@ -177,27 +180,44 @@ struct PairBuf {
   uint32_t sc[NSETS][2 * V];                     // 4V scales (16-bit) per set
 };
 
-// Registers per pair buffer -> how many pairs to keep in flight.
-template <int BITS, int V, int NSETS>
+// Pairs in flight per wave: one with dynamic assignment (the waves' own count
+// supplies the depth), two for the static fallback.
+template <bool DYN>
 constexpr int pipeline_depth() {
-  constexpr int wpk = BITS == 8 ? 2 : 1;
-  constexpr int regs = NSETS * (4 * V * wpk + (BITS == 5 ? 2 * V : 0) + 2 * V) + 8;
-  constexpr int d = 140 / regs;  // leaves ~110 registers for the compute
-  return d < 2 ? 2 : (d > 6 ? 6 : d);
+  return DYN ? 1 : 2;
 }
 
-template <int BITS, bool SBF16, int V, int NSETS>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
-  constexpr int NB = pipeline_depth<BITS, V, NSETS>();
-  constexpr int WPK = BITS == 8 ? 2 : 1;
-  constexpr int TILE = 16 * V;
-  __shared__ float red[kWaves * NSETS * TILE * 8];
+// Shared-memory layout of one workgroup: per-wave X staging slots, then (dynamic
+// assignment) one partial-sum block per pair and the pair counter, or (static
+// assignment) one partial-sum block per wave.
+struct Smem {
   // Per-wave staging of the X block of one pair: 8 token rows of 128 k (bf16),
   // rows padded to 272 B against bank conflicts, then a zero block that the
   // lanes of the other group half read at the same step offsets (16 B each at
   // 0, 32, 64, 96), so every lane reads one address without a select.
-  constexpr uint32_t XROW = 272, XZERO = 112, XSLOT = 8 * XROW + XZERO;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kWaves * XSLOT];
+  static constexpr uint32_t XROW = 272, XZERO = 112, XSLOT = 8 * XROW + XZERO;
+  static constexpr uint32_t XS = kWaves * XSLOT;
+  // a partial-sum block holds [set][token][column] fp32, token rows padded by
+  // 4 floats so the 8 token writes of one column hit distinct banks
+  static __host__ __device__ constexpr uint32_t block_floats(int nsets, int tile) {
+    return (uint32_t)nsets * 8u * (uint32_t)(tile + 4);
+  }
+  static __host__ __device__ constexpr uint32_t bytes(bool dyn, int pairs, int nsets, int tile) {
+    return XS + (dyn ? (uint32_t)pairs : (uint32_t)kWaves) * block_floats(nsets, tile) * 4u + 16u;
+  }
+};
+
+template <int BITS, bool SBF16, int V, int NSETS, bool DYN>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+  constexpr int NB = pipeline_depth<DYN>();
+  constexpr int WPK = BITS == 8 ? 2 : 1;
+  constexpr int TILE = 16 * V;
+  constexpr uint32_t XROW = Smem::XROW, XZERO = Smem::XZERO;
+  constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* const part = reinterpret_cast<float*>(smem + Smem::XS);
+  const int nblk = DYN ? a.pairs : kWaves;
+  uint32_t* const counter = reinterpret_cast<uint32_t*>(part + (uint32_t)nblk * BLK);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   // B slot j = m carries token t = m & 7 for group half h = m >> 3; only the
   // k-slots of that half are non-zero.
   const int t = m & 7, h = m >> 3;
-  uint8_t* const xslot = xs + wave * XSLOT;
+  uint8_t* const xslot = smem + wave * Smem::XSLOT;
 #pragma unroll
   for (int s = 0; s < NSETS; ++s) {
     const uint32_t col = (uint32_t)(c0 + s * a.up_off + V * m);
@@ -244,13 +264,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   const bool b_on = (q >> 1) == h;
   const uint32_t bsrc = b_on ? (uint32_t)t * XROW + lane_kb * 16u : 8u * XROW;
   if (lane < XZERO / 16) *reinterpret_cast<u32x4*>(xslot + 8 * XROW + 16u * (uint32_t)lane) = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (DYN) {
+    if (threadIdx.x == 0) *counter = (uint32_t)(kWaves * NB);
+    __syncthreads();
+  }
 
-  const int pbase = wave * a.ppw;
-
-  auto issue = [&](PairBuf<BITS, V, NSETS>& buf, int pi) {
-    const int p = pbase + pi;
-    // Wave-uniform flags (bitwise, so that no lane-divergent branch appears).
-    const bool valid = (pi < a.ppw) & (p < a.pairs);
+  // Loads of pair p (wave uniform; p >= pairs loads nothing).  Flags are
+  // combined bitwise so that no lane-divergent branch appears.
+  auto issue = [&](PairBuf<BITS, V, NSETS>& buf, int p) {
+    const bool valid = p < a.pairs;
     // last pair of an odd group count: its second group does not exist
     const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
     const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb : kOOB;
@@ -290,7 +312,36 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
                         Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
 
-  auto compute = [&](const PairBuf<BITS, V, NSETS>& buf) {
+  // Slots j and j + 8 hold the two group halves of token j: add them, then the
+  // lanes of the first half write the tile block [set][token][column].
+  auto store_block = [&](f32x4 (&v)[NSETS][V], float* blk) {
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int other = __builtin_amdgcn_mov_dpp(__float_as_int(v[s][i][r]), 0x128 /* row_ror:8 */, 0xF,
+                                                     0xF, false);
+          v[s][i][r] += __int_as_float(other);
+        }
+    if (h == 0) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int col = V * (4 * q + r) + i;
+            blk[((uint32_t)s * 8u + (uint32_t)t) * (uint32_t)(TILE + 4) + (uint32_t)col] = v[s][i][r];
+          }
+    }
+  };
+
+  // Multiply one pair.  Dynamic assignment: the pair's scaled partial goes to
+  // its own block (the final sum runs over pairs in order, whichever wave did
+  // them).  Static assignment: it accumulates into the wave's registers.
+  auto compute = [&](const PairBuf<BITS, V, NSETS>& buf, int p) {
     // stage the pair's X rows, then read the four B fragments back (LDS is in
     // order within a wave, so no barrier is needed)
     *reinterpret_cast<u32x4*>(xslot + (uint32_t)xrow * XROW + (uint32_t)xkb * 16u) =
@@ -334,70 +385,99 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         }
       }
     }
+    if constexpr (DYN) {
+      f32x4 pv[NSETS][V];
 #pragma unroll
-    for (int s = 0; s < NSETS; ++s)
+      for (int s = 0; s < NSETS; ++s)
 #pragma unroll
-      for (int i = 0; i < V; ++i)
+        for (int i = 0; i < V; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = V * r + i;
-          const float sc = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
-          acc[s][i][r] = __builtin_fmaf(sc, dp[s][i][r], acc[s][i][r]);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int e = V * r + i;
+            pv[s][i][r] = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16) * dp[s][i][r];
+          }
+      store_block(pv, part + (uint32_t)p * BLK);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+        for (int i = 0; i < V; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = V * r + i;
+            const float sc = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
+            acc[s][i][r] = __builtin_fmaf(sc, dp[s][i][r], acc[s][i][r]);
+          }
+    }
   };
 
-  // NB pairs in flight per wave.  Inside the main loop loads are issued without
-  // a branch (a pair past the wave's range gets out-of-range offsets: no
-  // memory traffic, zeros), so no branch separates a load from its use and the
-  // counter wait before each compute covers exactly that pair's loads; the
-  // scheduling barriers keep the pairs' loads in issue order.
+  // NB pairs in flight per wave.  Loads are issued without a branch (a pair
+  // past the end loads nothing), so no branch separates a load from its use
+  // and the counter wait before each compute covers exactly that pair's loads;
+  // the scheduling barriers keep the pairs' loads in issue order.
   PairBuf<BITS, V, NSETS> buf[NB];
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    issue(buf[u], u);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  int it = 0;
-  for (; it + NB < a.ppw; it += NB) {
+  if constexpr (DYN) {
+    // Pairs are handed out by a workgroup counter, so waves that get their data
+    // sooner (the older waves of each SIMD win issue arbitration) take more of
+    // them.  The first NB pairs of each wave are fixed (wave w starts with pairs
+    // w, w + 12, ...), the counter hands out the rest.  A wave's pairs come in
+    // increasing order and are computed in issue order, so the first
+    // out-of-range pair ends the wave's work.
+    auto grab = [&](uint32_t n) -> int {
+      uint32_t v = 0;
+      if (lane == 0) v = __hip_atomic_fetch_add(counter, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return (int)__builtin_amdgcn_readfirstlane(v);
+    };
+    int pidx[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      compute(buf[u]);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(buf[u], it + u + NB);
+      pidx[u] = wave + kWaves * u;
+      issue(buf[u], pidx[u]);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  // the last (up to NB) pairs are already in flight: no more loads
+    // Only the compute and the counter grab sit under (wave-uniform) branches;
+    // the loads do not, or the counter waits would lose their depth.  Once a
+    // wave's pairs run out, its remaining slots issue out-of-range loads.
+    do {
 #pragma unroll
-  for (int u = 0; u < NB; ++u)
-    if (it + u < a.ppw) compute(buf[u]);
-
-  // Slots j and j + 8 hold the two group halves of token j: add them.
-#pragma unroll
-  for (int s = 0; s < NSETS; ++s)
-#pragma unroll
-    for (int i = 0; i < V; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int other = __builtin_amdgcn_mov_dpp(__float_as_int(acc[s][i][r]), 0x128 /* row_ror:8 */, 0xF,
-                                                   0xF, false);
-        acc[s][i][r] += __int_as_float(other);
+      for (int u = 0; u < NB; ++u) {
+        const bool live = pidx[u] < a.pairs;
+        if (live) compute(buf[u], pidx[u]);
+        __builtin_amdgcn_sched_barrier(0);
+        pidx[u] = live ? grab(1u) : a.pairs;
+        issue(buf[u], pidx[u]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-  if (h == 0) {
+    } while (pidx[0] < a.pairs);
+  } else {
+    const int pbase = wave * a.ppw;
+    const int pend = min(pbase + a.ppw, a.pairs);
 #pragma unroll
-    for (int s = 0; s < NSETS; ++s)
+    for (int u = 0; u < NB; ++u) {
+      issue(buf[u], pbase + u < pend ? pbase + u : a.pairs);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    int it = 0;
+    for (; it + NB < a.ppw; it += NB) {
 #pragma unroll
-      for (int i = 0; i < V; ++i)
+      for (int u = 0; u < NB; ++u) {
+        compute(buf[u], pbase + it + u);
+        __builtin_amdgcn_sched_barrier(0);
+        const int nx = pbase + it + u + NB;
+        issue(buf[u], nx < pend ? nx : a.pairs);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // the last (up to NB) pairs are already in flight: no more loads
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int col = V * (4 * q + r) + i;
-          red[((wave * NSETS + s) * TILE + col) * 8 + t] = acc[s][i][r];
-        }
+    for (int u = 0; u < NB; ++u)
+      if (it + u < a.ppw && pbase + it + u < pend) compute(buf[u], pbase + it + u);
+    store_block(acc, part + (uint32_t)wave * BLK);
   }
   __syncthreads();
 
-  // Sum the waves in a fixed order, round, store (consecutive threads write
-  // consecutive columns of one token row).
+  // Sum the blocks (pairs, or waves) in a fixed order, round, store
+  // (consecutive threads write consecutive columns of one token row).
   uint16_t* y = static_cast<uint16_t*>(a.y);
   for (int idx = threadIdx.x; idx < 8 * TILE; idx += kThreads) {
     const int tt = idx / TILE, col = idx % TILE;
@@ -405,8 +485,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     float v[NSETS];
 #pragma unroll
     for (int s = 0; s < NSETS; ++s) {
+      const float* src = part + ((uint32_t)s * 8u + (uint32_t)tt) * (uint32_t)(TILE + 4) + (uint32_t)col;
       float sum = 0.f;
-      for (int w = 0; w < kWaves; ++w) sum += red[((w * NSETS + s) * TILE + col) * 8 + tt];
+      for (int k = 0; k < nblk; ++k) sum += src[(uint32_t)k * BLK];
       v[s] = sum;
     }
     float out;
@@ -491,6 +572,8 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 
 namespace {
 
+constexpr uint32_t kMaxLds = 160u * 1024u;  // LDS of one CDNA4 workgroup
+
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -522,30 +605,47 @@ int choose_v(int N, int cus, int vmax) {
   return best_v;
 }
 
-template <int BITS, bool SBF16, int NSETS>
-hipError_t launch_v(int v, const dev::GemmArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)a.ntiles), block(dev::kThreads);
-  if constexpr (NSETS == 1) {
-    switch (v) {
-      case 1: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 1, 1>), grid, block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 2, 1>), grid, block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 3, 1>), grid, block, 0, st, a); break;
-      default: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 4, 1>), grid, block, 0, st, a); break;
-    }
-  } else {
-    switch (v) {
-      case 1: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 1, 2>), grid, block, 0, st, a); break;
-      default: hipLaunchKernelGGL((dev::gemm_kernel<BITS, SBF16, 2, 2>), grid, block, 0, st, a); break;
-    }
+// One instantiation.  Its LDS (X staging + partial-sum blocks) can exceed the
+// default 64 KiB dynamic limit, so the limit is raised once per kernel to the
+// 160 KiB of a CDNA4 workgroup (idempotent: a race only repeats the call).
+template <int BITS, bool SBF16, int V, int NSETS, bool DYN>
+hipError_t launch_one(const dev::GemmArgs& a, uint32_t lds, hipStream_t st) {
+  auto kern = dev::gemm_kernel<BITS, SBF16, V, NSETS, DYN>;
+  static bool raised = false;
+  if (lds > 64u * 1024u && !raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e != hipSuccess) return e;
+    raised = true;
   }
+  hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(dev::kThreads), lds, st, a);
   return hipGetLastError();
 }
 
-template <int NSETS>
-hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, hipStream_t st) {
-  if (f.bits == 4) return f.scale_bf16 ? launch_v<4, true, NSETS>(v, a, st) : launch_v<4, false, NSETS>(v, a, st);
-  if (f.bits == 5) return f.scale_bf16 ? launch_v<5, true, NSETS>(v, a, st) : launch_v<5, false, NSETS>(v, a, st);
-  return f.scale_bf16 ? launch_v<8, true, NSETS>(v, a, st) : launch_v<8, false, NSETS>(v, a, st);
+template <int BITS, bool SBF16, int NSETS, bool DYN>
+hipError_t launch_v(int v, const dev::GemmArgs& a, uint32_t lds, hipStream_t st) {
+  if constexpr (NSETS == 1) {
+    switch (v) {
+      case 1: return launch_one<BITS, SBF16, 1, 1, DYN>(a, lds, st);
+      case 2: return launch_one<BITS, SBF16, 2, 1, DYN>(a, lds, st);
+      case 3: return launch_one<BITS, SBF16, 3, 1, DYN>(a, lds, st);
+      default: return launch_one<BITS, SBF16, 4, 1, DYN>(a, lds, st);
+    }
+  } else {
+    switch (v) {
+      case 1: return launch_one<BITS, SBF16, 1, 2, DYN>(a, lds, st);
+      default: return launch_one<BITS, SBF16, 2, 2, DYN>(a, lds, st);
+    }
+  }
+}
+
+template <int NSETS, bool DYN>
+hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, uint32_t lds, hipStream_t st) {
+  if (f.bits == 4)
+    return f.scale_bf16 ? launch_v<4, true, NSETS, DYN>(v, a, lds, st) : launch_v<4, false, NSETS, DYN>(v, a, lds, st);
+  if (f.bits == 5)
+    return f.scale_bf16 ? launch_v<5, true, NSETS, DYN>(v, a, lds, st) : launch_v<5, false, NSETS, DYN>(v, a, lds, st);
+  return f.scale_bf16 ? launch_v<8, true, NSETS, DYN>(v, a, lds, st) : launch_v<8, false, NSETS, DYN>(v, a, lds, st);
 }
 
 // Shared validation and launch of ngq_gemm (nsets 1) and ngq_swiglu_gemm (2).
@@ -583,7 +683,17 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   a.ppw = (a.pairs + dev::kWaves - 1) / dev::kWaves;
   a.ntiles = (Nout + 16 * v - 1) / (16 * v);
   a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
-  hipError_t e = nsets == 1 ? launch_fmt<1>(f, v, a, (hipStream_t)stream) : launch_fmt<2>(f, v, a, (hipStream_t)stream);
+  // Dynamic pair assignment needs one partial-sum block per pair in LDS; very
+  // long K falls back to static ranges (one block per wave).
+  const uint32_t lds_dyn = dev::Smem::bytes(true, a.pairs, nsets, 16 * v);
+  const bool dyn = lds_dyn <= kMaxLds;
+  const uint32_t lds = dyn ? lds_dyn : dev::Smem::bytes(false, a.pairs, nsets, 16 * v);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (nsets == 1)
+    e = dyn ? launch_fmt<1, true>(f, v, a, lds, st) : launch_fmt<1, false>(f, v, a, lds, st);
+  else
+    e = dyn ? launch_fmt<2, true>(f, v, a, lds, st) : launch_fmt<2, false>(f, v, a, lds, st);
   return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
 
