@@ -10,8 +10,10 @@ replicas totalling > 1 GiB, so every step streams its weights from HBM rather
 than from the 256 MB Infinity Cache.  Steps are timed with HIP events on the
 stream the kernels run on.  The line printed also carries the sweep the metric
 asks for (T = 1, 2, 4, 8 for the int4 QK and int5 gate/value projections, and
-the SwiGLU pair), the roofline of the dominant kernel, a parity check of the
-timed configuration against the oracle and the oracle's own CPU time.
+the SwiGLU pair), the stacked-layer sweep (64 layers of distinct weights,
+eager and as a replayed graph), the roofline of the dominant kernel, a parity
+check of the timed configuration against the oracle and the oracle's own CPU
+time.
 """
 from __future__ import annotations
 
@@ -44,6 +46,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-calibration", action="store_true")
     p.add_argument("--sweep-steps", type=int, default=100)
+    p.add_argument("--no-stack", action="store_true", help="skip the stacked-layer sweep")
+    p.add_argument("--stack-layers", type=int, default=64)
+    p.add_argument("--stack-passes", type=int, default=5)
     return p.parse_args()
 
 
@@ -194,6 +199,59 @@ def parity_check(ngq, rot, y_dev):
     return rep, (x, packed, scales)
 
 
+def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8)):
+    """The stacked-layer sweep: `layers` layers with distinct weights (QK, gate/
+    value, gate/up + SwiGLU, down, RMS rescale each), chained through the
+    rescaled down output.  Timed per full pass from x0, eager (one library call
+    at a time from Python) and as a captured graph replayed; the weights far
+    exceed the caches, so every pass streams them from HBM."""
+    import numpy as np
+    import torch
+
+    import synthetic
+    from groupwise_int_weight_amd.stack import Stack, layer_bytes
+
+    weights = synthetic.device_stack(layers, ngq.ngq_packed_bytes, seed=0)
+    out = []
+    for T in Ts:
+        st = Stack(weights, T)
+        x0 = torch.from_numpy(synthetic.stack_x0(T).view(np.int16)).to("cuda").view(torch.bfloat16)
+        cur = torch.cuda.current_stream()
+        st.forward(x0, cur.cuda_stream)  # warm-up pass
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(passes):
+            st.forward(x0, cur.cuda_stream)
+        e1.record()
+        e1.synchronize()
+        eager_ms = e0.elapsed_time(e1) / passes
+        eager_x = st.x.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st.forward(x0, torch.cuda.current_stream().cuda_stream)
+        g.replay()  # untimed upload
+        torch.cuda.synchronize()
+        same = bool(torch.equal(st.x, eager_x))
+        e0.record()
+        for _ in range(passes):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        graph_ms = e0.elapsed_time(e1) / passes
+        same = same and bool(torch.equal(st.x, eager_x))
+        del g
+        b = layer_bytes(T, ngq.ngq_packed_bytes) * layers
+        out.append({"T": T, "layers": layers, "passes": passes,
+                    "eager_us_per_layer": eager_ms * 1e3 / layers, "graph_us_per_layer": graph_ms * 1e3 / layers,
+                    "graph_ms_per_pass": graph_ms, "bytes_per_pass": b, "GBps": b / graph_ms / 1e6,
+                    "pct_peak": 100 * b / graph_ms / 1e6 / PEAK_GBS, "graph_matches_eager": same})
+        del st
+    del weights
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, T, host_inputs, bytes_full):
     """The oracle as it stands, on the host cores, over a column sample of the
     same projection; scaled to the full projection's bytes."""
@@ -288,6 +346,8 @@ def main():
         for t in (1, 8):
             sweep.extend(run_swiglu(ngq, t, args.sweep_steps, 10))
 
+    stack = None if args.no_stack else run_stack(ngq, args.stack_layers, args.stack_passes)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, T, host_inputs, nbytes)
 
     traffic = traffic_for(args.workload, T)
@@ -326,6 +386,7 @@ def main():
         "calibration": calib,
         "parity": parity,
         "sweep": sweep,
+        "stack": stack,
         "context": {"rtx4090_single_op_us": {"attention_q5_gate_value_t8": 39.936, "gdn_qk_q4_t8": 31.744},
                     "note": "the pages' own timings on another GPU with unstated shapes; not a target"},
     }

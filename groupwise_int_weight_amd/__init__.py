@@ -41,6 +41,7 @@ SIGNATURES = {
     "ngq_swiglu_gemm": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR]),
     "ngq_unpack_codes": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_dequant_f32": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR]),
+    "ngq_rms_rescale": (_INT, [_INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
     "ngq_strerror": (ctypes.c_char_p, [_INT]),
     "ngq_version": (_INT, []),
@@ -170,6 +171,19 @@ def ngq_swiglu_gemm(x, wq_gate_up, scales_gate_up, bits: int, N_ff: int, h=None,
     return h
 
 
+def ngq_rms_rescale(z, x=None, stream=None):
+    """x[t][:] (bf16) = z[t][:] / rms(z[t][:]); x may be z itself (in place)."""
+    import torch
+
+    T, N = z.shape
+    if z.dtype != torch.bfloat16:
+        raise TypeError("z must be bfloat16")
+    if x is None:
+        x = torch.empty_like(z)
+    _check(lib().ngq_rms_rescale(T, N, _dev_ptr(z, "z"), _dev_ptr(x, "x"), _stream(stream)), "ngq_rms_rescale")
+    return x
+
+
 def ngq_unpack_codes(wq, K: int, N: int, bits: int, group: int = NGQ_GROUP, stream=None):
     import torch
 
@@ -195,7 +209,7 @@ def ngq_stream_read(buf, sink, stream=None):
 
 
 __all__ = [
-    "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
+    "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
     "ngq_packed_bytes", "ngq_scale_bytes", "ngq_strerror", "ngq_version", "NgqError", "NgqLibraryMissing",
     "lib", "SIGNATURES",
 ]

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libngq.so")
 
-SOURCES = [os.path.join(CSRC, "ngq_host.cpp"), os.path.join(CSRC, "ngq_gemm.hip")]
+SOURCES = [os.path.join(CSRC, n) for n in ("ngq_host.cpp", "ngq_gemm.hip", "ngq_rescale.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -109,6 +109,16 @@ int ngq_gemm(int T, int K, int N, int bits, int group, const void* x, const void
 int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
                     const void* wq_gate_up, const void* scales_gate_up, void* h, void* stream);
 
+/* Per-token RMS rescale of a bf16 block (not a step the pages describe: it
+ * chains the output of one stacked layer into the next at unit scale):
+ *   x[t][n] = bf16( z[t][n] / sqrt((1/N) sum_n z[t][n]^2) ),  all-zero row -> zeros
+ * No epsilon, no learned weight.  Evaluated in fp64 and rounded once, to
+ * nearest even, from the fp64 quotient.
+ *   z : device bf16 [T][N];  x : device bf16 [T][N], overwritten.  x == z
+ *       (in place) is allowed; any other overlap is NGQ_ERR_ARG.
+ * 0 <= T <= 65535, 0 <= N <= 2^24; T == 0 or N == 0 is a no-op. */
+int ngq_rms_rescale(int T, int N, const void* z, void* x, void* stream);
+
 /* Debug export: the signed codes as the GEMM kernels unpack them.
  *   wq : device, ngq_pack layout;  codes : device int8 [K][N], overwritten. */
 int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream);

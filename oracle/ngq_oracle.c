@@ -22,8 +22,8 @@
  * the symmetric dequantisation w = c * s with one scale per 64 consecutive
  * k and column, int4 codes stored offset-binary 8 per 32-bit word along K,
  * int5 stored as a low-nibble plane plus a one-bit high plane, fp32
- * accumulation and bf16 output are the benchmark spec's and are restated
- * below as the layout this oracle reads.
+ * accumulation and bf16 output are therefore readings, not quotations, and
+ * are restated below as the layout this oracle reads.
  *
  * Packed layout (all words little-endian, row-major, column index fastest):
  *   int4: P0 = u32[K/8][N];  bits 4i..4i+3 of word (kb,n) hold u = c+8
@@ -316,7 +316,10 @@ int oracle_round_bf16_array(int count, const double* v, uint16_t* out) {
 }
 
 /* Per-row RMS rescale used to chain layers of the stack sweep:
- * x'[t][:] = bf16( z[t][:] / sqrt(mean_k z[t][k]^2) ), no epsilon, fp64. */
+ * x'[t][:] = bf16( z[t][:] / sqrt(mean_k z[t][k]^2) ), no epsilon, fp64.
+ * The pages describe no such step (it is harness, not method).  A row whose
+ * mean square is zero has no scale to divide by; without an epsilon the
+ * plainest result is the row itself, i.e. zeros. */
 int oracle_rms_rescale(int T, int N, const uint16_t* z, uint16_t* out) {
   for (int t = 0; t < T; ++t) {
     double ss = 0.0;
@@ -326,7 +329,7 @@ int oracle_rms_rescale(int T, int N, const uint16_t* z, uint16_t* out) {
     }
     double r = sqrt(ss / (double)N);
     for (int n = 0; n < N; ++n)
-      out[(size_t)t * N + n] = oracle_round_bf16(oracle_bf16_to_f64(z[(size_t)t * N + n]) / r);
+      out[(size_t)t * N + n] = r > 0.0 ? oracle_round_bf16(oracle_bf16_to_f64(z[(size_t)t * N + n]) / r) : 0;
   }
   return 0;
 }

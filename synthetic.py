@@ -7,8 +7,8 @@ take their inputs from here, so the HIP path and the oracle see the same bits.
 
 Workloads (shapes of the Qwen3.8-27B projections named on the pages: the GDN
 QK projection, the attention gate/value projection and the SwiGLU MLP of the
-NInfer-4090 V3 topic, section "What V3 did"; sizes and distributions as the
-task states them):
+NInfer-4090 V3 topic, section "What V3 did"; the pages give no sizes or
+distributions, so these are readings):
 
   tiny      T=1, K=256,  N=256,   int4, fp16 scales U[1e-3, 2e-2]
   qk        T in 1..8, K=5120, N=8192,  int4, fp16 scales U[1e-3, 2e-2]
@@ -116,3 +116,38 @@ def device_replicas(w: Workload, T: int, replicas: int, packed_bytes: int, seed:
     s = s.to(torch.bfloat16 if w.scale_bf16 else torch.float16)
     x = torch.randn((T, w.K), device=device, generator=g).to(torch.bfloat16)
     return wq, s, x
+
+
+# ---- the stacked-layer sweep ---------------------------------------------------------
+# Per layer: the QK projection, the gate/value projection, the fused gate/up
+# projection and the down projection, each with its own seeded weights.
+STACK_PROJECTIONS = ("qk", "gv", "gate_up", "down")
+STACK_CONFIG_ID = 4
+
+
+def device_stack(layers: int, packed_bytes, seed: int = 0, device: str = "cuda"):
+    """Distinct weights for `layers` stacked layers, drawn on the device: a list
+    of {projection name: (packed uint8 tensor, scale tensor)}.  Packed bytes are
+    uniform (uniform codes over the full range); scales are uniform over the
+    workload's range, rounded to its 16-bit scale type.  `packed_bytes(K, N,
+    bits)` gives the size of a packed matrix."""
+    import torch
+
+    out = []
+    for layer in range(layers):
+        d = {}
+        for j, name in enumerate(STACK_PROJECTIONS):
+            w = WORKLOADS[name]
+            g = torch.Generator(device=device)
+            g.manual_seed(((int(seed) * 1_000_003 + STACK_CONFIG_ID) * 4099 + layer) * 8 + j)
+            wq = torch.randint(0, 256, (int(packed_bytes(w.K, w.N, w.bits)),), dtype=torch.uint8, device=device,
+                               generator=g)
+            s = torch.rand((w.K // GROUP, w.N), device=device, generator=g) * (w.scale_hi - w.scale_lo) + w.scale_lo
+            d[name] = (wq, s.to(torch.bfloat16 if w.scale_bf16 else torch.float16))
+        out.append(d)
+    return out
+
+
+def stack_x0(T: int, seed: int = 0) -> np.ndarray:
+    """The first layer's input, bf16 bits [T][5120], N(0,1)."""
+    return draw_x(T, HIDDEN, rng(seed, STACK_CONFIG_ID, 0, _X))

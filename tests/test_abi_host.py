@@ -35,7 +35,7 @@ def header_functions():
 def test_header_declares_the_boundary():
     names = header_functions()
     for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_packed_bytes", "ngq_scale_bytes",
-                     "ngq_unpack_codes", "ngq_dequant_f32", "ngq_strerror"]:
+                     "ngq_unpack_codes", "ngq_dequant_f32", "ngq_rms_rescale", "ngq_strerror"]:
         assert required in names
 
 
@@ -150,6 +150,28 @@ def test_empty_calls_are_no_ops(ngq):
     assert L.ngq_unpack_codes(0, 4, 4, 64, None, None, None) == 0
     assert L.ngq_dequant_f32(64, 0, 4, 64, None, None, None, None) == 0
     assert L.ngq_stream_read(None, 0, None, None) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 64, X, Y), -2),            # T < 0
+    ((1, -4, X, Y), -2),             # N < 0
+    ((1, (1 << 24) + 1, X, Y), -2),  # N too large
+    ((65536, 4, X, Y), -2),          # T too large
+    ((1, 64, None, Y), -1),          # null z
+    ((1, 64, X, None), -1),          # null x
+    ((1, 64, X + 2, Y), -4),         # misaligned z
+    ((1, 64, X, Y + 8), -4),         # misaligned x
+    ((2, 64, X, X + 64), -1),        # partial overlap (in place, x == z, is allowed)
+    ((65535, 1 << 15, X, Y), -3),    # block >= 2 GiB
+])
+def test_rms_rescale_rejects_bad_arguments(ngq, args, status):
+    assert ngq.lib().ngq_rms_rescale(*args, None) == status
+
+
+def test_rms_rescale_empty_is_no_op(ngq):
+    L = ngq.lib()
+    assert L.ngq_rms_rescale(0, 64, None, None, None) == 0
+    assert L.ngq_rms_rescale(3, 0, None, None, None) == 0
 
 
 def test_debug_exports_reject_bad_arguments(ngq):

@@ -202,13 +202,14 @@ def test_swiglu_and_down_full_size(ngq, orc, T):
     h64, g, u = swiglu_reference(orc, x, packed_o, scales, wgu.K, N_ff, 4, False, cols)
     check_swiglu(hb[:, cols], h64, g, u, f"swiglu T{T}")
     del codes, packed, packed_o
-    # down projection consumes the GPU's own bf16 h
-    dcodes, dscales, _ = synthetic.make_inputs(wdn, T, seed=0)
+    # down projection: K = N_ff, its activations drawn by the generator (the
+    # oracle never takes a GPU result as input)
+    dcodes, dscales, dx = synthetic.make_inputs(wdn, T, seed=0)
     dpacked = ngq.ngq_pack(dcodes, 4)
-    y = ngq.ngq_gemm(h, dev_u8(dpacked), dev_scales(dscales, False), 4, wdn.N)
+    y = ngq.ngq_gemm(dev_bf16(dx), dev_u8(dpacked), dev_scales(dscales, False), 4, wdn.N)
     yb = host_bits(y)
     dcols = sample_cols(wdn.N, seed=20 + T)
-    y64, axw, axs = orc.gemm(hb, orc.pack(dcodes, 4), dscales, wdn.K, wdn.N, 4, False, cols=dcols, nthreads=8,
+    y64, axw, axs = orc.gemm(dx, orc.pack(dcodes, 4), dscales, wdn.K, wdn.N, 4, False, cols=dcols, nthreads=8,
                              with_bounds=True)
     assert_parity(compare(yb[:, dcols], y64, axw, axs, wdn.K, 4), f"down T{T}")
 

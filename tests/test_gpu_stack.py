@@ -1,0 +1,178 @@
+"""GPU tests of the stacked-layer sweep: the RMS rescale kernel against the
+oracle, the first layer's projections against the oracle, and properties of
+the chained layers (finite, unit mean square per row, deterministic, and a
+captured graph replays to the eager result bit for bit).
+
+The oracle only ever sees generator inputs: the projections of layer 0 take
+the seeded x0, the rescale takes seeded z.  Layers after the first consume
+the GPU's own activations, so the chain is checked through properties that
+hold at any depth rather than against the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synthetic
+from tests.parity import assert_parity, bf16_bits_to_f64, compare
+from tests.test_gpu_parity import check_swiglu, dev_bf16, host_bits, sample_cols, swiglu_reference
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ngq():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device visible")
+    import groupwise_int_weight_amd as g
+
+    g.lib()  # raises when the library is not built: no fallback exists
+    return g
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+
+    oracle.lib()
+    return oracle
+
+
+def cur_stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---- RMS rescale ----------------------------------------------------------------------
+
+def rescale_check(zb, gb, orc):
+    """Bit-exact against the oracle, except an element whose GPU value is the
+    other bf16 neighbour of a quotient within 2^-40 (relative) of their
+    midpoint: the kernel sums the squares in a different order than the
+    oracle, an fp64 difference of at most N 2^-53 relative in the mean
+    square, half that in the root."""
+    ob = orc.rms_rescale(zb)
+    diff = ob != gb
+    if not diff.any():
+        return 0
+    z = bf16_bits_to_f64(zb)
+    ms = np.mean(z ** 2, axis=1, keepdims=True)
+    q = z / np.sqrt(ms)
+    mid = 0.5 * (bf16_bits_to_f64(ob) + bf16_bits_to_f64(gb))
+    near = np.abs(q - mid) <= 2.0 ** -40 * np.abs(q)
+    one = np.abs(ob.astype(np.int32) - gb.astype(np.int32)) == 1
+    assert np.all((near & one)[diff]), np.argwhere(diff)[:5]
+    return int(diff.sum())
+
+
+@pytest.mark.parametrize("T,N", [(1, 5120), (8, 5120), (5, 17408), (3, 1000), (2, 4), (8, 8)])
+def test_rms_rescale_matches_oracle(ngq, orc, T, N):
+    g = np.random.default_rng(1000 * T + N)
+    # rows of very different magnitudes, including bf16 subnormal entries
+    mags = np.array([1.0, 1e-30, 3e20, 1e-3, 17.0, 1e-38, 2.0 ** 100, 0.5])[:T]
+    z = synthetic.f32_to_bf16_bits((g.standard_normal((T, N)) * mags[:, None]).astype(np.float32))
+    z[0, :3] = [0x8000, 0x0000, 0x0001]  # -0, +0 and the smallest subnormal
+    x = ngq.ngq_rms_rescale(dev_bf16(z))
+    exempt = rescale_check(z, host_bits(x), orc)
+    assert exempt <= 2
+
+
+def test_rms_rescale_in_place_and_zero_row(ngq, orc):
+    g = np.random.default_rng(5)
+    z = synthetic.f32_to_bf16_bits(g.standard_normal((4, 5120)).astype(np.float32))
+    z[2] = 0
+    zd = dev_bf16(z)
+    out = host_bits(ngq.ngq_rms_rescale(zd))
+    ngq.ngq_rms_rescale(zd, x=zd)  # in place
+    assert np.array_equal(host_bits(zd), out)
+    assert np.all(out[2] == 0)
+    rescale_check(z, out, orc)
+
+
+# ---- stacked layers -------------------------------------------------------------------
+
+_STACK = {}
+
+
+def stack_layers(ngq, layers):
+    if _STACK.get("n", 0) < layers:
+        _STACK.clear()
+        torch.cuda.empty_cache()
+        _STACK["w"] = synthetic.device_stack(layers, ngq.ngq_packed_bytes, seed=0)
+        _STACK["n"] = layers
+    return _STACK["w"][:layers]
+
+
+def to_host_u8(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def to_host_u16(t):
+    torch.cuda.synchronize()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_stack_first_layer_matches_oracle(ngq, orc, T):
+    from groupwise_int_weight_amd.stack import Stack
+
+    layers = stack_layers(ngq, 2)
+    st = Stack(layers, T)
+    x0 = synthetic.stack_x0(T, seed=0)
+    st.x.copy_(dev_bf16(x0))
+    st.layer(0, cur_stream())
+    for name, out, sbf16 in (("qk", st.q, False), ("gv", st.v, True)):
+        w = synthetic.WORKLOADS[name]
+        wq, s = layers[0][name]
+        cols = sample_cols(w.N, seed=30 + T)
+        y64, axw, axs = orc.gemm(x0, to_host_u8(wq), to_host_u16(s), w.K, w.N, w.bits, sbf16, cols=cols,
+                                 nthreads=8, with_bounds=True)
+        assert_parity(compare(host_bits(out)[:, cols], y64, axw, axs, w.K, w.bits), f"stack {name} T{T}")
+    wq, s = layers[0]["gate_up"]
+    cols = sample_cols(synthetic.N_FF, seed=40 + T)
+    h64, g, u = swiglu_reference(orc, x0, to_host_u8(wq), to_host_u16(s), synthetic.HIDDEN, synthetic.N_FF, 4,
+                                 False, cols)
+    check_swiglu(host_bits(st.h)[:, cols], h64, g, u, f"stack swiglu T{T}")
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_stack_chain_properties_and_graph_replay(ngq, T):
+    from groupwise_int_weight_amd.stack import Stack
+
+    L = 4
+    layers = stack_layers(ngq, L)
+    st = Stack(layers, T)
+    x0 = dev_bf16(synthetic.stack_x0(T, seed=0))
+    eager = to_host_u16(st.forward(x0, cur_stream()))
+    again = to_host_u16(st.forward(x0, cur_stream()))
+    assert np.array_equal(eager, again)  # deterministic
+    v = bf16_bits_to_f64(eager)
+    assert np.all(np.isfinite(v))
+    # every row leaves the rescale with unit mean square, up to bf16 rounding
+    assert np.all(np.abs(np.mean(v ** 2, axis=1) - 1.0) < 2.0 ** -7)
+    # the chain actually moves: the output is not the input
+    assert not np.array_equal(eager, to_host_u16(x0))
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.x.copy_(x0)
+        for i in range(L):  # warm-up on the capture stream
+            st.layer(i, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        s = torch.cuda.current_stream().cuda_stream
+        for i in range(L):
+            st.layer(i, s)
+    for rep in range(3):
+        st.x.copy_(x0)
+        graph.replay()
+        got = to_host_u16(st.x)
+        assert np.array_equal(got, eager), rep
+        # eager work between replays
+        st.forward(x0, cur_stream(), layers=1)
+        torch.cuda.synchronize()
+    assert math.isfinite(float(v.sum()))

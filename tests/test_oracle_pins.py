@@ -378,3 +378,51 @@ def test_rms_rescale(oracle_lib):
     r = math.sqrt(12.5)
     assert out[0, 0] == oracle_lib.round_bf16(3 / r) and out[0, 1] == oracle_lib.round_bf16(4 / r)
     assert np.all(out[1] == 0x3F80)
+
+
+def exact_rms_rescale_bits(z_bits):
+    """Brute force: the quotient z / sqrt(mean z^2) to 80 significant digits
+    (Decimal's square root is correctly rounded, and exact when the root is a
+    terminating decimal), then the exhaustive bf16 rounding of that value."""
+    import decimal
+
+    ctx = decimal.Context(prec=80)
+    out = np.zeros_like(z_bits)
+    for t in range(z_bits.shape[0]):
+        vals = [Fraction(bf16_ref(b)) for b in z_bits[t]]
+        ms = sum(v * v for v in vals) / len(vals)
+        if ms == 0:
+            continue
+        r = ctx.sqrt(ctx.divide(decimal.Decimal(ms.numerator), decimal.Decimal(ms.denominator)))
+        for n, v in enumerate(vals):
+            q = ctx.divide(decimal.Decimal(v.numerator), decimal.Decimal(v.denominator))
+            out[t, n] = rne_bf16_fraction(Fraction(ctx.divide(q, r)))
+    return out
+
+
+def test_rms_rescale_brute_force(oracle_lib):
+    g = np.random.default_rng(11)
+    rows = [g.standard_normal(37) * 10.0 ** e for e in (-38, -5, 0, 3, 30)]
+    rows.append(np.where(np.arange(37) == 5, 1e-3, 1e-42))  # one large entry, the rest subnormal
+    z = synthetic.f32_to_bf16_bits(np.array(rows, np.float32))
+    assert np.array_equal(oracle_lib.rms_rescale(z), exact_rms_rescale_bits(z))
+
+
+def test_rms_rescale_scale_invariant_and_zero_row(oracle_lib):
+    g = np.random.default_rng(12)
+    z = synthetic.f32_to_bf16_bits(g.standard_normal((3, 512)).astype(np.float32))
+    base = oracle_lib.rms_rescale(z)
+    for j in (-20, -1, 1, 7):
+        zs = synthetic.f32_to_bf16_bits((bf16_bits_f32(z) * np.float32(2.0 ** j)).astype(np.float32))
+        assert np.array_equal(oracle_lib.rms_rescale(zs), base)  # power-of-two scaling cancels exactly
+    # a row with zero mean square: zeros; the other rows are unaffected
+    z[1] = 0
+    out = oracle_lib.rms_rescale(z)
+    assert np.all(out[1] == 0) and np.array_equal(out[[0, 2]], base[[0, 2]])
+    # unit mean square up to the output rounding (relative half-ulp 2^-8 per element)
+    v = bf16_bits_f32(out[[0, 2]]).astype(np.float64)
+    assert np.all(np.abs(np.mean(v ** 2, axis=1) - 1.0) < 2.0 ** -7)
+
+
+def bf16_bits_f32(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
