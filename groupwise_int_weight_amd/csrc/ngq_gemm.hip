@@ -82,54 +82,40 @@ __device__ __forceinline__ void load_words(uint32_t* d, __amdgpu_buffer_rsrc_t r
   }
 }
 
-// ---- unpack: one 8-k block of one column -> eight bf16 (128 + u), k order ----
+// ---- unpack: one 8-k block of one column -> eight bf16 (128 + u) ----
 
-// High bits of int5 for one 8-k block: byte `byte_idx` of the P1 word holds
-// them for k = 8*block + 0..7.  Returns them at bit 4 of each byte, split into
-// k 0..3 (hi_e) and k 4..7 (hi_f).  x * 0x204081 copies 4 bits to offsets 0,
-// 7, 14, 21 without overlap; the mask keeps bit i of the nibble at 8 i + 4.
-__device__ __forceinline__ void int5_high_bits(uint32_t p1word, uint32_t byte_idx, uint32_t& hi_e,
-                                               uint32_t& hi_f) {
-  const uint32_t sh = 8u * byte_idx;
-  const uint32_t lo4 = __builtin_amdgcn_ubfe(p1word, sh, 4u) << 4;
-  const uint32_t hi4 = __builtin_amdgcn_ubfe(p1word, sh + 4u, 4u) << 4;
-  hi_e = (lo4 * 0x00204081u) & 0x10101010u;
-  hi_f = (hi4 * 0x00204081u) & 0x10101010u;
-}
-
-// Eight 4-bit fields of a P0 word (field i = k i) plus optional 5th bits to
-// eight bf16 values 128 + u in k order: two byte permutes spread the nibbles to
-// one byte each, two more permutes put the exponent byte 0x43 above each.
-__device__ __forceinline__ u32x4 nibbles_to_bf16(uint32_t w, uint32_t hi_e, uint32_t hi_f) {
-  const uint32_t w4 = w >> 4;
-  const uint32_t e = (__builtin_amdgcn_perm(w4, w, 0x05010400u) & 0x0F0F0F0Fu) | hi_e;  // k0 k1 k2 k3
-  const uint32_t f = (__builtin_amdgcn_perm(w4, w, 0x07030602u) & 0x0F0F0F0Fu) | hi_f;  // k4 k5 k6 k7
-  const uint32_t ex = 0x43434343u;
+// Unpack in the interleaved k order: dword j of the result holds k = j (low
+// half) and k = j + 4 (high half) of an 8-k block, each as the bf16 value
+// 128 + u.  hb: the block's eight 5th bits (bit i for k = i), 0 for int4; they
+// are spread to bits 4..7 (k 0..3) and 20..23 (k 4..7) and shifted into
+// place with the nibbles.
+__device__ __forceinline__ u32x4 nibbles_to_bf16_il(uint32_t w, uint32_t hb) {
+  const uint32_t hs = ((hb & 0x0Fu) << 4) | ((hb & 0xF0u) << 16);
   u32x4 r;
-  r[0] = __builtin_amdgcn_perm(ex, e, 0x04010400u);
-  r[1] = __builtin_amdgcn_perm(ex, e, 0x04030402u);
-  r[2] = __builtin_amdgcn_perm(ex, f, 0x04010400u);
-  r[3] = __builtin_amdgcn_perm(ex, f, 0x04030402u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r[j] = ((w >> (4 * j)) & 0x000F000Fu) | 0x43004300u | ((hs >> j) & 0x00100010u);
   return r;
 }
 
-// Two int8 words (k 0..3, k 4..7) to eight bf16 values u (exact: u <= 255 has
-// at most 8 significant bits, so the upper half of its fp32 is its bf16).
-__device__ __forceinline__ u32x4 bytes_to_bf16(uint32_t w0, uint32_t w1) {
-  const uint32_t a0 = __float_as_uint((float)(w0 & 0xFFu));
-  const uint32_t a1 = __float_as_uint((float)((w0 >> 8) & 0xFFu));
-  const uint32_t a2 = __float_as_uint((float)((w0 >> 16) & 0xFFu));
-  const uint32_t a3 = __float_as_uint((float)(w0 >> 24));
-  const uint32_t b0 = __float_as_uint((float)(w1 & 0xFFu));
-  const uint32_t b1 = __float_as_uint((float)((w1 >> 8) & 0xFFu));
-  const uint32_t b2 = __float_as_uint((float)((w1 >> 16) & 0xFFu));
-  const uint32_t b3 = __float_as_uint((float)(w1 >> 24));
+// int8 in the interleaved order: w0 holds k 0..3, w1 k 4..7; each byte u is
+// converted exactly (u <= 255 has at most 8 significant bits) and the upper
+// halves of the fp32 values are its bf16.
+__device__ __forceinline__ u32x4 bytes_to_bf16_il(uint32_t w0, uint32_t w1) {
   u32x4 r;
-  r[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-  r[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-  r[3] = __builtin_amdgcn_perm(b3, b2, 0x07060302u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = __float_as_uint((float)((w0 >> (8 * j)) & 0xFFu));
+    const uint32_t hi = __float_as_uint((float)((w1 >> (8 * j)) & 0xFFu));
+    r[j] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+  }
   return r;
+}
+
+// An X chunk of 8 bf16 (k order 0..7, two per dword) in the interleaved order.
+__device__ __forceinline__ u32x4 interleave_x(const uint32_t (&d)[4]) {
+  return u32x4{__builtin_amdgcn_perm(d[2], d[0], 0x05040100u), __builtin_amdgcn_perm(d[2], d[0], 0x07060302u),
+               __builtin_amdgcn_perm(d[3], d[1], 0x05040100u), __builtin_amdgcn_perm(d[3], d[1], 0x07060302u)};
 }
 
 template <int BITS>
@@ -344,10 +330,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   auto compute = [&](const PairBuf<BITS, V, NSETS>& buf, int p) {
     // stage the pair's X rows, then read the four B fragments back (LDS is in
     // order within a wave, so no barrier is needed)
-    *reinterpret_cast<u32x4*>(xslot + (uint32_t)xrow * XROW + (uint32_t)xkb * 16u) =
-        u32x4{buf.x[0][0], buf.x[0][1], buf.x[0][2], buf.x[0][3]};
-    *reinterpret_cast<u32x4*>(xslot + (uint32_t)(xrow + 4) * XROW + (uint32_t)xkb * 16u) =
-        u32x4{buf.x[1][0], buf.x[1][1], buf.x[1][2], buf.x[1][3]};
+    *reinterpret_cast<u32x4*>(xslot + (uint32_t)xrow * XROW + (uint32_t)xkb * 16u) = interleave_x(buf.x[0]);
+    *reinterpret_cast<u32x4*>(xslot + (uint32_t)(xrow + 4) * XROW + (uint32_t)xkb * 16u) = interleave_x(buf.x[1]);
     bf16x8 bfrag[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -371,14 +355,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         for (int i = 0; i < V; ++i) {
           u32x4 av;
           if constexpr (BITS == 4) {
-            av = nibbles_to_bf16(buf.a[s][st][i], 0u, 0u);
+            av = nibbles_to_bf16_il(buf.a[s][st][i], 0u);
           } else if constexpr (BITS == 5) {
-            uint32_t he, hf;
             // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
-            int5_high_bits(buf.p1[s][st >> 1][i], 2u * (uint32_t)(st & 1) + (uint32_t)(q & 1), he, hf);
-            av = nibbles_to_bf16(buf.a[s][st][i], he, hf);
+            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
+                                                                                 8u * (uint32_t)(q & 1), 8u);
+            av = nibbles_to_bf16_il(buf.a[s][st][i], hb);
           } else {
-            av = bytes_to_bf16(buf.a[s][st][i], buf.a[s][st][V + i]);
+            av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
           }
           dp[s][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag[st],
                                                              dp[s][i], 0, 0, 0);
@@ -500,6 +484,298 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   }
 }
 
+// ---- X-resident kernel ------------------------------------------------------
+//
+// The activations X (T x K bf16, at most 80 KB for K = 5120) are staged in LDS
+// once per workgroup, so the loop over group pairs issues only weight and
+// scale loads.  X is stored with each 8-k block in the order k = 0, 4, 1, 5,
+// 2, 6, 3, 7, the order in which the unpack produces weights.
+//
+// A workgroup may own several tiles (tile r, r + G, ... for its rank r among
+// G workgroups); X stays resident across them and the pair stream runs on
+// across a tile boundary, so the next tile's first loads are in flight while
+// a tile is reduced and stored.  Wave w takes pairs w, w + W, w + 2W, ... of
+// every tile, NB of them in flight, so the waves of a workgroup move through K
+// together; each wave accumulates its pairs in registers and the waves'
+// partials are summed in wave order, so results do not depend on timing.
+
+// LDS of the X-resident kernel: a zero block (bytes 0..127, read by the lanes
+// whose B slot belongs to the other group half or to a token >= T), the token
+// rows of X (row stride 2K + 16 bytes, so the 8 rows of one k offset fall in
+// distinct banks), then one partial-sum block per wave.
+struct XSmem {
+  static constexpr uint32_t ZERO = 128;
+  static __host__ __device__ constexpr uint32_t xrow(int K) { return 2u * (uint32_t)K + 16u; }
+  static __host__ __device__ constexpr uint32_t x_end(int T, int K) { return ZERO + (uint32_t)T * xrow(K); }
+  static __host__ __device__ constexpr uint32_t bytes(int T, int K, int waves, int nsets, int tile) {
+    return x_end(T, K) + (uint32_t)waves * Smem::block_floats(nsets, tile) * 4u;
+  }
+};
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also makes the
+// wave's earlier global stores visible, which on this target waits for every
+// outstanding vector memory operation, loads included; the weight loads in
+// flight across a tile boundary must not be drained that way.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int BITS, int V, int NSETS>
+struct WBuf {
+  static constexpr int WPK = BITS == 8 ? 2 : 1;
+  uint32_t a[NSETS][4][V * WPK];
+  uint32_t p1[NSETS][2][BITS == 5 ? V : 1];
+  uint32_t sc[NSETS][2 * V];
+};
+
+// XL: X chunks (16 bytes) per thread in the prologue; W waves; NB pairs in
+// flight per wave.
+template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, int XL>
+__global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
+  constexpr int WPK = BITS == 8 ? 2 : 1;
+  constexpr int TILE = 16 * V;
+  constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const uint32_t XROW = XSmem::xrow(a.K);
+  float* const part = reinterpret_cast<float*>(smem + XSmem::x_end(a.T, a.K));
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, q = lane >> 4;
+  const int t = m & 7, h = m >> 3;
+
+  // rank of this workgroup with the workgroups of one XCD (b % 8) numbered
+  // consecutively, so that one XCD works on neighbouring tiles at a time
+  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
+  const int rank = xcd * (G >> 3) + min(xcd, G & 7) + (b >> 3);
+  const int my_tiles = (a.ntiles - rank + G - 1) / G;
+
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+
+  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
+  const uint32_t lane_kb = 8u * (uint32_t)(q >> 1) + (uint32_t)(q & 1);
+  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];  // tile-independent parts
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s) {
+    const uint32_t col = (uint32_t)(s * a.up_off + V * m);
+    offA[s] = lane_kb * WPK * rowb + col * 4u;
+    offP1[s] = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
+    offS[s] = (uint32_t)h * (uint32_t)a.Ncols * 2u + (uint32_t)(s * a.up_off + 4 * V * q) * 2u;
+  }
+  // B fragment source: this lane's token row at its k-slot, or the zero block
+  const bool b_on = ((q >> 1) == h) & (t < a.T);
+  const uint32_t bsrc = XSmem::ZERO + (uint32_t)t * XROW + lane_kb * 16u;
+
+  // -- prologue: X loads first, then the first pairs' weights; the X wait
+  // below then leaves those weights in flight.
+  const int nch = a.T * (a.K >> 3);  // 16-byte chunks of X
+  const int rowch = a.K >> 3;
+  uint32_t xv[XL][4];
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    const int c = threadIdx.x + W * 64 * j;
+    const uint32_t off = c < nch ? (uint32_t)c * 16u : kOOB;  // X rows are contiguous in memory
+    load_words<4>(xv[j], rX, off);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Loads of pair p of the workgroup's tile ti (nothing when either is out of
+  // range).  Flags are combined bitwise so that no lane-divergent branch
+  // appears.
+  auto issue_at = [&](WBuf<BITS, V, NSETS>& buf, int ti, int p) {
+    const bool valid = (ti < my_tiles) & (p < a.pairs);
+    const uint32_t c0 = (uint32_t)((rank + G * ti) * TILE);
+    const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb + c0 * 4u : kOOB;
+    const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb + c0 * 4u : kOOB;
+    const uint32_t ps = valid ? (uint32_t)p * rowb + c0 * 2u : kOOB;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const uint32_t o = offA[s] + pa + (uint32_t)st * 2u * WPK * rowb;
+        load_words<V>(&buf.a[s][st][0], rW, o);
+        if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
+      }
+    }
+    if constexpr (BITS == 5) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        load_words<V>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
+        load_words<V>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) load_words<2 * V>(&buf.sc[s][0], rS, offS[s] + ps);
+  };
+
+  // item (tile i, slot k) is pair wave + W k of tile i; every tile has cntp
+  // slots (the same for all waves, a multiple of NB), of
+  // which the first cnt are real pairs
+  const int cnt = a.pairs > wave ? (a.pairs - wave + W - 1) / W : 0;
+  const int cntp = a.ppw;
+  int is_tile = 0, is_k = 0;  // next item to issue
+  auto issue_next = [&](WBuf<BITS, V, NSETS>& buf) {
+    issue_at(buf, is_tile, is_k < cnt ? wave + W * is_k : a.pairs);
+    if (++is_k == cntp) {
+      is_k = 0;
+      ++is_tile;
+    }
+  };
+
+  WBuf<BITS, V, NSETS> buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    issue_next(buf[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // -- X into LDS in the interleaved order (waits for the X loads only), the
+  // zero block, barrier
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    const int c = threadIdx.x + W * 64 * j;
+    if (c < nch) {
+      const int tt = c / rowch, kc = c - tt * rowch;
+      *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(xv[j]);
+    }
+  }
+  if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
+  lds_barrier();
+
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+  f32x4 acc[NSETS][V];
+  auto clear_acc = [&]() {
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  clear_acc();
+
+  // per-group partial sums of one pair (before scaling)
+  auto pair_sums = [&](const WBuf<BITS, V, NSETS>& buf, int p, f32x4 (&dp)[NSETS][V]) {
+    // the second group of the last pair of an odd group count does not exist:
+    // its lanes read zeros
+    const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
+    const bool on = b_on & !(half & (h == 1));
+    const uint32_t src = on ? bsrc + (uint32_t)p * 256u : 0u;
+    bf16x8 bfrag[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      bfrag[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + src + (uint32_t)st * 32u));
+    // -(128 + bias) * sum_k x over each group half: seeds every partial sum
+    f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfrag[st], dx, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) dp[s][i] = dx;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          u32x4 av;
+          if constexpr (BITS == 4) {
+            av = nibbles_to_bf16_il(buf.a[s][st][i], 0u);
+          } else if constexpr (BITS == 5) {
+            // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
+            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
+                                                                                 8u * (uint32_t)(q & 1), 8u);
+            av = nibbles_to_bf16_il(buf.a[s][st][i], hb);
+          } else {
+            av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
+          }
+          dp[s][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag[st],
+                                                             dp[s][i], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // slots j and j + 8 hold the two group halves of token j: add them; the
+  // lanes of the first half write the block [set][token][column]
+  auto store_block = [&](f32x4 (&v)[NSETS][V], float* blk) {
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int other = __builtin_amdgcn_mov_dpp(__float_as_int(v[s][i][r]), 0x128 /* row_ror:8 */, 0xF,
+                                                     0xF, false);
+          const float sum = v[s][i][r] + __int_as_float(other);
+          if (h == 0)
+            blk[((uint32_t)s * 8u + (uint32_t)t) * (uint32_t)(TILE + 4) + (uint32_t)(V * (4 * q + r) + i)] = sum;
+        }
+  };
+
+  // the tile's outputs: blocks summed in order, SwiGLU or plain, rounded
+  uint16_t* y = static_cast<uint16_t*>(a.y);
+  auto finish_tile = [&](int ti) {
+    const int c0 = (rank + G * ti) * TILE;
+    for (int idx = threadIdx.x; idx < 8 * TILE; idx += W * 64) {
+      const int tt = idx / TILE, col = idx % TILE;
+      if (tt >= a.T || c0 + col >= a.Nout) continue;
+      float v[NSETS];
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const float* src = part + ((uint32_t)s * 8u + (uint32_t)tt) * (uint32_t)(TILE + 4) + (uint32_t)col;
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < W; ++k) sum += src[(uint32_t)k * BLK];
+        v[s] = sum;
+      }
+      float out;
+      if constexpr (NSETS == 2) {
+        out = v[0] * v[1] / (1.0f + expf(-v[0]));  // SiLU(gate) * up
+      } else {
+        out = v[0];
+      }
+      y[(size_t)tt * a.Nout + c0 + col] = f32_to_bf16_rne(out);
+    }
+  };
+
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    for (int kk = 0; kk < cntp; kk += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        if (kk + u < cnt) {
+          f32x4 dp[NSETS][V];
+          pair_sums(buf[u], wave + W * (kk + u), dp);
+#pragma unroll
+          for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int e = V * r + i;
+                acc[s][i][r] =
+                    __builtin_fmaf(scale_to_f32(buf[u].sc[s][e >> 1], e & 1, SBF16), dp[s][i][r], acc[s][i][r]);
+              }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue_next(buf[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    store_block(acc, part + (uint32_t)wave * BLK);
+    clear_acc();
+    lds_barrier();
+    finish_tile(ti);
+    lds_barrier();
+  }
+}
+
 // ---- debug kernels: the GEMM's unpack and scale decoding, materialised ----
 
 template <int BITS, bool SBF16, bool DEQUANT>
@@ -511,14 +787,13 @@ __global__ __launch_bounds__(256) void unpack_kernel(const void* wq, uint32_t p0
   const uint32_t* p0 = static_cast<const uint32_t*>(wq);
   u32x4 v;
   if constexpr (BITS == 4) {
-    v = nibbles_to_bf16(p0[(size_t)kb * N + n], 0u, 0u);
+    v = nibbles_to_bf16_il(p0[(size_t)kb * N + n], 0u);
   } else if constexpr (BITS == 5) {
     const uint32_t* p1 = reinterpret_cast<const uint32_t*>(static_cast<const char*>(wq) + p0_bytes);
-    uint32_t he, hf;
-    int5_high_bits(p1[(size_t)(kb >> 2) * N + n], (uint32_t)(kb & 3), he, hf);
-    v = nibbles_to_bf16(p0[(size_t)kb * N + n], he, hf);
+    v = nibbles_to_bf16_il(p0[(size_t)kb * N + n],
+                           __builtin_amdgcn_ubfe(p1[(size_t)(kb >> 2) * N + n], 8u * (uint32_t)(kb & 3), 8u));
   } else {
-    v = bytes_to_bf16(p0[(size_t)(2 * kb) * N + n], p0[(size_t)(2 * kb + 1) * N + n]);
+    v = bytes_to_bf16_il(p0[(size_t)(2 * kb) * N + n], p0[(size_t)(2 * kb + 1) * N + n]);
   }
   float sc = 1.0f;
   if constexpr (DEQUANT) {
@@ -528,9 +803,10 @@ __global__ __launch_bounds__(256) void unpack_kernel(const void* wq, uint32_t p0
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
+    // element e of the interleaved block is k = (e >> 1) + 4 (e & 1)
     const uint32_t bits16 = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
     const float val = __uint_as_float(bits16 << 16) - (float)Code<BITS>::offset;  // the code, exact
-    const size_t o = (size_t)(8 * kb + e) * N + n;
+    const size_t o = (size_t)(8 * kb + (e >> 1) + 4 * (e & 1)) * N + n;
     if constexpr (DEQUANT)
       static_cast<float*>(out)[o] = val * sc;
     else
@@ -585,14 +861,15 @@ int cu_count() {
   return cus;
 }
 
-// Columns per lane V: the tile count should fill the CUs in whole rounds
-// (one 8-wave workgroup per CU at a time).  Efficiency = tiles / (rounds * CUs);
-// on a tie prefer the larger V when the rounds are full (fewer, longer tiles
-// read X fewer times), else the smaller V (more CUs busy in the last round).
-int choose_v(int N, int cus, int vmax) {
-  int best_v = 1;
+// Columns per lane V in [vmin, vmax]: the tile count should fill the CUs in
+// whole rounds (one workgroup per CU at a time).  Efficiency = tiles / (rounds
+// * CUs); on a tie prefer the larger V when the rounds are full (fewer, longer
+// tiles), else the smaller V (more CUs busy in the last round).
+int choose_v(int N, int cus, int vmin, int vmax) {
+  vmin = std::min(vmin, vmax);
+  int best_v = vmin;
   double best_eff = -1.0;
-  for (int v = vmax; v >= 1; --v) {
+  for (int v = vmax; v >= vmin; --v) {
     const long tiles = (N + 16L * v - 1) / (16L * v);
     const long rounds = (tiles + cus - 1) / cus;
     const double eff = (double)tiles / (double)(rounds * cus);
@@ -620,6 +897,73 @@ hipError_t launch_one(const dev::GemmArgs& a, uint32_t lds, hipStream_t st) {
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(dev::kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+// X-resident kernel configurations (measured on MI355X): 16 waves with one
+// pair in flight each for a single round of 32-column tiles, 8 waves with two
+// pairs each otherwise.  XL covers T K <= XL * W * 512.
+struct XCfg {
+  int W, NB, XL;
+};
+constexpr XCfg kX16 = {16, 1, 5}, kX8a = {8, 2, 10}, kX8b = {8, 2, 18};
+
+// Widest tile (columns per lane) that compiles without register spills.
+constexpr int xres_vmax(int bits, int nsets, int xl) {
+  if (nsets == 2) return bits == 8 ? 1 : 2;
+  return bits == 8 ? 2 : (bits == 5 && xl == kX8b.XL ? 3 : 4);
+}
+
+template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, int XL>
+hipError_t launch_xres_one(const dev::GemmArgs& a, int grid, uint32_t lds, hipStream_t st) {
+  auto kern = dev::gemm_xres_kernel<BITS, SBF16, V, NSETS, W, NB, XL>;
+  static bool raised = false;
+  if (lds > 64u * 1024u && !raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+// v is at most xres_vmax(BITS, NSETS, XL) (the caller chose it so); only those
+// widths are instantiated.
+template <int BITS, bool SBF16, int NSETS, int W, int NB, int XL>
+hipError_t launch_xres_vx(int v, const dev::GemmArgs& a, int grid, uint32_t lds, hipStream_t st) {
+  constexpr int VM = xres_vmax(BITS, NSETS, XL);
+  if constexpr (VM >= 4) {
+    if (v >= 4) return launch_xres_one<BITS, SBF16, 4, NSETS, W, NB, XL>(a, grid, lds, st);
+  }
+  if constexpr (VM >= 3) {
+    if (v == 3) return launch_xres_one<BITS, SBF16, 3, NSETS, W, NB, XL>(a, grid, lds, st);
+  }
+  if constexpr (VM >= 2) {
+    if (v == 2) return launch_xres_one<BITS, SBF16, 2, NSETS, W, NB, XL>(a, grid, lds, st);
+  }
+  return launch_xres_one<BITS, SBF16, 1, NSETS, W, NB, XL>(a, grid, lds, st);
+}
+
+template <int BITS, bool SBF16, int NSETS>
+hipError_t launch_xres_v(const XCfg& c, int v, const dev::GemmArgs& a, int grid, uint32_t lds, hipStream_t st) {
+  if (c.W == kX16.W) {
+    if constexpr (NSETS == 1) return launch_xres_vx<BITS, SBF16, 1, kX16.W, kX16.NB, kX16.XL>(v, a, grid, lds, st);
+  }
+  if (c.XL == kX8a.XL) return launch_xres_vx<BITS, SBF16, NSETS, kX8a.W, kX8a.NB, kX8a.XL>(v, a, grid, lds, st);
+  return launch_xres_vx<BITS, SBF16, NSETS, kX8b.W, kX8b.NB, kX8b.XL>(v, a, grid, lds, st);
+}
+
+template <int NSETS>
+hipError_t launch_xres(const Format& f, const XCfg& c, int v, const dev::GemmArgs& a, int grid, uint32_t lds,
+                       hipStream_t st) {
+  if (f.bits == 4)
+    return f.scale_bf16 ? launch_xres_v<4, true, NSETS>(c, v, a, grid, lds, st)
+                        : launch_xres_v<4, false, NSETS>(c, v, a, grid, lds, st);
+  if (f.bits == 5)
+    return f.scale_bf16 ? launch_xres_v<5, true, NSETS>(c, v, a, grid, lds, st)
+                        : launch_xres_v<5, false, NSETS>(c, v, a, grid, lds, st);
+  return f.scale_bf16 ? launch_xres_v<8, true, NSETS>(c, v, a, grid, lds, st)
+                      : launch_xres_v<8, false, NSETS>(c, v, a, grid, lds, st);
 }
 
 template <int BITS, bool SBF16, int NSETS, bool DYN>
@@ -673,23 +1017,63 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     return NGQ_ERR_UNSUPPORTED;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, wq, wb0 + wb1) || overlaps(y, yb, scales, sb)) return NGQ_ERR_ARG;
 
-  const int vmax = nsets == 1 ? 4 : 2;
-  const int v = choose_v(Nout, cu_count(), vmax);
+  const int cus = cu_count();
+  // Tiles of at least 32 columns where N allows: a 16-column tile reads 64 of
+  // every 128 weight bytes of a row per cache line, and streams at about half
+  // the rate (measured).
+  const int vmin = Nout >= 32 ? 2 : 1;
+  const long xchunks = (long)T * K / 8;
+  const int pairs = (K / kGroup + 1) / 2;
+  const int v_pp = choose_v(Nout, cus, vmin, nsets == 1 ? 4 : 2);  // per-pair-X kernel
+  const long tiles_pp = (Nout + 16L * v_pp - 1) / (16L * v_pp);
+  // Kernel choice (measured on MI355X):
+  //  - one round of tiles, one output set and the per-pair-X kernel's blocks
+  //    fit in LDS: per-pair X with dynamic pair assignment, except for
+  //    32-column tiles, where 16 waves of the X-resident kernel are faster;
+  //  - otherwise the X-resident kernel with 8 waves when X fits in LDS;
+  //  - otherwise per-pair X (dynamic, or static ranges for very long K).
+  XCfg xc = kX8a;
+  bool xres = false;
+  int v = v_pp;
+  uint32_t lds = 0;
+  const bool one_round = nsets == 1 && tiles_pp <= cus && dev::Smem::bytes(true, pairs, nsets, 16 * v_pp) <= kMaxLds;
+  if (K > 0 && one_round && v_pp == 2 && xchunks <= (long)kX16.XL * kX16.W * 64 &&
+      dev::XSmem::bytes(T, K, kX16.W, nsets, 32) <= kMaxLds) {
+    xres = true;
+    xc = kX16;
+    lds = dev::XSmem::bytes(T, K, kX16.W, nsets, 32);
+  } else if (K > 0 && !one_round && xchunks <= (long)kX8b.XL * kX8b.W * 64) {
+    xc = xchunks <= (long)kX8a.XL * kX8a.W * 64 ? kX8a : kX8b;
+    const int vx = choose_v(Nout, cus, vmin, xres_vmax(f.bits, nsets, xc.XL));
+    const uint32_t lx = dev::XSmem::bytes(T, K, xc.W, nsets, 16 * vx);
+    if (lx <= kMaxLds) {
+      xres = true;
+      v = vx;
+      lds = lx;
+    }
+  }
   dev::GemmArgs a;
   a.x = x; a.wq = wq; a.scales = scales; a.y = y;
   a.T = T; a.K = K; a.Nout = Nout; a.Ncols = Ncols; a.up_off = nsets == 2 ? Nout : 0;
   a.G = K / kGroup;
-  a.pairs = (a.G + 1) / 2;
+  a.pairs = pairs;
   a.ppw = (a.pairs + dev::kWaves - 1) / dev::kWaves;
   a.ntiles = (Nout + 16 * v - 1) / (16 * v);
   a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (xres) {
+    const int per = (a.pairs + xc.W - 1) / xc.W;
+    a.ppw = (per + xc.NB - 1) / xc.NB * xc.NB;
+    const int grid = std::min(a.ntiles, cus);
+    e = nsets == 1 ? launch_xres<1>(f, xc, v, a, grid, lds, st) : launch_xres<2>(f, xc, v, a, grid, lds, st);
+    return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+  }
   // Dynamic pair assignment needs one partial-sum block per pair in LDS; very
   // long K falls back to static ranges (one block per wave).
   const uint32_t lds_dyn = dev::Smem::bytes(true, a.pairs, nsets, 16 * v);
   const bool dyn = lds_dyn <= kMaxLds;
-  const uint32_t lds = dyn ? lds_dyn : dev::Smem::bytes(false, a.pairs, nsets, 16 * v);
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
+  lds = dyn ? lds_dyn : dev::Smem::bytes(false, a.pairs, nsets, 16 * v);
   if (nsets == 1)
     e = dyn ? launch_fmt<1, true>(f, v, a, lds, st) : launch_fmt<1, false>(f, v, a, lds, st);
   else
