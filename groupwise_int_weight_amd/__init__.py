@@ -28,6 +28,7 @@ NGQ_INT4, NGQ_INT5, NGQ_INT8 = 4, 5, 8
 NGQ_SCALE_BF16 = 0x100
 NGQ_GROUP = 64
 NGQ_MAX_T = 8
+NGQ_KERNEL_AUTO, NGQ_KERNEL_PERPAIR_DYN, NGQ_KERNEL_PERPAIR_STATIC, NGQ_KERNEL_XRES16, NGQ_KERNEL_XRES8 = 0, 1, 2, 3, 4
 
 # Every function the header declares, with its ctypes signature.
 _SIZE = ctypes.c_size_t
@@ -43,6 +44,7 @@ SIGNATURES = {
     "ngq_dequant_f32": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR]),
     "ngq_rms_rescale": (_INT, [_INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
+    "ngq_debug_force_kernel": (_INT, [_INT]),
     "ngq_strerror": (ctypes.c_char_p, [_INT]),
     "ngq_version": (_INT, []),
 }
@@ -208,8 +210,18 @@ def ngq_stream_read(buf, sink, stream=None):
                                  _stream(stream)), "ngq_stream_read")
 
 
+def ngq_debug_force_kernel(path: int) -> int:
+    """Force a kernel path for later calls (NGQ_KERNEL_AUTO restores the
+    per-shape choice); returns the previous setting."""
+    prev = int(lib().ngq_debug_force_kernel(int(path)))
+    if prev < 0:
+        raise NgqError(prev, "ngq_debug_force_kernel")
+    return prev
+
+
 __all__ = [
     "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
+    "ngq_debug_force_kernel",
     "ngq_packed_bytes", "ngq_scale_bytes", "ngq_strerror", "ngq_version", "NgqError", "NgqLibraryMissing",
     "lib", "SIGNATURES",
 ]

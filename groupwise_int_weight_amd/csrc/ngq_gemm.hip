@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "ngq_internal.h"
 
@@ -850,6 +851,10 @@ namespace {
 
 constexpr uint32_t kMaxLds = 160u * 1024u;  // LDS of one CDNA4 workgroup
 
+// Kernel path forced by ngq_debug_force_kernel (NGQ_KERNEL_AUTO: the library
+// chooses per shape).
+std::atomic<int> kernel_override{NGQ_KERNEL_AUTO};
+
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -1026,31 +1031,44 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   const int pairs = (K / kGroup + 1) / 2;
   const int v_pp = choose_v(Nout, cus, vmin, nsets == 1 ? 4 : 2);  // per-pair-X kernel
   const long tiles_pp = (Nout + 16L * v_pp - 1) / (16L * v_pp);
+  const bool pp_dyn_fits = dev::Smem::bytes(true, pairs, nsets, 16 * v_pp) <= kMaxLds;
+  // An X-resident configuration for this shape: its tile width and LDS, or
+  // false when X does not fit or the prologue does not cover it.
+  auto xres_fits = [&](const XCfg& c, int& vx, uint32_t& lx) -> bool {
+    if (K == 0 || (nsets == 2 && c.W == kX16.W) || xchunks > (long)c.XL * c.W * 64) return false;
+    vx = c.W == kX16.W ? std::min(v_pp, xres_vmax(f.bits, nsets, c.XL))
+                       : choose_v(Nout, cus, vmin, xres_vmax(f.bits, nsets, c.XL));
+    lx = dev::XSmem::bytes(T, K, c.W, nsets, 16 * vx);
+    return lx <= kMaxLds;
+  };
+  const XCfg x8 = xchunks <= (long)kX8a.XL * kX8a.W * 64 ? kX8a : kX8b;
   // Kernel choice (measured on MI355X):
   //  - one round of tiles, one output set and the per-pair-X kernel's blocks
   //    fit in LDS: per-pair X with dynamic pair assignment, except for
   //    32-column tiles, where 16 waves of the X-resident kernel are faster;
   //  - otherwise the X-resident kernel with 8 waves when X fits in LDS;
   //  - otherwise per-pair X (dynamic, or static ranges for very long K).
-  XCfg xc = kX8a;
-  bool xres = false;
-  int v = v_pp;
-  uint32_t lds = 0;
-  const bool one_round = nsets == 1 && tiles_pp <= cus && dev::Smem::bytes(true, pairs, nsets, 16 * v_pp) <= kMaxLds;
-  if (K > 0 && one_round && v_pp == 2 && xchunks <= (long)kX16.XL * kX16.W * 64 &&
-      dev::XSmem::bytes(T, K, kX16.W, nsets, 32) <= kMaxLds) {
-    xres = true;
-    xc = kX16;
-    lds = dev::XSmem::bytes(T, K, kX16.W, nsets, 32);
-  } else if (K > 0 && !one_round && xchunks <= (long)kX8b.XL * kX8b.W * 64) {
-    xc = xchunks <= (long)kX8a.XL * kX8a.W * 64 ? kX8a : kX8b;
-    const int vx = choose_v(Nout, cus, vmin, xres_vmax(f.bits, nsets, xc.XL));
-    const uint32_t lx = dev::XSmem::bytes(T, K, xc.W, nsets, 16 * vx);
-    if (lx <= kMaxLds) {
-      xres = true;
-      v = vx;
-      lds = lx;
-    }
+  int path = kernel_override.load(std::memory_order_relaxed);
+  XCfg xc = x8;
+  int v = v_pp, vx = 0;
+  uint32_t lx = 0;
+  if (path == NGQ_KERNEL_AUTO) {
+    const bool one_round = nsets == 1 && tiles_pp <= cus && pp_dyn_fits;
+    if (one_round && v_pp == 2 && xres_fits(kX16, vx, lx))
+      path = NGQ_KERNEL_XRES16;
+    else if (!one_round && xres_fits(x8, vx, lx))
+      path = NGQ_KERNEL_XRES8;
+    else
+      path = pp_dyn_fits ? NGQ_KERNEL_PERPAIR_DYN : NGQ_KERNEL_PERPAIR_STATIC;
+  } else if (path == NGQ_KERNEL_XRES16 || path == NGQ_KERNEL_XRES8) {
+    if (!xres_fits(path == NGQ_KERNEL_XRES16 ? kX16 : x8, vx, lx)) return NGQ_ERR_UNSUPPORTED;
+  } else if (path == NGQ_KERNEL_PERPAIR_DYN && !pp_dyn_fits) {
+    return NGQ_ERR_UNSUPPORTED;
+  }
+  const bool xres = path == NGQ_KERNEL_XRES16 || path == NGQ_KERNEL_XRES8;
+  if (xres) {
+    xc = path == NGQ_KERNEL_XRES16 ? kX16 : x8;
+    v = vx;
   }
   dev::GemmArgs a;
   a.x = x; a.wq = wq; a.scales = scales; a.y = y;
@@ -1066,14 +1084,13 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     const int per = (a.pairs + xc.W - 1) / xc.W;
     a.ppw = (per + xc.NB - 1) / xc.NB * xc.NB;
     const int grid = std::min(a.ntiles, cus);
-    e = nsets == 1 ? launch_xres<1>(f, xc, v, a, grid, lds, st) : launch_xres<2>(f, xc, v, a, grid, lds, st);
+    e = nsets == 1 ? launch_xres<1>(f, xc, v, a, grid, lx, st) : launch_xres<2>(f, xc, v, a, grid, lx, st);
     return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
   }
   // Dynamic pair assignment needs one partial-sum block per pair in LDS; very
-  // long K falls back to static ranges (one block per wave).
-  const uint32_t lds_dyn = dev::Smem::bytes(true, a.pairs, nsets, 16 * v);
-  const bool dyn = lds_dyn <= kMaxLds;
-  lds = dyn ? lds_dyn : dev::Smem::bytes(false, a.pairs, nsets, 16 * v);
+  // long K uses static ranges (one block per wave).
+  const bool dyn = path == NGQ_KERNEL_PERPAIR_DYN;
+  const uint32_t lds = dev::Smem::bytes(dyn, a.pairs, nsets, 16 * v);
   if (nsets == 1)
     e = dyn ? launch_fmt<1, true>(f, v, a, lds, st) : launch_fmt<1, false>(f, v, a, lds, st);
   else
@@ -1142,4 +1159,9 @@ extern "C" int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* 
   hipLaunchKernelGGL(dev::stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      static_cast<const dev::u32x4*>(buf), n16, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
+extern "C" int ngq_debug_force_kernel(int path) {
+  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_XRES8) return NGQ_ERR_ARG;
+  return kernel_override.exchange(path);
 }

@@ -128,6 +128,20 @@ int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* 
 int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const void* scales, float* w,
                     void* stream);
 
+/* Debug export: force the kernel path of ngq_gemm / ngq_swiglu_gemm for every
+ * later call in the process (tests use it to run each path on the same
+ * shapes).  NGQ_KERNEL_AUTO restores the per-shape choice.  A forced path
+ * that cannot serve a shape (X or the partial sums do not fit in LDS, or the
+ * 16-wave kernel with the SwiGLU epilogue) makes those calls return
+ * NGQ_ERR_UNSUPPORTED.  Returns the previous setting, or NGQ_ERR_ARG for an
+ * unknown path.  Not thread-safe with respect to calls that are running. */
+#define NGQ_KERNEL_AUTO 0
+#define NGQ_KERNEL_PERPAIR_DYN 1    /* X per pair, pairs handed out dynamically */
+#define NGQ_KERNEL_PERPAIR_STATIC 2 /* X per pair, static pair ranges per wave */
+#define NGQ_KERNEL_XRES16 3         /* X resident in LDS, 16 waves, one pair each */
+#define NGQ_KERNEL_XRES8 4          /* X resident in LDS, 8 waves, two pairs each */
+int ngq_debug_force_kernel(int path);
+
 /* Bandwidth calibration: stream `bytes` (a multiple of 16) from device memory
  * `buf` with 128-bit loads and write one word per workgroup to `sink`
  * (device, at least 16384 bytes) so the reads cannot be elided.  Used by the

@@ -174,6 +174,15 @@ def test_rms_rescale_empty_is_no_op(ngq):
     assert L.ngq_rms_rescale(3, 0, None, None, None) == 0
 
 
+def test_force_kernel_roundtrip(ngq):
+    """The kernel-path override is host state only: set, read back, reject."""
+    prev = ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_XRES8)
+    assert ngq.ngq_debug_force_kernel(prev) == ngq.NGQ_KERNEL_XRES8
+    assert ngq.lib().ngq_debug_force_kernel(9) == ngq.NGQ_ERR_ARG
+    assert ngq.lib().ngq_debug_force_kernel(-1) == ngq.NGQ_ERR_ARG
+    assert ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_AUTO) == prev
+
+
 def test_debug_exports_reject_bad_arguments(ngq):
     L = ngq.lib()
     assert L.ngq_unpack_codes(100, 4, 4, 64, W, Y, None) == -2
