@@ -79,8 +79,9 @@ class Rotation:
 
 def time_steps(launch, replicas, steps, warmup):
     """Average GPU time of one launch: `warmup` eager launches, then exactly
-    `steps` launches (rotating through the replicas) captured in one HIP graph
-    and replayed once between two events on the capturing stream.  The graph
+    `steps` launches (rotating through the replicas) captured in one HIP graph,
+    replayed twice untimed and once between two events on the capturing
+    stream.  The graph
     removes the host's per-launch cost (~10 us through Python), so the events
     bracket back-to-back kernels, as a serving loop would replay them."""
     import torch
@@ -92,7 +93,8 @@ def time_steps(launch, replicas, steps, warmup):
     with torch.cuda.graph(g):
         for i in range(steps):
             launch(i % replicas)
-    g.replay()  # untimed: first replay uploads the graph
+    g.replay()  # untimed: the first replay uploads the graph
+    g.replay()  # untimed: settles clocks after the preceding work
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)

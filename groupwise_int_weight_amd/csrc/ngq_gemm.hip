@@ -90,12 +90,35 @@ __device__ __forceinline__ void load_words(uint32_t* d, __amdgpu_buffer_rsrc_t r
 // 128 + u.  hb: the block's eight 5th bits (bit i for k = i), 0 for int4; they
 // are spread to bits 4..7 (k 0..3) and 20..23 (k 4..7) and shifted into
 // place with the nibbles.
-__device__ __forceinline__ u32x4 nibbles_to_bf16_il(uint32_t w, uint32_t hb) {
+// The masks come in as values the compiler cannot fold (a kernel argument
+// and a vector register): with two literal operands, or two scalar ones, it
+// splits each and-or in two, since a three-operand VALU instruction takes no
+// literal and at most one scalar operand on this target.
+struct UnpackMasks {
+  uint32_t nib;   // 0x000F000F
+  uint32_t base;  // 0x43004300
+  uint32_t hi;    // 0x00100010
+};
+constexpr UnpackMasks kMasks = {0x000F000Fu, 0x43004300u, 0x00100010u};
+
+__device__ __forceinline__ u32x4 nibbles_to_bf16_il(uint32_t w, const UnpackMasks& mk) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = ((w >> (4 * j)) & mk.nib) | mk.base;
+  return r;
+}
+
+// int5: the high bits are first merged into the base pattern, then the
+// nibbles; each merge is one three-input bitwise op ((a & b) | c, truth
+// table 0xEA), so an output register costs two shifts and two ops.
+__device__ __forceinline__ u32x4 nibbles5_to_bf16_il(uint32_t w, uint32_t hb, const UnpackMasks& mk) {
   const uint32_t hs = ((hb & 0x0Fu) << 4) | ((hb & 0xF0u) << 16);
   u32x4 r;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    r[j] = ((w >> (4 * j)) & 0x000F000Fu) | 0x43004300u | ((hs >> j) & 0x00100010u);
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t hi = __builtin_amdgcn_bitop3_b32(hs >> j, mk.hi, mk.base, 0xEA);
+    r[j] = __builtin_amdgcn_bitop3_b32(w >> (4 * j), mk.nib, hi, 0xEA);
+  }
   return r;
 }
 
@@ -156,6 +179,7 @@ struct GemmArgs {
   int ppw;     // pairs per wave
   int ntiles;  // workgroups
   uint32_t p0_bytes, p1_bytes, s_bytes, x_bytes;
+  uint32_t mask_nib, mask_base, mask_hi;  // the unpack constants (UnpackMasks)
 };
 
 template <int BITS, int V, int NSETS>
@@ -222,6 +246,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  // the base pattern lives in a vector register (an empty asm hides its
+  // value), so each and-or takes one scalar and one vector constant
+  uint32_t vbase = a.mask_base;
+  asm volatile("" : "+v"(vbase));
+  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
 
   const uint32_t rowb = (uint32_t)a.Ncols * 4u;  // bytes of one packed row
   // Within a pair (16 k-blocks of 8 k), k-slot q of step s reads k-block
@@ -356,12 +385,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
         for (int i = 0; i < V; ++i) {
           u32x4 av;
           if constexpr (BITS == 4) {
-            av = nibbles_to_bf16_il(buf.a[s][st][i], 0u);
+            av = nibbles_to_bf16_il(buf.a[s][st][i], mk);
           } else if constexpr (BITS == 5) {
             // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
             const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
                                                                                  8u * (uint32_t)(q & 1), 8u);
-            av = nibbles_to_bf16_il(buf.a[s][st][i], hb);
+            av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, mk);
           } else {
             av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
           }
@@ -557,6 +586,11 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  // the base pattern lives in a vector register (an empty asm hides its
+  // value), so each and-or takes one scalar and one vector constant
+  uint32_t vbase = a.mask_base;
+  asm volatile("" : "+v"(vbase));
+  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
 
   const uint32_t rowb = (uint32_t)a.Ncols * 4u;
   const uint32_t lane_kb = 8u * (uint32_t)(q >> 1) + (uint32_t)(q & 1);
@@ -687,12 +721,12 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
         for (int i = 0; i < V; ++i) {
           u32x4 av;
           if constexpr (BITS == 4) {
-            av = nibbles_to_bf16_il(buf.a[s][st][i], 0u);
+            av = nibbles_to_bf16_il(buf.a[s][st][i], mk);
           } else if constexpr (BITS == 5) {
             // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
             const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
                                                                                  8u * (uint32_t)(q & 1), 8u);
-            av = nibbles_to_bf16_il(buf.a[s][st][i], hb);
+            av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, mk);
           } else {
             av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
           }
@@ -788,11 +822,11 @@ __global__ __launch_bounds__(256) void unpack_kernel(const void* wq, uint32_t p0
   const uint32_t* p0 = static_cast<const uint32_t*>(wq);
   u32x4 v;
   if constexpr (BITS == 4) {
-    v = nibbles_to_bf16_il(p0[(size_t)kb * N + n], 0u);
+    v = nibbles_to_bf16_il(p0[(size_t)kb * N + n], kMasks);
   } else if constexpr (BITS == 5) {
     const uint32_t* p1 = reinterpret_cast<const uint32_t*>(static_cast<const char*>(wq) + p0_bytes);
-    v = nibbles_to_bf16_il(p0[(size_t)kb * N + n],
-                           __builtin_amdgcn_ubfe(p1[(size_t)(kb >> 2) * N + n], 8u * (uint32_t)(kb & 3), 8u));
+    v = nibbles5_to_bf16_il(p0[(size_t)kb * N + n],
+                            __builtin_amdgcn_ubfe(p1[(size_t)(kb >> 2) * N + n], 8u * (uint32_t)(kb & 3), 8u), kMasks);
   } else {
     v = bytes_to_bf16_il(p0[(size_t)(2 * kb) * N + n], p0[(size_t)(2 * kb + 1) * N + n]);
   }
@@ -1078,6 +1112,7 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   a.ppw = (a.pairs + dev::kWaves - 1) / dev::kWaves;
   a.ntiles = (Nout + 16 * v - 1) / (16 * v);
   a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
+  a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (xres) {
