@@ -938,13 +938,13 @@ hipError_t launch_one(const dev::GemmArgs& a, uint32_t lds, hipStream_t st) {
   return hipGetLastError();
 }
 
-// X-resident kernel configurations (measured on MI355X): 16 waves with one
+// X-resident kernel configurations (measured on MI355X): 14 waves with one
 // pair in flight each for a single round of 32-column tiles, 8 waves with two
 // pairs each otherwise.  XL covers T K <= XL * W * 512.
 struct XCfg {
   int W, NB, XL;
 };
-constexpr XCfg kX16 = {16, 1, 5}, kX8a = {8, 2, 10}, kX8b = {8, 2, 18};
+constexpr XCfg kX14 = {14, 1, 6}, kX8a = {8, 2, 10}, kX8b = {8, 2, 18};
 
 // Widest tile (columns per lane) that compiles without register spills.
 constexpr int xres_vmax(int bits, int nsets, int xl) {
@@ -985,8 +985,8 @@ hipError_t launch_xres_vx(int v, const dev::GemmArgs& a, int grid, uint32_t lds,
 
 template <int BITS, bool SBF16, int NSETS>
 hipError_t launch_xres_v(const XCfg& c, int v, const dev::GemmArgs& a, int grid, uint32_t lds, hipStream_t st) {
-  if (c.W == kX16.W) {
-    if constexpr (NSETS == 1) return launch_xres_vx<BITS, SBF16, 1, kX16.W, kX16.NB, kX16.XL>(v, a, grid, lds, st);
+  if (c.W == kX14.W) {
+    if constexpr (NSETS == 1) return launch_xres_vx<BITS, SBF16, 1, kX14.W, kX14.NB, kX14.XL>(v, a, grid, lds, st);
   }
   if (c.XL == kX8a.XL) return launch_xres_vx<BITS, SBF16, NSETS, kX8a.W, kX8a.NB, kX8a.XL>(v, a, grid, lds, st);
   return launch_xres_vx<BITS, SBF16, NSETS, kX8b.W, kX8b.NB, kX8b.XL>(v, a, grid, lds, st);
@@ -1069,8 +1069,8 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   // An X-resident configuration for this shape: its tile width and LDS, or
   // false when X does not fit or the prologue does not cover it.
   auto xres_fits = [&](const XCfg& c, int& vx, uint32_t& lx) -> bool {
-    if (K == 0 || (nsets == 2 && c.W == kX16.W) || xchunks > (long)c.XL * c.W * 64) return false;
-    vx = c.W == kX16.W ? std::min(v_pp, xres_vmax(f.bits, nsets, c.XL))
+    if (K == 0 || (nsets == 2 && c.W == kX14.W) || xchunks > (long)c.XL * c.W * 64) return false;
+    vx = c.W == kX14.W ? std::min(v_pp, xres_vmax(f.bits, nsets, c.XL))
                        : choose_v(Nout, cus, vmin, xres_vmax(f.bits, nsets, c.XL));
     lx = dev::XSmem::bytes(T, K, c.W, nsets, 16 * vx);
     return lx <= kMaxLds;
@@ -1079,7 +1079,7 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   // Kernel choice (measured on MI355X):
   //  - one round of tiles, one output set and the per-pair-X kernel's blocks
   //    fit in LDS: per-pair X with dynamic pair assignment, except for
-  //    32-column tiles, where 16 waves of the X-resident kernel are faster;
+  //    32-column tiles, where 14 waves of the X-resident kernel are faster;
   //  - otherwise the X-resident kernel with 8 waves when X fits in LDS;
   //  - otherwise per-pair X (dynamic, or static ranges for very long K).
   int path = kernel_override.load(std::memory_order_relaxed);
@@ -1088,20 +1088,20 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   uint32_t lx = 0;
   if (path == NGQ_KERNEL_AUTO) {
     const bool one_round = nsets == 1 && tiles_pp <= cus && pp_dyn_fits;
-    if (one_round && v_pp == 2 && xres_fits(kX16, vx, lx))
-      path = NGQ_KERNEL_XRES16;
+    if (one_round && v_pp == 2 && xres_fits(kX14, vx, lx))
+      path = NGQ_KERNEL_XRES14;
     else if (!one_round && xres_fits(x8, vx, lx))
       path = NGQ_KERNEL_XRES8;
     else
       path = pp_dyn_fits ? NGQ_KERNEL_PERPAIR_DYN : NGQ_KERNEL_PERPAIR_STATIC;
-  } else if (path == NGQ_KERNEL_XRES16 || path == NGQ_KERNEL_XRES8) {
-    if (!xres_fits(path == NGQ_KERNEL_XRES16 ? kX16 : x8, vx, lx)) return NGQ_ERR_UNSUPPORTED;
+  } else if (path == NGQ_KERNEL_XRES14 || path == NGQ_KERNEL_XRES8) {
+    if (!xres_fits(path == NGQ_KERNEL_XRES14 ? kX14 : x8, vx, lx)) return NGQ_ERR_UNSUPPORTED;
   } else if (path == NGQ_KERNEL_PERPAIR_DYN && !pp_dyn_fits) {
     return NGQ_ERR_UNSUPPORTED;
   }
-  const bool xres = path == NGQ_KERNEL_XRES16 || path == NGQ_KERNEL_XRES8;
+  const bool xres = path == NGQ_KERNEL_XRES14 || path == NGQ_KERNEL_XRES8;
   if (xres) {
-    xc = path == NGQ_KERNEL_XRES16 ? kX16 : x8;
+    xc = path == NGQ_KERNEL_XRES14 ? kX14 : x8;
     v = vx;
   }
   dev::GemmArgs a;

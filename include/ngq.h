@@ -132,13 +132,13 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
  * later call in the process (tests use it to run each path on the same
  * shapes).  NGQ_KERNEL_AUTO restores the per-shape choice.  A forced path
  * that cannot serve a shape (X or the partial sums do not fit in LDS, or the
- * 16-wave kernel with the SwiGLU epilogue) makes those calls return
+ * 14-wave kernel with the SwiGLU epilogue) makes those calls return
  * NGQ_ERR_UNSUPPORTED.  Returns the previous setting, or NGQ_ERR_ARG for an
  * unknown path.  Not thread-safe with respect to calls that are running. */
 #define NGQ_KERNEL_AUTO 0
 #define NGQ_KERNEL_PERPAIR_DYN 1    /* X per pair, pairs handed out dynamically */
 #define NGQ_KERNEL_PERPAIR_STATIC 2 /* X per pair, static pair ranges per wave */
-#define NGQ_KERNEL_XRES16 3         /* X resident in LDS, 16 waves, one pair each */
+#define NGQ_KERNEL_XRES14 3         /* X resident in LDS, 14 waves, one pair each */
 #define NGQ_KERNEL_XRES8 4          /* X resident in LDS, 8 waves, two pairs each */
 int ngq_debug_force_kernel(int path);
 

@@ -1,7 +1,7 @@
 """Every kernel path of ngq_gemm / ngq_swiglu_gemm against the oracle.
 
 The library picks a kernel per shape (per-pair X with dynamic or static pair
-assignment, X resident in LDS with 16 or 8 waves).  Here each path is forced
+assignment, X resident in LDS with 14 or 8 waves).  Here each path is forced
 through the debug export and run on the same ragged shapes: odd group counts
 (the last group pair has one group), N not a multiple of the tile, several
 tiles per workgroup, long K, every bit width and both scale types.  A path
@@ -18,7 +18,7 @@ from tests.test_gpu_parity import dev_bf16, dev_scales, dev_u8, host_bits, make
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-PATHS = {1: "perpair_dyn", 2: "perpair_static", 3: "xres16", 4: "xres8"}
+PATHS = {1: "perpair_dyn", 2: "perpair_static", 3: "xres14", 4: "xres8"}
 
 
 @pytest.fixture(scope="module")
