@@ -204,9 +204,11 @@ def parity_check(ngq, rot, y_dev):
 def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8)):
     """The stacked-layer sweep: `layers` layers with distinct weights (QK, gate/
     value, gate/up + SwiGLU, down, RMS rescale each), chained through the
-    rescaled down output.  Timed per full pass from x0, eager (one library call
-    at a time from Python) and as a captured graph replayed; the weights far
-    exceed the caches, so every pass streams them from HBM."""
+    rescaled down output.  Timed per full pass from x0: eager (one library call
+    at a time from Python) and as a captured graph, every call in order on one
+    stream; and, for comparison, as a graph with QK and gate/value on side
+    streams beside gate/up and down.  The weights far exceed the caches, so
+    every pass streams them from HBM."""
     import numpy as np
     import torch
 
@@ -215,40 +217,46 @@ def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8)):
 
     weights = synthetic.device_stack(layers, ngq.ngq_packed_bytes, seed=0)
     out = []
-    for T in Ts:
-        st = Stack(weights, T)
-        x0 = torch.from_numpy(synthetic.stack_x0(T).view(np.int16)).to("cuda").view(torch.bfloat16)
-        cur = torch.cuda.current_stream()
-        st.forward(x0, cur.cuda_stream)  # warm-up pass
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(passes):
-            st.forward(x0, cur.cuda_stream)
-        e1.record()
-        e1.synchronize()
-        eager_ms = e0.elapsed_time(e1) / passes
-        eager_x = st.x.clone()
+
+    def time_graph(st, x0):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            st.forward(x0, torch.cuda.current_stream().cuda_stream)
+            st.forward(x0)
         g.replay()  # untimed upload
+        g.replay()
         torch.cuda.synchronize()
-        same = bool(torch.equal(st.x, eager_x))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(passes):
             g.replay()
         e1.record()
         e1.synchronize()
-        graph_ms = e0.elapsed_time(e1) / passes
-        same = same and bool(torch.equal(st.x, eager_x))
-        del g
+        return e0.elapsed_time(e1) / passes, st.x.clone()
+
+    for T in Ts:
+        x0 = torch.from_numpy(synthetic.stack_x0(T).view(np.int16)).to("cuda").view(torch.bfloat16)
+        st = Stack(weights, T)
+        st.forward(x0)  # warm-up pass
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(passes):
+            st.forward(x0)
+        e1.record()
+        e1.synchronize()
+        eager_ms = e0.elapsed_time(e1) / passes
+        eager_x = st.x.clone()
+        graph_ms, gx = time_graph(st, x0)
+        conc = Stack(weights, T, concurrent=True)
+        conc_ms, cx = time_graph(conc, x0)
+        same = bool(torch.equal(gx, eager_x)) and bool(torch.equal(cx, eager_x))
         b = layer_bytes(T, ngq.ngq_packed_bytes) * layers
         out.append({"T": T, "layers": layers, "passes": passes,
                     "eager_us_per_layer": eager_ms * 1e3 / layers, "graph_us_per_layer": graph_ms * 1e3 / layers,
+                    "side_streams_graph_us_per_layer": conc_ms * 1e3 / layers,
                     "graph_ms_per_pass": graph_ms, "bytes_per_pass": b, "GBps": b / graph_ms / 1e6,
                     "pct_peak": 100 * b / graph_ms / 1e6 / PEAK_GBS, "graph_matches_eager": same})
-        del st
+        del st, conc
     del weights
     torch.cuda.empty_cache()
     return out

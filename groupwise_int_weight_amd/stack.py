@@ -10,7 +10,8 @@ The projections are those the NInfer-4090 V3 topic ("What V3 did") routes at
 T=8; only the down output feeds the next layer, the q and v outputs are
 written and not used (they stand for the attention inputs, which are outside
 this library).  Each step is one library call through the C ABI with raw
-device pointers; this module only orders the calls and keeps the buffers.
+device pointers; this module only orders the calls (on up to three streams)
+and keeps the buffers.
 """
 from __future__ import annotations
 
@@ -39,21 +40,30 @@ def layer_bytes(T: int, packed_bytes) -> int:
 
 class Stack:
     """Layers of device weights (from `layers`: a list of {name: (packed, scales)})
-    and the work buffers of one token count T."""
+    and the work buffers of one token count T.
 
-    def __init__(self, layers, T: int, device="cuda"):
+    By default every call runs in order on the main stream.  With `concurrent`
+    the QK and gate/value projections, which only read x, run on two side
+    streams beside the gate/up and down projections, and the main stream waits
+    for them before the rescale overwrites x.  On MI355X that is slower: each
+    projection kernel keeps one persistent workgroup per CU, and a kernel
+    running beside it delays the workgroups that own its tiles."""
+
+    def __init__(self, layers, T: int, device="cuda", concurrent: bool = False):
         import torch
 
         if not 1 <= T <= 8:
             raise ValueError("T must be in 1..8")
         self.T = T
         self.layers = layers
+        self.concurrent = concurrent
         bf = torch.bfloat16
         self.q = torch.empty((T, 8192), dtype=bf, device=device)
         self.v = torch.empty((T, 12288), dtype=bf, device=device)
         self.h = torch.empty((T, N_FF), dtype=bf, device=device)
         self.z = torch.empty((T, HIDDEN), dtype=bf, device=device)
         self.x = torch.empty((T, HIDDEN), dtype=bf, device=device)  # the running activation
+        self.side = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device)) if concurrent else ()
         self._calls = []
         for lw in layers:
             calls = []
@@ -63,27 +73,52 @@ class Stack:
                 calls.append((kind, K, N, flag, wq.data_ptr(), s.data_ptr()))
             self._calls.append(calls)
 
-    def layer(self, i: int, stream: int):
-        """Enqueue layer i on `stream` (a hipStream_t as int): x -> x."""
+    def layer(self, i: int, stream=None):
+        """Enqueue layer i (x -> x) on `stream` (a torch.cuda.Stream; the current
+        stream by default)."""
+        import torch
+
+        main = torch.cuda.current_stream() if stream is None else stream
         L = lib()
         T = self.T
         xp, qp, vp, hp, zp = (t.data_ptr() for t in (self.x, self.q, self.v, self.h, self.z))
         (_, K0, N0, f0, w0, s0), (_, K1, N1, f1, w1, s1), (_, K2, N2, f2, w2, s2), (_, K3, N3, f3, w3, s3) = \
             self._calls[i]
-        for st, where in (
-            (L.ngq_gemm(T, K0, N0, f0, NGQ_GROUP, xp, w0, s0, qp, stream), "qk"),
-            (L.ngq_gemm(T, K1, N1, f1, NGQ_GROUP, xp, w1, s1, vp, stream), "gv"),
-            (L.ngq_swiglu_gemm(T, K2, N2, f2, NGQ_GROUP, xp, w2, s2, hp, stream), "gate_up"),
-            (L.ngq_gemm(T, K3, N3, f3, NGQ_GROUP, hp, w3, s3, zp, stream), "down"),
-            (L.ngq_rms_rescale(T, HIDDEN, zp, xp, stream), "rescale"),
-        ):
+
+        def check(st, where):
             if st != 0:
                 raise NgqError(st, f"layer {i} {where}")
 
-    def forward(self, x0, stream: int, layers: int | None = None):
+        if self.concurrent:
+            x_ready = torch.cuda.Event()
+            x_ready.record(main)
+            sq, sv = self.side
+            sq.wait_event(x_ready)
+            sv.wait_event(x_ready)
+            check(L.ngq_gemm(T, K0, N0, f0, NGQ_GROUP, xp, w0, s0, qp, sq.cuda_stream), "qk")
+            check(L.ngq_gemm(T, K1, N1, f1, NGQ_GROUP, xp, w1, s1, vp, sv.cuda_stream), "gv")
+            q_done, v_done = torch.cuda.Event(), torch.cuda.Event()
+            q_done.record(sq)
+            v_done.record(sv)
+        else:
+            check(L.ngq_gemm(T, K0, N0, f0, NGQ_GROUP, xp, w0, s0, qp, main.cuda_stream), "qk")
+            check(L.ngq_gemm(T, K1, N1, f1, NGQ_GROUP, xp, w1, s1, vp, main.cuda_stream), "gv")
+        check(L.ngq_swiglu_gemm(T, K2, N2, f2, NGQ_GROUP, xp, w2, s2, hp, main.cuda_stream), "gate_up")
+        check(L.ngq_gemm(T, K3, N3, f3, NGQ_GROUP, hp, w3, s3, zp, main.cuda_stream), "down")
+        if self.concurrent:
+            main.wait_event(q_done)  # x is overwritten next: QK and gate/value must be done reading it
+            main.wait_event(v_done)
+        check(L.ngq_rms_rescale(T, HIDDEN, zp, xp, main.cuda_stream), "rescale")
+
+    def forward(self, x0, stream=None, layers: int | None = None):
         """Copy x0 (device bf16 [T][5120]) into the running activation and enqueue
-        the first `layers` layers (all by default).  Returns the activation."""
-        self.x.copy_(x0)
+        the first `layers` layers (all by default) on `stream`.  Returns the
+        activation."""
+        import torch
+
+        main = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(main):
+            self.x.copy_(x0)
         for i in range(len(self.layers) if layers is None else layers):
-            self.layer(i, stream)
+            self.layer(i, main)
         return self.x

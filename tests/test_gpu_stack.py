@@ -121,7 +121,8 @@ def test_stack_first_layer_matches_oracle(ngq, orc, T):
     st = Stack(layers, T)
     x0 = synthetic.stack_x0(T, seed=0)
     st.x.copy_(dev_bf16(x0))
-    st.layer(0, cur_stream())
+    st.layer(0)
+    torch.cuda.synchronize()
     for name, out, sbf16 in (("qk", st.q, False), ("gv", st.v, True)):
         w = synthetic.WORKLOADS[name]
         wq, s = layers[0][name]
@@ -136,17 +137,20 @@ def test_stack_first_layer_matches_oracle(ngq, orc, T):
     check_swiglu(host_bits(st.h)[:, cols], h64, g, u, f"stack swiglu T{T}")
 
 
-@pytest.mark.parametrize("T", [1, 8])
-def test_stack_chain_properties_and_graph_replay(ngq, T):
+@pytest.mark.parametrize("T,concurrent", [(1, True), (8, True), (8, False)])
+def test_stack_chain_properties_and_graph_replay(ngq, T, concurrent):
     from groupwise_int_weight_amd.stack import Stack
 
     L = 4
     layers = stack_layers(ngq, L)
-    st = Stack(layers, T)
+    st = Stack(layers, T, concurrent=concurrent)
     x0 = dev_bf16(synthetic.stack_x0(T, seed=0))
-    eager = to_host_u16(st.forward(x0, cur_stream()))
-    again = to_host_u16(st.forward(x0, cur_stream()))
+    eager = to_host_u16(st.forward(x0))
+    again = to_host_u16(st.forward(x0))
     assert np.array_equal(eager, again)  # deterministic
+    if concurrent:
+        # the side streams change only the order of independent work
+        assert np.array_equal(eager, to_host_u16(Stack(layers, T, concurrent=False).forward(x0)))
     v = bf16_bits_to_f64(eager)
     assert np.all(np.isfinite(v))
     # every row leaves the rescale with unit mean square, up to bf16 rounding
@@ -160,19 +164,18 @@ def test_stack_chain_properties_and_graph_replay(ngq, T):
     with torch.cuda.stream(side):
         st.x.copy_(x0)
         for i in range(L):  # warm-up on the capture stream
-            st.layer(i, side.cuda_stream)
+            st.layer(i, side)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        s = torch.cuda.current_stream().cuda_stream
         for i in range(L):
-            st.layer(i, s)
+            st.layer(i)
     for rep in range(3):
         st.x.copy_(x0)
         graph.replay()
         got = to_host_u16(st.x)
         assert np.array_equal(got, eager), rep
         # eager work between replays
-        st.forward(x0, cur_stream(), layers=1)
+        st.forward(x0, layers=1)
         torch.cuda.synchronize()
     assert math.isfinite(float(v.sum()))
