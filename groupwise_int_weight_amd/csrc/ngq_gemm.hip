@@ -7,13 +7,18 @@
 // single-operator timings on an RTX 4090 ("Measured data"), not a kernel; the
 // design below is written for CDNA4.
 //
-// Work decomposition.  One workgroup (8 waves) owns a tile of 16*V output
-// columns over the whole K, so no partial sum ever leaves the workgroup and the
-// result is deterministic.  The waves of a workgroup split K into contiguous
-// ranges of group pairs and meet once, at the end, in LDS.  V (1..4 columns per
-// lane) is picked per shape so that the number of tiles fills the 256 CUs in
-// whole rounds; consecutive tiles go to the same XCD (workgroup b runs on XCD
-// b % 8), so neighbouring columns that share a cache line share an L2.
+// Work decomposition.  A workgroup owns a tile of 16*V output columns over the
+// whole K (or several such tiles, one after another), so no partial sum ever
+// leaves the workgroup and the result is deterministic.  Its waves share K in
+// units of 128-k group pairs, either interleaved (wave w takes pairs w, w + W,
+// ..., so the waves move through K together) or handed out by an LDS counter,
+// and meet once per tile in LDS, where the partials are summed in a fixed
+// order.  V (1..4 columns per lane) is picked per shape so that the tiles
+// fill the 256 CUs in whole rounds, with tiles of at least 32 columns where N
+// allows; consecutive tiles go to the same XCD (workgroup b runs on XCD
+// b % 8), so neighbouring columns that share a cache line share an L2.  Two
+// kernels implement this: gemm_kernel loads each pair's X with its weights,
+// gemm_xres_kernel stages X in LDS once; the host picks one per shape.
 //
 // Inner step.  The path streams packed weights once from HBM and is bandwidth
 // bound, but at T=8 a VALU-only dot product would need ~4.5 VALU lane-ops per
@@ -464,28 +469,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
       }
     } while (pidx[0] < a.pairs);
   } else {
-    const int pbase = wave * a.ppw;
-    const int pend = min(pbase + a.ppw, a.pairs);
+    // Wave w takes pairs w, w + 12, w + 24, ...: the waves move through K
+    // together, so the chip streams a narrow band of weight rows at a time.
+    // A slot past the last pair loads nothing and adds zero.
+    auto pair_of = [&](int i) { return wave + kWaves * i; };
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      issue(buf[u], pbase + u < pend ? pbase + u : a.pairs);
+      issue(buf[u], pair_of(u));
       __builtin_amdgcn_sched_barrier(0);
     }
     int it = 0;
     for (; it + NB < a.ppw; it += NB) {
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
-        compute(buf[u], pbase + it + u);
+        compute(buf[u], pair_of(it + u));
         __builtin_amdgcn_sched_barrier(0);
-        const int nx = pbase + it + u + NB;
-        issue(buf[u], nx < pend ? nx : a.pairs);
+        issue(buf[u], pair_of(it + u + NB));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // the last (up to NB) pairs are already in flight: no more loads
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      if (it + u < a.ppw && pbase + it + u < pend) compute(buf[u], pbase + it + u);
+      if (it + u < a.ppw && pair_of(it + u) < a.pairs) compute(buf[u], pair_of(it + u));
     store_block(acc, part + (uint32_t)wave * BLK);
   }
   __syncthreads();
