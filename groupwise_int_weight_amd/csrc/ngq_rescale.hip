@@ -8,7 +8,8 @@
 // to nearest even, from the fp64 quotient, so the only difference from an
 // exact evaluation is the summation order of the squares (each square of a
 // bf16 value is exact in fp64).  The block is T x N with T <= 8 in the decode
-// path, so the kernel is latency bound; one workgroup handles one row.
+// path, so the kernel is latency bound: one workgroup handles one row, or,
+// unless the call is in place, eight workgroups share it.
 #include <hip/hip_runtime.h>
 
 #include "ngq_internal.h"
@@ -103,6 +104,49 @@ __global__ __launch_bounds__(kRowThreads) void rms_rescale_kernel(const uint16_t
   }
 }
 
+// The same result with each row spread over S workgroups (grid S x T): every
+// workgroup reads the whole row and computes the same fixed-order sum of
+// squares (so all slices use the same bits of r), then scales only its own
+// 1/S of the row.  The per-element work of a row then runs on S CUs instead
+// of one.  Not for in-place use: a slice written early could be read by
+// another workgroup's first pass.
+template <int S>
+__global__ __launch_bounds__(kRowThreads) void rms_rescale_split_kernel(const uint16_t* z, uint16_t* x, int N) {
+  const size_t row = (size_t)blockIdx.y * (size_t)N;
+  const r32x4* z8 = reinterpret_cast<const r32x4*>(z + row);
+  r32x4* x8 = reinterpret_cast<r32x4*>(x + row);
+  const int nch = N / 8;
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < nch; c += kRowThreads) {
+    const r32x4 w = z8[c];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double lo = bf16_bits_to_f64(w[j]), hi = bf16_bits_to_f64(w[j] >> 16);
+      ss += lo * lo;
+      ss += hi * hi;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  __shared__ double wsum[kRowThreads / 64];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const double tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  const double r = sqrt(tot / (double)N);
+  const int per = (nch + S - 1) / S;
+  const int c0 = blockIdx.x * per, c1 = min(c0 + per, nch);
+  for (int c = c0 + threadIdx.x; c < c1; c += kRowThreads) {
+    const r32x4 w = z8[c];
+    r32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = r > 0.0 ? f64_to_bf16_rne(bf16_bits_to_f64(w[j]) / r) : 0u;
+      const uint32_t hi = r > 0.0 ? f64_to_bf16_rne(bf16_bits_to_f64(w[j] >> 16) / r) : 0u;
+      o[j] = lo | (hi << 16);
+    }
+    x8[c] = o;
+  }
+}
+
 }  // namespace dev
 }  // namespace ngq
 
@@ -120,7 +164,10 @@ extern "C" int ngq_rms_rescale(int T, int N, const void* z, void* x, void* strea
   hipStream_t st = (hipStream_t)stream;
   const uint16_t* zi = static_cast<const uint16_t*>(z);
   uint16_t* xo = static_cast<uint16_t*>(x);
-  if (N % 8 == 0)
+  if (N % 8 == 0 && x != z && N >= 8 * 64 * 8)
+    hipLaunchKernelGGL(dev::rms_rescale_split_kernel<8>, dim3(8u, (unsigned)T), dim3(dev::kRowThreads), 0, st, zi, xo,
+                       N);
+  else if (N % 8 == 0)
     hipLaunchKernelGGL(dev::rms_rescale_kernel<true>, dim3((unsigned)T), dim3(dev::kRowThreads), 0, st, zi, xo, N);
   else
     hipLaunchKernelGGL(dev::rms_rescale_kernel<false>, dim3((unsigned)T), dim3(dev::kRowThreads), 0, st, zi, xo, N);
