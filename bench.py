@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-stack", action="store_true", help="skip the stacked-layer sweep")
     p.add_argument("--stack-layers", type=int, default=64)
     p.add_argument("--stack-passes", type=int, default=5)
+    p.add_argument("--stack-t", type=int, nargs="*", default=[1, 2, 4, 8], help="token counts of the stack sweep")
+    p.add_argument("--no-stack-side", action="store_true", help="skip the side-stream comparison graph")
     return p.parse_args()
 
 
@@ -201,7 +203,7 @@ def parity_check(ngq, rot, y_dev):
     return rep, (x, packed, scales)
 
 
-def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8)):
+def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
     """The stacked-layer sweep: `layers` layers with distinct weights (QK, gate/
     value, gate/up + SwiGLU, down, RMS rescale each), chained through the
     rescaled down output.  Timed per full pass from x0: eager (one library call
@@ -247,16 +249,20 @@ def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8)):
         eager_ms = e0.elapsed_time(e1) / passes
         eager_x = st.x.clone()
         graph_ms, gx = time_graph(st, x0)
-        conc = Stack(weights, T, concurrent=True)
-        conc_ms, cx = time_graph(conc, x0)
-        same = bool(torch.equal(gx, eager_x)) and bool(torch.equal(cx, eager_x))
+        same = bool(torch.equal(gx, eager_x))
+        conc_ms = None
+        if side:
+            conc = Stack(weights, T, concurrent=True)
+            conc_ms, cx = time_graph(conc, x0)
+            same = same and bool(torch.equal(cx, eager_x))
+            del conc
         b = layer_bytes(T, ngq.ngq_packed_bytes) * layers
         out.append({"T": T, "layers": layers, "passes": passes,
                     "eager_us_per_layer": eager_ms * 1e3 / layers, "graph_us_per_layer": graph_ms * 1e3 / layers,
-                    "side_streams_graph_us_per_layer": conc_ms * 1e3 / layers,
+                    "side_streams_graph_us_per_layer": None if conc_ms is None else conc_ms * 1e3 / layers,
                     "graph_ms_per_pass": graph_ms, "bytes_per_pass": b, "GBps": b / graph_ms / 1e6,
                     "pct_peak": 100 * b / graph_ms / 1e6 / PEAK_GBS, "graph_matches_eager": same})
-        del st, conc
+        del st
     del weights
     torch.cuda.empty_cache()
     return out
@@ -353,8 +359,17 @@ def main():
                 torch.cuda.empty_cache()
         for t in (1, 8):
             sweep.extend(run_swiglu(ngq, t, args.sweep_steps, 10))
+        wl = synthetic.WORKLOADS["qk8"]  # int8: reported, not part of the metric
+        for t in (1, 8):
+            ms_t, r, _ = run_projection(ngq, wl, t, args.sweep_steps, 10)
+            b = algorithmic_bytes(ngq, wl, t)
+            sweep.append({"workload": f"qk-shaped int8 K={wl.K} N={wl.N}", "T": t, "us": ms_t * 1e3,
+                          "GBps": b / ms_t / 1e6, "pct_peak": 100 * b / ms_t / 1e6 / PEAK_GBS})
+            del r
+            torch.cuda.empty_cache()
 
-    stack = None if args.no_stack else run_stack(ngq, args.stack_layers, args.stack_passes)
+    stack = None if args.no_stack else run_stack(ngq, args.stack_layers, args.stack_passes, tuple(args.stack_t),
+                                                 side=not args.no_stack_side)
 
     # last: its 4 GiB stream and 1 GiB copies leave the next measurement slow
     calib = {} if args.no_calibration else calibrate(ngq)

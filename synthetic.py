@@ -15,6 +15,7 @@ distributions, so these are readings):
   gv        T in 1..8, K=5120, N=12288, int5, bf16 scales U[5e-4, 1e-2]
   gate_up   T in 1..8, K=5120, N=2*17408 (gate | up), int4, fp16 scales
   down      T in 1..8, K=17408, N=5120, int4, fp16 scales
+  qk8       T in 1..8, K=5120, N=8192,  int8, fp16 scales (the QK shape in int8)
 
 Codes are uniform over the full signed range of the width, X is N(0,1)
 rounded to bf16, scales are uniform and rounded to the 16-bit scale type.
@@ -46,6 +47,8 @@ WORKLOADS = {
     "gv": Workload("gv", 5120, 12288, 5, True, 5e-4, 1e-2, 2),
     "gate_up": Workload("gate_up", 5120, 2 * 17408, 4, False, 1e-3, 2e-2, 3),
     "down": Workload("down", 17408, 5120, 4, False, 1e-3, 2e-2, 3),
+    # int8 is in the format list but in no measured workload: the QK shape
+    "qk8": Workload("qk8", 5120, 8192, 8, False, 1e-3, 2e-2, 5),
 }
 N_FF = 17408
 HIDDEN = 5120

@@ -152,7 +152,7 @@ def closed_form_rms(w):
 
 
 @pytest.mark.parametrize("name,T", [("qk", 8), ("qk", 1), ("qk", 2), ("qk", 4),
-                                    ("gv", 8), ("gv", 1), ("gv", 2), ("gv", 4)])
+                                    ("gv", 8), ("gv", 1), ("gv", 2), ("gv", 4), ("qk8", 8), ("qk8", 1)])
 def test_gemm_full_size(ngq, orc, name, T):
     w, codes, scales, x = full_inputs(name)
     cols = sample_cols(w.N, seed=T)
