@@ -250,6 +250,10 @@ def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
         eager_x = st.x.clone()
         graph_ms, gx = time_graph(st, x0)
         same = bool(torch.equal(gx, eager_x))
+        fz = Stack(weights, T, fused=True)
+        fused_ms, fx = time_graph(fz, x0)
+        fused_same = bool(torch.equal(fx, eager_x))
+        del fz
         conc_ms = None
         if side:
             conc = Stack(weights, T, concurrent=True)
@@ -259,6 +263,7 @@ def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
         b = layer_bytes(T, ngq.ngq_packed_bytes) * layers
         out.append({"T": T, "layers": layers, "passes": passes,
                     "eager_us_per_layer": eager_ms * 1e3 / layers, "graph_us_per_layer": graph_ms * 1e3 / layers,
+                    "fused_graph_us_per_layer": fused_ms * 1e3 / layers, "fused_matches_eager": fused_same,
                     "side_streams_graph_us_per_layer": None if conc_ms is None else conc_ms * 1e3 / layers,
                     "graph_ms_per_pass": graph_ms, "bytes_per_pass": b, "GBps": b / graph_ms / 1e6,
                     "pct_peak": 100 * b / graph_ms / 1e6 / PEAK_GBS, "graph_matches_eager": same})

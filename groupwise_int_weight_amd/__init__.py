@@ -28,12 +28,21 @@ NGQ_INT4, NGQ_INT5, NGQ_INT8 = 4, 5, 8
 NGQ_SCALE_BF16 = 0x100
 NGQ_GROUP = 64
 NGQ_MAX_T = 8
+NGQ_MAX_PROJ = 4
 NGQ_KERNEL_AUTO, NGQ_KERNEL_PERPAIR_DYN, NGQ_KERNEL_PERPAIR_STATIC, NGQ_KERNEL_XRES14, NGQ_KERNEL_XRES8 = 0, 1, 2, 3, 4
 
 # Every function the header declares, with its ctypes signature.
 _SIZE = ctypes.c_size_t
 _INT = ctypes.c_int
 _PTR = ctypes.c_void_p
+
+
+class NgqProj(ctypes.Structure):
+    """struct ngq_proj: one projection of an ngq_multi_gemm call."""
+    _fields_ = [("bits", _INT), ("n", _INT), ("swiglu", _INT), ("reserved", _INT),
+                ("wq", _PTR), ("scales", _PTR), ("y", _PTR)]
+
+
 SIGNATURES = {
     "ngq_packed_bytes": (_SIZE, [_INT, _INT, _INT, _INT]),
     "ngq_scale_bytes": (_SIZE, [_INT, _INT, _INT, _INT]),
@@ -42,6 +51,7 @@ SIGNATURES = {
     "ngq_swiglu_gemm": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR]),
     "ngq_unpack_codes": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_dequant_f32": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR]),
+    "ngq_multi_gemm": (_INT, [_INT, _INT, _INT, _PTR, ctypes.POINTER(NgqProj), _INT, _PTR]),
     "ngq_rms_rescale": (_INT, [_INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
     "ngq_debug_force_kernel": (_INT, [_INT]),
@@ -173,6 +183,29 @@ def ngq_swiglu_gemm(x, wq_gate_up, scales_gate_up, bits: int, N_ff: int, h=None,
     return h
 
 
+def ngq_multi_gemm(x, projs, group: int = NGQ_GROUP, stream=None):
+    """Several projections of the same x in one launch.  `projs` is a list of
+    dicts with keys wq, scales, bits, n and optionally swiglu (False) and y;
+    returns the list of outputs y[T][n] (bf16), each what ngq_gemm (or
+    ngq_swiglu_gemm when swiglu) computes for its projection."""
+    import torch
+
+    T, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    arr = (NgqProj * max(1, len(projs)))()
+    outs = []
+    for i, p in enumerate(projs):
+        y = p.get("y")
+        if y is None:
+            y = torch.empty((T, int(p["n"])), dtype=torch.bfloat16, device=x.device)
+        outs.append(y)
+        arr[i] = NgqProj(_format_bits(p["bits"], p["scales"]), int(p["n"]), int(bool(p.get("swiglu", False))), 0,
+                         _dev_ptr(p["wq"], "wq"), _dev_ptr(p["scales"], "scales"), _dev_ptr(y, "y"))
+    _check(lib().ngq_multi_gemm(T, K, group, _dev_ptr(x, "x"), arr, len(projs), _stream(stream)), "ngq_multi_gemm")
+    return outs
+
+
 def ngq_rms_rescale(z, x=None, stream=None):
     """x[t][:] (bf16) = z[t][:] / rms(z[t][:]); x may be z itself (in place)."""
     import torch
@@ -220,8 +253,8 @@ def ngq_debug_force_kernel(path: int) -> int:
 
 
 __all__ = [
-    "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
+    "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
     "ngq_debug_force_kernel",
     "ngq_packed_bytes", "ngq_scale_bytes", "ngq_strerror", "ngq_version", "NgqError", "NgqLibraryMissing",
-    "lib", "SIGNATURES",
+    "lib", "SIGNATURES", "NgqProj",
 ]

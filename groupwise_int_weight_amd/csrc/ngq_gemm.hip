@@ -42,6 +42,12 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstring>
+#include <deque>
+#include <mutex>
+#include <queue>
+#include <utility>
+#include <vector>
 
 #include "ngq_internal.h"
 
@@ -566,71 +572,117 @@ struct WBuf {
   uint32_t sc[NSETS][2 * V];
 };
 
-// XL: X chunks (16 bytes) per thread in the prologue; W waves; NB pairs in
-// flight per wave.
-template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, int XL>
-__global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
-  constexpr int WPK = BITS == 8 ? 2 : 1;
-  constexpr int TILE = 16 * V;
-  constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const uint32_t XROW = XSmem::xrow(a.K);
-  float* const part = reinterpret_cast<float*>(smem + XSmem::x_end(a.T, a.K));
+// The per-lane constants of an X-resident workgroup: operand row m and k-slot
+// q, B slot token t and group half h, whether that slot is live, and where in
+// LDS its B fragments start.
+struct XresLane {
+  int wave, m, q, t, h;
+  uint32_t lane_kb;
+  bool b_on;
+  uint32_t bsrc;
+  UnpackMasks mk;
+};
 
+// One projection as the tile runner sees it.
+struct ProjView {
+  const void* wq;
+  const void* scales;
+  void* y;
+  uint32_t p0_bytes, p1_bytes, s_bytes;
+  int Nout, Ncols, up_off;
+};
+
+// Shape constants shared by every projection of a launch.
+struct XresShape {
+  int T, K, G, pairs, ppw;
+};
+
+__device__ __forceinline__ XresLane xres_lane(int T, int K, uint32_t mask_nib, uint32_t mask_base, uint32_t mask_hi) {
+  XresLane ln;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m = lane & 15, q = lane >> 4;
-  const int t = m & 7, h = m >> 3;
-
-  // rank of this workgroup with the workgroups of one XCD (b % 8) numbered
-  // consecutively, so that one XCD works on neighbouring tiles at a time
-  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
-  const int rank = xcd * (G >> 3) + min(xcd, G & 7) + (b >> 3);
-  const int my_tiles = (a.ntiles - rank + G - 1) / G;
-
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
-  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
-  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  ln.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  ln.m = lane & 15;
+  ln.q = lane >> 4;
+  ln.t = ln.m & 7;
+  ln.h = ln.m >> 3;
+  ln.lane_kb = 8u * (uint32_t)(ln.q >> 1) + (uint32_t)(ln.q & 1);
+  // B fragment source: this lane's token row at its k-slot, or the zero block
+  ln.b_on = ((ln.q >> 1) == ln.h) & (ln.t < T);
+  ln.bsrc = XSmem::ZERO + (uint32_t)ln.t * XSmem::xrow(K) + ln.lane_kb * 16u;
   // the base pattern lives in a vector register (an empty asm hides its
   // value), so each and-or takes one scalar and one vector constant
-  uint32_t vbase = a.mask_base;
+  uint32_t vbase = mask_base;
   asm volatile("" : "+v"(vbase));
-  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
+  ln.mk = UnpackMasks{mask_nib, vbase, mask_hi};
+  return ln;
+}
 
-  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
-  const uint32_t lane_kb = 8u * (uint32_t)(q >> 1) + (uint32_t)(q & 1);
-  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];  // tile-independent parts
-#pragma unroll
-  for (int s = 0; s < NSETS; ++s) {
-    const uint32_t col = (uint32_t)(s * a.up_off + V * m);
-    offA[s] = lane_kb * WPK * rowb + col * 4u;
-    offP1[s] = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
-    offS[s] = (uint32_t)h * (uint32_t)a.Ncols * 2u + (uint32_t)(s * a.up_off + 4 * V * q) * 2u;
-  }
-  // B fragment source: this lane's token row at its k-slot, or the zero block
-  const bool b_on = ((q >> 1) == h) & (t < a.T);
-  const uint32_t bsrc = XSmem::ZERO + (uint32_t)t * XROW + lane_kb * 16u;
-
-  // -- prologue: X loads first, then the first pairs' weights; the X wait
-  // below then leaves those weights in flight.
-  const int nch = a.T * (a.K >> 3);  // 16-byte chunks of X
-  const int rowch = a.K >> 3;
-  uint32_t xv[XL][4];
+// The X prologue: XL 16-byte chunks of X per thread, loaded before any weight
+// (x_stage writes them to LDS once the first pairs' loads are issued).
+template <int XL, int W>
+__device__ __forceinline__ void x_load(uint32_t (&xv)[XL][4], const void* x, uint32_t x_bytes, int T, int K) {
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(x, x_bytes);
+  const int nch = T * (K >> 3);
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
     const int c = threadIdx.x + W * 64 * j;
     const uint32_t off = c < nch ? (uint32_t)c * 16u : kOOB;  // X rows are contiguous in memory
     load_words<4>(xv[j], rX, off);
   }
-  __builtin_amdgcn_sched_barrier(0);
+}
 
-  // Loads of pair p of the workgroup's tile ti (nothing when either is out of
-  // range).  Flags are combined bitwise so that no lane-divergent branch
-  // appears.
+// X into LDS in the interleaved order (waits for the X loads only), the zero
+// block, barrier.
+template <int XL, int W>
+__device__ __forceinline__ void x_stage(uint8_t* smem, const uint32_t (&xv)[XL][4], int T, int K) {
+  const int nch = T * (K >> 3), rowch = K >> 3;
+  const uint32_t XROW = XSmem::xrow(K);
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    const int c = threadIdx.x + W * 64 * j;
+    if (c < nch) {
+      const int tt = c / rowch, kc = c - tt * rowch;
+      *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(xv[j]);
+    }
+  }
+  if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
+  lds_barrier();
+}
+
+// The tile loop of the X-resident kernels: `ntiles` column tiles of one
+// projection, tile i being tile tbase + tstride * i of 16 V columns, with the
+// pair pipeline running on across tile boundaries.  `stage` runs once, right
+// after the first pairs' loads are issued (the X staging of the prologue, or
+// nothing when X is already in LDS).  The LDS partial-sum region is free on
+// entry and on return.
+template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, class Stage>
+__device__ __forceinline__ void xres_tiles(const ProjView& pv, const XresShape& sh, const XresLane& ln, uint8_t* smem,
+                                           int tbase, int tstride, int ntiles, Stage&& stage) {
+  constexpr int WPK = BITS == 8 ? 2 : 1;
+  constexpr int TILE = 16 * V;
+  constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
+  float* const part = reinterpret_cast<float*>(smem + XSmem::x_end(sh.T, sh.K));
+  const int wave = ln.wave, m = ln.m, q = ln.q, t = ln.t, h = ln.h;
+
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(pv.wq, pv.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(pv.wq) + pv.p0_bytes, pv.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(pv.scales, pv.s_bytes);
+
+  const uint32_t rowb = (uint32_t)pv.Ncols * 4u;
+  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];  // tile-independent parts
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s) {
+    const uint32_t col = (uint32_t)(s * pv.up_off + V * m);
+    offA[s] = ln.lane_kb * WPK * rowb + col * 4u;
+    offP1[s] = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
+    offS[s] = (uint32_t)h * (uint32_t)pv.Ncols * 2u + (uint32_t)(s * pv.up_off + 4 * V * q) * 2u;
+  }
+
+  // Loads of pair p of tile i (nothing when either is out of range).  Flags
+  // are combined bitwise so that no lane-divergent branch appears.
   auto issue_at = [&](WBuf<BITS, V, NSETS>& buf, int ti, int p) {
-    const bool valid = (ti < my_tiles) & (p < a.pairs);
-    const uint32_t c0 = (uint32_t)((rank + G * ti) * TILE);
+    const bool valid = (ti < ntiles) & (p < sh.pairs);
+    const uint32_t c0 = (uint32_t)((tbase + tstride * ti) * TILE);
     const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb + c0 * 4u : kOOB;
     const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb + c0 * 4u : kOOB;
     const uint32_t ps = valid ? (uint32_t)p * rowb + c0 * 2u : kOOB;
@@ -654,14 +706,14 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
     for (int s = 0; s < NSETS; ++s) load_words<2 * V>(&buf.sc[s][0], rS, offS[s] + ps);
   };
 
-  // item (tile i, slot k) is pair wave + W k of tile i; every tile has cntp
-  // slots (the same for all waves, a multiple of NB), of
-  // which the first cnt are real pairs
-  const int cnt = a.pairs > wave ? (a.pairs - wave + W - 1) / W : 0;
-  const int cntp = a.ppw;
+  // item (tile i, slot k) is pair wave + W k of tile i; every tile has ppw
+  // slots (the same for all waves, a multiple of NB), of which the first cnt
+  // are real pairs
+  const int cnt = sh.pairs > wave ? (sh.pairs - wave + W - 1) / W : 0;
+  const int cntp = sh.ppw;
   int is_tile = 0, is_k = 0;  // next item to issue
   auto issue_next = [&](WBuf<BITS, V, NSETS>& buf) {
-    issue_at(buf, is_tile, is_k < cnt ? wave + W * is_k : a.pairs);
+    issue_at(buf, is_tile, is_k < cnt ? wave + W * is_k : sh.pairs);
     if (++is_k == cntp) {
       is_k = 0;
       ++is_tile;
@@ -674,19 +726,7 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
     issue_next(buf[u]);
     __builtin_amdgcn_sched_barrier(0);
   }
-
-  // -- X into LDS in the interleaved order (waits for the X loads only), the
-  // zero block, barrier
-#pragma unroll
-  for (int j = 0; j < XL; ++j) {
-    const int c = threadIdx.x + W * 64 * j;
-    if (c < nch) {
-      const int tt = c / rowch, kc = c - tt * rowch;
-      *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(xv[j]);
-    }
-  }
-  if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
-  lds_barrier();
+  stage();
 
   const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
                         Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
@@ -703,9 +743,9 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
   auto pair_sums = [&](const WBuf<BITS, V, NSETS>& buf, int p, f32x4 (&dp)[NSETS][V]) {
     // the second group of the last pair of an odd group count does not exist:
     // its lanes read zeros
-    const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
-    const bool on = b_on & !(half & (h == 1));
-    const uint32_t src = on ? bsrc + (uint32_t)p * 256u : 0u;
+    const bool half = (p == sh.pairs - 1) & ((sh.G & 1) != 0);
+    const bool on = ln.b_on & !(half & (h == 1));
+    const uint32_t src = on ? ln.bsrc + (uint32_t)p * 256u : 0u;
     bf16x8 bfrag[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -727,12 +767,12 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
         for (int i = 0; i < V; ++i) {
           u32x4 av;
           if constexpr (BITS == 4) {
-            av = nibbles_to_bf16_il(buf.a[s][st][i], mk);
+            av = nibbles_to_bf16_il(buf.a[s][st][i], ln.mk);
           } else if constexpr (BITS == 5) {
             // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
             const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
                                                                                  8u * (uint32_t)(q & 1), 8u);
-            av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, mk);
+            av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, ln.mk);
           } else {
             av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
           }
@@ -761,12 +801,12 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
   };
 
   // the tile's outputs: blocks summed in order, SwiGLU or plain, rounded
-  uint16_t* y = static_cast<uint16_t*>(a.y);
+  uint16_t* y = static_cast<uint16_t*>(pv.y);
   auto finish_tile = [&](int ti) {
-    const int c0 = (rank + G * ti) * TILE;
+    const int c0 = (tbase + tstride * ti) * TILE;
     for (int idx = threadIdx.x; idx < 8 * TILE; idx += W * 64) {
       const int tt = idx / TILE, col = idx % TILE;
-      if (tt >= a.T || c0 + col >= a.Nout) continue;
+      if (tt >= sh.T || c0 + col >= pv.Nout) continue;
       float v[NSETS];
 #pragma unroll
       for (int s = 0; s < NSETS; ++s) {
@@ -782,11 +822,11 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
       } else {
         out = v[0];
       }
-      y[(size_t)tt * a.Nout + c0 + col] = f32_to_bf16_rne(out);
+      y[(size_t)tt * pv.Nout + c0 + col] = f32_to_bf16_rne(out);
     }
   };
 
-  for (int ti = 0; ti < my_tiles; ++ti) {
+  for (int ti = 0; ti < ntiles; ++ti) {
     for (int kk = 0; kk < cntp; kk += NB) {
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
@@ -814,6 +854,149 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
     lds_barrier();
     finish_tile(ti);
     lds_barrier();
+  }
+}
+
+// XL: X chunks (16 bytes) per thread in the prologue; W waves; NB pairs in
+// flight per wave.
+template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, int XL>
+__global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const XresLane ln = xres_lane(a.T, a.K, a.mask_nib, a.mask_base, a.mask_hi);
+  // rank of this workgroup with the workgroups of one XCD (b % 8) numbered
+  // consecutively, so that one XCD works on neighbouring tiles at a time
+  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
+  const int rank = xcd * (G >> 3) + min(xcd, G & 7) + (b >> 3);
+  const int my_tiles = (a.ntiles - rank + G - 1) / G;
+
+  // -- prologue: X loads first, then the first pairs' weights; the X wait in
+  // x_stage then leaves those weights in flight.
+  uint32_t xv[XL][4];
+  x_load<XL, W>(xv, a.x, a.x_bytes, a.T, a.K);
+  __builtin_amdgcn_sched_barrier(0);
+  const ProjView pv{a.wq, a.scales, a.y, a.p0_bytes, a.p1_bytes, a.s_bytes, a.Nout, a.Ncols, a.up_off};
+  const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw};
+  xres_tiles<BITS, SBF16, V, NSETS, W, NB>(pv, sh, ln, smem, rank, G, my_tiles,
+                                           [&]() { x_stage<XL, W>(smem, xv, a.T, a.K); });
+}
+
+// ---- several projections of one X in one launch ----------------------------
+//
+// The projections of a layer that read the same activations (QK, gate/value
+// and gate/up) run as one persistent launch: X is staged once per workgroup,
+// the launch and its ramp are paid once, and the tiles of all projections are
+// spread over the workgroups by cost (host-planned, longest tiles first to
+// the least loaded workgroup), which also evens out projections whose tile
+// count is not a multiple of the CU count.  Workgroup r (by XCD-grouped rank)
+// owns a contiguous range of each projection's tiles and runs them projection
+// by projection with the X-resident tile loop.
+
+constexpr int kMultiMaxProj = 4;
+constexpr int kMultiMaxWg = 256;
+constexpr int kMultiW = 8, kMultiNB = 2, kMultiXL = 10;
+
+// Tile runner of a projection: bit width, scale type and output sets.
+__host__ __device__ constexpr int multi_kind(int bits, bool sbf16, int nsets) {
+  return (bits == 4 ? 0 : bits == 5 ? 1 : 2) * 4 + (sbf16 ? 2 : 0) + (nsets - 1);
+}
+// Tile width (columns per lane) of each runner: 32-column tiles, except int8
+// with two output sets, which needs 16 to stay within registers.
+__host__ __device__ constexpr int multi_v(int bits, int nsets) { return bits == 8 && nsets == 2 ? 1 : 2; }
+
+struct MultiProj {
+  const void* wq;
+  const void* scales;
+  void* y;
+  uint32_t p0_bytes, p1_bytes, s_bytes;
+  int Nout, Ncols, up_off;
+  int kind;
+};
+
+struct MultiArgs {
+  const void* x;
+  uint32_t x_bytes;
+  int T, K, G, pairs, ppw, nproj;
+  uint32_t mask_nib, mask_base, mask_hi;
+  MultiProj proj[kMultiMaxProj];
+  // tiles of projection p owned by the workgroup of rank r; its first tile is
+  // the sum of the counts of the ranks before it
+  uint8_t cnt[kMultiMaxProj][kMultiMaxWg];
+};
+
+// X chunks of the rows beyond the prologue's XL per thread, staged in further
+// rounds (long K at large T only); then the zero block and the barrier.
+template <int XL, int W>
+__device__ __forceinline__ void x_stage_rounds(uint8_t* smem, const uint32_t (&xv)[XL][4], const void* x,
+                                               uint32_t x_bytes, int T, int K) {
+  const int nch = T * (K >> 3), rowch = K >> 3;
+  const uint32_t XROW = XSmem::xrow(K);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(x, x_bytes);
+  auto put = [&](const uint32_t (&d)[4], int c) {
+    if (c < nch) {
+      const int tt = c / rowch, kc = c - tt * rowch;
+      *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(d);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < XL; ++j) put(xv[j], threadIdx.x + W * 64 * j);
+  for (int base = XL * W * 64; base < nch; base += XL * W * 64) {
+    uint32_t xr[XL][4];
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int c = base + threadIdx.x + W * 64 * j;
+      load_words<4>(xr[j], rX, c < nch ? (uint32_t)c * 16u : kOOB);
+    }
+#pragma unroll
+    for (int j = 0; j < XL; ++j) put(xr[j], base + threadIdx.x + W * 64 * j);
+  }
+  if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
+  lds_barrier();
+}
+
+__global__ __launch_bounds__(kMultiW * 64) void gemm_multi_kernel(MultiArgs a) {
+  constexpr int W = kMultiW, NB = kMultiNB, XL = kMultiXL;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const XresLane ln = xres_lane(a.T, a.K, a.mask_nib, a.mask_base, a.mask_hi);
+  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
+  const int rank = xcd * (G >> 3) + min(xcd, G & 7) + (b >> 3);
+
+  uint32_t xv[XL][4];
+  x_load<XL, W>(xv, a.x, a.x_bytes, a.T, a.K);
+  __builtin_amdgcn_sched_barrier(0);
+
+  bool staged = false;
+  auto stage = [&]() {
+    if (!staged) x_stage_rounds<XL, W>(smem, xv, a.x, a.x_bytes, a.T, a.K);
+    staged = true;
+  };
+  const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw};
+  const int lane = threadIdx.x & 63;
+  for (int p = 0; p < a.nproj; ++p) {
+    // this rank's first tile of projection p: lane l sums the counts of the
+    // ranks 4l .. 4l+3 that precede it
+    const uint32_t w4 = reinterpret_cast<const uint32_t*>(&a.cnt[p][0])[lane];
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += (4 * lane + j < rank) ? (w4 >> (8 * j)) & 0xFFu : 0u;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += (uint32_t)__shfl_xor((int)s, off, 64);
+    const int first = __builtin_amdgcn_readfirstlane((int)s);
+    const int count = a.cnt[p][rank];
+    if (count == 0) continue;
+    const MultiProj& mp = a.proj[p];
+    const ProjView pv{mp.wq, mp.scales, mp.y, mp.p0_bytes, mp.p1_bytes, mp.s_bytes, mp.Nout, mp.Ncols, mp.up_off};
+    switch (mp.kind) {
+#define NGQ_MULTI_CASE(BITS, SBF16, NSETS)                                                                     \
+  case multi_kind(BITS, SBF16, NSETS):                                                                         \
+    xres_tiles<BITS, SBF16, multi_v(BITS, NSETS), NSETS, W, NB>(pv, sh, ln, smem, first, 1, count, stage);       \
+    break;
+      NGQ_MULTI_CASE(4, false, 1) NGQ_MULTI_CASE(4, false, 2) NGQ_MULTI_CASE(4, true, 1) NGQ_MULTI_CASE(4, true, 2)
+      NGQ_MULTI_CASE(5, false, 1) NGQ_MULTI_CASE(5, false, 2) NGQ_MULTI_CASE(5, true, 1) NGQ_MULTI_CASE(5, true, 2)
+      NGQ_MULTI_CASE(8, false, 1) NGQ_MULTI_CASE(8, false, 2) NGQ_MULTI_CASE(8, true, 1) NGQ_MULTI_CASE(8, true, 2)
+#undef NGQ_MULTI_CASE
+      default:
+        break;
+    }
   }
 }
 
@@ -1164,6 +1347,170 @@ int run_unpack(int K, int N, int bits, int group, const void* wq, const void* sc
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
 
+
+// ---- several projections of one X in one launch (host) ----
+
+// Tiles per projection and workgroup for one shape (see gemm_multi_kernel).
+struct MultiPlan {
+  int key[3 + 2 * dev::kMultiMaxProj];  // grid bound, K, nproj, then (kind, Nout) per projection
+  int grid;
+  uint8_t cnt[dev::kMultiMaxProj][dev::kMultiMaxWg];
+};
+
+// Longest tiles first, each to the least loaded workgroup (lowest rank on a
+// tie).  The cost of a tile is its weight and scale bytes.  Returns false
+// when a workgroup would own more than 255 tiles of one projection.
+bool make_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, MultiPlan& pl) {
+  struct P {
+    double cost;
+    int p, tiles;
+  } ps[dev::kMultiMaxProj];
+  long total = 0;
+  for (int p = 0; p < nproj; ++p) {
+    const int kd = kind[p], bits = kd / 4 == 0 ? 4 : (kd / 4 == 1 ? 5 : 8), nsets = kd % 2 + 1;
+    const int cols = 16 * dev::multi_v(bits, nsets);
+    ps[p].p = p;
+    ps[p].tiles = (nout[p] + cols - 1) / cols;
+    ps[p].cost = (double)cols * nsets * K * ((double)bits / 8.0 + 2.0 / kGroup);
+    total += ps[p].tiles;
+  }
+  pl.grid = (int)std::min<long>(total, wg_max);
+  std::memset(pl.cnt, 0, sizeof(pl.cnt));
+  if (pl.grid == 0) return true;
+  std::stable_sort(ps, ps + nproj, [](const P& a, const P& b) { return a.cost > b.cost; });
+  using Slot = std::pair<double, int>;  // (load, rank)
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  for (int r = 0; r < pl.grid; ++r) heap.push({0.0, r});
+  for (int i = 0; i < nproj; ++i) {
+    for (int k = 0; k < ps[i].tiles; ++k) {
+      Slot s = heap.top();
+      heap.pop();
+      if (pl.cnt[ps[i].p][s.second] == 255) return false;
+      ++pl.cnt[ps[i].p][s.second];
+      s.first += ps[i].cost;
+      heap.push(s);
+    }
+  }
+  return true;
+}
+
+// The plan of a shape, computed once and kept (a few shapes per process).
+const MultiPlan* get_plan(int K, int nproj, const int* kind, const int* nout, int wg_max) {
+  static std::mutex mu;
+  static std::deque<MultiPlan> plans;
+  int key[3 + 2 * dev::kMultiMaxProj] = {wg_max, K, nproj};
+  for (int p = 0; p < nproj; ++p) {
+    key[3 + 2 * p] = kind[p];
+    key[4 + 2 * p] = nout[p];
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  for (const MultiPlan& pl : plans)
+    if (std::memcmp(pl.key, key, sizeof(key)) == 0) return &pl;
+  MultiPlan pl;
+  std::memcpy(pl.key, key, sizeof(key));
+  if (!make_plan(K, nproj, kind, nout, wg_max, pl)) return nullptr;
+  if (plans.size() == 16) plans.pop_front();
+  plans.push_back(pl);
+  return &plans.back();
+}
+
+int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int nproj, void* stream) {
+  if (projs == nullptr || nproj < 1 || nproj > NGQ_MAX_PROJ) return NGQ_ERR_ARG;
+  if (T < 0 || T > NGQ_MAX_T) return NGQ_ERR_SHAPE;
+  Format f[NGQ_MAX_PROJ];
+  int rc;
+  for (int p = 0; p < nproj; ++p) {
+    if ((rc = parse_format(projs[p].bits, group, &f[p])) != NGQ_OK) return rc;
+    if ((projs[p].swiglu != 0 && projs[p].swiglu != 1) || projs[p].reserved != 0) return NGQ_ERR_ARG;
+    if ((rc = check_kn(K, projs[p].n)) != NGQ_OK) return rc;
+    if ((long)projs[p].n * (projs[p].swiglu + 1) > (1L << 30)) return NGQ_ERR_SHAPE;
+  }
+  if (T == 0) return NGQ_OK;
+  const size_t xb = (size_t)T * K * 2;
+  if (xb >= kMaxBuffer) return NGQ_ERR_UNSUPPORTED;
+  if (K > 0 && (rc = check_ptr(x)) != NGQ_OK) return rc;
+  // the projections with work, their buffers and sizes
+  dev::MultiArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int kind[NGQ_MAX_PROJ], nout[NGQ_MAX_PROJ];
+  size_t wbytes[NGQ_MAX_PROJ], sbytes[NGQ_MAX_PROJ], ybytes[NGQ_MAX_PROJ];
+  const ngq_proj* live[NGQ_MAX_PROJ];
+  int n = 0, nsets_max = 1, v_max = 1;
+  for (int p = 0; p < nproj; ++p) {
+    const ngq_proj& pr = projs[p];
+    if (pr.n == 0) continue;
+    const int nsets = pr.swiglu + 1, Ncols = pr.n * nsets;
+    const size_t wb0 = p0_bytes(K, Ncols, f[p].bits), wb1 = p1_bytes(K, Ncols, f[p].bits);
+    const size_t sb = (size_t)(K / kGroup) * Ncols * 2, yb = (size_t)T * pr.n * 2;
+    if ((rc = check_ptr(pr.y)) != NGQ_OK) return rc;
+    if (K > 0) {
+      if ((rc = check_ptr(pr.wq)) != NGQ_OK) return rc;
+      if ((rc = check_ptr(pr.scales)) != NGQ_OK) return rc;
+    }
+    if (yb >= kMaxBuffer || wb0 + wb1 >= kMaxBuffer || sb >= kMaxBuffer) return NGQ_ERR_UNSUPPORTED;
+    live[n] = &pr;
+    wbytes[n] = wb0 + wb1;
+    sbytes[n] = sb;
+    ybytes[n] = yb;
+    kind[n] = dev::multi_kind(f[p].bits, f[p].scale_bf16, nsets);
+    nout[n] = pr.n;
+    nsets_max = std::max(nsets_max, nsets);
+    v_max = std::max(v_max, dev::multi_v(f[p].bits, nsets));
+    dev::MultiProj& mp = a.proj[n];
+    mp.wq = pr.wq;
+    mp.scales = pr.scales;
+    mp.y = pr.y;
+    mp.p0_bytes = (uint32_t)wb0;
+    mp.p1_bytes = (uint32_t)wb1;
+    mp.s_bytes = (uint32_t)sb;
+    mp.Nout = pr.n;
+    mp.Ncols = Ncols;
+    mp.up_off = nsets == 2 ? pr.n : 0;
+    mp.kind = kind[n];
+    ++n;
+  }
+  // every output overlaps no input and no other output
+  for (int i = 0; i < n; ++i) {
+    if (K > 0 && overlaps(live[i]->y, ybytes[i], x, xb)) return NGQ_ERR_ARG;
+    for (int j = 0; j < n; ++j) {
+      if (K > 0 && (overlaps(live[i]->y, ybytes[i], live[j]->wq, wbytes[j]) ||
+                    overlaps(live[i]->y, ybytes[i], live[j]->scales, sbytes[j])))
+        return NGQ_ERR_ARG;
+      if (j != i && overlaps(live[i]->y, ybytes[i], live[j]->y, ybytes[j])) return NGQ_ERR_ARG;
+    }
+  }
+  const uint32_t lds =
+      dev::XSmem::bytes(T, K, dev::kMultiW, 1, 0) +
+      (uint32_t)dev::kMultiW * dev::Smem::block_floats(nsets_max, 16 * v_max) * 4u;
+  if (lds > kMaxLds) return NGQ_ERR_UNSUPPORTED;
+  if (n == 0) return NGQ_OK;
+  const MultiPlan* pl = get_plan(K, n, kind, nout, std::min(cu_count(), dev::kMultiMaxWg));
+  if (pl == nullptr) return NGQ_ERR_UNSUPPORTED;
+  a.x = x;
+  a.x_bytes = (uint32_t)xb;
+  a.T = T;
+  a.K = K;
+  a.G = K / kGroup;
+  a.pairs = (a.G + 1) / 2;
+  const int per = (a.pairs + dev::kMultiW - 1) / dev::kMultiW;
+  a.ppw = (per + dev::kMultiNB - 1) / dev::kMultiNB * dev::kMultiNB;
+  a.nproj = n;
+  a.mask_nib = dev::kMasks.nib;
+  a.mask_base = dev::kMasks.base;
+  a.mask_hi = dev::kMasks.hi;
+  std::memcpy(a.cnt, pl->cnt, sizeof(a.cnt));
+  static std::once_flag raised;
+  static hipError_t raise_err = hipSuccess;
+  std::call_once(raised, [] {
+    raise_err = hipFuncSetAttribute(reinterpret_cast<const void*>(dev::gemm_multi_kernel),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  });
+  if (raise_err != hipSuccess) return NGQ_ERR_HIP;
+  hipLaunchKernelGGL(dev::gemm_multi_kernel, dim3((unsigned)pl->grid), dim3(dev::kMultiW * 64), lds,
+                     (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace ngq
 
@@ -1177,6 +1524,11 @@ extern "C" int ngq_gemm(int T, int K, int N, int bits, int group, const void* x,
 extern "C" int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
                                const void* wq_gate_up, const void* scales_gate_up, void* h, void* stream) {
   return run_gemm(2, T, K, N_ff, bits, group, x, wq_gate_up, scales_gate_up, h, stream);
+}
+
+extern "C" int ngq_multi_gemm(int T, int K, int group, const void* x, const ngq_proj* projs, int nproj,
+                              void* stream) {
+  return run_multi(T, K, group, x, projs, nproj, stream);
 }
 
 extern "C" int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream) {

@@ -11,11 +11,12 @@ T=8; only the down output feeds the next layer, the q and v outputs are
 written and not used (they stand for the attention inputs, which are outside
 this library).  Each step is one library call through the C ABI with raw
 device pointers; this module only orders the calls (on up to three streams)
-and keeps the buffers.
+and keeps the buffers.  With `fused`, the three projections of x are one
+ngq_multi_gemm call.
 """
 from __future__ import annotations
 
-from . import NGQ_GROUP, NGQ_SCALE_BF16, NgqError, lib
+from . import NGQ_GROUP, NGQ_SCALE_BF16, NgqError, NgqProj, lib
 
 HIDDEN = 5120
 N_FF = 17408
@@ -42,18 +43,23 @@ class Stack:
     """Layers of device weights (from `layers`: a list of {name: (packed, scales)})
     and the work buffers of one token count T.
 
-    By default every call runs in order on the main stream.  With `concurrent`
+    By default every call runs in order on the main stream.  With `fused` the
+    QK, gate/value and gate/up projections are one ngq_multi_gemm launch (X
+    staged once, the tiles of all three balanced over the CUs).  With `concurrent`
     the QK and gate/value projections, which only read x, run on two side
     streams beside the gate/up and down projections, and the main stream waits
     for them before the rescale overwrites x.  On MI355X that is slower: each
     projection kernel keeps one persistent workgroup per CU, and a kernel
     running beside it delays the workgroups that own its tiles."""
 
-    def __init__(self, layers, T: int, device="cuda", concurrent: bool = False):
+    def __init__(self, layers, T: int, device="cuda", concurrent: bool = False, fused: bool = False):
         import torch
 
         if not 1 <= T <= 8:
             raise ValueError("T must be in 1..8")
+        if concurrent and fused:
+            raise ValueError("concurrent and fused are exclusive")
+        self.fused = fused
         self.T = T
         self.layers = layers
         self.concurrent = concurrent
@@ -65,6 +71,7 @@ class Stack:
         self.x = torch.empty((T, HIDDEN), dtype=bf, device=device)  # the running activation
         self.side = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device)) if concurrent else ()
         self._calls = []
+        self._multi = []
         for lw in layers:
             calls = []
             for name, K, N, bits, sbf16, kind in LAYER_PLAN:
@@ -72,6 +79,10 @@ class Stack:
                 flag = bits | (NGQ_SCALE_BF16 if sbf16 else 0)
                 calls.append((kind, K, N, flag, wq.data_ptr(), s.data_ptr()))
             self._calls.append(calls)
+            # the projections of x as one ngq_multi_gemm call
+            outs = (self.q, self.v, self.h)
+            self._multi.append((NgqProj * 3)(*(NgqProj(f, N, int(kind == "swiglu"), 0, w, sc, o.data_ptr())
+                                               for (kind, _, N, f, w, sc), o in zip(calls[:3], outs))))
 
     def layer(self, i: int, stream=None):
         """Enqueue layer i (x -> x) on `stream` (a torch.cuda.Stream; the current
@@ -89,6 +100,11 @@ class Stack:
             if st != 0:
                 raise NgqError(st, f"layer {i} {where}")
 
+        if self.fused:
+            check(L.ngq_multi_gemm(T, HIDDEN, NGQ_GROUP, xp, self._multi[i], 3, main.cuda_stream), "qk+gv+gate_up")
+            check(L.ngq_gemm(T, K3, N3, f3, NGQ_GROUP, hp, w3, s3, zp, main.cuda_stream), "down")
+            check(L.ngq_rms_rescale(T, HIDDEN, zp, xp, main.cuda_stream), "rescale")
+            return
         if self.concurrent:
             x_ready = torch.cuda.Event()
             x_ready.record(main)

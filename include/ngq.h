@@ -109,6 +109,39 @@ int ngq_gemm(int T, int K, int N, int bits, int group, const void* x, const void
 int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
                     const void* wq_gate_up, const void* scales_gate_up, void* h, void* stream);
 
+/* Several projections of the same activations in one launch.  The
+ * projections of a layer that read one x (in the stacked sweep: QK,
+ * gate/value and the gate/up pair) are computed as one persistent kernel, so
+ * X is staged once and the tiles of all of them are balanced over the CUs
+ * together.  Each projection computes exactly what ngq_gemm (swiglu = 0) or
+ * ngq_swiglu_gemm (swiglu = 1) computes for it: the same formula, fp32
+ * accumulation and bf16 rounding.
+ *   x     : device bf16 [T][K], shared by every projection
+ *   projs : host array of nproj (1..NGQ_MAX_PROJ) descriptions, read during
+ *           the call only:
+ *     bits   : NGQ_INT4 | NGQ_INT5 | NGQ_INT8, optionally | NGQ_SCALE_BF16
+ *     n      : output columns (N, or N_ff with swiglu); n % 4 == 0; 0 = skip
+ *     swiglu : 0 plain, 1 gate/up with the SiLU(gate) * up epilogue
+ *     reserved : must be 0
+ *     wq, scales : device, as for ngq_gemm over n (plain) or 2 n (swiglu)
+ *                  columns
+ *     y      : device bf16 [T][n], overwritten; no output may overlap x, any
+ *              projection's wq or scales, or another output
+ * K % 64 == 0; T == 0 is a no-op.  X and the partial sums must fit in the
+ * workgroup's LDS (T * (2 K + 16) + 128 bytes for X: K up to ~9000 at T = 8),
+ * otherwise NGQ_ERR_UNSUPPORTED. */
+#define NGQ_MAX_PROJ 4
+typedef struct ngq_proj {
+  int bits;
+  int n;
+  int swiglu;
+  int reserved;
+  const void* wq;
+  const void* scales;
+  void* y;
+} ngq_proj;
+int ngq_multi_gemm(int T, int K, int group, const void* x, const ngq_proj* projs, int nproj, void* stream);
+
 /* Per-token RMS rescale of a bf16 block (not a step the pages describe: it
  * chains the output of one stacked layer into the next at unit scale):
  *   x[t][n] = bf16( z[t][n] / sqrt((1/N) sum_n z[t][n]^2) ),  all-zero row -> zeros

@@ -34,8 +34,8 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     names = header_functions()
-    for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_packed_bytes", "ngq_scale_bytes",
-                     "ngq_unpack_codes", "ngq_dequant_f32", "ngq_rms_rescale", "ngq_strerror"]:
+    for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_packed_bytes",
+                     "ngq_scale_bytes", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_rms_rescale", "ngq_strerror"]:
         assert required in names
 
 
@@ -172,6 +172,43 @@ def test_rms_rescale_empty_is_no_op(ngq):
     L = ngq.lib()
     assert L.ngq_rms_rescale(0, 64, None, None, None) == 0
     assert L.ngq_rms_rescale(3, 0, None, None, None) == 0
+
+
+def multi_call(ngq, T, K, projs, x=X, nproj=None, group=64):
+    arr = (ngq.NgqProj * max(1, len(projs)))(*[ngq.NgqProj(*p) for p in projs])
+    return ngq.lib().ngq_multi_gemm(T, K, group, x, arr, len(projs) if nproj is None else nproj, None)
+
+
+# (bits, n, swiglu, reserved, wq, scales, y)
+P_OK = (4, 64, 0, 0, W, S, Y)
+
+
+@pytest.mark.parametrize("T,K,projs,nproj,status", [
+    (1, 64, [P_OK], 0, -1),                                        # no projection
+    (1, 64, [P_OK] * 4, 5, -1),                                    # more than NGQ_MAX_PROJ
+    (9, 64, [P_OK], None, -2),                                     # T > 8
+    (1, 100, [P_OK], None, -2),                                    # K % 64
+    (1, 64, [(4, 66, 0, 0, W, S, Y)], None, -2),                   # n % 4
+    (1, 64, [(7, 64, 0, 0, W, S, Y)], None, -3),                   # bits
+    (1, 64, [(4, 64, 2, 0, W, S, Y)], None, -1),                   # swiglu flag
+    (1, 64, [(4, 64, 0, 1, W, S, Y)], None, -1),                   # reserved field
+    (1, 64, [(4, 64, 0, 0, W, S, None)], None, -1),                # null output
+    (1, 64, [(4, 64, 0, 0, None, S, Y)], None, -1),                # null wq
+    (1, 64, [(4, 64, 0, 0, W, S, Y + 2)], None, -4),               # misaligned output
+    (1, 64, [(4, 64, 0, 0, W, S, X)], None, -1),                   # output overlaps x
+    (1, 64, [P_OK, (5, 64, 0, 0, W + 4096, S, W + 16)], None, -1),  # output overlaps another wq
+    (1, 64, [P_OK, (4, 64, 0, 0, W, S, Y + 64)], None, -1),        # two outputs overlap
+    (8, 65536, [P_OK], None, -3),                                  # X does not fit in LDS
+])
+def test_multi_rejects_bad_arguments(ngq, T, K, projs, nproj, status):
+    assert multi_call(ngq, T, K, projs, nproj=nproj) == status
+
+
+def test_multi_empty_calls_are_no_ops(ngq):
+    """T == 0, or every projection zero-width, returns OK without a HIP call."""
+    assert multi_call(ngq, 0, 64, [P_OK], x=None) == 0
+    assert multi_call(ngq, 3, 64, [(4, 0, 0, 0, W, S, Y), (5, 0, 1, 0, W, S, Y)]) == 0
+    assert ngq.lib().ngq_multi_gemm(1, 64, 64, X, None, 1, None) == -1
 
 
 def test_force_kernel_roundtrip(ngq):

@@ -137,20 +137,23 @@ def test_stack_first_layer_matches_oracle(ngq, orc, T):
     check_swiglu(host_bits(st.h)[:, cols], h64, g, u, f"stack swiglu T{T}")
 
 
-@pytest.mark.parametrize("T,concurrent", [(1, True), (8, True), (8, False)])
-def test_stack_chain_properties_and_graph_replay(ngq, T, concurrent):
+@pytest.mark.parametrize("T,mode", [(1, "concurrent"), (8, "concurrent"), (8, "in_order"), (1, "fused"),
+                                    (8, "fused")])
+def test_stack_chain_properties_and_graph_replay(ngq, T, mode):
     from groupwise_int_weight_amd.stack import Stack
 
     L = 4
     layers = stack_layers(ngq, L)
-    st = Stack(layers, T, concurrent=concurrent)
+    st = Stack(layers, T, concurrent=mode == "concurrent", fused=mode == "fused")
     x0 = dev_bf16(synthetic.stack_x0(T, seed=0))
     eager = to_host_u16(st.forward(x0))
     again = to_host_u16(st.forward(x0))
     assert np.array_equal(eager, again)  # deterministic
-    if concurrent:
-        # the side streams change only the order of independent work
-        assert np.array_equal(eager, to_host_u16(Stack(layers, T, concurrent=False).forward(x0)))
+    if mode != "in_order":
+        # The side streams change only the order of independent work.  The
+        # fused call runs gate/up with the same 8-wave tile loop as the
+        # separate call, and only the down output (computed from h) chains.
+        assert np.array_equal(eager, to_host_u16(Stack(layers, T).forward(x0)))
     v = bf16_bits_to_f64(eager)
     assert np.all(np.isfinite(v))
     # every row leaves the rescale with unit mean square, up to bf16 rounding
