@@ -46,6 +46,7 @@
 #include <deque>
 #include <mutex>
 #include <queue>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -640,29 +641,151 @@ __device__ __forceinline__ void x_stage(uint8_t* smem, const uint32_t (&xv)[XL][
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
     const int c = threadIdx.x + W * 64 * j;
+    // an empty asm makes the chunk a value of this point: where staging sits
+    // in a loop, the interleave is not hoisted above the first weight loads
+    // (it would wait for X before they are issued)
+    uint32_t d[4] = {xv[j][0], xv[j][1], xv[j][2], xv[j][3]};
+    asm volatile("" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]));
     if (c < nch) {
       const int tt = c / rowch, kc = c - tt * rowch;
-      *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(xv[j]);
+      *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(d);
     }
   }
   if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
   lds_barrier();
 }
 
+// Per-group partial sums of pair p of a tile, before scaling: the pair's
+// weight words in `buf` against X in LDS, each lane's B slot being token t of
+// group half h.  The -(128 + bias) sum_k x term seeds every partial.
+template <int BITS, int V, int NSETS, class Buf>
+__device__ __forceinline__ void pair_partials(const Buf& buf, int p, const XresShape& sh, const XresLane& ln,
+                                              const uint8_t* smem, f32x4 (&dp)[NSETS][V]) {
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+  // the second group of the last pair of an odd group count does not exist:
+  // its lanes read zeros
+  const bool half = (p == sh.pairs - 1) & ((sh.G & 1) != 0);
+  const bool on = ln.b_on & !(half & (ln.h == 1));
+  const uint32_t src = on ? ln.bsrc + (uint32_t)p * 256u : 0u;
+  bf16x8 bfrag[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    bfrag[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + src + (uint32_t)st * 32u));
+  f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfrag[st], dx, 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i) dp[s][i] = dx;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        u32x4 av;
+        if constexpr (BITS == 4) {
+          av = nibbles_to_bf16_il(buf.a[s][st][i], ln.mk);
+        } else if constexpr (BITS == 5) {
+          // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
+          const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
+                                                                               8u * (uint32_t)(ln.q & 1), 8u);
+          av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, ln.mk);
+        } else {
+          av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
+        }
+        dp[s][i] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag[st], dp[s][i], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// acc += s * partial for every output of the pair (its scales in `buf`)
+template <int V, int NSETS, class Buf>
+__device__ __forceinline__ void scale_accumulate(const Buf& buf, bool sbf16, const f32x4 (&dp)[NSETS][V],
+                                                 f32x4 (&acc)[NSETS][V]) {
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = V * r + i;
+        acc[s][i][r] = __builtin_fmaf(scale_to_f32(buf.sc[s][e >> 1], e & 1, sbf16), dp[s][i][r], acc[s][i][r]);
+      }
+}
+
+// A wave's partial block of a tile into LDS: slots j and j + 8 hold the two
+// group halves of token j, added here; the lanes of the first half write the
+// block [set][token][column].
+template <int V, int NSETS>
+__device__ __forceinline__ void store_partials(const f32x4 (&v)[NSETS][V], const XresLane& ln, float* blk) {
+  constexpr int TILE = 16 * V;
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int other =
+            __builtin_amdgcn_mov_dpp(__float_as_int(v[s][i][r]), 0x128 /* row_ror:8 */, 0xF, 0xF, false);
+        const float sum = v[s][i][r] + __int_as_float(other);
+        if (ln.h == 0)
+          blk[((uint32_t)s * 8u + (uint32_t)ln.t) * (uint32_t)(TILE + 4) + (uint32_t)(V * (4 * ln.q + r) + i)] = sum;
+      }
+}
+
+// The outputs of the tile at column c0: the W wave blocks summed in wave
+// order, SwiGLU or plain, rounded to bf16.
+template <int V, int NSETS, int W>
+__device__ __forceinline__ void finish_outputs(const float* part, const ProjView& pv, int T, int c0) {
+  constexpr int TILE = 16 * V;
+  constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
+  uint16_t* y = static_cast<uint16_t*>(pv.y);
+  for (int idx = threadIdx.x; idx < 8 * TILE; idx += W * 64) {
+    const int tt = idx / TILE, col = idx % TILE;
+    if (tt >= T || c0 + col >= pv.Nout) continue;
+    float v[NSETS];
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) {
+      const float* src = part + ((uint32_t)s * 8u + (uint32_t)tt) * (uint32_t)(TILE + 4) + (uint32_t)col;
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < W; ++k) sum += src[(uint32_t)k * BLK];
+      v[s] = sum;
+    }
+    float out;
+    if constexpr (NSETS == 2) {
+      out = v[0] * v[1] / (1.0f + expf(-v[0]));  // SiLU(gate) * up
+    } else {
+      out = v[0];
+    }
+    y[(size_t)tt * pv.Nout + c0 + col] = f32_to_bf16_rne(out);
+  }
+}
+
 // The tile loop of the X-resident kernels: `ntiles` column tiles of one
 // projection, tile i being tile tbase + tstride * i of 16 V columns, with the
-// pair pipeline running on across tile boundaries.  `stage` runs once, right
-// after the first pairs' loads are issued (the X staging of the prologue, or
-// nothing when X is already in LDS).  The LDS partial-sum region is free on
-// entry and on return.
-template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, class Stage>
+// pair pipeline running on across tile boundaries.  `buf` holds NB pairs in
+// flight; when `primed`, the first NB pairs were issued into it before the
+// call.  `stage` runs once, right after the first pairs' loads are issued (the
+// X staging of the prologue, or nothing when X is already in LDS).  In the
+// last NB slots of the last tile, `drain(buf[u], u)` issues what follows the
+// loop into the freed buffers (the next segment's first pairs, or nothing).
+// The LDS partial-sum region is free on entry and on return.
+template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, class Buf, class Stage, class Drain>
 __device__ __forceinline__ void xres_tiles(const ProjView& pv, const XresShape& sh, const XresLane& ln, uint8_t* smem,
-                                           int tbase, int tstride, int ntiles, Stage&& stage) {
+                                           int tbase, int tstride, int ntiles, Buf (&buf)[NB], bool primed,
+                                           Stage&& stage, Drain&& drain) {
   constexpr int WPK = BITS == 8 ? 2 : 1;
   constexpr int TILE = 16 * V;
   constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
   float* const part = reinterpret_cast<float*>(smem + XSmem::x_end(sh.T, sh.K));
-  const int wave = ln.wave, m = ln.m, q = ln.q, t = ln.t, h = ln.h;
+  const int wave = ln.wave, m = ln.m, q = ln.q, h = ln.h;
 
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(pv.wq, pv.p0_bytes);
   const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(pv.wq) + pv.p0_bytes, pv.p1_bytes);
@@ -680,7 +803,7 @@ __device__ __forceinline__ void xres_tiles(const ProjView& pv, const XresShape& 
 
   // Loads of pair p of tile i (nothing when either is out of range).  Flags
   // are combined bitwise so that no lane-divergent branch appears.
-  auto issue_at = [&](WBuf<BITS, V, NSETS>& buf, int ti, int p) {
+  auto issue_at = [&](Buf& buf, int ti, int p) {
     const bool valid = (ti < ntiles) & (p < sh.pairs);
     const uint32_t c0 = (uint32_t)((tbase + tstride * ti) * TILE);
     const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb + c0 * 4u : kOOB;
@@ -712,24 +835,21 @@ __device__ __forceinline__ void xres_tiles(const ProjView& pv, const XresShape& 
   const int cnt = sh.pairs > wave ? (sh.pairs - wave + W - 1) / W : 0;
   const int cntp = sh.ppw;
   int is_tile = 0, is_k = 0;  // next item to issue
-  auto issue_next = [&](WBuf<BITS, V, NSETS>& buf) {
-    issue_at(buf, is_tile, is_k < cnt ? wave + W * is_k : sh.pairs);
+  auto issue_next = [&](Buf& b, bool do_issue) {
+    if (do_issue) issue_at(b, is_tile, is_k < cnt ? wave + W * is_k : sh.pairs);
     if (++is_k == cntp) {
       is_k = 0;
       ++is_tile;
     }
   };
 
-  WBuf<BITS, V, NSETS> buf[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
-    issue_next(buf[u]);
+    issue_next(buf[u], !primed);
     __builtin_amdgcn_sched_barrier(0);
   }
   stage();
 
-  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
-                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
   f32x4 acc[NSETS][V];
   auto clear_acc = [&]() {
 #pragma unroll
@@ -739,120 +859,36 @@ __device__ __forceinline__ void xres_tiles(const ProjView& pv, const XresShape& 
   };
   clear_acc();
 
-  // per-group partial sums of one pair (before scaling)
-  auto pair_sums = [&](const WBuf<BITS, V, NSETS>& buf, int p, f32x4 (&dp)[NSETS][V]) {
-    // the second group of the last pair of an odd group count does not exist:
-    // its lanes read zeros
-    const bool half = (p == sh.pairs - 1) & ((sh.G & 1) != 0);
-    const bool on = ln.b_on & !(half & (h == 1));
-    const uint32_t src = on ? ln.bsrc + (uint32_t)p * 256u : 0u;
-    bf16x8 bfrag[4];
+  // one slot block: each buffer's pair computed and scaled, then refilled
+  // (by the next item, or, in the final block, by `drain`)
+  auto run_block = [&](int kk, bool final_block) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
-      bfrag[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + src + (uint32_t)st * 32u));
-    // -(128 + bias) * sum_k x over each group half: seeds every partial sum
-    f32x4 dx = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-      dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfrag[st], dx, 0, 0, 0);
-#pragma unroll
-    for (int s = 0; s < NSETS; ++s)
-#pragma unroll
-      for (int i = 0; i < V; ++i) dp[s][i] = dx;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-      for (int s = 0; s < NSETS; ++s) {
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          u32x4 av;
-          if constexpr (BITS == 4) {
-            av = nibbles_to_bf16_il(buf.a[s][st][i], ln.mk);
-          } else if constexpr (BITS == 5) {
-            // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
-            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
-                                                                                 8u * (uint32_t)(q & 1), 8u);
-            av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, ln.mk);
-          } else {
-            av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
-          }
-          dp[s][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag[st],
-                                                             dp[s][i], 0, 0, 0);
-        }
+    for (int u = 0; u < NB; ++u) {
+      if (kk + u < cnt) {
+        f32x4 dp[NSETS][V];
+        pair_partials<BITS, V, NSETS>(buf[u], wave + W * (kk + u), sh, ln, smem, dp);
+        scale_accumulate<V, NSETS>(buf[u], SBF16, dp, acc);
       }
-    }
-  };
-
-  // slots j and j + 8 hold the two group halves of token j: add them; the
-  // lanes of the first half write the block [set][token][column]
-  auto store_block = [&](f32x4 (&v)[NSETS][V], float* blk) {
-#pragma unroll
-    for (int s = 0; s < NSETS; ++s)
-#pragma unroll
-      for (int i = 0; i < V; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int other = __builtin_amdgcn_mov_dpp(__float_as_int(v[s][i][r]), 0x128 /* row_ror:8 */, 0xF,
-                                                     0xF, false);
-          const float sum = v[s][i][r] + __int_as_float(other);
-          if (h == 0)
-            blk[((uint32_t)s * 8u + (uint32_t)t) * (uint32_t)(TILE + 4) + (uint32_t)(V * (4 * q + r) + i)] = sum;
-        }
-  };
-
-  // the tile's outputs: blocks summed in order, SwiGLU or plain, rounded
-  uint16_t* y = static_cast<uint16_t*>(pv.y);
-  auto finish_tile = [&](int ti) {
-    const int c0 = (tbase + tstride * ti) * TILE;
-    for (int idx = threadIdx.x; idx < 8 * TILE; idx += W * 64) {
-      const int tt = idx / TILE, col = idx % TILE;
-      if (tt >= sh.T || c0 + col >= pv.Nout) continue;
-      float v[NSETS];
-#pragma unroll
-      for (int s = 0; s < NSETS; ++s) {
-        const float* src = part + ((uint32_t)s * 8u + (uint32_t)tt) * (uint32_t)(TILE + 4) + (uint32_t)col;
-        float sum = 0.f;
-#pragma unroll
-        for (int k = 0; k < W; ++k) sum += src[(uint32_t)k * BLK];
-        v[s] = sum;
-      }
-      float out;
-      if constexpr (NSETS == 2) {
-        out = v[0] * v[1] / (1.0f + expf(-v[0]));  // SiLU(gate) * up
-      } else {
-        out = v[0];
-      }
-      y[(size_t)tt * pv.Nout + c0 + col] = f32_to_bf16_rne(out);
+      __builtin_amdgcn_sched_barrier(0);
+      if (final_block)
+        drain(buf[u], u);
+      else
+        issue_next(buf[u], true);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   for (int ti = 0; ti < ntiles; ++ti) {
-    for (int kk = 0; kk < cntp; kk += NB) {
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        if (kk + u < cnt) {
-          f32x4 dp[NSETS][V];
-          pair_sums(buf[u], wave + W * (kk + u), dp);
-#pragma unroll
-          for (int s = 0; s < NSETS; ++s)
-#pragma unroll
-            for (int i = 0; i < V; ++i)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int e = V * r + i;
-                acc[s][i][r] =
-                    __builtin_fmaf(scale_to_f32(buf[u].sc[s][e >> 1], e & 1, SBF16), dp[s][i][r], acc[s][i][r]);
-              }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        issue_next(buf[u]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    store_block(acc, part + (uint32_t)wave * BLK);
+    // the final block of the last tile is peeled off: only there does
+    // `drain` refill the buffers
+    const bool last = ti == ntiles - 1 && cntp > 0;
+    const int kk_end = last ? cntp - NB : cntp;
+    for (int kk = 0; kk < kk_end; kk += NB) run_block(kk, false);
+    if (last) run_block(cntp - NB, true);
+    store_partials<V, NSETS>(acc, ln, part + (uint32_t)wave * BLK);
     clear_acc();
     lds_barrier();
-    finish_tile(ti);
+    finish_outputs<V, NSETS, W>(part, pv, sh.T, (tbase + tstride * ti) * TILE);
     lds_barrier();
   }
 }
@@ -876,8 +912,10 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   const ProjView pv{a.wq, a.scales, a.y, a.p0_bytes, a.p1_bytes, a.s_bytes, a.Nout, a.Ncols, a.up_off};
   const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw};
-  xres_tiles<BITS, SBF16, V, NSETS, W, NB>(pv, sh, ln, smem, rank, G, my_tiles,
-                                           [&]() { x_stage<XL, W>(smem, xv, a.T, a.K); });
+  WBuf<BITS, V, NSETS> buf[NB];
+  xres_tiles<BITS, SBF16, V, NSETS, W, NB>(
+      pv, sh, ln, smem, rank, G, my_tiles, buf, false, [&]() { x_stage<XL, W>(smem, xv, a.T, a.K); },
+      [](WBuf<BITS, V, NSETS>&, int) {});
 }
 
 // ---- several projections of one X in one launch ----------------------------
@@ -887,9 +925,10 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
 // the launch and its ramp are paid once, and the tiles of all projections are
 // spread over the workgroups by cost (host-planned, longest tiles first to
 // the least loaded workgroup), which also evens out projections whose tile
-// count is not a multiple of the CU count.  Workgroup r (by XCD-grouped rank)
-// owns a contiguous range of each projection's tiles and runs them projection
-// by projection with the X-resident tile loop.
+// count is not a multiple of the CU count.  Workgroup r owns a contiguous
+// range of each projection's tiles and runs them projection by projection
+// with the X-resident tile loop, the pair pipeline running on from one
+// projection into the next.
 
 constexpr int kMultiMaxProj = 4;
 constexpr int kMultiMaxWg = 256;
@@ -915,31 +954,25 @@ struct MultiProj {
 struct MultiArgs {
   const void* x;
   uint32_t x_bytes;
-  int T, K, G, pairs, ppw, nproj;
+  int T, K, G, pairs, ppw;
   uint32_t mask_nib, mask_base, mask_hi;
   MultiProj proj[kMultiMaxProj];
-  // tiles of projection p owned by the workgroup of rank r; its first tile is
-  // the sum of the counts of the ranks before it
-  uint8_t cnt[kMultiMaxProj][kMultiMaxWg];
+  // the workgroup of rank r owns tiles first[r][p] .. first[r + 1][p] - 1 of
+  // projection p: one 16-byte scalar load gives a workgroup all its ranges
+  uint16_t first[kMultiMaxWg + 1][kMultiMaxProj];
 };
 
-// X chunks of the rows beyond the prologue's XL per thread, staged in further
-// rounds (long K at large T only); then the zero block and the barrier.
+// X into LDS when it exceeds XL chunks per thread (long K at large T): the
+// zero block, then X in rounds of XL chunks per thread, and the barrier.  Run
+// before any weight load is issued (its loop would otherwise leave the
+// compiler unable to tell which loads are in flight).
 template <int XL, int W>
-__device__ __forceinline__ void x_stage_rounds(uint8_t* smem, const uint32_t (&xv)[XL][4], const void* x,
-                                               uint32_t x_bytes, int T, int K) {
+__device__ __forceinline__ void x_stage_rounds(uint8_t* smem, const void* x, uint32_t x_bytes, int T, int K) {
   const int nch = T * (K >> 3), rowch = K >> 3;
   const uint32_t XROW = XSmem::xrow(K);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(x, x_bytes);
-  auto put = [&](const uint32_t (&d)[4], int c) {
-    if (c < nch) {
-      const int tt = c / rowch, kc = c - tt * rowch;
-      *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(d);
-    }
-  };
-#pragma unroll
-  for (int j = 0; j < XL; ++j) put(xv[j], threadIdx.x + W * 64 * j);
-  for (int base = XL * W * 64; base < nch; base += XL * W * 64) {
+  if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
+  for (int base = 0; base < nch; base += XL * W * 64) {
     uint32_t xr[XL][4];
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
@@ -947,49 +980,102 @@ __device__ __forceinline__ void x_stage_rounds(uint8_t* smem, const uint32_t (&x
       load_words<4>(xr[j], rX, c < nch ? (uint32_t)c * 16u : kOOB);
     }
 #pragma unroll
-    for (int j = 0; j < XL; ++j) put(xr[j], base + threadIdx.x + W * 64 * j);
+    for (int j = 0; j < XL; ++j) {
+      const int c = base + threadIdx.x + W * 64 * j;
+      if (c < nch) {
+        const int tt = c / rowch, kc = c - tt * rowch;
+        *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(xr[j]);
+      }
+    }
   }
-  if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
   lds_barrier();
 }
 
+// This workgroup's tile ranges (rows b and b + 1 of the table, one 16-byte
+// scalar load) and the range of projection p in them.
+struct MultiRanges {
+  uint32_t r0, r1, r2, r3;
+  __device__ int get(int p, int& f) const {
+    const uint32_t lo = p < 2 ? r0 : r1, hi = p < 2 ? r2 : r3, sh16 = 16u * (uint32_t)(p & 1);
+    f = (int)((lo >> sh16) & 0xFFFFu);
+    return (int)((hi >> sh16) & 0xFFFFu) - f;
+  }
+  // the next projection after `from` with tiles here (kMultiMaxProj: none)
+  __device__ int next(int from, int& f, int& n) const {
+    int q = from + 1;
+    while (q < kMultiMaxProj && (n = get(q, f)) == 0) ++q;
+    return q;
+  }
+};
+
+__device__ __forceinline__ ProjView multi_view(const MultiProj& mp) {
+  return ProjView{mp.wq, mp.scales, mp.y, mp.p0_bytes, mp.p1_bytes, mp.s_bytes, mp.Nout, mp.Ncols, mp.up_off};
+}
+
+// The start of a fused launch: every argument needed before the first weight
+// loads is read with no read depending on another, so that the scalar loads
+// go out together (each dependent argument read would add a round trip before
+// the weights are issued): the tile ranges, projection 0's buffers (the host
+// lists first a projection every workgroup has tiles of, when one exists) and
+// the shape.  The other descriptors' kinds are read too, which brings every
+// descriptor's cache line into the scalar cache for later segments.
+__device__ __forceinline__ MultiRanges multi_start(const MultiArgs& a, ProjView& pv0, int& kind0) {
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(&a.first[blockIdx.x][0]);
+  const MultiRanges rg{row[0], row[1], row[2], row[3]};
+  pv0 = multi_view(a.proj[0]);
+  kind0 = a.proj[0].kind;
+  // empty asm statements that use the values keep their loads in this first
+  // round trip (the compiler would otherwise sink them below the X loads)
+  asm volatile("" ::"s"(rg.r0), "s"(rg.r1), "s"(rg.r2), "s"(rg.r3), "s"(pv0.wq), "s"(pv0.scales), "s"(pv0.y),
+               "s"(pv0.p0_bytes), "s"(pv0.p1_bytes), "s"(pv0.s_bytes), "s"(pv0.Nout), "s"(pv0.Ncols),
+               "s"(pv0.up_off), "s"(kind0));
+  asm volatile("" ::"s"(a.x), "s"(a.x_bytes), "s"(a.T), "s"(a.K), "s"(a.G), "s"(a.pairs), "s"(a.ppw),
+               "s"(a.mask_nib), "s"(a.mask_base), "s"(a.mask_hi), "s"(a.proj[1].kind), "s"(a.proj[2].kind),
+               "s"(a.proj[3].kind));
+  return rg;
+}
+
+// BIGX: X exceeds the prologue's XL chunks per thread and is staged in rounds
+// before the first weight loads; otherwise the first projection's first
+// pairs are issued before X is staged, and the two loads overlap.
+template <bool BIGX>
 __global__ __launch_bounds__(kMultiW * 64) void gemm_multi_kernel(MultiArgs a) {
   constexpr int W = kMultiW, NB = kMultiNB, XL = kMultiXL;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  ProjView pv0;
+  int kind0;
+  const MultiRanges rg = multi_start(a, pv0, kind0);
   const XresLane ln = xres_lane(a.T, a.K, a.mask_nib, a.mask_base, a.mask_hi);
-  const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
-  const int rank = xcd * (G >> 3) + min(xcd, G & 7) + (b >> 3);
+  const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw};
 
-  uint32_t xv[XL][4];
-  x_load<XL, W>(xv, a.x, a.x_bytes, a.T, a.K);
+  uint32_t xv[BIGX ? 1 : XL][4];
+  if constexpr (BIGX)
+    x_stage_rounds<XL, W>(smem, a.x, a.x_bytes, a.T, a.K);
+  else
+    x_load<XL, W>(xv, a.x, a.x_bytes, a.T, a.K);
   __builtin_amdgcn_sched_barrier(0);
 
-  bool staged = false;
+  bool staged = BIGX;
   auto stage = [&]() {
-    if (!staged) x_stage_rounds<XL, W>(smem, xv, a.x, a.x_bytes, a.T, a.K);
+    if constexpr (!BIGX) {
+      if (!staged) x_stage<XL, W>(smem, xv, a.T, a.K);
+    }
     staged = true;
   };
-  const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw};
-  const int lane = threadIdx.x & 63;
-  for (int p = 0; p < a.nproj; ++p) {
-    // this rank's first tile of projection p: lane l sums the counts of the
-    // ranks 4l .. 4l+3 that precede it
-    const uint32_t w4 = reinterpret_cast<const uint32_t*>(&a.cnt[p][0])[lane];
-    uint32_t s = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += (4 * lane + j < rank) ? (w4 >> (8 * j)) & 0xFFu : 0u;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += (uint32_t)__shfl_xor((int)s, off, 64);
-    const int first = __builtin_amdgcn_readfirstlane((int)s);
-    const int count = a.cnt[p][rank];
-    if (count == 0) continue;
-    const MultiProj& mp = a.proj[p];
-    const ProjView pv{mp.wq, mp.scales, mp.y, mp.p0_bytes, mp.p1_bytes, mp.s_bytes, mp.Nout, mp.Ncols, mp.up_off};
-    switch (mp.kind) {
-#define NGQ_MULTI_CASE(BITS, SBF16, NSETS)                                                                     \
-  case multi_kind(BITS, SBF16, NSETS):                                                                         \
-    xres_tiles<BITS, SBF16, multi_v(BITS, NSETS), NSETS, W, NB>(pv, sh, ln, smem, first, 1, count, stage);       \
-    break;
+  auto no_drain = [](auto&, int) {};
+  for (int p = 0; p < kMultiMaxProj; ++p) {
+    int f = 0;
+    const int n = rg.get(p, f);
+    if (n == 0) continue;
+    const ProjView pv = p == 0 ? pv0 : multi_view(a.proj[p]);
+    switch (p == 0 ? kind0 : a.proj[p].kind) {
+#define NGQ_MULTI_CASE(BITS, SBF16, NSETS)                                                                       \
+  case multi_kind(BITS, SBF16, NSETS): {                                                                         \
+    WBuf<BITS, multi_v(BITS, NSETS), NSETS> buf[NB];                                                             \
+    xres_tiles<BITS, SBF16, multi_v(BITS, NSETS), NSETS, W, NB>(pv, sh, ln, smem, f, 1, n, buf, false, stage,     \
+                                                                no_drain);                                       \
+    break;                                                                                                       \
+  }
       NGQ_MULTI_CASE(4, false, 1) NGQ_MULTI_CASE(4, false, 2) NGQ_MULTI_CASE(4, true, 1) NGQ_MULTI_CASE(4, true, 2)
       NGQ_MULTI_CASE(5, false, 1) NGQ_MULTI_CASE(5, false, 2) NGQ_MULTI_CASE(5, true, 1) NGQ_MULTI_CASE(5, true, 2)
       NGQ_MULTI_CASE(8, false, 1) NGQ_MULTI_CASE(8, false, 2) NGQ_MULTI_CASE(8, true, 1) NGQ_MULTI_CASE(8, true, 2)
@@ -1354,12 +1440,12 @@ int run_unpack(int K, int N, int bits, int group, const void* wq, const void* sc
 struct MultiPlan {
   int key[3 + 2 * dev::kMultiMaxProj];  // grid bound, K, nproj, then (kind, Nout) per projection
   int grid;
-  uint8_t cnt[dev::kMultiMaxProj][dev::kMultiMaxWg];
+  uint16_t first[dev::kMultiMaxWg + 1][dev::kMultiMaxProj];
 };
 
 // Longest tiles first, each to the least loaded workgroup (lowest rank on a
 // tie).  The cost of a tile is its weight and scale bytes.  Returns false
-// when a workgroup would own more than 255 tiles of one projection.
+// when a projection has more tiles than the table holds.
 bool make_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, MultiPlan& pl) {
   struct P {
     double cost;
@@ -1372,11 +1458,13 @@ bool make_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, M
     ps[p].p = p;
     ps[p].tiles = (nout[p] + cols - 1) / cols;
     ps[p].cost = (double)cols * nsets * K * ((double)bits / 8.0 + 2.0 / kGroup);
+    if (ps[p].tiles > 65535) return false;  // the first-tile table holds 16 bits
     total += ps[p].tiles;
   }
   pl.grid = (int)std::min<long>(total, wg_max);
-  std::memset(pl.cnt, 0, sizeof(pl.cnt));
+  std::memset(pl.first, 0, sizeof(pl.first));
   if (pl.grid == 0) return true;
+  int cnt[dev::kMultiMaxProj][dev::kMultiMaxWg] = {};
   std::stable_sort(ps, ps + nproj, [](const P& a, const P& b) { return a.cost > b.cost; });
   using Slot = std::pair<double, int>;  // (load, rank)
   std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
@@ -1385,11 +1473,13 @@ bool make_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, M
     for (int k = 0; k < ps[i].tiles; ++k) {
       Slot s = heap.top();
       heap.pop();
-      if (pl.cnt[ps[i].p][s.second] == 255) return false;
-      ++pl.cnt[ps[i].p][s.second];
+      ++cnt[ps[i].p][s.second];
       s.first += ps[i].cost;
       heap.push(s);
     }
+  }
+  for (int p = 0; p < nproj; ++p) {
+    for (int r = 0; r < pl.grid; ++r) pl.first[r + 1][p] = (uint16_t)(pl.first[r][p] + cnt[p][r]);
   }
   return true;
 }
@@ -1479,11 +1569,32 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
       if (j != i && overlaps(live[i]->y, ybytes[i], live[j]->y, ybytes[j])) return NGQ_ERR_ARG;
     }
   }
-  const uint32_t lds =
-      dev::XSmem::bytes(T, K, dev::kMultiW, 1, 0) +
-      (uint32_t)dev::kMultiW * dev::Smem::block_floats(nsets_max, 16 * v_max) * 4u;
+  const uint32_t lds = dev::XSmem::bytes(T, K, dev::kMultiW, 1, 0) +
+                       (uint32_t)dev::kMultiW * dev::Smem::block_floats(nsets_max, 16 * v_max) * 4u;
   if (lds > kMaxLds) return NGQ_ERR_UNSUPPORTED;
   if (n == 0) return NGQ_OK;
+  // The projection with the most tiles first: every workgroup has tiles of it
+  // (when any projection has as many tiles as workgroups), so each one finds
+  // its first segment without scanning.
+  {
+    int order[NGQ_MAX_PROJ];
+    for (int i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order, order + n, [&](int i, int j) {
+      return (nout[i] + 31) / 32 > (nout[j] + 31) / 32;
+    });
+    dev::MultiProj mp[NGQ_MAX_PROJ];
+    int kd[NGQ_MAX_PROJ], no[NGQ_MAX_PROJ];
+    for (int i = 0; i < n; ++i) {
+      mp[i] = a.proj[order[i]];
+      kd[i] = kind[order[i]];
+      no[i] = nout[order[i]];
+    }
+    for (int i = 0; i < n; ++i) {
+      a.proj[i] = mp[i];
+      kind[i] = kd[i];
+      nout[i] = no[i];
+    }
+  }
   const MultiPlan* pl = get_plan(K, n, kind, nout, std::min(cu_count(), dev::kMultiMaxWg));
   if (pl == nullptr) return NGQ_ERR_UNSUPPORTED;
   a.x = x;
@@ -1494,19 +1605,23 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
   a.pairs = (a.G + 1) / 2;
   const int per = (a.pairs + dev::kMultiW - 1) / dev::kMultiW;
   a.ppw = (per + dev::kMultiNB - 1) / dev::kMultiNB * dev::kMultiNB;
-  a.nproj = n;
   a.mask_nib = dev::kMasks.nib;
   a.mask_base = dev::kMasks.base;
   a.mask_hi = dev::kMasks.hi;
-  std::memcpy(a.cnt, pl->cnt, sizeof(a.cnt));
+  std::memcpy(a.first, pl->first, sizeof(a.first));
+  using Kern = void (*)(dev::MultiArgs);
+  static const Kern kernels[2] = {dev::gemm_multi_kernel<false>, dev::gemm_multi_kernel<true>};
   static std::once_flag raised;
   static hipError_t raise_err = hipSuccess;
   std::call_once(raised, [] {
-    raise_err = hipFuncSetAttribute(reinterpret_cast<const void*>(dev::gemm_multi_kernel),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    for (Kern k : kernels)
+      if (raise_err == hipSuccess)
+        raise_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)kMaxLds);
   });
   if (raise_err != hipSuccess) return NGQ_ERR_HIP;
-  hipLaunchKernelGGL(dev::gemm_multi_kernel, dim3((unsigned)pl->grid), dim3(dev::kMultiW * 64), lds,
+  const bool big_x = (long)T * (K / 8) > (long)dev::kMultiXL * dev::kMultiW * 64;
+  hipLaunchKernelGGL(kernels[big_x ? 1 : 0], dim3((unsigned)pl->grid), dim3(dev::kMultiW * 64), lds,
                      (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }

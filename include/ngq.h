@@ -129,7 +129,8 @@ int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
  *              projection's wq or scales, or another output
  * K % 64 == 0; T == 0 is a no-op.  X and the partial sums must fit in the
  * workgroup's LDS (T * (2 K + 16) + 128 bytes for X: K up to ~9000 at T = 8),
- * otherwise NGQ_ERR_UNSUPPORTED. */
+ * otherwise NGQ_ERR_UNSUPPORTED.  Any mix of bit widths, scale types and
+ * plain / SwiGLU projections may share a call. */
 #define NGQ_MAX_PROJ 4
 typedef struct ngq_proj {
   int bits;

@@ -98,7 +98,8 @@ def run_case(ngq, orc, T, K, specs, seed, full_cols_below=2048):
 CASES = [
     # T, K, [(bits, bf16 scales, n, swiglu)]
     (8, 1088, [(4, False, 96, False), (5, True, 100, False), (4, False, 36, True)]),   # odd group count
-    (3, 320, [(8, False, 64, False), (8, True, 20, True), (5, False, 36, True), (4, True, 8, False)]),
+    (3, 320, [(4, True, 64, False), (4, False, 20, True), (5, False, 36, True), (5, True, 8, False)]),  # 4 kinds
+    (6, 448, [(8, False, 64, False), (8, True, 100, True), (5, True, 4, False)]),       # int8, SwiGLU too
     (5, 512, [(4, False, 4, False)]),                                                   # one narrow tile
     (2, 64, [(5, True, 260, False), (4, False, 0, False), (4, False, 1028, True)]),     # one group; n = 0
     (7, 256, [(4, False, 16416, False), (5, True, 8224, True)]),                        # many tiles per workgroup
