@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--stack-passes", type=int, default=5)
     p.add_argument("--stack-t", type=int, nargs="*", default=[1, 2, 4, 8], help="token counts of the stack sweep")
     p.add_argument("--no-stack-side", action="store_true", help="skip the side-stream comparison graph")
+    p.add_argument("--fused", type=int, default=0, metavar="T",
+                   help="time only the fused qk + gv + gate/up launch at T tokens (for profiling) and exit")
     return p.parse_args()
 
 
@@ -206,11 +208,13 @@ def parity_check(ngq, rot, y_dev):
 def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
     """The stacked-layer sweep: `layers` layers with distinct weights (QK, gate/
     value, gate/up + SwiGLU, down, RMS rescale each), chained through the
-    rescaled down output.  Timed per full pass from x0: eager (one library call
-    at a time from Python) and as a captured graph, every call in order on one
-    stream; and, for comparison, as a graph with QK and gate/value on side
-    streams beside gate/up and down.  The weights far exceed the caches, so
-    every pass streams them from HBM."""
+    rescaled down output.  Timed per full pass from x0 as a captured graph with
+    the three projections of x fused into one ngq_multi_gemm call (the
+    reported figure), and for comparison eager (one library call at a time
+    from Python, unfused), as a graph of the unfused calls in order, and as a
+    graph with QK and gate/value on side streams.  Every variant must produce
+    the eager output bit for bit.  The weights far exceed the caches, so every
+    pass streams them from HBM."""
     import numpy as np
     import torch
 
@@ -262,12 +266,61 @@ def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
             del conc
         b = layer_bytes(T, ngq.ngq_packed_bytes) * layers
         out.append({"T": T, "layers": layers, "passes": passes,
-                    "eager_us_per_layer": eager_ms * 1e3 / layers, "graph_us_per_layer": graph_ms * 1e3 / layers,
-                    "fused_graph_us_per_layer": fused_ms * 1e3 / layers, "fused_matches_eager": fused_same,
-                    "side_streams_graph_us_per_layer": None if conc_ms is None else conc_ms * 1e3 / layers,
-                    "graph_ms_per_pass": graph_ms, "bytes_per_pass": b, "GBps": b / graph_ms / 1e6,
-                    "pct_peak": 100 * b / graph_ms / 1e6 / PEAK_GBS, "graph_matches_eager": same})
+                    "eager_us_per_layer": eager_ms * 1e3 / layers,
+                    "graph_us_per_layer": fused_ms * 1e3 / layers, "graph_ms_per_pass": fused_ms,
+                    "bytes_per_pass": b, "GBps": b / fused_ms / 1e6, "pct_peak": 100 * b / fused_ms / 1e6 / PEAK_GBS,
+                    "graph_matches_eager": fused_same,
+                    "unfused_graph_us_per_layer": graph_ms * 1e3 / layers, "unfused_graph_matches_eager": same,
+                    "side_streams_graph_us_per_layer": None if conc_ms is None else conc_ms * 1e3 / layers})
         del st
+    del weights
+    torch.cuda.empty_cache()
+    return out
+
+
+HIDDEN = 5120
+
+
+def run_fused(ngq, Ts, steps, sets=8):
+    """The three projections of one x (QK, gate/value, gate/up + SwiGLU) as one
+    ngq_multi_gemm launch, rotating over `sets` distinct weight sets (1.3 GB,
+    past the caches), timed per launch in a captured graph."""
+    import numpy as np
+    import torch
+
+    import synthetic
+    from groupwise_int_weight_amd.stack import LAYER_PLAN, Stack
+
+    weights = synthetic.device_stack(sets, ngq.ngq_packed_bytes, seed=1)
+    out = []
+    for T in Ts:
+        st = Stack(weights, T)
+        st.x.copy_(torch.from_numpy(synthetic.stack_x0(T).view(np.int16)).to("cuda").view(torch.bfloat16))
+
+        def launches(k):
+            for i in range(k):
+                st.project(i % sets)
+        launches(sets)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launches(steps)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        b = 0
+        for name, K, N, bits, _, kind in LAYER_PLAN[:3]:
+            ncols = 2 * N if kind == "swiglu" else N
+            b += ngq.ngq_packed_bytes(K, ncols, bits) + (K // 64) * ncols * 2 + 2 * T * N
+        b += 2 * T * HIDDEN  # x, read once
+        out.append({"workload": "qk + gv + gate/up-SwiGLU in one ngq_multi_gemm", "T": T, "us": ms * 1e3,
+                    "GBps": b / ms / 1e6, "pct_peak": 100 * b / ms / 1e6 / PEAK_GBS})
+        del g, st
     del weights
     torch.cuda.empty_cache()
     return out
@@ -332,6 +385,9 @@ def main():
     assert torch.cuda.is_available(), "bench needs a HIP device"
     torch.cuda.set_device(0)
     ngq.lib()
+    if args.fused:
+        print(json.dumps({"fused": run_fused(ngq, (args.fused,), args.sweep_steps)}), flush=True)
+        return
 
     w = synthetic.WORKLOADS[args.workload]
     T = args.T
@@ -364,6 +420,7 @@ def main():
                 torch.cuda.empty_cache()
         for t in (1, 8):
             sweep.extend(run_swiglu(ngq, t, args.sweep_steps, 10))
+        sweep.extend(run_fused(ngq, (1, 8), args.sweep_steps))
         wl = synthetic.WORKLOADS["qk8"]  # int8: reported, not part of the metric
         for t in (1, 8):
             ms_t, r, _ = run_projection(ngq, wl, t, args.sweep_steps, 10)

@@ -46,6 +46,7 @@
 #include <deque>
 #include <mutex>
 #include <queue>
+#include <tuple>
 #include <type_traits>
 #include <utility>
 #include <vector>
@@ -957,9 +958,12 @@ struct MultiArgs {
   int T, K, G, pairs, ppw;
   uint32_t mask_nib, mask_base, mask_hi;
   MultiProj proj[kMultiMaxProj];
-  // the workgroup of rank r owns tiles first[r][p] .. first[r + 1][p] - 1 of
-  // projection p: one 16-byte scalar load gives a workgroup all its ranges
-  uint16_t first[kMultiMaxWg + 1][kMultiMaxProj];
+  // workgroup b owns tiles first[b][p] .. first[b][p] + count[b][p] - 1 of
+  // projection p (two scalar loads give a workgroup all its ranges); the host
+  // places neighbouring ranges on one XCD, so the scale cache lines that two
+  // neighbouring tiles share are fetched into one L2
+  uint16_t first[kMultiMaxWg][kMultiMaxProj];
+  uint8_t count[kMultiMaxWg][kMultiMaxProj];
 };
 
 // X into LDS when it exceeds XL chunks per thread (long K at large T): the
@@ -991,14 +995,13 @@ __device__ __forceinline__ void x_stage_rounds(uint8_t* smem, const void* x, uin
   lds_barrier();
 }
 
-// This workgroup's tile ranges (rows b and b + 1 of the table, one 16-byte
-// scalar load) and the range of projection p in them.
+// This workgroup's tile ranges (its row of the table) and the range of
+// projection p in them.
 struct MultiRanges {
-  uint32_t r0, r1, r2, r3;
+  uint32_t f01, f23, cnt;
   __device__ int get(int p, int& f) const {
-    const uint32_t lo = p < 2 ? r0 : r1, hi = p < 2 ? r2 : r3, sh16 = 16u * (uint32_t)(p & 1);
-    f = (int)((lo >> sh16) & 0xFFFFu);
-    return (int)((hi >> sh16) & 0xFFFFu) - f;
+    f = (int)(((p < 2 ? f01 : f23) >> (16u * (uint32_t)(p & 1))) & 0xFFFFu);
+    return (int)((cnt >> (8u * (uint32_t)p)) & 0xFFu);
   }
   // the next projection after `from` with tiles here (kMultiMaxProj: none)
   __device__ int next(int from, int& f, int& n) const {
@@ -1021,12 +1024,12 @@ __device__ __forceinline__ ProjView multi_view(const MultiProj& mp) {
 // descriptor's cache line into the scalar cache for later segments.
 __device__ __forceinline__ MultiRanges multi_start(const MultiArgs& a, ProjView& pv0, int& kind0) {
   const uint32_t* row = reinterpret_cast<const uint32_t*>(&a.first[blockIdx.x][0]);
-  const MultiRanges rg{row[0], row[1], row[2], row[3]};
+  const MultiRanges rg{row[0], row[1], *reinterpret_cast<const uint32_t*>(&a.count[blockIdx.x][0])};
   pv0 = multi_view(a.proj[0]);
   kind0 = a.proj[0].kind;
   // empty asm statements that use the values keep their loads in this first
   // round trip (the compiler would otherwise sink them below the X loads)
-  asm volatile("" ::"s"(rg.r0), "s"(rg.r1), "s"(rg.r2), "s"(rg.r3), "s"(pv0.wq), "s"(pv0.scales), "s"(pv0.y),
+  asm volatile("" ::"s"(rg.f01), "s"(rg.f23), "s"(rg.cnt), "s"(pv0.wq), "s"(pv0.scales), "s"(pv0.y),
                "s"(pv0.p0_bytes), "s"(pv0.p1_bytes), "s"(pv0.s_bytes), "s"(pv0.Nout), "s"(pv0.Ncols),
                "s"(pv0.up_off), "s"(kind0));
   asm volatile("" ::"s"(a.x), "s"(a.x_bytes), "s"(a.T), "s"(a.K), "s"(a.G), "s"(a.pairs), "s"(a.ppw),
@@ -1440,12 +1443,15 @@ int run_unpack(int K, int N, int bits, int group, const void* wq, const void* sc
 struct MultiPlan {
   int key[3 + 2 * dev::kMultiMaxProj];  // grid bound, K, nproj, then (kind, Nout) per projection
   int grid;
-  uint16_t first[dev::kMultiMaxWg + 1][dev::kMultiMaxProj];
+  uint16_t first[dev::kMultiMaxWg][dev::kMultiMaxProj];
+  uint8_t count[dev::kMultiMaxWg][dev::kMultiMaxProj];
 };
 
 // Longest tiles first, each to the least loaded workgroup (lowest rank on a
-// tie).  The cost of a tile is its weight and scale bytes.  Returns false
-// when a projection has more tiles than the table holds.
+// tie).  The cost of a tile is its weight and scale bytes.  Ranks own
+// contiguous tile ranges and are placed on blocks XCD-grouped (block b runs
+// on XCD b % 8; ranks r, r + 1, ... of one XCD are its blocks in order).
+// Returns false when a projection has more tiles than the table holds.
 bool make_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, MultiPlan& pl) {
   struct P {
     double cost;
@@ -1463,23 +1469,40 @@ bool make_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, M
   }
   pl.grid = (int)std::min<long>(total, wg_max);
   std::memset(pl.first, 0, sizeof(pl.first));
+  std::memset(pl.count, 0, sizeof(pl.count));
   if (pl.grid == 0) return true;
   int cnt[dev::kMultiMaxProj][dev::kMultiMaxWg] = {};
   std::stable_sort(ps, ps + nproj, [](const P& a, const P& b) { return a.cost > b.cost; });
-  using Slot = std::pair<double, int>;  // (load, rank)
+  // (load, tie order, rank); on equal loads the tie order takes one rank of
+  // each XCD in turn, so the more loaded ranks spread over the XCDs
+  const int G = pl.grid, per_xcd = (G + 7) / 8;
+  using Slot = std::tuple<double, int, int>;
   std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
-  for (int r = 0; r < pl.grid; ++r) heap.push({0.0, r});
+  for (int r = 0; r < G; ++r) heap.push({0.0, (r % per_xcd) * 8 + r / per_xcd, r});
   for (int i = 0; i < nproj; ++i) {
     for (int k = 0; k < ps[i].tiles; ++k) {
       Slot s = heap.top();
       heap.pop();
-      ++cnt[ps[i].p][s.second];
-      s.first += ps[i].cost;
+      ++cnt[ps[i].p][std::get<2>(s)];
+      std::get<0>(s) += ps[i].cost;
       heap.push(s);
     }
   }
+  int start[dev::kMultiMaxProj][dev::kMultiMaxWg];  // first tile of each rank
   for (int p = 0; p < nproj; ++p) {
-    for (int r = 0; r < pl.grid; ++r) pl.first[r + 1][p] = (uint16_t)(pl.first[r][p] + cnt[p][r]);
+    int acc = 0;
+    for (int r = 0; r < G; ++r) {
+      if (cnt[p][r] > 255) return false;  // the count table holds 8 bits
+      start[p][r] = acc;
+      acc += cnt[p][r];
+    }
+  }
+  for (int b = 0; b < G; ++b) {
+    const int xcd = b & 7, r = xcd * (G >> 3) + std::min(xcd, G & 7) + (b >> 3);
+    for (int p = 0; p < nproj; ++p) {
+      pl.first[b][p] = (uint16_t)start[p][r];
+      pl.count[b][p] = (uint8_t)cnt[p][r];
+    }
   }
   return true;
 }
@@ -1609,6 +1632,7 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
   a.mask_base = dev::kMasks.base;
   a.mask_hi = dev::kMasks.hi;
   std::memcpy(a.first, pl->first, sizeof(a.first));
+  std::memcpy(a.count, pl->count, sizeof(a.count));
   using Kern = void (*)(dev::MultiArgs);
   static const Kern kernels[2] = {dev::gemm_multi_kernel<false>, dev::gemm_multi_kernel<true>};
   static std::once_flag raised;

@@ -84,6 +84,16 @@ class Stack:
             self._multi.append((NgqProj * 3)(*(NgqProj(f, N, int(kind == "swiglu"), 0, w, sc, o.data_ptr())
                                                for (kind, _, N, f, w, sc), o in zip(calls[:3], outs))))
 
+    def project(self, i: int, stream=None):
+        """Enqueue only the three projections of x of layer i (QK, gate/value,
+        gate/up + SwiGLU) as one ngq_multi_gemm call."""
+        import torch
+
+        main = torch.cuda.current_stream() if stream is None else stream
+        st = lib().ngq_multi_gemm(self.T, HIDDEN, NGQ_GROUP, self.x.data_ptr(), self._multi[i], 3, main.cuda_stream)
+        if st != 0:
+            raise NgqError(st, f"layer {i} qk+gv+gate_up")
+
     def layer(self, i: int, stream=None):
         """Enqueue layer i (x -> x) on `stream` (a torch.cuda.Stream; the current
         stream by default)."""
@@ -101,7 +111,7 @@ class Stack:
                 raise NgqError(st, f"layer {i} {where}")
 
         if self.fused:
-            check(L.ngq_multi_gemm(T, HIDDEN, NGQ_GROUP, xp, self._multi[i], 3, main.cuda_stream), "qk+gv+gate_up")
+            self.project(i, main)
             check(L.ngq_gemm(T, K3, N3, f3, NGQ_GROUP, hp, w3, s3, zp, main.cuda_stream), "down")
             check(L.ngq_rms_rescale(T, HIDDEN, zp, xp, main.cuda_stream), "rescale")
             return
