@@ -10,10 +10,11 @@ replicas totalling > 1 GiB, so every step streams its weights from HBM rather
 than from the 256 MB Infinity Cache.  Steps are timed with HIP events on the
 stream the kernels run on.  The line printed also carries the sweep the metric
 asks for (T = 1, 2, 4, 8 for the int4 QK and int5 gate/value projections, and
-the SwiGLU pair), the stacked-layer sweep (64 layers of distinct weights,
-eager and as a replayed graph), the roofline of the dominant kernel, a parity
-check of the timed configuration against the oracle and the oracle's own CPU
-time.
+the SwiGLU pair, the fused QK + gate/value + gate/up launch and the split-K
+down projection), the stacked-layer sweep (64 layers of distinct weights,
+eager and as replayed graphs), the roofline of the dominant kernel, and the
+CPU leg: the oracle's own CPU time and, from the same oracle, the parity of
+the timed configuration.
 """
 from __future__ import annotations
 
@@ -169,6 +170,9 @@ def run_swiglu(ngq, T, steps, warmup):
     ms_gu = time_steps(lambda i: ngq.ngq_swiglu_gemm(rg.x, rg.wq[i], rg.s[i], 4, n_ff, h=h), rg.replicas, steps,
                        warmup)
     ms_dn = time_steps(lambda i: ngq.ngq_gemm(h, rd.wq[i], rd.s[i], 4, wdn.N, y=y), rd.replicas, steps, warmup)
+    ws = torch.empty(ngq.ngq_splitk_workspace_bytes(wdn.K, wdn.N, 4), dtype=torch.uint8, device="cuda")
+    ms_sk = time_steps(lambda i: ngq.ngq_gemm_splitk(h, rd.wq[i], rd.s[i], 4, wdn.N, y=y, workspace=ws),
+                       rd.replicas, steps, warmup)
     b_gu = algorithmic_bytes(ngq, wgu, T, n_out=n_ff)
     b_dn = algorithmic_bytes(ngq, wdn, T)
     del rg, rd
@@ -178,43 +182,38 @@ def run_swiglu(ngq, T, steps, warmup):
          "GBps": b_gu / ms_gu / 1e6, "pct_peak": 100 * b_gu / ms_gu / 1e6 / PEAK_GBS},
         {"workload": "down int4 K=17408 N=5120", "T": T, "us": ms_dn * 1e3,
          "GBps": b_dn / ms_dn / 1e6, "pct_peak": 100 * b_dn / ms_dn / 1e6 / PEAK_GBS},
+        {"workload": "down int4 K=17408 N=5120, ngq_gemm_splitk (two launches)", "T": T, "us": ms_sk * 1e3,
+         "GBps": b_dn / ms_sk / 1e6, "pct_peak": 100 * b_dn / ms_sk / 1e6 / PEAK_GBS},
     ]
 
 
-def parity_check(ngq, rot, y_dev):
-    """Recompute replica 0 and compare sampled columns with the oracle."""
+def gpu_output(ngq, rot, y_dev):
+    """Recompute replica 0 on the GPU; host copies of its inputs and output."""
     import numpy as np
     import torch
 
-    import oracle
-    from tests.parity import compare
-
-    w, T = rot.w, rot.T
+    w = rot.w
     ngq.ngq_gemm(rot.x, rot.wq[0], rot.s[0], w.bits, w.N, y=y_dev)
     torch.cuda.synchronize()
     yb = y_dev.view(torch.int16).cpu().numpy().view(np.uint16)
     packed = rot.wq[0].cpu().numpy()
     scales = rot.s[0].view(torch.int16).cpu().numpy().view(np.uint16)
     x = rot.x.view(torch.int16).cpu().numpy().view(np.uint16)
-    g = np.random.default_rng(7)
-    cols = np.unique(np.concatenate([np.arange(32), np.arange(w.N - 32, w.N), g.integers(0, w.N, 192)]))
-    y64, axw, axs = oracle.gemm(x, packed, scales, w.K, w.N, w.bits, w.scale_bf16, cols=cols.astype(np.int32),
-                                nthreads=8, with_bounds=True)
-    rep = compare(yb[:, cols], y64, axw, axs, w.K, w.bits)
-    rep["columns_checked"] = int(cols.size)
-    return rep, (x, packed, scales)
+    return x, packed, scales, yb
 
 
 def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
     """The stacked-layer sweep: `layers` layers with distinct weights (QK, gate/
     value, gate/up + SwiGLU, down, RMS rescale each), chained through the
     rescaled down output.  Timed per full pass from x0 as a captured graph with
-    the three projections of x fused into one ngq_multi_gemm call (the
-    reported figure), and for comparison eager (one library call at a time
-    from Python, unfused), as a graph of the unfused calls in order, and as a
-    graph with QK and gate/value on side streams.  Every variant must produce
-    the eager output bit for bit.  The weights far exceed the caches, so every
-    pass streams them from HBM."""
+    the three projections of x fused into one ngq_multi_gemm call and the
+    down projection split over K (the reported figure), and for comparison
+    eager (one library call at a time from Python, unfused), as a graph of the
+    unfused calls in order, and as a graph with QK and gate/value on side
+    streams.  Each graph must reproduce its own eager output bit for bit; the
+    fused chain follows the unfused one up to rounding (its down projection
+    groups the fp32 sums differently).  The weights far exceed the caches, so
+    every pass streams them from HBM."""
     import numpy as np
     import torch
 
@@ -255,8 +254,14 @@ def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
         graph_ms, gx = time_graph(st, x0)
         same = bool(torch.equal(gx, eager_x))
         fz = Stack(weights, T, fused=True)
+        fz.forward(x0)
+        fused_eager_x = fz.x.clone()
         fused_ms, fx = time_graph(fz, x0)
-        fused_same = bool(torch.equal(fx, eager_x))
+        fused_same = bool(torch.equal(fx, fused_eager_x))
+        # the split-K down projection groups its sums differently: the fused
+        # chain follows the unfused one up to rounding
+        fused_rel = float(torch.linalg.vector_norm((fx.float() - eager_x.float())) /
+                          torch.linalg.vector_norm(eager_x.float()))
         del fz
         conc_ms = None
         if side:
@@ -269,7 +274,7 @@ def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
                     "eager_us_per_layer": eager_ms * 1e3 / layers,
                     "graph_us_per_layer": fused_ms * 1e3 / layers, "graph_ms_per_pass": fused_ms,
                     "bytes_per_pass": b, "GBps": b / fused_ms / 1e6, "pct_peak": 100 * b / fused_ms / 1e6 / PEAK_GBS,
-                    "graph_matches_eager": fused_same,
+                    "graph_matches_eager": fused_same, "rel_l2_vs_unfused": fused_rel,
                     "unfused_graph_us_per_layer": graph_ms * 1e3 / layers, "unfused_graph_matches_eager": same,
                     "side_streams_graph_us_per_layer": None if conc_ms is None else conc_ms * 1e3 / layers})
         del st
@@ -326,14 +331,17 @@ def run_fused(ngq, Ts, steps, sets=8):
     return out
 
 
-def cpu_baseline(w, T, host_inputs, bytes_full):
-    """The oracle as it stands, on the host cores, over a column sample of the
-    same projection; scaled to the full projection's bytes."""
+def cpu_baseline(w, T, host, bytes_full):
+    """The CPU leg: the oracle as it stands timed on the host cores over the
+    whole projection of replica 0, and the parity of the GPU's output for that
+    replica against the oracle on sampled columns (the only place bench.py
+    runs the oracle)."""
     import numpy as np
 
     import oracle
+    from tests.parity import compare
 
-    x, packed, scales = host_inputs
+    x, packed, scales, yb = host
     threads = max(1, min(16, os.cpu_count() or 1))
     ncols = w.N  # the whole projection: ~8 s of single-core work at T=8
     cols = np.arange(ncols, dtype=np.int32)
@@ -341,7 +349,7 @@ def cpu_baseline(w, T, host_inputs, bytes_full):
     oracle.gemm(x, packed, scales, w.K, w.N, w.bits, w.scale_bf16, cols=cols, nthreads=threads)
     dt = time.perf_counter() - t0
     frac = ncols / w.N
-    return {
+    cpu = {
         "value": bytes_full * frac / dt / 1e9,
         "unit": "GB/s",
         "cores": threads,
@@ -350,6 +358,13 @@ def cpu_baseline(w, T, host_inputs, bytes_full):
                   f"{threads} threads), {dt:.2f} s wall; value = its algorithmic bytes / wall time",
         "us_per_projection_equiv": dt / frac * 1e6,
     }
+    g = np.random.default_rng(7)
+    pcols = np.unique(np.concatenate([np.arange(32), np.arange(w.N - 32, w.N), g.integers(0, w.N, 192)]))
+    y64, axw, axs = oracle.gemm(x, packed, scales, w.K, w.N, w.bits, w.scale_bf16, cols=pcols.astype(np.int32),
+                                nthreads=8, with_bounds=True)
+    parity = compare(yb[:, pcols], y64, axw, axs, w.K, w.bits)
+    parity["columns_checked"] = int(pcols.size)
+    return cpu, parity
 
 
 def kernel_sha():
@@ -400,8 +415,7 @@ def main():
     ngq.ngq_gemm(rot.x, rot.wq[last], rot.s[last], w.bits, w.N, y=y)
     torch.cuda.synchronize()
     graph_ok = bool(torch.equal(y_graph, y))
-    parity, host_inputs = parity_check(ngq, rot, y)
-    parity["graph_replay_matches_eager"] = graph_ok
+    host = gpu_output(ngq, rot, y)
     cold = rot.cold_bytes
     replicas = rot.replicas
     del rot
@@ -436,7 +450,9 @@ def main():
     # last: its 4 GiB stream and 1 GiB copies leave the next measurement slow
     calib = {} if args.no_calibration else calibrate(ngq)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, T, host_inputs, nbytes)
+    cpu, parity = (None, {"oracle": "not run (--no-cpu-baseline)"}) if args.no_cpu_baseline else \
+        cpu_baseline(w, T, host, nbytes)
+    parity["graph_replay_matches_eager"] = graph_ok
 
     traffic = traffic_for(args.workload, T)
     names = {"qk": "GDN-QK-like Q4 projection", "gv": "attention gate/value-like Q5 projection"}

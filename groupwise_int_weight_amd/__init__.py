@@ -52,6 +52,8 @@ SIGNATURES = {
     "ngq_unpack_codes": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_dequant_f32": (_INT, [_INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR]),
     "ngq_multi_gemm": (_INT, [_INT, _INT, _INT, _PTR, ctypes.POINTER(NgqProj), _INT, _PTR]),
+    "ngq_splitk_workspace_bytes": (_SIZE, [_INT, _INT, _INT, _INT]),
+    "ngq_gemm_splitk": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR, _SIZE, _PTR]),
     "ngq_rms_rescale": (_INT, [_INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
     "ngq_debug_force_kernel": (_INT, [_INT]),
@@ -183,6 +185,31 @@ def ngq_swiglu_gemm(x, wq_gate_up, scales_gate_up, bits: int, N_ff: int, h=None,
     return h
 
 
+def ngq_splitk_workspace_bytes(K: int, N: int, bits: int, group: int = NGQ_GROUP) -> int:
+    return int(lib().ngq_splitk_workspace_bytes(K, N, bits, group))
+
+
+def ngq_gemm_splitk(x, wq, scales, bits: int, N: int, y=None, workspace=None, group: int = NGQ_GROUP, stream=None):
+    """ngq_gemm with K split over several workgroups per column tile (long K,
+    few tiles); `workspace` (a device uint8 tensor of at least
+    ngq_splitk_workspace_bytes bytes) is allocated when not given."""
+    import torch
+
+    T, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(16, ngq_splitk_workspace_bytes(K, N, bits, group)), dtype=torch.uint8,
+                                device=x.device)
+    st = lib().ngq_gemm_splitk(T, K, N, _format_bits(bits, scales), group, _dev_ptr(x, "x"), _dev_ptr(wq, "wq"),
+                               _dev_ptr(scales, "scales"), _dev_ptr(y, "y"), _dev_ptr(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "ngq_gemm_splitk")
+    return y
+
+
 def ngq_multi_gemm(x, projs, group: int = NGQ_GROUP, stream=None):
     """Several projections of the same x in one launch.  `projs` is a list of
     dicts with keys wq, scales, bits, n and optionally swiglu (False) and y;
@@ -253,7 +280,8 @@ def ngq_debug_force_kernel(path: int) -> int:
 
 
 __all__ = [
-    "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
+    "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_gemm_splitk", "ngq_splitk_workspace_bytes",
+    "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
     "ngq_debug_force_kernel",
     "ngq_packed_bytes", "ngq_scale_bytes", "ngq_strerror", "ngq_version", "NgqError", "NgqLibraryMissing",
     "lib", "SIGNATURES", "NgqProj",

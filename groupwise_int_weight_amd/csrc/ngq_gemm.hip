@@ -594,9 +594,11 @@ struct ProjView {
   int Nout, Ncols, up_off;
 };
 
-// Shape constants shared by every projection of a launch.
+// Shape constants shared by every projection of a launch.  K is the length
+// of the X rows in LDS: the whole K, or a K slice of pairs p0 .. pend - 1
+// (split K); G and pairs count the groups and pairs of the whole K.
 struct XresShape {
-  int T, K, G, pairs, ppw;
+  int T, K, G, pairs, ppw, p0, pend;
 };
 
 __device__ __forceinline__ XresLane xres_lane(int T, int K, uint32_t mask_nib, uint32_t mask_base, uint32_t mask_hi) {
@@ -656,6 +658,58 @@ __device__ __forceinline__ void x_stage(uint8_t* smem, const uint32_t (&xv)[XL][
   lds_barrier();
 }
 
+// The loads of one pair of a column tile: P0 (two rows per 8-k block for
+// int8), the int5 high bits and the scales, bounds-checked (an invalid pair
+// reads out of range: nothing).  The lane's offsets within a tile are
+// computed once.
+template <int BITS, int V, int NSETS>
+struct PairLoads {
+  static constexpr int WPK = BITS == 8 ? 2 : 1;
+  __amdgpu_buffer_rsrc_t rW, rP1, rS;
+  uint32_t rowb, offA[NSETS], offP1[NSETS], offS[NSETS];
+
+  __device__ __forceinline__ PairLoads(const ProjView& pv, const XresLane& ln) {
+    rW = make_rsrc(pv.wq, pv.p0_bytes);
+    rP1 = make_rsrc(static_cast<const char*>(pv.wq) + pv.p0_bytes, pv.p1_bytes);
+    rS = make_rsrc(pv.scales, pv.s_bytes);
+    rowb = (uint32_t)pv.Ncols * 4u;
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) {
+      const uint32_t col = (uint32_t)(s * pv.up_off + V * ln.m);
+      offA[s] = ln.lane_kb * WPK * rowb + col * 4u;
+      offP1[s] = 2u * (uint32_t)(ln.q >> 1) * rowb + col * 4u;
+      offS[s] = (uint32_t)ln.h * (uint32_t)pv.Ncols * 2u + (uint32_t)(s * pv.up_off + 4 * V * ln.q) * 2u;
+    }
+  }
+
+  // pair p of the tile at column c0 (flags combined bitwise, so that no
+  // lane-divergent branch appears)
+  template <class Buf>
+  __device__ __forceinline__ void issue(Buf& buf, uint32_t c0, int p, bool valid) const {
+    const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb + c0 * 4u : kOOB;
+    const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb + c0 * 4u : kOOB;
+    const uint32_t ps = valid ? (uint32_t)p * rowb + c0 * 2u : kOOB;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const uint32_t o = offA[s] + pa + (uint32_t)st * 2u * WPK * rowb;
+        load_words<V>(&buf.a[s][st][0], rW, o);
+        if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
+      }
+    }
+    if constexpr (BITS == 5) {
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        load_words<V>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
+        load_words<V>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) load_words<2 * V>(&buf.sc[s][0], rS, offS[s] + ps);
+  }
+};
+
 // Per-group partial sums of pair p of a tile, before scaling: the pair's
 // weight words in `buf` against X in LDS, each lane's B slot being token t of
 // group half h.  The -(128 + bias) sum_k x term seeds every partial.
@@ -668,7 +722,7 @@ __device__ __forceinline__ void pair_partials(const Buf& buf, int p, const XresS
   // its lanes read zeros
   const bool half = (p == sh.pairs - 1) & ((sh.G & 1) != 0);
   const bool on = ln.b_on & !(half & (ln.h == 1));
-  const uint32_t src = on ? ln.bsrc + (uint32_t)p * 256u : 0u;
+  const uint32_t src = on ? ln.bsrc + (uint32_t)(p - sh.p0) * 256u : 0u;
   bf16x8 bfrag[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st)
@@ -777,67 +831,32 @@ __device__ __forceinline__ void finish_outputs(const float* part, const ProjView
 // X staging of the prologue, or nothing when X is already in LDS).  In the
 // last NB slots of the last tile, `drain(buf[u], u)` issues what follows the
 // loop into the freed buffers (the next segment's first pairs, or nothing).
-// The LDS partial-sum region is free on entry and on return.
-template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, class Buf, class Stage, class Drain>
+// `finish(part, c0)` turns the wave blocks of the tile at column c0 into its
+// outputs.  The LDS partial-sum region is free on entry and on return.
+template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, class Buf, class Stage, class Drain, class Finish>
 __device__ __forceinline__ void xres_tiles(const ProjView& pv, const XresShape& sh, const XresLane& ln, uint8_t* smem,
                                            int tbase, int tstride, int ntiles, Buf (&buf)[NB], bool primed,
-                                           Stage&& stage, Drain&& drain) {
-  constexpr int WPK = BITS == 8 ? 2 : 1;
+                                           Stage&& stage, Drain&& drain, Finish&& finish) {
   constexpr int TILE = 16 * V;
   constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
   float* const part = reinterpret_cast<float*>(smem + XSmem::x_end(sh.T, sh.K));
-  const int wave = ln.wave, m = ln.m, q = ln.q, h = ln.h;
+  const int wave = ln.wave;
 
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(pv.wq, pv.p0_bytes);
-  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(pv.wq) + pv.p0_bytes, pv.p1_bytes);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(pv.scales, pv.s_bytes);
-
-  const uint32_t rowb = (uint32_t)pv.Ncols * 4u;
-  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];  // tile-independent parts
-#pragma unroll
-  for (int s = 0; s < NSETS; ++s) {
-    const uint32_t col = (uint32_t)(s * pv.up_off + V * m);
-    offA[s] = ln.lane_kb * WPK * rowb + col * 4u;
-    offP1[s] = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
-    offS[s] = (uint32_t)h * (uint32_t)pv.Ncols * 2u + (uint32_t)(s * pv.up_off + 4 * V * q) * 2u;
-  }
-
-  // Loads of pair p of tile i (nothing when either is out of range).  Flags
-  // are combined bitwise so that no lane-divergent branch appears.
+  const PairLoads<BITS, V, NSETS> ld(pv, ln);
+  // loads of pair p of tile i (nothing when either is out of range)
   auto issue_at = [&](Buf& buf, int ti, int p) {
-    const bool valid = (ti < ntiles) & (p < sh.pairs);
-    const uint32_t c0 = (uint32_t)((tbase + tstride * ti) * TILE);
-    const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb + c0 * 4u : kOOB;
-    const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb + c0 * 4u : kOOB;
-    const uint32_t ps = valid ? (uint32_t)p * rowb + c0 * 2u : kOOB;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-      for (int s = 0; s < NSETS; ++s) {
-        const uint32_t o = offA[s] + pa + (uint32_t)st * 2u * WPK * rowb;
-        load_words<V>(&buf.a[s][st][0], rW, o);
-        if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
-      }
-    }
-    if constexpr (BITS == 5) {
-#pragma unroll
-      for (int s = 0; s < NSETS; ++s) {
-        load_words<V>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
-        load_words<V>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < NSETS; ++s) load_words<2 * V>(&buf.sc[s][0], rS, offS[s] + ps);
+    ld.issue(buf, (uint32_t)((tbase + tstride * ti) * TILE), p, (ti < ntiles) & (p < sh.pend));
   };
 
   // item (tile i, slot k) is pair wave + W k of tile i; every tile has ppw
   // slots (the same for all waves, a multiple of NB), of which the first cnt
   // are real pairs
-  const int cnt = sh.pairs > wave ? (sh.pairs - wave + W - 1) / W : 0;
+  const int npairs = sh.pend - sh.p0;
+  const int cnt = npairs > wave ? (npairs - wave + W - 1) / W : 0;
   const int cntp = sh.ppw;
   int is_tile = 0, is_k = 0;  // next item to issue
   auto issue_next = [&](Buf& b, bool do_issue) {
-    if (do_issue) issue_at(b, is_tile, is_k < cnt ? wave + W * is_k : sh.pairs);
+    if (do_issue) issue_at(b, is_tile, is_k < cnt ? sh.p0 + wave + W * is_k : sh.pend);
     if (++is_k == cntp) {
       is_k = 0;
       ++is_tile;
@@ -867,7 +886,7 @@ __device__ __forceinline__ void xres_tiles(const ProjView& pv, const XresShape& 
     for (int u = 0; u < NB; ++u) {
       if (kk + u < cnt) {
         f32x4 dp[NSETS][V];
-        pair_partials<BITS, V, NSETS>(buf[u], wave + W * (kk + u), sh, ln, smem, dp);
+        pair_partials<BITS, V, NSETS>(buf[u], sh.p0 + wave + W * (kk + u), sh, ln, smem, dp);
         scale_accumulate<V, NSETS>(buf[u], SBF16, dp, acc);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -889,7 +908,7 @@ __device__ __forceinline__ void xres_tiles(const ProjView& pv, const XresShape& 
     store_partials<V, NSETS>(acc, ln, part + (uint32_t)wave * BLK);
     clear_acc();
     lds_barrier();
-    finish_outputs<V, NSETS, W>(part, pv, sh.T, (tbase + tstride * ti) * TILE);
+    finish(part, (tbase + tstride * ti) * TILE);
     lds_barrier();
   }
 }
@@ -912,11 +931,12 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
   x_load<XL, W>(xv, a.x, a.x_bytes, a.T, a.K);
   __builtin_amdgcn_sched_barrier(0);
   const ProjView pv{a.wq, a.scales, a.y, a.p0_bytes, a.p1_bytes, a.s_bytes, a.Nout, a.Ncols, a.up_off};
-  const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw};
+  const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw, 0, a.pairs};
   WBuf<BITS, V, NSETS> buf[NB];
   xres_tiles<BITS, SBF16, V, NSETS, W, NB>(
       pv, sh, ln, smem, rank, G, my_tiles, buf, false, [&]() { x_stage<XL, W>(smem, xv, a.T, a.K); },
-      [](WBuf<BITS, V, NSETS>&, int) {});
+      [](WBuf<BITS, V, NSETS>&, int) {},
+      [&](const float* part, int c0) { finish_outputs<V, NSETS, W>(part, pv, a.T, c0); });
 }
 
 // ---- several projections of one X in one launch ----------------------------
@@ -1049,7 +1069,7 @@ __global__ __launch_bounds__(kMultiW * 64) void gemm_multi_kernel(MultiArgs a) {
   int kind0;
   const MultiRanges rg = multi_start(a, pv0, kind0);
   const XresLane ln = xres_lane(a.T, a.K, a.mask_nib, a.mask_base, a.mask_hi);
-  const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw};
+  const XresShape sh{a.T, a.K, a.G, a.pairs, a.ppw, 0, a.pairs};
 
   uint32_t xv[BIGX ? 1 : XL][4];
   if constexpr (BIGX)
@@ -1075,8 +1095,10 @@ __global__ __launch_bounds__(kMultiW * 64) void gemm_multi_kernel(MultiArgs a) {
 #define NGQ_MULTI_CASE(BITS, SBF16, NSETS)                                                                       \
   case multi_kind(BITS, SBF16, NSETS): {                                                                         \
     WBuf<BITS, multi_v(BITS, NSETS), NSETS> buf[NB];                                                             \
-    xres_tiles<BITS, SBF16, multi_v(BITS, NSETS), NSETS, W, NB>(pv, sh, ln, smem, f, 1, n, buf, false, stage,     \
-                                                                no_drain);                                       \
+    xres_tiles<BITS, SBF16, multi_v(BITS, NSETS), NSETS, W, NB>(                                                 \
+        pv, sh, ln, smem, f, 1, n, buf, false, stage, no_drain, [&](const float* part, int c0) {                  \
+          finish_outputs<multi_v(BITS, NSETS), NSETS, W>(part, pv, a.T, c0);                                      \
+        });                                                                                                      \
     break;                                                                                                       \
   }
       NGQ_MULTI_CASE(4, false, 1) NGQ_MULTI_CASE(4, false, 2) NGQ_MULTI_CASE(4, true, 1) NGQ_MULTI_CASE(4, true, 2)
@@ -1087,6 +1109,123 @@ __global__ __launch_bounds__(kMultiW * 64) void gemm_multi_kernel(MultiArgs a) {
         break;
     }
   }
+}
+
+// ---- split K: long K over few column tiles ----------------------------------
+//
+// A projection with long K and few 32-column tiles (the down projection: K =
+// 17408, 160 tiles) leaves CUs idle with one workgroup per tile, and at T = 8
+// its X does not fit in LDS.  Here K is cut into S slices of whole group pairs
+// and a unit is one column tile over one slice.  A workgroup of kSplitWaves
+// waves takes kSplitWaves tiles of slice b % S (with S = 8, each XCD works on
+// one slice and its workgroups share that slice of X through their L2); only
+// that slice of X is staged in LDS, and each wave streams its own unit's
+// pairs, kSplitNB in flight, with no pair slot left empty and no barrier after
+// the staging.  Each unit's fp32 sum goes to partial[slice][t][n] in a
+// caller's workspace, and a second kernel adds the S partials of every output
+// in slice order and rounds to bf16, so the result is deterministic.
+
+constexpr int kSplitWaves = 5, kSplitNB = 4;
+
+struct SplitArgs {
+  const void* x;
+  const void* wq;
+  const void* scales;
+  float* partial;  // [S][T][N]
+  int T, K, N, G, pairs, ntiles, S, pps;
+  uint32_t p0_bytes, p1_bytes, s_bytes, x_bytes;
+  uint32_t mask_nib, mask_base, mask_hi;
+};
+
+// XL chunks per thread of a K slice of X: chunk c is 16 bytes at k-chunk
+// c % (kx / 8) of row c / (kx / 8), rows of K.
+template <int XL, int W>
+__device__ __forceinline__ void x_load_slice(uint32_t (&xv)[XL][4], const void* x, uint32_t x_bytes, int T, int K,
+                                             int k0, int kx) {
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(x, x_bytes);
+  const int rowch = kx >> 3, nch = T * rowch;
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    const int c = threadIdx.x + W * 64 * j;
+    const int tt = c / rowch, kc = c - tt * rowch;
+    const uint32_t off = c < nch ? ((uint32_t)tt * (uint32_t)K + (uint32_t)k0) * 2u + (uint32_t)kc * 16u : kOOB;
+    load_words<4>(xv[j], rX, off);
+  }
+}
+
+template <int BITS, bool SBF16, int XL>
+__global__ __launch_bounds__(kSplitWaves * 64) void gemm_splitk_kernel(SplitArgs a) {
+  constexpr int W = kSplitWaves, NB = kSplitNB, V = 2, TILE = 16 * V;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int b = blockIdx.x, ks = b % a.S, j = b / a.S;
+  const int p0 = ks * a.pps, pend = min(p0 + a.pps, a.pairs), n = pend - p0;
+  const int kx = min(a.K, pend * 128) - p0 * 128;  // the slice's k (its last pair may hold one group)
+  const XresLane ln = xres_lane(a.T, kx, a.mask_nib, a.mask_base, a.mask_hi);
+  const int tile = j * W + ln.wave;  // past the last tile, the wave only helps stage X
+  const bool live = tile < a.ntiles;
+  const uint32_t c0 = (uint32_t)(tile * TILE);
+  uint32_t xv[XL][4];
+  x_load_slice<XL, W>(xv, a.x, a.x_bytes, a.T, a.K, p0 * 128, kx);
+  __builtin_amdgcn_sched_barrier(0);
+  const ProjView pv{a.wq, a.scales, nullptr, a.p0_bytes, a.p1_bytes, a.s_bytes, a.N, a.N, 0};
+  const PairLoads<BITS, V, 1> ld(pv, ln);
+  const XresShape sh{a.T, kx, a.G, a.pairs, 0, p0, pend};
+  WBuf<BITS, V, 1> buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    ld.issue(buf[u], c0, p0 + u, live & (u < n));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  x_stage<XL, W>(smem, xv, a.T, kx);
+
+  f32x4 acc[1][V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[0][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < n; k += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (k + u < n) {
+        f32x4 dp[1][V];
+        pair_partials<BITS, V, 1>(buf[u], p0 + k + u, sh, ln, smem, dp);
+        scale_accumulate<V, 1>(buf[u], SBF16, dp, acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      ld.issue(buf[u], c0, p0 + k + u + NB, live & (k + u + NB < n));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // slots j and j + 8 hold the two group halves of token j: added here, and
+  // the lanes of the first half write the unit's sums
+  float* const out = a.partial + (size_t)ks * a.T * a.N;
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int other =
+          __builtin_amdgcn_mov_dpp(__float_as_int(acc[0][i][r]), 0x128 /* row_ror:8 */, 0xF, 0xF, false);
+      const float sum = acc[0][i][r] + __int_as_float(other);
+      const int col = (int)c0 + V * (4 * ln.q + r) + i;
+      if (live & (ln.h == 0) & (ln.t < a.T) & (col < a.N)) out[(size_t)ln.t * a.N + col] = sum;
+    }
+}
+
+// y[e] = bf16(partial[0][e] + partial[1][e] + ... + partial[S-1][e]), in slice
+// order; e runs over the T N outputs, four per thread (N % 4 == 0).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int S, int TN,
+                                                            uint16_t* __restrict__ y) {
+  const int e = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (e >= TN) return;
+  float4 acc = *reinterpret_cast<const float4*>(partial + e);
+  for (int ks = 1; ks < S; ++ks) {
+    const float4 v = *reinterpret_cast<const float4*>(partial + (size_t)ks * TN + e);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const uint32_t lo = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+  const uint32_t hi = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+  *reinterpret_cast<u32x2*>(y + e) = u32x2{lo, hi};
 }
 
 // ---- debug kernels: the GEMM's unpack and scale decoding, materialised ----
@@ -1650,6 +1789,97 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
 
+
+// ---- split K (host) ----
+
+constexpr int kSplitMax = 8;  // slices; the workspace is sized for this many
+
+// Workspace bytes of the split-K call: the fp32 partials of kSplitMax slices
+// at NGQ_MAX_T tokens.
+size_t splitk_workspace_bytes(int N) { return (size_t)kSplitMax * NGQ_MAX_T * (size_t)N * 4u; }
+
+// Slices for a shape: 8 (one per XCD) when X does not fit the X-resident
+// kernel's prologue (T K > 73728: the down projection at T >= 5), each slice
+// keeps at least 8 pairs and the tiles alone would leave CUs idle; 1 means no
+// split (the call runs as ngq_gemm).  Measured on MI355X for the down
+// projection (K = 17408, N = 5120): split 18.1 us against 19.1 at T = 8, but
+// no gain where X fits (17.8 against 17.7 at T = 4, 17.0 against 15.9 at
+// T = 1): with every CU busy the slices still stream at ~3 TB/s, and the
+// second launch costs ~2 us.
+int choose_splits(int T, int K, int pairs, int ntiles, int cus) {
+  if ((long)T * K <= 73728L || ntiles >= cus || pairs < kSplitMax * 8) return 1;
+  return kSplitMax;
+}
+
+template <int BITS, bool SBF16>
+hipError_t launch_splitk_b(int xl, const dev::SplitArgs& a, int grid, uint32_t lds, hipStream_t st) {
+  auto one = [&](auto kern) {
+    static bool raised = false;
+    if (lds > 64u * 1024u && !raised) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(dev::kSplitWaves * 64), lds, st, a);
+    return hipGetLastError();
+  };
+  if (xl <= 7) return one(dev::gemm_splitk_kernel<BITS, SBF16, 7>);
+  return one(dev::gemm_splitk_kernel<BITS, SBF16, 18>);
+}
+
+int run_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq, const void* scales, void* y,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  Format f;
+  int rc = parse_format(bits, group, &f);
+  if (rc != NGQ_OK) return rc;
+  if (T < 0 || T > NGQ_MAX_T) return NGQ_ERR_SHAPE;
+  if ((rc = check_kn(K, N)) != NGQ_OK) return rc;
+  const int pairs = (K / kGroup + 1) / 2, ntiles = (N + 31) / 32, cus = cu_count();
+  const int S = choose_splits(T, K, pairs, ntiles, cus);
+  if (S == 1) return run_gemm(1, T, K, N, bits, group, x, wq, scales, y, stream);
+  if (T == 0 || N == 0) return NGQ_OK;
+  const size_t xb = (size_t)T * K * 2, yb = (size_t)T * N * 2;
+  const size_t wb0 = p0_bytes(K, N, f.bits), wb1 = p1_bytes(K, N, f.bits), sb = (size_t)(K / kGroup) * N * 2;
+  const size_t pb = (size_t)S * T * N * 4;
+  if ((rc = check_ptr(y)) != NGQ_OK || (rc = check_ptr(x)) != NGQ_OK || (rc = check_ptr(wq)) != NGQ_OK ||
+      (rc = check_ptr(scales)) != NGQ_OK || (rc = check_ptr(workspace)) != NGQ_OK)
+    return rc;
+  if (workspace_bytes < pb) return NGQ_ERR_ARG;
+  if (xb >= kMaxBuffer || yb >= kMaxBuffer || wb0 + wb1 >= kMaxBuffer || sb >= kMaxBuffer || pb >= kMaxBuffer)
+    return NGQ_ERR_UNSUPPORTED;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, wq, wb0 + wb1) || overlaps(y, yb, scales, sb) ||
+      overlaps(workspace, pb, x, xb) || overlaps(workspace, pb, wq, wb0 + wb1) ||
+      overlaps(workspace, pb, scales, sb) || overlaps(workspace, pb, y, yb))
+    return NGQ_ERR_ARG;
+  dev::SplitArgs a;
+  a.x = x; a.wq = wq; a.scales = scales; a.partial = static_cast<float*>(workspace);
+  a.T = T; a.K = K; a.N = N; a.G = K / kGroup; a.pairs = pairs; a.ntiles = ntiles; a.S = S;
+  a.pps = (pairs + S - 1) / S;
+  a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
+  a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
+  const int kx = a.pps * 128;  // the longest slice
+  const long xchunks = (long)T * kx / 8;
+  const int xl = (int)((xchunks + dev::kSplitWaves * 64 - 1) / (dev::kSplitWaves * 64));
+  if (xl > 18) return NGQ_ERR_UNSUPPORTED;
+  const uint32_t lds = dev::XSmem::x_end(T, kx);
+  if (lds > kMaxLds) return NGQ_ERR_UNSUPPORTED;
+  const int grid = S * ((ntiles + dev::kSplitWaves - 1) / dev::kSplitWaves);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (f.bits == 4)
+    e = f.scale_bf16 ? launch_splitk_b<4, true>(xl, a, grid, lds, st) : launch_splitk_b<4, false>(xl, a, grid, lds, st);
+  else if (f.bits == 5)
+    e = f.scale_bf16 ? launch_splitk_b<5, true>(xl, a, grid, lds, st) : launch_splitk_b<5, false>(xl, a, grid, lds, st);
+  else
+    e = f.scale_bf16 ? launch_splitk_b<8, true>(xl, a, grid, lds, st) : launch_splitk_b<8, false>(xl, a, grid, lds, st);
+  if (e != hipSuccess) return NGQ_ERR_HIP;
+  const int TN = T * N;
+  hipLaunchKernelGGL(dev::splitk_reduce_kernel, dim3((unsigned)((TN / 4 + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const float*>(workspace), S, TN, static_cast<uint16_t*>(y));
+  return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace ngq
 
@@ -1668,6 +1898,17 @@ extern "C" int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, cons
 extern "C" int ngq_multi_gemm(int T, int K, int group, const void* x, const ngq_proj* projs, int nproj,
                               void* stream) {
   return run_multi(T, K, group, x, projs, nproj, stream);
+}
+
+extern "C" size_t ngq_splitk_workspace_bytes(int K, int N, int bits, int group) {
+  Format f;
+  if (parse_format(bits, group, &f) != NGQ_OK || check_kn(K, N) != NGQ_OK) return 0;
+  return splitk_workspace_bytes(N);
+}
+
+extern "C" int ngq_gemm_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                               const void* scales, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_splitk(T, K, N, bits, group, x, wq, scales, y, workspace, workspace_bytes, stream);
 }
 
 extern "C" int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream) {

@@ -45,7 +45,9 @@ class Stack:
 
     By default every call runs in order on the main stream.  With `fused` the
     QK, gate/value and gate/up projections are one ngq_multi_gemm launch (X
-    staged once, the tiles of all three balanced over the CUs).  With `concurrent`
+    staged once, the tiles of all three balanced over the CUs) and the down
+    projection is ngq_gemm_splitk (its 160 column tiles alone leave CUs
+    idle).  With `concurrent`
     the QK and gate/value projections, which only read x, run on two side
     streams beside the gate/up and down projections, and the main stream waits
     for them before the rescale overwrites x.  On MI355X that is slower: each
@@ -70,6 +72,11 @@ class Stack:
         self.z = torch.empty((T, HIDDEN), dtype=bf, device=device)
         self.x = torch.empty((T, HIDDEN), dtype=bf, device=device)  # the running activation
         self.side = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device)) if concurrent else ()
+        self.ws = None
+        if fused:  # the split-K down projection's workspace
+            _, K3, N3, bits3, _, _ = LAYER_PLAN[3]
+            self.ws = torch.empty(lib().ngq_splitk_workspace_bytes(K3, N3, bits3, NGQ_GROUP), dtype=torch.uint8,
+                                  device=device)
         self._calls = []
         self._multi = []
         for lw in layers:
@@ -112,7 +119,8 @@ class Stack:
 
         if self.fused:
             self.project(i, main)
-            check(L.ngq_gemm(T, K3, N3, f3, NGQ_GROUP, hp, w3, s3, zp, main.cuda_stream), "down")
+            check(L.ngq_gemm_splitk(T, K3, N3, f3, NGQ_GROUP, hp, w3, s3, zp, self.ws.data_ptr(), self.ws.numel(),
+                                    main.cuda_stream), "down")
             check(L.ngq_rms_rescale(T, HIDDEN, zp, xp, main.cuda_stream), "rescale")
             return
         if self.concurrent:

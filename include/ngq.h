@@ -109,6 +109,29 @@ int ngq_gemm(int T, int K, int N, int bits, int group, const void* x, const void
 int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
                     const void* wq_gate_up, const void* scales_gate_up, void* h, void* stream);
 
+/* Bytes of the workspace ngq_gemm_splitk needs for a K x N projection at any
+ * T <= 8 (fp32 partial sums of up to 8 K slices); 0 when the arguments are
+ * invalid.  Host only, no HIP call. */
+size_t ngq_splitk_workspace_bytes(int K, int N, int bits, int group);
+
+/* ngq_gemm for long K and few 32-column tiles (a down projection: K = 17408,
+ * N = 5120), with K split into slices of whole group pairs so that every CU
+ * has work and only a slice of X has to fit in LDS.  Each slice's fp32 sum
+ * goes to `workspace`, and a second kernel on the same stream adds the
+ * slices' sums in slice order and rounds to bf16.
+ *   workspace : device, at least ngq_splitk_workspace_bytes(K, N, bits, group)
+ *               bytes, 16-byte aligned; no initial contents are needed; it
+ *               must not overlap the other buffers, and calls that may run
+ *               at the same time must not share it (too small: NGQ_ERR_ARG)
+ * Shapes, formats and status codes as ngq_gemm.  K is split only where X
+ * does not fit the single-pass kernel's LDS (T K > 73728: the down projection
+ * at T >= 5), the tiles alone leave CUs idle and every slice keeps 8 pairs;
+ * otherwise the call runs as ngq_gemm and the workspace is not used.
+ * The fp32 sums are grouped differently from ngq_gemm's, so the two can
+ * differ in the last bit; each is deterministic. */
+int ngq_gemm_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                    const void* scales, void* y, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Several projections of the same activations in one launch.  The
  * projections of a layer that read one x (in the stacked sweep: QK,
  * gate/value and the gate/up pair) are computed as one persistent kernel, so

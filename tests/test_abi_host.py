@@ -34,7 +34,7 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     names = header_functions()
-    for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_packed_bytes",
+    for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_gemm_splitk", "ngq_packed_bytes",
                      "ngq_scale_bytes", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_rms_rescale", "ngq_strerror"]:
         assert required in names
 
@@ -209,6 +209,29 @@ def test_multi_empty_calls_are_no_ops(ngq):
     assert multi_call(ngq, 0, 64, [P_OK], x=None) == 0
     assert multi_call(ngq, 3, 64, [(4, 0, 0, 0, W, S, Y), (5, 0, 1, 0, W, S, Y)]) == 0
     assert ngq.lib().ngq_multi_gemm(1, 64, 64, X, None, 1, None) == -1
+
+
+@pytest.mark.parametrize("args,status", [
+    ((9, 17408, 5120, 4, 64, X, W, S, Y, 0x500000, 1 << 21), -2),          # T > 8
+    ((8, 17400, 5120, 4, 64, X, W, S, Y, 0x500000, 1 << 21), -2),          # K % 64
+    ((8, 17408, 5120, 7, 64, X, W, S, Y, 0x500000, 1 << 21), -3),          # bits
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, None, 1 << 21), -1),              # null workspace
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, 0x500008, 1 << 21), -4),          # misaligned workspace
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, 0x500000, 1 << 16), -1),          # workspace too small
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, Y + 64, 1 << 21), -1),            # workspace overlaps y
+    ((8, 17408, 5120, 4, 64, X, W, S, X, 0x500000, 1 << 21), -1),          # y overlaps x
+])
+def test_splitk_rejects_bad_arguments(ngq, args, status):
+    assert ngq.lib().ngq_gemm_splitk(*args, None) == status
+
+
+def test_splitk_workspace_and_empty_calls(ngq):
+    L = ngq.lib()
+    # fp32 partials of 8 slices at 8 tokens
+    assert ngq.ngq_splitk_workspace_bytes(17408, 5120, 4) == 8 * 8 * 5120 * 4
+    assert ngq.ngq_splitk_workspace_bytes(17408, 5122, 4) == 0
+    assert ngq.ngq_splitk_workspace_bytes(100, 5120, 4) == 0
+    assert L.ngq_gemm_splitk(0, 17408, 5120, 4, 64, None, None, None, None, None, 0, None) == 0
 
 
 def test_force_kernel_roundtrip(ngq):

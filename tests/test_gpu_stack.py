@@ -149,11 +149,15 @@ def test_stack_chain_properties_and_graph_replay(ngq, T, mode):
     eager = to_host_u16(st.forward(x0))
     again = to_host_u16(st.forward(x0))
     assert np.array_equal(eager, again)  # deterministic
-    if mode != "in_order":
-        # The side streams change only the order of independent work.  The
-        # fused call runs gate/up with the same 8-wave tile loop as the
-        # separate call, and only the down output (computed from h) chains.
+    if mode == "concurrent":
+        # the side streams change only the order of independent work
         assert np.array_equal(eager, to_host_u16(Stack(layers, T).forward(x0)))
+    if mode == "fused":
+        # The split-K down projection groups its fp32 sums differently, so the
+        # chain leaves the in-order one by rounding differences only.
+        ref = bf16_bits_to_f64(to_host_u16(Stack(layers, T).forward(x0)))
+        got = bf16_bits_to_f64(eager)
+        assert np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref)
     v = bf16_bits_to_f64(eager)
     assert np.all(np.isfinite(v))
     # every row leaves the rescale with unit mean square, up to bf16 rounding
