@@ -173,8 +173,18 @@ def run_swiglu(ngq, T, steps, warmup):
     ws = torch.empty(ngq.ngq_splitk_workspace_bytes(wdn.K, wdn.N, 4), dtype=torch.uint8, device="cuda")
     ms_sk = time_steps(lambda i: ngq.ngq_gemm_splitk(h, rd.wq[i], rd.s[i], 4, wdn.N, y=y, workspace=ws),
                        rd.replicas, steps, warmup)
+    xn = torch.empty((T, wdn.N), dtype=torch.bfloat16, device="cuda")
+
+    def two_calls(i):
+        ngq.ngq_gemm(h, rd.wq[i], rd.s[i], 4, wdn.N, y=y)
+        ngq.ngq_rms_rescale(y, x=xn)
+
+    ms_dr = time_steps(two_calls, rd.replicas, steps, warmup)
+    ms_fr = time_steps(lambda i: ngq.ngq_gemm_rescale(h, rd.wq[i], rd.s[i], 4, wdn.N, y=y, x_next=xn, workspace=ws),
+                       rd.replicas, steps, warmup)
     b_gu = algorithmic_bytes(ngq, wgu, T, n_out=n_ff)
     b_dn = algorithmic_bytes(ngq, wdn, T)
+    b_dr = b_dn + 2 * T * wdn.N  # and the rescaled rows written
     del rg, rd
     torch.cuda.empty_cache()
     return [
@@ -184,6 +194,10 @@ def run_swiglu(ngq, T, steps, warmup):
          "GBps": b_dn / ms_dn / 1e6, "pct_peak": 100 * b_dn / ms_dn / 1e6 / PEAK_GBS},
         {"workload": "down int4 K=17408 N=5120, ngq_gemm_splitk (two launches)", "T": T, "us": ms_sk * 1e3,
          "GBps": b_dn / ms_sk / 1e6, "pct_peak": 100 * b_dn / ms_sk / 1e6 / PEAK_GBS},
+        {"workload": "down + RMS rescale, ngq_gemm then ngq_rms_rescale", "T": T, "us": ms_dr * 1e3,
+         "GBps": b_dr / ms_dr / 1e6, "pct_peak": 100 * b_dr / ms_dr / 1e6 / PEAK_GBS},
+        {"workload": "down + RMS rescale, ngq_gemm_rescale (split K, fused closing kernel)", "T": T,
+         "us": ms_fr * 1e3, "GBps": b_dr / ms_fr / 1e6, "pct_peak": 100 * b_dr / ms_fr / 1e6 / PEAK_GBS},
     ]
 
 

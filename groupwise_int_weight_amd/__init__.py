@@ -55,6 +55,7 @@ SIGNATURES = {
     "ngq_splitk_workspace_bytes": (_SIZE, [_INT, _INT, _INT, _INT]),
     "ngq_gemm_splitk": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR, _SIZE, _PTR]),
     "ngq_rms_rescale": (_INT, [_INT, _INT, _PTR, _PTR, _PTR]),
+    "ngq_gemm_rescale": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR, _PTR, _SIZE, _PTR]),
     "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
     "ngq_debug_force_kernel": (_INT, [_INT]),
     "ngq_strerror": (ctypes.c_char_p, [_INT]),
@@ -244,6 +245,30 @@ def ngq_rms_rescale(z, x=None, stream=None):
         x = torch.empty_like(z)
     _check(lib().ngq_rms_rescale(T, N, _dev_ptr(z, "z"), _dev_ptr(x, "x"), _stream(stream)), "ngq_rms_rescale")
     return x
+
+
+def ngq_gemm_rescale(x, wq, scales, bits: int, N: int, y=None, x_next=None, workspace=None,
+                     group: int = NGQ_GROUP, stream=None):
+    """The projection y = x . W (as ngq_gemm_splitk) and x_next = the RMS
+    rescale of y (as ngq_rms_rescale) in one call; returns (y, x_next)."""
+    import torch
+
+    T, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if x_next is None:
+        x_next = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(16, ngq_splitk_workspace_bytes(K, N, bits, group)), dtype=torch.uint8,
+                                device=x.device)
+    st = lib().ngq_gemm_rescale(T, K, N, _format_bits(bits, scales), group, _dev_ptr(x, "x"), _dev_ptr(wq, "wq"),
+                                _dev_ptr(scales, "scales"), _dev_ptr(y, "y"), _dev_ptr(x_next, "x_next"),
+                                _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check(st, "ngq_gemm_rescale")
+    return y, x_next
 
 
 def ngq_unpack_codes(wq, K: int, N: int, bits: int, group: int = NGQ_GROUP, stream=None):

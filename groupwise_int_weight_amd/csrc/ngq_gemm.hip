@@ -51,6 +51,7 @@
 #include <utility>
 #include <vector>
 
+#include "ngq_bf16.h"
 #include "ngq_internal.h"
 
 namespace ngq {
@@ -169,13 +170,6 @@ __device__ __forceinline__ float scale_to_f32(uint32_t dw, int half, bool bf16) 
   const uint32_t bits = half ? (dw >> 16) : (dw & 0xFFFFu);
   if (bf16) return __uint_as_float(bits << 16);
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
 }
 
 struct GemmArgs {
@@ -1828,19 +1822,35 @@ hipError_t launch_splitk_b(int xl, const dev::SplitArgs& a, int grid, uint32_t l
   return one(dev::gemm_splitk_kernel<BITS, SBF16, 18>);
 }
 
+// x_next == nullptr: ngq_gemm_splitk.  Otherwise ngq_gemm_rescale: the same
+// projection, then x_next = the RMS rescale of y.  Its split is taken at every
+// T where the tiles leave CUs idle: the closing kernel then also does the
+// rescale, so the split's second launch replaces the rescale's own.
 int run_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq, const void* scales, void* y,
-               void* workspace, size_t workspace_bytes, void* stream) {
+               void* x_next, void* workspace, size_t workspace_bytes, void* stream) {
   Format f;
   int rc = parse_format(bits, group, &f);
   if (rc != NGQ_OK) return rc;
   if (T < 0 || T > NGQ_MAX_T) return NGQ_ERR_SHAPE;
   if ((rc = check_kn(K, N)) != NGQ_OK) return rc;
+  const bool fuse = x_next != nullptr;
   const int pairs = (K / kGroup + 1) / 2, ntiles = (N + 31) / 32, cus = cu_count();
-  const int S = choose_splits(T, K, pairs, ntiles, cus);
-  if (S == 1) return run_gemm(1, T, K, N, bits, group, x, wq, scales, y, stream);
-  if (T == 0 || N == 0) return NGQ_OK;
+  const int S = fuse ? (ntiles < cus && pairs >= kSplitMax * 8 ? kSplitMax : 1) : choose_splits(T, K, pairs, ntiles, cus);
   const size_t xb = (size_t)T * K * 2, yb = (size_t)T * N * 2;
   const size_t wb0 = p0_bytes(K, N, f.bits), wb1 = p1_bytes(K, N, f.bits), sb = (size_t)(K / kGroup) * N * 2;
+  if (fuse && T > 0 && N > 0) {
+    if ((rc = check_ptr(x_next)) != NGQ_OK) return rc;
+    if (yb >= kMaxBuffer) return NGQ_ERR_UNSUPPORTED;
+    if (overlaps(x_next, yb, x, xb) || overlaps(x_next, yb, wq, wb0 + wb1) || overlaps(x_next, yb, scales, sb) ||
+        overlaps(x_next, yb, y, yb) || (S > 1 && overlaps(x_next, yb, workspace, (size_t)S * T * N * 4)))
+      return NGQ_ERR_ARG;
+  }
+  if (S == 1) {
+    rc = run_gemm(1, T, K, N, bits, group, x, wq, scales, y, stream);
+    if (rc != NGQ_OK || !fuse) return rc;
+    return ngq_rms_rescale(T, N, y, x_next, stream);
+  }
+  if (T == 0 || N == 0) return NGQ_OK;
   const size_t pb = (size_t)S * T * N * 4;
   if ((rc = check_ptr(y)) != NGQ_OK || (rc = check_ptr(x)) != NGQ_OK || (rc = check_ptr(wq)) != NGQ_OK ||
       (rc = check_ptr(scales)) != NGQ_OK || (rc = check_ptr(workspace)) != NGQ_OK)
@@ -1874,10 +1884,13 @@ int run_splitk(int T, int K, int N, int bits, int group, const void* x, const vo
   else
     e = f.scale_bf16 ? launch_splitk_b<8, true>(xl, a, grid, lds, st) : launch_splitk_b<8, false>(xl, a, grid, lds, st);
   if (e != hipSuccess) return NGQ_ERR_HIP;
+  if (fuse && reduce_rescale_fits(N))
+    return launch_reduce_rescale(static_cast<const float*>(workspace), S, T, N, y, x_next, stream);
   const int TN = T * N;
   hipLaunchKernelGGL(dev::splitk_reduce_kernel, dim3((unsigned)((TN / 4 + 255) / 256)), dim3(256), 0, st,
                      static_cast<const float*>(workspace), S, TN, static_cast<uint16_t*>(y));
-  return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return NGQ_ERR_HIP;
+  return fuse ? ngq_rms_rescale(T, N, y, x_next, stream) : NGQ_OK;
 }
 
 }  // namespace
@@ -1908,7 +1921,14 @@ extern "C" size_t ngq_splitk_workspace_bytes(int K, int N, int bits, int group) 
 
 extern "C" int ngq_gemm_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq,
                                const void* scales, void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_splitk(T, K, N, bits, group, x, wq, scales, y, workspace, workspace_bytes, stream);
+  return run_splitk(T, K, N, bits, group, x, wq, scales, y, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int ngq_gemm_rescale(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                                const void* scales, void* y, void* x_next, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (x_next == nullptr) return NGQ_ERR_ARG;
+  return run_splitk(T, K, N, bits, group, x, wq, scales, y, x_next, workspace, workspace_bytes, stream);
 }
 
 extern "C" int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream) {

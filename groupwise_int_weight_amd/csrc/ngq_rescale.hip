@@ -9,9 +9,13 @@
 // exact evaluation is the summation order of the squares (each square of a
 // bf16 value is exact in fp64).  The block is T x N with T <= 8 in the decode
 // path, so the kernel is latency bound: one workgroup handles one row, or,
-// unless the call is in place, eight workgroups share it.
+// unless the call is in place, eight workgroups share it.  The same row
+// kernel also closes a split-K projection (ngq_gemm_rescale): it adds the
+// slices' fp32 sums, rounds them to the projection's bf16 output and rescales
+// that, in one launch.
 #include <hip/hip_runtime.h>
 
+#include "ngq_bf16.h"
 #include "ngq_internal.h"
 
 namespace ngq {
@@ -20,36 +24,6 @@ namespace dev {
 typedef uint32_t r32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowThreads = 256;
-
-// bf16 pattern -> fp64, decoded from the fields (no fp32 step, so subnormal
-// inputs do not depend on the fp32 denormal mode)
-__device__ __forceinline__ double bf16_bits_to_f64(uint32_t b) {
-  const uint32_t ex = (b >> 7) & 0xFFu, man = b & 0x7Fu;
-  double v;
-  if (ex == 0xFFu)
-    v = man ? __builtin_nan("") : __builtin_inf();
-  else
-    v = ex ? ldexp((double)(128u + man), (int)ex - 134) : ldexp((double)man, -133);
-  return (b & 0x8000u) ? -v : v;
-}
-
-// bf16 nearest-even rounding of an fp64 value, taken directly from fp64 (no
-// intermediate fp32 rounding).  With a in [2^E, 2^(E+1)) the bf16 ulp is
-// 2^u, u = max(E, -126) - 7 (8 significant bits; below 2^-126 the subnormal
-// ulp 2^-133).  m = rint(a / 2^u) is the significand in ulps, rounded with
-// ties to even (the scaling is by a power of two, exact); the pattern is then
-// ((u + 133) << 7) + m, which also covers m = 256 (carry into the next binade)
-// and the subnormals (u = -133).  Inputs here are finite with |v| <= sqrt(N).
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
-  const uint32_t sign = signbit(v) ? 0x8000u : 0u;  // -0 keeps its sign
-  const double a = fabs(v);
-  if (a == 0.0) return (uint16_t)sign;
-  int e;
-  (void)frexp(a, &e);  // a = f 2^e with f in [0.5, 1), so E = e - 1
-  const int u = max(e - 1, -126) - 7;
-  const uint32_t m = (uint32_t)rint(ldexp(a, -u));
-  return (uint16_t)((((uint32_t)(u + 133) << 7) + m) | sign);
-}
 
 // One row per workgroup.  VEC: rows start 16-byte aligned (N % 8 == 0), so the
 // row is read in 8-element chunks.
@@ -104,50 +78,130 @@ __global__ __launch_bounds__(kRowThreads) void rms_rescale_kernel(const uint16_t
   }
 }
 
-// The same result with each row spread over S workgroups (grid S x T): every
-// workgroup reads the whole row and computes the same fixed-order sum of
-// squares (so all slices use the same bits of r), then scales only its own
-// 1/S of the row.  The per-element work of a row then runs on S CUs instead
-// of one.  Not for in-place use: a slice written early could be read by
-// another workgroup's first pass.
-template <int S>
-__global__ __launch_bounds__(kRowThreads) void rms_rescale_split_kernel(const uint16_t* z, uint16_t* x, int N) {
-  const size_t row = (size_t)blockIdx.y * (size_t)N;
-  const r32x4* z8 = reinterpret_cast<const r32x4*>(z + row);
-  r32x4* x8 = reinterpret_cast<r32x4*>(x + row);
-  const int nch = N / 8;
-  double ss = 0.0;
-  for (int c = threadIdx.x; c < nch; c += kRowThreads) {
-    const r32x4 w = z8[c];
+// Rows spread over several workgroups.  Grid R x T: workgroup (j, t) builds
+// the whole of row t as bf16 words in LDS, computing the fixed-order sum of
+// squares on the way (so every workgroup of the row gets the same bits of r),
+// then writes its own 1/R of the row's chunks, one word (two elements) per
+// thread.  Not for in-place use: a slice written early could be read by
+// another workgroup's first pass.  The row comes either from a bf16 block z
+// (ngq_rms_rescale) or from the fp32 slice sums of a split-K projection, which
+// are added in slice order and rounded to bf16 first (the projection's own
+// output, written here too): one chunk -> thread mapping and one order of the
+// squares serve both, so a fused call gives the bits ngq_rms_rescale gives
+// for the same row.
+constexpr int kSplitRowThreads = 512;
+constexpr int kRowParts = 8;  // workgroups per row
+
+// squares of the eight bf16 of a 16-byte chunk, in element order
+__device__ __forceinline__ void add_squares(const r32x4 w, double& ss) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const double lo = bf16_bits_to_f64(w[j]), hi = bf16_bits_to_f64(w[j] >> 16);
-      ss += lo * lo;
-      ss += hi * hi;
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  __shared__ double wsum[kRowThreads / 64];
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const double tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  const double r = sqrt(tot / (double)N);
-  const int per = (nch + S - 1) / S;
-  const int c0 = blockIdx.x * per, c1 = min(c0 + per, nch);
-  for (int c = c0 + threadIdx.x; c < c1; c += kRowThreads) {
-    const r32x4 w = z8[c];
-    r32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = r > 0.0 ? f64_to_bf16_rne(bf16_bits_to_f64(w[j]) / r) : 0u;
-      const uint32_t hi = r > 0.0 ? f64_to_bf16_rne(bf16_bits_to_f64(w[j] >> 16) / r) : 0u;
-      o[j] = lo | (hi << 16);
-    }
-    x8[c] = o;
+  for (int j = 0; j < 4; ++j) {
+    const double lo = bf16_bits_to_f64(w[j]), hi = bf16_bits_to_f64(w[j] >> 16);
+    ss += lo * lo;
+    ss += hi * hi;
   }
 }
 
+// r = sqrt(mean square) from the per-thread sums: xor-shuffle tree in each
+// wave, then the wave sums in wave order.  Contains the workgroup barrier.
+__device__ __forceinline__ double row_rms(double ss, int N) {
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  __shared__ double wsum[kSplitRowThreads / 64];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  double tot = wsum[0];
+#pragma unroll
+  for (int i = 1; i < kSplitRowThreads / 64; ++i) tot += wsum[i];
+  return sqrt(tot / (double)N);
+}
+
+// this workgroup's 1/kRowParts of the row, from the LDS words: x = z / r
+// rounded to bf16 (zeros for a zero row), and z itself when y is given
+__device__ __forceinline__ void write_part(const uint32_t* zw, int nch, double r, uint32_t* y, uint32_t* x) {
+  const int per = (nch + kRowParts - 1) / kRowParts;
+  const int c0 = blockIdx.x * per, c1 = min(c0 + per, nch);
+  for (int i = 4 * c0 + (int)threadIdx.x; i < 4 * c1; i += kSplitRowThreads) {
+    const uint32_t w = zw[i];
+    if (y) y[i] = w;
+    const uint32_t lo = r > 0.0 ? f64_to_bf16_rne(bf16_bits_to_f64(w) / r) : 0u;
+    const uint32_t hi = r > 0.0 ? f64_to_bf16_rne(bf16_bits_to_f64(w >> 16) / r) : 0u;
+    x[i] = lo | (hi << 16);
+  }
+}
+
+// z bf16 [T][N] -> x; N % 8 == 0; 2 N bytes of dynamic LDS
+__global__ __launch_bounds__(kSplitRowThreads) void rms_rescale_split_kernel(const uint16_t* z, uint16_t* x, int N) {
+  extern __shared__ r32x4 zrow[];
+  const size_t row = (size_t)blockIdx.y * (size_t)N;
+  const r32x4* z8 = reinterpret_cast<const r32x4*>(z + row);
+  const int nch = N / 8;
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < nch; c += kSplitRowThreads) {
+    const r32x4 w = z8[c];
+    zrow[c] = w;
+    add_squares(w, ss);
+  }
+  const double r = row_rms(ss, N);
+  write_part(reinterpret_cast<const uint32_t*>(zrow), nch, r, nullptr, reinterpret_cast<uint32_t*>(x + row));
+}
+
+// partial fp32 [S][T][N] -> y = bf16(partial[0] + ... + partial[S-1]) (slice
+// order, as the split-K reduction) and x = the rescale of y; N % 8 == 0; 2 N
+// bytes of dynamic LDS.  All S loads of a chunk are issued before the adds.
+template <int S>
+__global__ __launch_bounds__(kSplitRowThreads) void reduce_rescale_kernel(const float* __restrict__ partial, int T,
+                                                                          int N, uint16_t* y, uint16_t* x) {
+  extern __shared__ r32x4 zrow[];
+  const size_t row = (size_t)blockIdx.y * (size_t)N, TN = (size_t)T * (size_t)N;
+  const float4* p4 = reinterpret_cast<const float4*>(partial + row);
+  const int nch = N / 8;
+  double ss = 0.0;
+  for (int c = threadIdx.x; c < nch; c += kSplitRowThreads) {
+    float4 lo[S], hi[S];
+#pragma unroll
+    for (int ks = 0; ks < S; ++ks) {
+      lo[ks] = p4[ks * (TN / 4) + 2 * c];
+      hi[ks] = p4[ks * (TN / 4) + 2 * c + 1];
+    }
+    float4 a = lo[0], b = hi[0];
+#pragma unroll
+    for (int ks = 1; ks < S; ++ks) {
+      a.x += lo[ks].x; a.y += lo[ks].y; a.z += lo[ks].z; a.w += lo[ks].w;
+      b.x += hi[ks].x; b.y += hi[ks].y; b.z += hi[ks].z; b.w += hi[ks].w;
+    }
+    r32x4 w;
+    w[0] = f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16);
+    w[1] = f32_to_bf16_rne(a.z) | ((uint32_t)f32_to_bf16_rne(a.w) << 16);
+    w[2] = f32_to_bf16_rne(b.x) | ((uint32_t)f32_to_bf16_rne(b.y) << 16);
+    w[3] = f32_to_bf16_rne(b.z) | ((uint32_t)f32_to_bf16_rne(b.w) << 16);
+    zrow[c] = w;
+    add_squares(w, ss);
+  }
+  const double r = row_rms(ss, N);
+  write_part(reinterpret_cast<const uint32_t*>(zrow), nch, r, reinterpret_cast<uint32_t*>(y + row),
+             reinterpret_cast<uint32_t*>(x + row));
+}
+
 }  // namespace dev
+}  // namespace ngq
+
+namespace ngq {
+
+// Rows long enough to spread over kRowParts workgroups, whose bf16 copy fits
+// the LDS a workgroup may take without an attribute change (64 KB, with the
+// kernel's own 64 bytes).
+static bool split_rows(int N) { return N % 8 == 0 && N >= 4096 && N <= 30720; }
+
+bool reduce_rescale_fits(int N) { return split_rows(N); }
+
+int launch_reduce_rescale(const float* partial, int S, int T, int N, void* y, void* x, void* stream) {
+  if (S != 8 || !split_rows(N)) return NGQ_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(dev::reduce_rescale_kernel<8>, dim3((unsigned)dev::kRowParts, (unsigned)T),
+                     dim3(dev::kSplitRowThreads), (uint32_t)N * 2u, (hipStream_t)stream, partial, T, N,
+                     static_cast<uint16_t*>(y), static_cast<uint16_t*>(x));
+  return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
 }  // namespace ngq
 
 using namespace ngq;
@@ -164,9 +218,9 @@ extern "C" int ngq_rms_rescale(int T, int N, const void* z, void* x, void* strea
   hipStream_t st = (hipStream_t)stream;
   const uint16_t* zi = static_cast<const uint16_t*>(z);
   uint16_t* xo = static_cast<uint16_t*>(x);
-  if (N % 8 == 0 && x != z && N >= 8 * 64 * 8)
-    hipLaunchKernelGGL(dev::rms_rescale_split_kernel<8>, dim3(8u, (unsigned)T), dim3(dev::kRowThreads), 0, st, zi, xo,
-                       N);
+  if (split_rows(N) && x != z)
+    hipLaunchKernelGGL(dev::rms_rescale_split_kernel, dim3((unsigned)dev::kRowParts, (unsigned)T),
+                       dim3(dev::kSplitRowThreads), (uint32_t)N * 2u, st, zi, xo, N);
   else if (N % 8 == 0)
     hipLaunchKernelGGL(dev::rms_rescale_kernel<true>, dim3((unsigned)T), dim3(dev::kRowThreads), 0, st, zi, xo, N);
   else

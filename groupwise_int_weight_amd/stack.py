@@ -12,7 +12,8 @@ written and not used (they stand for the attention inputs, which are outside
 this library).  Each step is one library call through the C ABI with raw
 device pointers; this module only orders the calls (on up to three streams)
 and keeps the buffers.  With `fused`, the three projections of x are one
-ngq_multi_gemm call.
+ngq_multi_gemm call, and the down projection and the rescale one
+ngq_gemm_rescale call.
 """
 from __future__ import annotations
 
@@ -46,8 +47,9 @@ class Stack:
     By default every call runs in order on the main stream.  With `fused` the
     QK, gate/value and gate/up projections are one ngq_multi_gemm launch (X
     staged once, the tiles of all three balanced over the CUs) and the down
-    projection is ngq_gemm_splitk (its 160 column tiles alone leave CUs
-    idle).  With `concurrent`
+    projection with the rescale is ngq_gemm_rescale (K split, since its 160
+    column tiles alone leave CUs idle, and the rescale done by the kernel
+    that adds the slices).  With `concurrent`
     the QK and gate/value projections, which only read x, run on two side
     streams beside the gate/up and down projections, and the main stream waits
     for them before the rescale overwrites x.  On MI355X that is slower: each
@@ -119,9 +121,8 @@ class Stack:
 
         if self.fused:
             self.project(i, main)
-            check(L.ngq_gemm_splitk(T, K3, N3, f3, NGQ_GROUP, hp, w3, s3, zp, self.ws.data_ptr(), self.ws.numel(),
-                                    main.cuda_stream), "down")
-            check(L.ngq_rms_rescale(T, HIDDEN, zp, xp, main.cuda_stream), "rescale")
+            check(L.ngq_gemm_rescale(T, K3, N3, f3, NGQ_GROUP, hp, w3, s3, zp, xp, self.ws.data_ptr(),
+                                     self.ws.numel(), main.cuda_stream), "down+rescale")
             return
         if self.concurrent:
             x_ready = torch.cuda.Event()

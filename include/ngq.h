@@ -176,6 +176,24 @@ int ngq_multi_gemm(int T, int K, int group, const void* x, const ngq_proj* projs
  * 0 <= T <= 65535, 0 <= N <= 2^24; T == 0 or N == 0 is a no-op. */
 int ngq_rms_rescale(int T, int N, const void* z, void* x, void* stream);
 
+/* The last projection of a stacked layer with the rescale that closes it:
+ *   y      = X . dequant(Wq) in bf16, as ngq_gemm_splitk computes it, and
+ *   x_next = the per-token RMS rescale of y, as ngq_rms_rescale(T, N, y, x_next)
+ * computes it (bit for bit, given the same y).  Where the column tiles leave
+ * CUs idle (the down projection: K = 17408, N = 5120) K is split at every T,
+ * and the kernel that adds the slices' fp32 sums also rescales the rows, so
+ * the pair of results costs two launches; otherwise the call is ngq_gemm
+ * followed by ngq_rms_rescale.
+ *   x_next    : device bf16 [T][N], overwritten; must not overlap x, wq,
+ *               scales, y or the workspace (NGQ_ERR_ARG); null: NGQ_ERR_ARG
+ *   workspace : as for ngq_gemm_splitk (ngq_splitk_workspace_bytes bytes)
+ * Other arguments, shapes and status codes as ngq_gemm_splitk; the grouping
+ * of the fp32 sums can differ from ngq_gemm_splitk's at T <= 4 (split here,
+ * not there), so y can differ from it in the last bit. */
+int ngq_gemm_rescale(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                     const void* scales, void* y, void* x_next, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* Debug export: the signed codes as the GEMM kernels unpack them.
  *   wq : device, ngq_pack layout;  codes : device int8 [K][N], overwritten. */
 int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream);

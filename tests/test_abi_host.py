@@ -34,7 +34,8 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     names = header_functions()
-    for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_gemm_splitk", "ngq_packed_bytes",
+    for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_gemm_splitk", "ngq_gemm_rescale",
+                     "ngq_packed_bytes",
                      "ngq_scale_bytes", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_rms_rescale", "ngq_strerror"]:
         assert required in names
 
@@ -232,6 +233,30 @@ def test_splitk_workspace_and_empty_calls(ngq):
     assert ngq.ngq_splitk_workspace_bytes(17408, 5122, 4) == 0
     assert ngq.ngq_splitk_workspace_bytes(100, 5120, 4) == 0
     assert L.ngq_gemm_splitk(0, 17408, 5120, 4, 64, None, None, None, None, None, 0, None) == 0
+
+
+XN = 0x700000  # a next-activation buffer clear of the others
+
+
+@pytest.mark.parametrize("args,status", [
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, None, 0x500000, 1 << 21), -1),        # null x_next
+    ((9, 17408, 5120, 4, 64, X, W, S, Y, XN, 0x500000, 1 << 21), -2),          # T > 8
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, XN + 8, 0x500000, 1 << 21), -4),      # misaligned x_next
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, Y + 64, 0x500000, 1 << 21), -1),      # x_next overlaps y
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, X, 0x500000, 1 << 21), -1),           # x_next overlaps x
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, W + 4096, 0x500000, 1 << 21), -1),    # x_next overlaps wq
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, 0x510000, 0x500000, 1 << 21), -1),    # x_next overlaps the workspace
+    ((1, 17408, 5120, 4, 64, X, W, S, Y, XN, 0x500000, 1 << 16), -1),          # workspace too small (split at T = 1)
+    ((8, 17408, 5120, 4, 64, X, W, S, Y, XN, None, 1 << 21), -1),              # null workspace
+])
+def test_gemm_rescale_rejects_bad_arguments(ngq, args, status):
+    assert ngq.lib().ngq_gemm_rescale(*args, None) == status
+
+
+def test_gemm_rescale_empty_calls(ngq):
+    L = ngq.lib()
+    assert L.ngq_gemm_rescale(0, 17408, 5120, 4, 64, None, None, None, None, XN, None, 0, None) == 0
+    assert L.ngq_gemm_rescale(0, 17408, 5120, 4, 64, None, None, None, None, None, None, 0, None) == -1
 
 
 def test_force_kernel_roundtrip(ngq):

@@ -89,6 +89,82 @@ def test_rms_rescale_in_place_and_zero_row(ngq, orc):
     rescale_check(z, out, orc)
 
 
+# ---- the down projection with the closing rescale (ngq_gemm_rescale) --------------------
+
+def gemm_rescale_case(ngq, orc, bits, sbf16, codes, scales, x, cols, what):
+    """y against the oracle (sampled columns), x_next against the oracle's
+    rescale of the GPU's own y and bit for bit against ngq_rms_rescale(y)."""
+    from tests.test_gpu_parity import dev_scales, dev_u8
+
+    K, N = codes.shape
+    packed = ngq.ngq_pack(codes, bits)
+    args = (dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits, N)
+    y, xn = ngq.ngq_gemm_rescale(*args)
+    yb, xb = host_bits(y), host_bits(xn)
+    y64, axw, axs = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, sbf16, cols=cols, nthreads=8,
+                             with_bounds=True)
+    assert_parity(compare(yb if cols is None else yb[:, cols], y64, axw, axs, K, bits), what)
+    assert np.array_equal(xb, host_bits(ngq.ngq_rms_rescale(y)))
+    rescale_check(yb, xb, orc)
+    return args, yb, xb
+
+
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_gemm_rescale_down_shape(ngq, orc, T):
+    w = synthetic.WORKLOADS["down"]
+    codes, scales, x = synthetic.make_inputs(w, T, seed=3)
+    if T == 8:
+        # rows of very different magnitudes, and a zero row (y = 0 -> x_next = 0)
+        mags = np.array([1.0, 1e-30, 3e20, 1e-3, 17.0, 0.0, 2.0 ** 60, 0.5], np.float32)
+        xf = (bf16_bits_to_f64(x) * mags[:, None]).astype(np.float32)
+        x = synthetic.f32_to_bf16_bits(xf)
+    args, yb, xb = gemm_rescale_case(ngq, orc, 4, False, codes, scales, x, sample_cols(w.N, seed=80 + T),
+                                     f"gemm_rescale down T{T}")
+    if T == 8:
+        assert np.all(yb[5] == 0) and np.all(xb[5] == 0)
+        # at T >= 5 the split is ngq_gemm_splitk's: the same y bits
+        assert np.array_equal(yb, host_bits(ngq.ngq_gemm_splitk(*args)))
+    # deterministic, and a captured graph replays to the same bits
+    ws = torch.empty(ngq.ngq_splitk_workspace_bytes(w.K, w.N, 4), dtype=torch.uint8, device="cuda")
+    yg = torch.empty((T, w.N), dtype=torch.bfloat16, device="cuda")
+    xg = torch.empty((T, w.N), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ngq.ngq_gemm_rescale(*args, y=yg, x_next=xg, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ngq.ngq_gemm_rescale(*args, y=yg, x_next=xg, workspace=ws)
+    for rep in range(3):
+        yg.fill_(1.0)
+        xg.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(yg), yb), rep
+        assert np.array_equal(host_bits(xg), xb), rep
+        ngq.ngq_rms_rescale(yg, x=xg)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("bits,sbf16,T,K,N", [
+    (4, False, 3, 12352, 100),  # split, N % 8 != 0: the plain reduction, then ngq_rms_rescale
+    (5, True, 6, 16384, 4104),  # split, 129 tiles, the fused closing kernel
+    (8, False, 2, 20480, 8),    # split, one tile
+    (4, True, 4, 4096, 64),     # 32 pairs: no split, ngq_gemm then ngq_rms_rescale
+])
+def test_gemm_rescale_ragged(ngq, orc, bits, sbf16, T, K, N):
+    from tests.test_gpu_parity import make
+
+    _, (codes, scales, x) = make(bits, sbf16, T, K, N, seed=K + N)
+    cols = None if N <= 512 else sample_cols(N, seed=90)
+    args, yb, _ = gemm_rescale_case(ngq, orc, bits, sbf16, codes, scales, x, cols, f"gemm_rescale b{bits} T{T} N{N}")
+    if K == 4096:
+        assert np.array_equal(yb, host_bits(ngq.ngq_gemm(*args)))
+
+
 # ---- stacked layers -------------------------------------------------------------------
 
 _STACK = {}
