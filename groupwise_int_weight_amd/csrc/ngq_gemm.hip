@@ -1222,6 +1222,237 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<u32x2*>(y + e) = u32x2{lo, hi};
 }
 
+// ---- many tokens: several requests verified together, 8 < T <= 64 -----------
+//
+// Requests verified together (T = requests x (drafts + 1), up to 64) still
+// stream every weight once.  The tokens run in blocks of 16 as the B
+// operand's 16 columns (no slot sharing), so each MFMA step covers 32 k of
+// one group: step st of a pair reads k-blocks 4 st .. 4 st + 3 (group st / 2),
+// k-slot q of a lane taking k-block 4 st + q.  X is too large for LDS (640 KB
+// at T = 64, K = 5120), so every wave reads its pair's X slice from memory
+// (L2, after the first workgroup of an XCD has fetched it) straight into B
+// fragments: lane m of k-slot q takes the 8 k of token 16 tb + m, put into
+// the interleaved k order of the unpack in registers.  A pair's unpacked
+// weights serve all token blocks, and the -(128 + bias) sum_k x term of each
+// group comes from one MFMA chain per token block shared by all columns.  A
+// workgroup of kWideWaves waves takes one 32-column tile; wave w takes pairs
+// w, w + W, ... with two in flight, and the wave sums are added in wave
+// order through LDS, 16 tokens at a time.
+
+constexpr int kWideWaves = 4;
+
+struct WideArgs {
+  const void* x;
+  const void* wq;
+  const void* scales;
+  void* y;
+  int T, K, Nout, Ncols, up_off, G, pairs, ntiles;
+  uint32_t p0_bytes, p1_bytes, s_bytes, x_bytes;
+  uint32_t mask_nib, mask_base, mask_hi;
+};
+
+template <int BITS, int V, int NSETS, int TB>
+struct WideBuf {
+  static constexpr int WPK = BITS == 8 ? 2 : 1;
+  uint32_t a[NSETS][4][V * WPK];             // [set][step][word]; int8: row 2kb words, then 2kb+1
+  uint32_t p1[NSETS][4][BITS == 5 ? V : 1];  // int5: the 32-k high-bit word of each step
+  uint32_t x[TB][4][4];                      // [token block][step][dword]
+  uint32_t sc[NSETS][2][2 * V];              // [set][group][4V 16-bit scales]
+};
+
+// LDS of the wave-sum exchange: per wave [set][16 tokens][32 + 4 columns] fp32
+__host__ __device__ constexpr uint32_t wide_block_floats(int nsets) { return (uint32_t)nsets * 16u * 36u; }
+
+template <int BITS, bool SBF16, int NSETS, int TB>
+__global__ __launch_bounds__(kWideWaves * 64) void gemm_wide_kernel(WideArgs a) {
+  constexpr int W = kWideWaves, V = 2, TILE = 16 * V, WPK = BITS == 8 ? 2 : 1, NB = 2;
+  constexpr uint32_t BLK = wide_block_floats(NSETS), ROW = TILE + 4;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* const part = reinterpret_cast<float*>(smem);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, q = lane >> 4;
+  // XCD-aware tile order, as in gemm_kernel
+  const int b = blockIdx.x, xcd = b & 7, per = a.ntiles >> 3, rem = a.ntiles & 7;
+  const int c0 = (xcd * per + min(xcd, rem) + (b >> 3)) * TILE;
+
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  uint32_t vbase = a.mask_base;
+  asm volatile("" : "+v"(vbase));
+  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
+
+  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
+  uint32_t offA[NSETS], offC[NSETS], offS[NSETS];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s) {
+    offC[s] = (uint32_t)(c0 + s * a.up_off + V * m) * 4u;
+    offA[s] = (uint32_t)q * WPK * rowb + offC[s];
+    offS[s] = (uint32_t)(c0 + s * a.up_off + 4 * V * q) * 2u;
+  }
+  uint32_t offX[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int t = 16 * tb + m;
+    offX[tb] = t < a.T ? (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)q * 16u : kOOB;
+  }
+
+  // loads of pair p (wave uniform; p >= pairs loads nothing)
+  auto issue = [&](WideBuf<BITS, V, NSETS, TB>& buf, int p) {
+    const bool valid = p < a.pairs;
+    // last pair of an odd group count: its second group does not exist (its
+    // weight, high-bit and scale rows lie past their buffers, but its X
+    // offsets would run into the next token's row, so they are cut here)
+    const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
+    const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb : kOOB;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const uint32_t o = offA[s] + pa + (uint32_t)st * 4u * WPK * rowb;
+        load_words<V>(&buf.a[s][st][0], rW, o);
+        if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
+      }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bool on = valid & !(half & (st >= 2));
+        load_words<4>(&buf.x[tb][st][0], rX, on ? offX[tb] + (uint32_t)p * 256u + (uint32_t)st * 64u : kOOB);
+      }
+    if constexpr (BITS == 5) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int s = 0; s < NSETS; ++s)
+          load_words<V>(&buf.p1[s][st][0], rP1, valid ? (uint32_t)(4 * p + st) * rowb + offC[s] : kOOB);
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        load_words<2 * V>(&buf.sc[s][g][0], rS,
+                          valid ? (uint32_t)(2 * p + g) * (uint32_t)a.Ncols * 2u + offS[s] : kOOB);
+  };
+
+  f32x4 acc[TB][NSETS][V];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[tb][s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+
+  auto compute = [&](const WideBuf<BITS, V, NSETS, TB>& buf) {
+    u32x4 av[4][NSETS][V];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          if constexpr (BITS == 4) {
+            av[st][s][i] = nibbles_to_bf16_il(buf.a[s][st][i], mk);
+          } else if constexpr (BITS == 5) {
+            // k-block 4 st + q is byte q of the step's 32-k high-bit word
+            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st][i], 8u * (uint32_t)q, 8u);
+            av[st][s][i] = nibbles5_to_bf16_il(buf.a[s][st][i], hb, mk);
+          } else {
+            av[st][s][i] = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
+          }
+        }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      bf16x8 bfrag[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) bfrag[st] = __builtin_bit_cast(bf16x8, interleave_x(buf.x[tb][st]));
+#pragma unroll
+      for (int gr = 0; gr < 2; ++gr) {
+        f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+        dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfrag[2 * gr], dx, 0, 0, 0);
+        dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfrag[2 * gr + 1], dx, 0, 0,
+                                                     0);
+#pragma unroll
+        for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            f32x4 dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[2 * gr][s][i]),
+                                                               bfrag[2 * gr], dx, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[2 * gr + 1][s][i]),
+                                                         bfrag[2 * gr + 1], dp, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int e = V * r + i;
+              const float sc = scale_to_f32(buf.sc[s][gr][e >> 1], e & 1, SBF16);
+              acc[tb][s][i][r] = __builtin_fmaf(sc, dp[r], acc[tb][s][i][r]);
+            }
+          }
+      }
+    }
+  };
+
+  // two pairs in flight per wave; loads are issued without a branch (a pair
+  // past the end loads nothing), and the scheduling barriers keep the pairs'
+  // loads in issue order, so each compute waits for exactly its own pair
+  WideBuf<BITS, V, NSETS, TB> buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    issue(buf[u], wave + W * u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int k = wave; k < a.pairs; k += NB * W) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int p = k + W * u;
+      if (p < a.pairs) compute(buf[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[u], p + NB * W);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // the wave sums, 16 tokens at a time: each wave writes its block, then the
+  // outputs add the W blocks in wave order
+  uint16_t* const y = static_cast<uint16_t*>(a.y);
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    if (tb > 0) __syncthreads();  // the previous round's blocks are read
+    float* const blk = part + (uint32_t)wave * BLK;
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          blk[((uint32_t)s * 16u + (uint32_t)m) * ROW + (uint32_t)(V * (4 * q + r) + i)] = acc[tb][s][i][r];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 16 * TILE; idx += W * 64) {
+      const int tt = idx / TILE, col = idx % TILE, t = 16 * tb + tt;
+      if (t >= a.T || c0 + col >= a.Nout) continue;
+      float v[NSETS];
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const float* src = part + ((uint32_t)s * 16u + (uint32_t)tt) * ROW + (uint32_t)col;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += src[(uint32_t)w * BLK];
+        v[s] = sum;
+      }
+      float out;
+      if constexpr (NSETS == 2) {
+        out = v[0] * v[1] / (1.0f + expf(-v[0]));  // SiLU(gate) * up
+      } else {
+        out = v[0];
+      }
+      y[(size_t)t * a.Nout + c0 + col] = f32_to_bf16_rne(out);
+    }
+  }
+}
+
 // ---- debug kernels: the GEMM's unpack and scale decoding, materialised ----
 
 template <int BITS, bool SBF16, bool DEQUANT>
@@ -1443,12 +1674,53 @@ hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, uint32_t l
 }
 
 // Shared validation and launch of ngq_gemm (nsets 1) and ngq_swiglu_gemm (2).
+// ---- many tokens (host) ----
+
+template <int BITS, bool SBF16, int NSETS>
+hipError_t launch_wide_b(int tb, const dev::WideArgs& a, uint32_t lds, hipStream_t st) {
+  auto one = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(dev::kWideWaves * 64), lds, st, a);
+    return hipGetLastError();
+  };
+  if (tb == 1) return one(dev::gemm_wide_kernel<BITS, SBF16, NSETS, 1>);
+  if (tb == 2) return one(dev::gemm_wide_kernel<BITS, SBF16, NSETS, 2>);
+  return one(dev::gemm_wide_kernel<BITS, SBF16, NSETS, 4>);
+}
+
+template <int NSETS>
+hipError_t launch_wide(const Format& f, int tb, const dev::WideArgs& a, uint32_t lds, hipStream_t st) {
+  if (f.bits == 4)
+    return f.scale_bf16 ? launch_wide_b<4, true, NSETS>(tb, a, lds, st) : launch_wide_b<4, false, NSETS>(tb, a, lds, st);
+  if (f.bits == 5)
+    return f.scale_bf16 ? launch_wide_b<5, true, NSETS>(tb, a, lds, st) : launch_wide_b<5, false, NSETS>(tb, a, lds, st);
+  return f.scale_bf16 ? launch_wide_b<8, true, NSETS>(tb, a, lds, st) : launch_wide_b<8, false, NSETS>(tb, a, lds, st);
+}
+
+// 8 < T <= 64, arguments already checked: one workgroup per 32-column tile,
+// 16 (T <= 16), 32 or 64 token rows per workgroup.
+int run_wide(int nsets, int T, int K, int Nout, int Ncols, const Format& f, const void* x, const void* wq,
+             const void* scales, void* y, size_t wb0, size_t wb1, size_t sb, size_t xb, void* stream) {
+  dev::WideArgs a;
+  a.x = x; a.wq = wq; a.scales = scales; a.y = y;
+  a.T = T; a.K = K; a.Nout = Nout; a.Ncols = Ncols; a.up_off = nsets == 2 ? Nout : 0;
+  a.G = K / kGroup;
+  a.pairs = (a.G + 1) / 2;
+  a.ntiles = (Nout + 31) / 32;
+  a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
+  a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
+  const int tb = T <= 16 ? 1 : T <= 32 ? 2 : 4;
+  const uint32_t lds = dev::kWideWaves * dev::wide_block_floats(nsets) * 4u;
+  const hipError_t e = nsets == 1 ? launch_wide<1>(f, tb, a, lds, (hipStream_t)stream)
+                                  : launch_wide<2>(f, tb, a, lds, (hipStream_t)stream);
+  return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
 int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void* x, const void* wq,
              const void* scales, void* y, void* stream) {
   Format f;
   int rc = parse_format(bits, group, &f);
   if (rc != NGQ_OK) return rc;
-  if (T < 0 || T > NGQ_MAX_T) return NGQ_ERR_SHAPE;
+  if (T < 0 || T > NGQ_MAX_T_VERIFY) return NGQ_ERR_SHAPE;
   if ((rc = check_kn(K, Nout)) != NGQ_OK) return rc;
   const long ncols_l = (long)Nout * nsets;
   if (ncols_l > (1L << 30)) return NGQ_ERR_SHAPE;
@@ -1466,6 +1738,7 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   if (xb >= kMaxBuffer || yb >= kMaxBuffer || wb0 + wb1 >= kMaxBuffer || sb >= kMaxBuffer)
     return NGQ_ERR_UNSUPPORTED;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, wq, wb0 + wb1) || overlaps(y, yb, scales, sb)) return NGQ_ERR_ARG;
+  if (T > NGQ_MAX_T) return run_wide(nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
 
   const int cus = cu_count();
   // Tiles of at least 32 columns where N allows: a 16-column tile reads 64 of

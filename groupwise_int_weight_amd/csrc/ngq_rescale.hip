@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kRowThreads) void rms_rescale_kernel(const uint16_t
 // output, written here too): one chunk -> thread mapping and one order of the
 // squares serve both, so a fused call gives the bits ngq_rms_rescale gives
 // for the same row.
-constexpr int kSplitRowThreads = 512;
+constexpr int kSplitRowThreads = 1024;
 constexpr int kRowParts = 8;  // workgroups per row
 
 // squares of the eight bf16 of a 16-byte chunk, in element order

@@ -2,8 +2,8 @@
  * ngq.h -- C ABI of libngq: small-T groupwise-int projections on MI355X (gfx950).
  *
  * The operation.  A decode or speculative-verify step of a groupwise-int
- * quantised model multiplies T <= 8 token activations by each quantised
- * projection matrix:
+ * quantised model multiplies T <= 8 token activations (up to 64 when
+ * several requests are verified together) by each quantised projection matrix:
  *
  *     Y[T x N] = X[T x K] . dequant(Wq[K x N]),   dequant: w[k][n] = c[k][n] * s[k/64][n]
  *
@@ -68,6 +68,7 @@ extern "C" {
 #define NGQ_SCALE_BF16 0x100
 #define NGQ_GROUP 64 /* the only supported group size */
 #define NGQ_MAX_T 8  /* tokens per call: plain decode (1) up to 7 drafts + 1 */
+#define NGQ_MAX_T_VERIFY 64 /* ngq_gemm / ngq_swiglu_gemm: up to 8 requests x 8 tokens */
 
 /* Bytes of the packed weight buffer (P0, plus P1 for int5) for a K x N
  * matrix; 0 when the arguments are invalid.  Host only, no HIP call. */
@@ -84,8 +85,14 @@ size_t ngq_scale_bytes(int K, int N, int bits, int group);
  * The NGQ_SCALE_BF16 flag is ignored here. */
 int ngq_pack(int K, int N, int bits, int group, const int8_t* codes, void* wq_out);
 
-/* Y = X . dequant(Wq) for 0 <= T <= 8 tokens (the projection of the "What V3
- * did" T-routing, NInfer-4090 V3 topic).
+/* Y = X . dequant(Wq) for 0 <= T <= 64 tokens.  T <= 8 is one request's
+ * decode or verify step (the projection of the "What V3 did" T-routing,
+ * NInfer-4090 V3 topic).  8 < T <= 64 is the verify rounds of several
+ * requests stacked into one call, so that the weights stream once for all of
+ * them: an engine serves up to 8 active requests (HotRepo page on
+ * Neroued/ninfer, "Constraints"), each verifying up to 7 drafts + 1 (the
+ * ninfer-ext README, "Recommended settings"; the V3 topic's "Measured data"
+ * runs 2, 4 and 8 requests with 7 drafts).
  *   x      : device bf16 [T][K]
  *   wq     : device, ngq_pack layout for K x N
  *   scales : device fp16|bf16 [K/64][N]
@@ -105,7 +112,8 @@ int ngq_gemm(int T, int K, int N, int bits, int group, const void* x, const void
  *                    projection
  *   scales_gate_up : device fp16|bf16 [K/64][2 N_ff]
  *   h              : device bf16 [T][N_ff], overwritten; must not overlap inputs
- * The down projection is a plain ngq_gemm with K = N_ff and x = h. */
+ * T as for ngq_gemm (0..64).  The down projection is a plain ngq_gemm with
+ * K = N_ff and x = h. */
 int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
                     const void* wq_gate_up, const void* scales_gate_up, void* h, void* stream);
 

@@ -111,7 +111,7 @@ X, W, S, Y = 0x100000, 0x200000, 0x300000, 0x400000
 
 
 @pytest.mark.parametrize("args,status", [
-    ((9, 64, 4, 4, 64, X, W, S, Y), -2),        # T > 8
+    ((65, 64, 4, 4, 64, X, W, S, Y), -2),       # T > 64
     ((-1, 64, 4, 4, 64, X, W, S, Y), -2),       # T < 0
     ((1, 100, 4, 4, 64, X, W, S, Y), -2),       # K % 64
     ((1, 64, 6, 4, 64, X, W, S, Y), -2),        # N % 4
@@ -128,6 +128,8 @@ X, W, S, Y = 0x100000, 0x200000, 0x300000, 0x400000
     ((1, 64, 4, 4, 64, X, W, S, X), -1),        # y overlaps x
     ((2, 64, 64, 4, 64, X, W, S, W + 16), -1),  # y overlaps wq
     ((1, 1 << 24, 512, 4, 64, X, W, S, Y), -3),  # packed weights >= 2 GiB
+    ((64, 64, 4, 4, 64, X, W, S, Y + 2), -4),   # misaligned y, T = 64
+    ((40, 64, 64, 4, 64, X, W, S, X + 64), -1),  # y overlaps x, T = 40
 ])
 def test_gemm_rejects_bad_arguments(ngq, args, status):
     assert ngq.lib().ngq_gemm(*args, None) == status
@@ -135,7 +137,7 @@ def test_gemm_rejects_bad_arguments(ngq, args, status):
 
 def test_swiglu_rejects_bad_arguments(ngq):
     L = ngq.lib()
-    assert L.ngq_swiglu_gemm(9, 64, 4, 4, 64, X, W, S, Y, None) == -2
+    assert L.ngq_swiglu_gemm(65, 64, 4, 4, 64, X, W, S, Y, None) == -2
     assert L.ngq_swiglu_gemm(1, 64, 6, 4, 64, X, W, S, Y, None) == -2
     assert L.ngq_swiglu_gemm(1, 64, 4, 4, 64, X, W, S, None, None) == -1
     # the up half makes wq 2 N_ff columns wide: h must not overlap it either
