@@ -439,7 +439,8 @@ def main():
     if not args.no_sweep:
         for name in ("qk", "gv"):
             wl = synthetic.WORKLOADS[name]
-            for t in (1, 2, 4, 8):
+            # T > 8: the verify rounds of several requests in one call
+            for t in (1, 2, 4, 8, 16, 32, 64):
                 ms_t, r, _ = run_projection(ngq, wl, t, args.sweep_steps, 10)
                 b = algorithmic_bytes(ngq, wl, t)
                 sweep.append({"workload": f"{name} int{wl.bits} K={wl.K} N={wl.N}", "T": t, "us": ms_t * 1e3,

@@ -1274,7 +1274,13 @@ __global__ __launch_bounds__(kWideWaves * 64) void gemm_wide_kernel(WideArgs a) 
   const int m = lane & 15, q = lane >> 4;
   // XCD-aware tile order, as in gemm_kernel
   const int b = blockIdx.x, xcd = b & 7, per = a.ntiles >> 3, rem = a.ntiles & 7;
-  const int c0 = (xcd * per + min(xcd, rem) + (b >> 3)) * TILE;
+  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
+  const int c0 = tile * TILE;
+  // Every workgroup reads the same X.  Starting each tile at a different pair
+  // (the pair order rotated by the tile index) keeps the workgroups of an XCD
+  // on different X lines at any moment instead of all queueing for the same
+  // few L2 lines.
+  const int rot = a.pairs > 0 ? tile % a.pairs : 0;
 
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
   const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
@@ -1299,9 +1305,11 @@ __global__ __launch_bounds__(kWideWaves * 64) void gemm_wide_kernel(WideArgs a) 
     offX[tb] = t < a.T ? (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)q * 16u : kOOB;
   }
 
-  // loads of pair p (wave uniform; p >= pairs loads nothing)
-  auto issue = [&](WideBuf<BITS, V, NSETS, TB>& buf, int p) {
-    const bool valid = p < a.pairs;
+  // loads of the v-th pair of the rotated order (wave uniform; v >= pairs
+  // loads nothing)
+  auto issue = [&](WideBuf<BITS, V, NSETS, TB>& buf, int v) {
+    const bool valid = v < a.pairs;
+    const int p = v + rot < a.pairs ? v + rot : v + rot - a.pairs;
     // last pair of an odd group count: its second group does not exist (its
     // weight, high-bit and scale rows lie past their buffers, but its X
     // offsets would run into the next token's row, so they are cut here)
