@@ -1235,9 +1235,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // the interleaved k order of the unpack in registers.  A pair's unpacked
 // weights serve all token blocks, and the -(128 + bias) sum_k x term of each
 // group comes from one MFMA chain per token block shared by all columns.  A
-// workgroup of kWideWaves waves takes one 32-column tile; wave w takes pairs
-// w, w + W, ... with two in flight, and the wave sums are added in wave
-// order through LDS, 16 tokens at a time.
+// workgroup of kWideWaves waves takes one tile of 16 V columns (V = 3 where
+// that makes one tile per CU, as for N = 12288); wave w takes pairs w, w + W,
+// ... with two in flight, and the wave sums are added in wave order through
+// LDS, 16 tokens at a time.
 
 constexpr int kWideWaves = 4;
 
@@ -1260,13 +1261,15 @@ struct WideBuf {
   uint32_t sc[NSETS][2][2 * V];              // [set][group][4V 16-bit scales]
 };
 
-// LDS of the wave-sum exchange: per wave [set][16 tokens][32 + 4 columns] fp32
-__host__ __device__ constexpr uint32_t wide_block_floats(int nsets) { return (uint32_t)nsets * 16u * 36u; }
+// LDS of the wave-sum exchange: per wave [set][16 tokens][16 V + 4 columns] fp32
+__host__ __device__ constexpr uint32_t wide_block_floats(int nsets, int v) {
+  return (uint32_t)nsets * 16u * (16u * (uint32_t)v + 4u);
+}
 
-template <int BITS, bool SBF16, int NSETS, int TB>
+template <int BITS, bool SBF16, int V, int NSETS, int TB>
 __global__ __launch_bounds__(kWideWaves * 64) void gemm_wide_kernel(WideArgs a) {
-  constexpr int W = kWideWaves, V = 2, TILE = 16 * V, WPK = BITS == 8 ? 2 : 1, NB = 2;
-  constexpr uint32_t BLK = wide_block_floats(NSETS), ROW = TILE + 4;
+  constexpr int W = kWideWaves, TILE = 16 * V, WPK = BITS == 8 ? 2 : 1, NB = 2;
+  constexpr uint32_t BLK = wide_block_floats(NSETS, V), ROW = TILE + 4;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* const part = reinterpret_cast<float*>(smem);
   const int lane = threadIdx.x & 63;
@@ -1685,27 +1688,36 @@ hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, uint32_t l
 // ---- many tokens (host) ----
 
 template <int BITS, bool SBF16, int NSETS>
-hipError_t launch_wide_b(int tb, const dev::WideArgs& a, uint32_t lds, hipStream_t st) {
+hipError_t launch_wide_b(int v, int tb, const dev::WideArgs& a, uint32_t lds, hipStream_t st) {
   auto one = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(dev::kWideWaves * 64), lds, st, a);
     return hipGetLastError();
   };
-  if (tb == 1) return one(dev::gemm_wide_kernel<BITS, SBF16, NSETS, 1>);
-  if (tb == 2) return one(dev::gemm_wide_kernel<BITS, SBF16, NSETS, 2>);
-  return one(dev::gemm_wide_kernel<BITS, SBF16, NSETS, 4>);
+  if constexpr (NSETS == 1) {
+    if (v == 3) return tb == 1 ? one(dev::gemm_wide_kernel<BITS, SBF16, 3, 1, 1>)
+                               : one(dev::gemm_wide_kernel<BITS, SBF16, 3, 1, 2>);
+  }
+  if (tb == 1) return one(dev::gemm_wide_kernel<BITS, SBF16, 2, NSETS, 1>);
+  if (tb == 2) return one(dev::gemm_wide_kernel<BITS, SBF16, 2, NSETS, 2>);
+  return one(dev::gemm_wide_kernel<BITS, SBF16, 2, NSETS, 4>);
 }
 
 template <int NSETS>
-hipError_t launch_wide(const Format& f, int tb, const dev::WideArgs& a, uint32_t lds, hipStream_t st) {
+hipError_t launch_wide(const Format& f, int v, int tb, const dev::WideArgs& a, uint32_t lds, hipStream_t st) {
   if (f.bits == 4)
-    return f.scale_bf16 ? launch_wide_b<4, true, NSETS>(tb, a, lds, st) : launch_wide_b<4, false, NSETS>(tb, a, lds, st);
+    return f.scale_bf16 ? launch_wide_b<4, true, NSETS>(v, tb, a, lds, st)
+                        : launch_wide_b<4, false, NSETS>(v, tb, a, lds, st);
   if (f.bits == 5)
-    return f.scale_bf16 ? launch_wide_b<5, true, NSETS>(tb, a, lds, st) : launch_wide_b<5, false, NSETS>(tb, a, lds, st);
-  return f.scale_bf16 ? launch_wide_b<8, true, NSETS>(tb, a, lds, st) : launch_wide_b<8, false, NSETS>(tb, a, lds, st);
+    return f.scale_bf16 ? launch_wide_b<5, true, NSETS>(v, tb, a, lds, st)
+                        : launch_wide_b<5, false, NSETS>(v, tb, a, lds, st);
+  return f.scale_bf16 ? launch_wide_b<8, true, NSETS>(v, tb, a, lds, st)
+                      : launch_wide_b<8, false, NSETS>(v, tb, a, lds, st);
 }
 
-// 8 < T <= 64, arguments already checked: one workgroup per 32-column tile,
-// 16 (T <= 16), 32 or 64 token rows per workgroup.
+// 8 < T <= 64, arguments already checked: one workgroup per tile of 32
+// columns, or 48 where that gives one tile per CU (plain projections at
+// T <= 32, whose registers allow it); 16 (T <= 16), 32 or 64 token rows per
+// workgroup.
 int run_wide(int nsets, int T, int K, int Nout, int Ncols, const Format& f, const void* x, const void* wq,
              const void* scales, void* y, size_t wb0, size_t wb1, size_t sb, size_t xb, void* stream) {
   dev::WideArgs a;
@@ -1713,13 +1725,14 @@ int run_wide(int nsets, int T, int K, int Nout, int Ncols, const Format& f, cons
   a.T = T; a.K = K; a.Nout = Nout; a.Ncols = Ncols; a.up_off = nsets == 2 ? Nout : 0;
   a.G = K / kGroup;
   a.pairs = (a.G + 1) / 2;
-  a.ntiles = (Nout + 31) / 32;
+  const int tb = T <= 16 ? 1 : T <= 32 ? 2 : 4;
+  const int v = nsets == 1 && tb <= 2 && Nout >= 32 ? choose_v(Nout, cu_count(), 2, 3) : 2;
+  a.ntiles = (Nout + 16 * v - 1) / (16 * v);
   a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
   a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
-  const int tb = T <= 16 ? 1 : T <= 32 ? 2 : 4;
-  const uint32_t lds = dev::kWideWaves * dev::wide_block_floats(nsets) * 4u;
-  const hipError_t e = nsets == 1 ? launch_wide<1>(f, tb, a, lds, (hipStream_t)stream)
-                                  : launch_wide<2>(f, tb, a, lds, (hipStream_t)stream);
+  const uint32_t lds = dev::kWideWaves * dev::wide_block_floats(nsets, v) * 4u;
+  const hipError_t e = nsets == 1 ? launch_wide<1>(f, v, tb, a, lds, (hipStream_t)stream)
+                                  : launch_wide<2>(f, v, tb, a, lds, (hipStream_t)stream);
   return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
 

@@ -47,6 +47,9 @@ SMALL = [
     (4, False, 64, 2048, 4100),  # ragged column tail
     (5, True, 24, 64, 40),       # a single group
     (8, False, 48, 1088, 132),   # 17 groups
+    (8, False, 32, 512, 12004),  # 48-column tiles (one per CU), a 4-column last tile
+    (4, True, 16, 256, 10000),   # 48-column tiles, a 16-column last tile
+    (5, False, 20, 384, 9000),   # 48-column tiles, int5
 ]
 
 
