@@ -28,9 +28,11 @@ NGQ_INT4, NGQ_INT5, NGQ_INT8 = 4, 5, 8
 NGQ_SCALE_BF16 = 0x100
 NGQ_GROUP = 64
 NGQ_MAX_T = 8
-NGQ_MAX_T_VERIFY = 64  # ngq_gemm / ngq_swiglu_gemm
+NGQ_MAX_T_VERIFY = 64  # several requests' verify rounds in one call
+NGQ_MAX_T_PREFILL = 16384  # ngq_gemm / ngq_swiglu_gemm
 NGQ_MAX_PROJ = 4
 NGQ_KERNEL_AUTO, NGQ_KERNEL_PERPAIR_DYN, NGQ_KERNEL_PERPAIR_STATIC, NGQ_KERNEL_XRES14, NGQ_KERNEL_XRES8 = 0, 1, 2, 3, 4
+NGQ_KERNEL_WIDE, NGQ_KERNEL_TILED = 5, 6
 
 # Every function the header declares, with its ctypes signature.
 _SIZE = ctypes.c_size_t

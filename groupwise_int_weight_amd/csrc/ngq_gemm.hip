@@ -1464,6 +1464,255 @@ __global__ __launch_bounds__(kWideWaves * 64) void gemm_wide_kernel(WideArgs a) 
   }
 }
 
+// ---- prefill-size T: token x column tiles ----------------------------------
+//
+// A prefill chunk (hundreds to thousands of tokens, the engine's
+// `--prefill-chunk` on the NInfer-4090 V3 topic) reuses every weight across
+// many tokens, so the work is a dense contraction and the MFMA units, not
+// the weight stream, set the pace.  One workgroup owns a tile of 64 weight
+// columns (64 output columns, or 32 gate + 32 up columns with the SwiGLU
+// epilogue) by 64 tokens; its 4 waves split K, wave w taking the groups
+// g = w, w + 4, ...  Per group a wave unpacks its 64 columns once (two 32-k
+// steps, the interleaved order of the decode kernels) and multiplies them
+// with 4 token blocks of 16: 32 MFMAs plus 8 for the -(128 + bias) sum_k x
+// term, then acc += s * partial per group.  Weights, scales and X go from
+// memory straight into registers, NB groups ahead.  The 4 wave sums meet in
+// LDS and are added in wave order (deterministic, no atomics).
+
+constexpr int kTiledWaves = 4;
+constexpr int kTiledTok = 64;   // tokens per tile: 4 MFMA token blocks
+constexpr int kTiledCols = 64;  // weight columns per tile: 16 lanes x 4
+
+struct TiledArgs {
+  const void* x;
+  const void* wq;
+  const void* scales;
+  void* y;
+  int T, K, Nout, Ncols, up_off, G, tiles_n, tiles;
+  uint32_t p0_bytes, p1_bytes, s_bytes, x_bytes;
+  uint32_t mask_nib, mask_base, mask_hi;
+};
+
+// LDS of the wave-sum exchange: per wave 64 values per lane
+__host__ __device__ constexpr uint32_t tiled_lds_bytes() { return (uint32_t)kTiledWaves * 64u * 64u * 4u; }
+
+template <int BITS, int NSETS>
+struct TiledBuf {
+  static constexpr int V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
+  uint32_t a[NSETS][2][V * WPK];             // [set][32-k step][word]; int8: row 2kb words, then 2kb+1
+  uint32_t p1[NSETS][2][BITS == 5 ? V : 1];  // int5: the step's 32-k high-bit word
+  uint32_t sc[NSETS][2 * V];                 // 4V 16-bit scales per set
+  uint32_t x[4][2][4];                       // [token block][step][dword]
+};
+
+template <int BITS, bool SBF16, int NSETS, int NB>
+__global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs a) {
+  constexpr int W = kTiledWaves, V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
+  constexpr int OCOLS = kTiledCols / NSETS;  // output columns per tile
+  constexpr int E = NSETS * V * 16;           // accumulators per lane (64)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* const part = reinterpret_cast<float*>(smem);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, q = lane >> 4;
+  // XCD-aware order: each XCD (block b runs on XCD b % 8) takes a contiguous
+  // range of tiles, token tile slowest, so the workgroups of one XCD share
+  // the X rows of a token tile in its L2
+  const int b = blockIdx.x, xcd = b & 7, per = a.tiles >> 3, rem = a.tiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
+  const int tt = tile / a.tiles_n, tn = tile - tt * a.tiles_n;
+  const int t0 = tt * kTiledTok, c0 = tn * OCOLS;
+
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  uint32_t vbase = a.mask_base;
+  asm volatile("" : "+v"(vbase));
+  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
+
+  // Lane (m, q) supplies, for set s and column i < V, operand row m of the
+  // A block (weight column c0 + s up_off + V m + i) at the 8 k of slot q, and
+  // token 16 tb + m of the B block; its results are rows 4q + r (weight
+  // columns c0 + s up_off + V (4q + r) + i) for token 16 tb + m.  Columns past
+  // the matrix read the next row or nothing: only their own (discarded)
+  // outputs see them.
+  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
+  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s) {
+    const uint32_t col = (uint32_t)(c0 + s * a.up_off + V * m);
+    offA[s] = (uint32_t)q * WPK * rowb + col * 4u;
+    offP1[s] = col * 4u;
+    offS[s] = (uint32_t)(c0 + s * a.up_off + 4 * V * q) * 2u;
+  }
+  uint32_t offX[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = t0 + 16 * tb + m;
+    offX[tb] = t < a.T ? (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)q * 16u : kOOB;
+  }
+
+  // loads of group g (g >= G loads nothing)
+  auto issue = [&](TiledBuf<BITS, NSETS>& buf, int g) {
+    const bool valid = g < a.G;
+    const uint32_t ga = valid ? (uint32_t)g * 8u * WPK * rowb : kOOB;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const uint32_t o = offA[s] + ga + (uint32_t)ks * 4u * WPK * rowb;
+        load_words<V>(&buf.a[s][ks][0], rW, o);
+        if constexpr (BITS == 8) load_words<V>(&buf.a[s][ks][V], rW, o + rowb);
+      }
+    if constexpr (BITS == 5) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int s = 0; s < NSETS; ++s)
+          load_words<V>(&buf.p1[s][ks][0], rP1, valid ? (uint32_t)(2 * g + ks) * rowb + offP1[s] : kOOB);
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+      load_words<2 * V>(&buf.sc[s][0], rS, valid ? (uint32_t)g * (uint32_t)a.Ncols * 2u + offS[s] : kOOB);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        load_words<4>(&buf.x[tb][ks][0], rX, valid ? offX[tb] + (uint32_t)g * 128u + (uint32_t)ks * 64u : kOOB);
+  };
+
+  f32x4 acc[NSETS][V][4];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[s][i][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+
+  auto compute = [&](const TiledBuf<BITS, NSETS>& buf) {
+    bf16x8 bfr[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) bfr[tb][ks] = __builtin_bit_cast(bf16x8, interleave_x(buf.x[tb][ks]));
+    f32x4 dx[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][0],
+                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][1], dx[tb], 0, 0,
+                                                       0);
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        u32x4 av[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if constexpr (BITS == 4) {
+            av[ks] = nibbles_to_bf16_il(buf.a[s][ks][i], mk);
+          } else if constexpr (BITS == 5) {
+            // k-block 4 ks + q is byte q of the step's 32-k high-bit word
+            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][ks][i], 8u * (uint32_t)q, 8u);
+            av[ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb, mk);
+          } else {
+            av[ks] = bytes_to_bf16_il(buf.a[s][ks][i], buf.a[s][ks][V + i]);
+          }
+        }
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = V * r + i;
+          sc[r] = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          f32x4 dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[0]), bfr[tb][0], dx[tb], 0,
+                                                             0, 0);
+          dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[1]), bfr[tb][1], dp, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[s][i][tb][r] = __builtin_fmaf(sc[r], dp[r], acc[s][i][tb][r]);
+        }
+      }
+  };
+
+  // NB groups in flight per wave; loads are issued without a branch (a group
+  // past the end loads nothing), and the scheduling barriers keep the groups'
+  // loads in issue order, so each compute waits for exactly its own group
+  TiledBuf<BITS, NSETS> buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    issue(buf[u], wave + W * u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int g = wave; g < a.G; g += NB * W) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int gg = g + W * u;
+      if (gg < a.G) compute(buf[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[u], gg + NB * W);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // the wave sums: value e of lane l of wave w at part[(w E + e) 64 + l]
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = ((s * V + i) * 4 + tb) * 4 + r;
+          part[((uint32_t)wave * E + (uint32_t)e) * 64u + (uint32_t)lane] = acc[s][i][tb][r];
+        }
+  __syncthreads();
+  // wave w finishes token block w: the four wave sums in wave order, then
+  // SwiGLU or plain, V consecutive output columns per store
+  const int tb = wave, t = t0 + 16 * tb + m;
+  uint16_t* const y = static_cast<uint16_t*>(a.y);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int col = c0 + V * (4 * q + r);
+    if (t >= a.T || col >= a.Nout) continue;
+    float v[NSETS][V];
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int e = ((s * V + i) * 4 + tb) * 4 + r;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += part[((uint32_t)w * E + (uint32_t)e) * 64u + (uint32_t)lane];
+        v[s][i] = sum;
+      }
+    uint32_t pk[V / 2];
+#pragma unroll
+    for (int i = 0; i < V; i += 2) {
+      float o0, o1;
+      if constexpr (NSETS == 2) {
+        o0 = v[0][i] * v[1][i] / (1.0f + expf(-v[0][i]));  // SiLU(gate) * up
+        o1 = v[0][i + 1] * v[1][i + 1] / (1.0f + expf(-v[0][i + 1]));
+      } else {
+        o0 = v[0][i];
+        o1 = v[0][i + 1];
+      }
+      pk[i / 2] = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+    }
+    uint16_t* dst = y + (size_t)t * a.Nout + col;
+    if constexpr (V == 4)
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+    else
+      *reinterpret_cast<uint32_t*>(dst) = pk[0];
+  }
+}
+
 // ---- debug kernels: the GEMM's unpack and scale decoding, materialised ----
 
 template <int BITS, bool SBF16, bool DEQUANT>
@@ -1598,6 +1847,11 @@ struct XCfg {
   int W, NB, XL;
 };
 constexpr XCfg kX14 = {14, 1, 6}, kX8a = {8, 2, 10}, kX8b = {8, 2, 18};
+
+// Token x column tiles: groups in flight per wave, and the smallest T routed
+// to them rather than to the 8 < T <= 64 kernel.
+constexpr int kTiledNB = 2;
+constexpr int kTiledFromT = 33;  // measured: from 33 tokens on, its 64-token tiles beat the 64-row verify kernel
 
 // Widest tile (columns per lane) that compiles without register spills.
 constexpr int xres_vmax(int bits, int nsets, int xl) {
@@ -1736,12 +1990,56 @@ int run_wide(int nsets, int T, int K, int Nout, int Ncols, const Format& f, cons
   return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
 
+template <int BITS, bool SBF16, int NSETS>
+hipError_t launch_tiled_b(const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
+  auto kern = dev::gemm_tiled_kernel<BITS, SBF16, NSETS, kTiledNB>;
+  static bool raised = false;
+  if (lds > 64u * 1024u && !raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)a.tiles), dim3(dev::kTiledWaves * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int NSETS>
+hipError_t launch_tiled(const Format& f, const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
+  if (f.bits == 4)
+    return f.scale_bf16 ? launch_tiled_b<4, true, NSETS>(a, lds, st) : launch_tiled_b<4, false, NSETS>(a, lds, st);
+  if (f.bits == 5)
+    return f.scale_bf16 ? launch_tiled_b<5, true, NSETS>(a, lds, st) : launch_tiled_b<5, false, NSETS>(a, lds, st);
+  return f.scale_bf16 ? launch_tiled_b<8, true, NSETS>(a, lds, st) : launch_tiled_b<8, false, NSETS>(a, lds, st);
+}
+
+// Token x column tiles (prefill-size T; any T >= 1 when forced), arguments
+// already checked: one workgroup per 64 tokens x 64 weight columns.
+int run_tiled(int nsets, int T, int K, int Nout, int Ncols, const Format& f, const void* x, const void* wq,
+              const void* scales, void* y, size_t wb0, size_t wb1, size_t sb, size_t xb, void* stream) {
+  dev::TiledArgs a;
+  a.x = x; a.wq = wq; a.scales = scales; a.y = y;
+  a.T = T; a.K = K; a.Nout = Nout; a.Ncols = Ncols; a.up_off = nsets == 2 ? Nout : 0;
+  a.G = K / kGroup;
+  const int ocols = dev::kTiledCols / nsets;
+  a.tiles_n = (Nout + ocols - 1) / ocols;
+  const long tiles = (long)a.tiles_n * ((T + dev::kTiledTok - 1) / dev::kTiledTok);
+  if (tiles > 0x7FFFFFFFL) return NGQ_ERR_SHAPE;
+  a.tiles = (int)tiles;
+  a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
+  a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
+  const uint32_t lds = dev::tiled_lds_bytes();
+  const hipError_t e = nsets == 1 ? launch_tiled<1>(f, a, lds, (hipStream_t)stream)
+                                  : launch_tiled<2>(f, a, lds, (hipStream_t)stream);
+  return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
 int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void* x, const void* wq,
              const void* scales, void* y, void* stream) {
   Format f;
   int rc = parse_format(bits, group, &f);
   if (rc != NGQ_OK) return rc;
-  if (T < 0 || T > NGQ_MAX_T_VERIFY) return NGQ_ERR_SHAPE;
+  if (T < 0 || T > NGQ_MAX_T_PREFILL) return NGQ_ERR_SHAPE;
   if ((rc = check_kn(K, Nout)) != NGQ_OK) return rc;
   const long ncols_l = (long)Nout * nsets;
   if (ncols_l > (1L << 30)) return NGQ_ERR_SHAPE;
@@ -1759,7 +2057,15 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   if (xb >= kMaxBuffer || yb >= kMaxBuffer || wb0 + wb1 >= kMaxBuffer || sb >= kMaxBuffer)
     return NGQ_ERR_UNSUPPORTED;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, wq, wb0 + wb1) || overlaps(y, yb, scales, sb)) return NGQ_ERR_ARG;
-  if (T > NGQ_MAX_T) return run_wide(nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
+  const int forced = kernel_override.load(std::memory_order_relaxed);
+  if (forced == NGQ_KERNEL_TILED)
+    return run_tiled(nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
+  if (forced == NGQ_KERNEL_WIDE && (T <= NGQ_MAX_T || T > NGQ_MAX_T_VERIFY)) return NGQ_ERR_UNSUPPORTED;
+  if (T > NGQ_MAX_T) {
+    if (forced != NGQ_KERNEL_WIDE && T >= kTiledFromT)
+      return run_tiled(nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
+    return run_wide(nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
+  }
 
   const int cus = cu_count();
   // Tiles of at least 32 columns where N allows: a 16-column tile reads 64 of
@@ -1787,7 +2093,7 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   //    32-column tiles, where 14 waves of the X-resident kernel are faster;
   //  - otherwise the X-resident kernel with 8 waves when X fits in LDS;
   //  - otherwise per-pair X (dynamic, or static ranges for very long K).
-  int path = kernel_override.load(std::memory_order_relaxed);
+  int path = forced;
   XCfg xc = x8;
   int v = v_pp, vx = 0;
   uint32_t lx = 0;
@@ -2249,6 +2555,6 @@ extern "C" int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* 
 }
 
 extern "C" int ngq_debug_force_kernel(int path) {
-  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_XRES8) return NGQ_ERR_ARG;
+  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_TILED) return NGQ_ERR_ARG;
   return kernel_override.exchange(path);
 }

@@ -108,7 +108,7 @@ extern "C" const char* ngq_strerror(int status) {
   switch (status) {
     case NGQ_OK: return "ok";
     case NGQ_ERR_ARG: return "invalid argument (null pointer, overlapping output or code out of range)";
-    case NGQ_ERR_SHAPE: return "unsupported shape (need 0 <= T <= 8, K % 64 == 0, N % 4 == 0)";
+    case NGQ_ERR_SHAPE: return "unsupported shape (T out of range for the call, K % 64 != 0 or N % 4 != 0)";
     case NGQ_ERR_UNSUPPORTED: return "unsupported format (bits 4/5/8, group 64, buffers < 2 GiB)";
     case NGQ_ERR_ALIGN: return "buffer not 16-byte aligned";
     case NGQ_ERR_HIP: return "HIP runtime error";

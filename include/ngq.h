@@ -69,6 +69,7 @@ extern "C" {
 #define NGQ_GROUP 64 /* the only supported group size */
 #define NGQ_MAX_T 8  /* tokens per call: plain decode (1) up to 7 drafts + 1 */
 #define NGQ_MAX_T_VERIFY 64 /* ngq_gemm / ngq_swiglu_gemm: up to 8 requests x 8 tokens */
+#define NGQ_MAX_T_PREFILL 16384 /* ngq_gemm / ngq_swiglu_gemm: prefill chunks */
 
 /* Bytes of the packed weight buffer (P0, plus P1 for int5) for a K x N
  * matrix; 0 when the arguments are invalid.  Host only, no HIP call. */
@@ -85,14 +86,16 @@ size_t ngq_scale_bytes(int K, int N, int bits, int group);
  * The NGQ_SCALE_BF16 flag is ignored here. */
 int ngq_pack(int K, int N, int bits, int group, const int8_t* codes, void* wq_out);
 
-/* Y = X . dequant(Wq) for 0 <= T <= 64 tokens.  T <= 8 is one request's
+/* Y = X . dequant(Wq) for 0 <= T <= 16384 tokens.  T <= 8 is one request's
  * decode or verify step (the projection of the "What V3 did" T-routing,
  * NInfer-4090 V3 topic).  8 < T <= 64 is the verify rounds of several
  * requests stacked into one call, so that the weights stream once for all of
  * them: an engine serves up to 8 active requests (HotRepo page on
  * Neroued/ninfer, "Constraints"), each verifying up to 7 drafts + 1 (the
  * ninfer-ext README, "Recommended settings"; the V3 topic's "Measured data"
- * runs 2, 4 and 8 requests with 7 drafts).
+ * runs 2, 4 and 8 requests with 7 drafts).  T > 64 is a prefill chunk (the
+ * V3 topic's quick start runs chunks of 1024 tokens), computed in token x
+ * column tiles.
  *   x      : device bf16 [T][K]
  *   wq     : device, ngq_pack layout for K x N
  *   scales : device fp16|bf16 [K/64][N]
@@ -112,7 +115,7 @@ int ngq_gemm(int T, int K, int N, int bits, int group, const void* x, const void
  *                    projection
  *   scales_gate_up : device fp16|bf16 [K/64][2 N_ff]
  *   h              : device bf16 [T][N_ff], overwritten; must not overlap inputs
- * T as for ngq_gemm (0..64).  The down projection is a plain ngq_gemm with
+ * T as for ngq_gemm (0..16384).  The down projection is a plain ngq_gemm with
  * K = N_ff and x = h. */
 int ngq_swiglu_gemm(int T, int K, int N_ff, int bits, int group, const void* x,
                     const void* wq_gate_up, const void* scales_gate_up, void* h, void* stream);
@@ -223,6 +226,8 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
 #define NGQ_KERNEL_PERPAIR_STATIC 2 /* X per pair, static pair ranges per wave */
 #define NGQ_KERNEL_XRES14 3         /* X resident in LDS, 14 waves, one pair each */
 #define NGQ_KERNEL_XRES8 4          /* X resident in LDS, 8 waves, two pairs each */
+#define NGQ_KERNEL_WIDE 5           /* 8 < T <= 64: token blocks of 16, X per pair */
+#define NGQ_KERNEL_TILED 6          /* token x column tiles (prefill), any T */
 int ngq_debug_force_kernel(int path);
 
 /* Bandwidth calibration: stream `bytes` (a multiple of 16) from device memory

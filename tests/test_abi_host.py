@@ -111,7 +111,7 @@ X, W, S, Y = 0x100000, 0x200000, 0x300000, 0x400000
 
 
 @pytest.mark.parametrize("args,status", [
-    ((65, 64, 4, 4, 64, X, W, S, Y), -2),       # T > 64
+    ((16385, 64, 4, 4, 64, X, W, S, Y), -2),    # T > 16384
     ((-1, 64, 4, 4, 64, X, W, S, Y), -2),       # T < 0
     ((1, 100, 4, 4, 64, X, W, S, Y), -2),       # K % 64
     ((1, 64, 6, 4, 64, X, W, S, Y), -2),        # N % 4
@@ -137,7 +137,7 @@ def test_gemm_rejects_bad_arguments(ngq, args, status):
 
 def test_swiglu_rejects_bad_arguments(ngq):
     L = ngq.lib()
-    assert L.ngq_swiglu_gemm(65, 64, 4, 4, 64, X, W, S, Y, None) == -2
+    assert L.ngq_swiglu_gemm(16385, 64, 4, 4, 64, X, W, S, Y, None) == -2
     assert L.ngq_swiglu_gemm(1, 64, 6, 4, 64, X, W, S, Y, None) == -2
     assert L.ngq_swiglu_gemm(1, 64, 4, 4, 64, X, W, S, None, None) == -1
     # the up half makes wq 2 N_ff columns wide: h must not overlap it either
@@ -265,7 +265,7 @@ def test_force_kernel_roundtrip(ngq):
     """The kernel-path override is host state only: set, read back, reject."""
     prev = ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_XRES8)
     assert ngq.ngq_debug_force_kernel(prev) == ngq.NGQ_KERNEL_XRES8
-    assert ngq.lib().ngq_debug_force_kernel(9) == ngq.NGQ_ERR_ARG
+    assert ngq.lib().ngq_debug_force_kernel(7) == ngq.NGQ_ERR_ARG
     assert ngq.lib().ngq_debug_force_kernel(-1) == ngq.NGQ_ERR_ARG
     assert ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_AUTO) == prev
 

@@ -1,5 +1,7 @@
 """ngq_gemm and ngq_swiglu_gemm with 8 < T <= 64 tokens (the verify rounds of
-several requests in one call) on the GPU, against the CPU oracle.
+several requests in one call) on the GPU, against the CPU oracle.  From 33
+tokens on the calls route to the token x column tiles of prefill; the 64-row
+verify kernel is also run there, forced.
 
 Small ragged shapes (odd group counts, so the last pair has one group; a
 column tail; every bit width and both scale types), every token-block
@@ -63,6 +65,19 @@ def test_verify_small(ngq, orc, bits, sbf16, T, K, N):
 def test_verify_token_counts(ngq, orc, T):
     _, (codes, scales, x) = make(4, False, T, 640, 200, seed=T)
     run_and_compare(ngq, orc, 4, False, codes, scales, x, what=f"verify T{T}")
+
+
+@pytest.mark.parametrize("bits,sbf16,T,K,N", [c for c in SMALL if c[2] > 32] + [(4, False, 33, 640, 200),
+                                                                              (5, True, 63, 320, 100)])
+def test_verify_wide_kernel_forced(ngq, orc, bits, sbf16, T, K, N):
+    """33 <= T <= 64 routes to the token x column tiles by default; the 64-row
+    verify kernel still serves it when forced."""
+    _, (codes, scales, x) = make(bits, sbf16, T, K, N, seed=T * 131 + K + N)
+    prev = ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_WIDE)
+    try:
+        run_and_compare(ngq, orc, bits, sbf16, codes, scales, x, what=f"wide forced b{bits} T{T} K{K} N{N}")
+    finally:
+        ngq.ngq_debug_force_kernel(prev)
 
 
 _FULL = {}
