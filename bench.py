@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/projection + effective HBM GB/s (% of peak) at T=1,2,4,8, K=5120 int4/int5"
 PEAK_GBS = 8000.0  # MI355X HBM3E peak
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (prefill-size T is a dense contraction)
 COLD_BYTES = 1 << 30
 KERNEL_SRC = os.path.join(ROOT, "groupwise_int_weight_amd", "csrc", "ngq_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -54,6 +55,9 @@ def parse():
     p.add_argument("--no-stack-side", action="store_true", help="skip the side-stream comparison graph")
     p.add_argument("--fused", type=int, default=0, metavar="T",
                    help="time only the fused qk + gv + gate/up launch at T tokens (for profiling) and exit")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prefill-size T sweep")
+    p.add_argument("--prefill-t", type=int, nargs="*", default=[128, 256, 512, 1024, 2048],
+                   help="token counts of the prefill sweep")
     return p.parse_args()
 
 
@@ -199,6 +203,43 @@ def run_swiglu(ngq, T, steps, warmup):
         {"workload": "down + RMS rescale, ngq_gemm_rescale (split K, fused closing kernel)", "T": T,
          "us": ms_fr * 1e3, "GBps": b_dr / ms_fr / 1e6, "pct_peak": 100 * b_dr / ms_fr / 1e6 / PEAK_GBS},
     ]
+
+
+def run_prefill(ngq, Ts, steps):
+    """Prefill-size T (token x column tiles): the QK, gate/value and down
+    projections at each T, and gate/up + SwiGLU at the largest, as TFLOP/s
+    against the dense bf16 MFMA peak (2 T K N flop per projection; the weights
+    are reused across the tokens, so the MFMA units bound it, not HBM)."""
+    import torch
+
+    import synthetic
+
+    out = []
+
+    def record(label, w, T, ms, n_out):
+        flop = 2.0 * T * w.K * w.N
+        b = algorithmic_bytes(ngq, w, T, n_out=n_out)
+        out.append({"workload": label, "T": T, "us": ms * 1e3, "TFLOPs": flop / ms / 1e9,
+                    "pct_mfma_bf16_peak": 100 * flop / ms / 1e9 / PEAK_BF16_TFLOPS, "GBps": b / ms / 1e6})
+
+    for T in Ts:
+        for name in ("qk", "gv", "down"):
+            w = synthetic.WORKLOADS[name]
+            ms, rot, _ = run_projection(ngq, w, T, steps, 3)
+            record(f"{name} int{w.bits} K={w.K} N={w.N}", w, T, ms, w.N)
+            del rot
+            torch.cuda.empty_cache()
+    if Ts:
+        T = max(Ts)
+        w = synthetic.WORKLOADS["gate_up"]
+        rot = Rotation(ngq, w, T)
+        h = torch.empty((T, synthetic.N_FF), dtype=torch.bfloat16, device="cuda")
+        ms = time_steps(lambda i: ngq.ngq_swiglu_gemm(rot.x, rot.wq[i], rot.s[i], 4, synthetic.N_FF, h=h),
+                        rot.replicas, steps, 3)
+        record("gate_up+SwiGLU int4 K=5120 N=2x17408", w, T, ms, synthetic.N_FF)
+        del rot
+        torch.cuda.empty_cache()
+    return out
 
 
 def gpu_output(ngq, rot, y_dev):
@@ -459,6 +500,8 @@ def main():
             del r
             torch.cuda.empty_cache()
 
+    prefill = None if args.no_prefill else run_prefill(ngq, tuple(args.prefill_t), min(args.sweep_steps, 20))
+
     stack = None if args.no_stack else run_stack(ngq, args.stack_layers, args.stack_passes, tuple(args.stack_t),
                                                  side=not args.no_stack_side)
 
@@ -505,6 +548,7 @@ def main():
         "calibration": calib,
         "parity": parity,
         "sweep": sweep,
+        "prefill": prefill,
         "stack": stack,
         "context": {"rtx4090_single_op_us": {"attention_q5_gate_value_t8": 39.936, "gdn_qk_q4_t8": 31.744},
                     "note": "the pages' own timings on another GPU with unstated shapes; not a target"},

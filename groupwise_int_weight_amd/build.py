@@ -26,6 +26,11 @@ FLAGS = [
     "-Wall",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the T > 8 kernels scale every MFMA
+    # result on the VALU, which otherwise first copies it out of an AGPR
+    # (one v_accvgpr_read per value); the decode kernels compile to the same
+    # code either way
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

@@ -1713,6 +1713,214 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
   }
 }
 
+// Large T: the 4 waves of a workgroup split the columns instead of K.  The
+// workgroup owns 256 weight columns (wave w: columns 64 w .. 64 w + 63) by
+// 64 tokens and walks every group; the group's X tile (64 tokens x 64 k) is
+// loaded once per workgroup, written to LDS in the interleaved k order
+// (double-buffered, one barrier per group) and read by all 4 waves, so each
+// byte of X fetched from L2 feeds 4x the MFMA work of the K-split kernel.
+// Each wave's sums are whole: outputs go from registers straight to memory.
+
+constexpr int kSxCols = 4 * kTiledCols;            // weight columns per workgroup
+constexpr uint32_t kSxRow = 2u * 64u + 16u;        // LDS bytes per token row of an X tile (padded)
+constexpr uint32_t kSxBuf = (uint32_t)kTiledTok * kSxRow;
+
+__host__ __device__ constexpr uint32_t tiled_sx_lds_bytes() { return 2u * kSxBuf; }
+
+template <int BITS, int NSETS>
+struct SxBuf {
+  static constexpr int V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
+  uint32_t a[NSETS][2][V * WPK];             // as TiledBuf
+  uint32_t p1[NSETS][2][BITS == 5 ? V : 1];
+  uint32_t sc[NSETS][2 * V];
+  uint32_t x[2][4];                          // this thread's two 16-byte chunks of the X tile
+};
+
+template <int BITS, bool SBF16, int NSETS, int NB>
+__global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledArgs a) {
+  constexpr int V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
+  constexpr int OCOLS = kSxCols / NSETS;  // output columns per workgroup
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, q = lane >> 4;
+  // XCD-aware order, token tile slowest, as in gemm_tiled_kernel
+  const int b = blockIdx.x, xcd = b & 7, per = a.tiles >> 3, rem = a.tiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
+  const int tt = tile / a.tiles_n, tn = tile - tt * a.tiles_n;
+  const int t0 = tt * kTiledTok;
+  const int c0 = tn * OCOLS + wave * (OCOLS / kTiledWaves);  // this wave's first output column
+
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  uint32_t vbase = a.mask_base;
+  asm volatile("" : "+v"(vbase));
+  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
+
+  // operand roles of lane (m, q) as in gemm_tiled_kernel, for this wave's columns
+  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
+  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s) {
+    const uint32_t col = (uint32_t)(c0 + s * a.up_off + V * m);
+    offA[s] = (uint32_t)q * WPK * rowb + col * 4u;
+    offP1[s] = col * 4u;
+    offS[s] = (uint32_t)(c0 + s * a.up_off + 4 * V * q) * 2u;
+  }
+  // X tile chunks of this thread: chunk j = tid + 256 u is token row j / 8,
+  // 16-byte k chunk j % 8 of the group
+  uint32_t offX[2], ldsX[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = (int)threadIdx.x + 256 * u, row = j >> 3, kc = j & 7, t = t0 + row;
+    offX[u] = t < a.T ? (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)kc * 16u : kOOB;
+    ldsX[u] = (uint32_t)row * kSxRow + (uint32_t)kc * 16u;
+  }
+  // B fragment of token block tb, step ks: row 16 tb + m, k chunk 4 ks + q
+  const uint32_t ldsB = (uint32_t)m * kSxRow + (uint32_t)q * 16u;
+
+  auto issue = [&](SxBuf<BITS, NSETS>& buf, int g) {
+    const bool valid = g < a.G;
+    const uint32_t ga = valid ? (uint32_t)g * 8u * WPK * rowb : kOOB;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const uint32_t o = offA[s] + ga + (uint32_t)ks * 4u * WPK * rowb;
+        load_words<V>(&buf.a[s][ks][0], rW, o);
+        if constexpr (BITS == 8) load_words<V>(&buf.a[s][ks][V], rW, o + rowb);
+      }
+    if constexpr (BITS == 5) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int s = 0; s < NSETS; ++s)
+          load_words<V>(&buf.p1[s][ks][0], rP1, valid ? (uint32_t)(2 * g + ks) * rowb + offP1[s] : kOOB);
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+      load_words<2 * V>(&buf.sc[s][0], rS, valid ? (uint32_t)g * (uint32_t)a.Ncols * 2u + offS[s] : kOOB);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) load_words<4>(&buf.x[u][0], rX, valid ? offX[u] + (uint32_t)g * 128u : kOOB);
+  };
+
+  f32x4 acc[NSETS][V][4];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[s][i][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+
+  // group g: its X chunks into LDS buffer g % 2, barrier, then the wave's MFMAs
+  auto compute = [&](const SxBuf<BITS, NSETS>& buf, int g) {
+    uint8_t* const xb = smem + (uint32_t)(g & 1) * kSxBuf;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(xb + ldsX[u]) = interleave_x(buf.x[u]);
+    lds_barrier();
+    bf16x8 bfr[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        bfr[tb][ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(xb + ldsB + (uint32_t)tb * 16u * kSxRow + (uint32_t)ks * 64u));
+    f32x4 dx[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][0],
+                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][1], dx[tb], 0, 0,
+                                                       0);
+    }
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        u32x4 av[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if constexpr (BITS == 4) {
+            av[ks] = nibbles_to_bf16_il(buf.a[s][ks][i], mk);
+          } else if constexpr (BITS == 5) {
+            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][ks][i], 8u * (uint32_t)q, 8u);
+            av[ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb, mk);
+          } else {
+            av[ks] = bytes_to_bf16_il(buf.a[s][ks][i], buf.a[s][ks][V + i]);
+          }
+        }
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = V * r + i;
+          sc[r] = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          f32x4 dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[0]), bfr[tb][0], dx[tb], 0,
+                                                             0, 0);
+          dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[1]), bfr[tb][1], dp, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[s][i][tb][r] = __builtin_fmaf(sc[r], dp[r], acc[s][i][tb][r]);
+        }
+      }
+  };
+
+  // NB groups in flight; every wave walks every group (the barrier inside
+  // compute is reached the same number of times by all waves)
+  SxBuf<BITS, NSETS> buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    issue(buf[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int g = 0; g < a.G; g += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (g + u < a.G) compute(buf[u], g + u);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[u], g + u + NB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // outputs from registers: token t0 + 16 tb + m, V consecutive columns
+  // c0 + V (4q + r) .. per (tb, r)
+  uint16_t* const y = static_cast<uint16_t*>(a.y);
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = t0 + 16 * tb + m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = c0 + V * (4 * q + r);
+      if (t >= a.T || col >= a.Nout) continue;
+      uint32_t pk[V / 2];
+#pragma unroll
+      for (int i = 0; i < V; i += 2) {
+        float o0, o1;
+        if constexpr (NSETS == 2) {
+          const float g0 = acc[0][i][tb][r], g1 = acc[0][i + 1][tb][r];
+          o0 = g0 * acc[1][i][tb][r] / (1.0f + expf(-g0));  // SiLU(gate) * up
+          o1 = g1 * acc[1][i + 1][tb][r] / (1.0f + expf(-g1));
+        } else {
+          o0 = acc[0][i][tb][r];
+          o1 = acc[0][i + 1][tb][r];
+        }
+        pk[i / 2] = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+      }
+      uint16_t* dst = y + (size_t)t * a.Nout + col;
+      if constexpr (V == 4)
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+      else
+        *reinterpret_cast<uint32_t*>(dst) = pk[0];
+    }
+  }
+}
+
 // ---- debug kernels: the GEMM's unpack and scale decoding, materialised ----
 
 template <int BITS, bool SBF16, bool DEQUANT>
@@ -1850,7 +2058,11 @@ constexpr XCfg kX14 = {14, 1, 6}, kX8a = {8, 2, 10}, kX8b = {8, 2, 18};
 
 // Token x column tiles: groups in flight per wave, and the smallest T routed
 // to them rather than to the 8 < T <= 64 kernel.
-constexpr int kTiledNB = 2;
+constexpr int kTiledNB = 2, kSxNB = 2;  // 3 in flight measured 2-4 % slower for the shared-X kernel
+// shared-X tiles once there are at least 0.6 per CU (measured crossover:
+// QK at T = 256, 0.5 per CU, is faster K-split; down at T = 512, 0.63 per CU,
+// shared)
+constexpr int kSxMinTiles10PerCu = 6;
 constexpr int kTiledFromT = 33;  // measured: from 33 tokens on, its 64-token tiles beat the 64-row verify kernel
 
 // Widest tile (columns per lane) that compiles without register spills.
@@ -2004,33 +2216,66 @@ hipError_t launch_tiled_b(const dev::TiledArgs& a, uint32_t lds, hipStream_t st)
   return hipGetLastError();
 }
 
-template <int NSETS>
+template <int BITS, bool SBF16, int NSETS>
+hipError_t launch_tiled_sx_b(const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((dev::gemm_tiled_sx_kernel<BITS, SBF16, NSETS, kSxNB>), dim3((unsigned)a.tiles),
+                     dim3(dev::kTiledWaves * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int NSETS, bool SX>
 hipError_t launch_tiled(const Format& f, const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
-  if (f.bits == 4)
-    return f.scale_bf16 ? launch_tiled_b<4, true, NSETS>(a, lds, st) : launch_tiled_b<4, false, NSETS>(a, lds, st);
-  if (f.bits == 5)
-    return f.scale_bf16 ? launch_tiled_b<5, true, NSETS>(a, lds, st) : launch_tiled_b<5, false, NSETS>(a, lds, st);
-  return f.scale_bf16 ? launch_tiled_b<8, true, NSETS>(a, lds, st) : launch_tiled_b<8, false, NSETS>(a, lds, st);
+  if constexpr (SX) {
+    if (f.bits == 4)
+      return f.scale_bf16 ? launch_tiled_sx_b<4, true, NSETS>(a, lds, st)
+                          : launch_tiled_sx_b<4, false, NSETS>(a, lds, st);
+    if (f.bits == 5)
+      return f.scale_bf16 ? launch_tiled_sx_b<5, true, NSETS>(a, lds, st)
+                          : launch_tiled_sx_b<5, false, NSETS>(a, lds, st);
+    return f.scale_bf16 ? launch_tiled_sx_b<8, true, NSETS>(a, lds, st)
+                        : launch_tiled_sx_b<8, false, NSETS>(a, lds, st);
+  } else {
+    if (f.bits == 4)
+      return f.scale_bf16 ? launch_tiled_b<4, true, NSETS>(a, lds, st) : launch_tiled_b<4, false, NSETS>(a, lds, st);
+    if (f.bits == 5)
+      return f.scale_bf16 ? launch_tiled_b<5, true, NSETS>(a, lds, st) : launch_tiled_b<5, false, NSETS>(a, lds, st);
+    return f.scale_bf16 ? launch_tiled_b<8, true, NSETS>(a, lds, st) : launch_tiled_b<8, false, NSETS>(a, lds, st);
+  }
 }
 
 // Token x column tiles (prefill-size T; any T >= 1 when forced), arguments
-// already checked: one workgroup per 64 tokens x 64 weight columns.
-int run_tiled(int nsets, int T, int K, int Nout, int Ncols, const Format& f, const void* x, const void* wq,
-              const void* scales, void* y, size_t wb0, size_t wb1, size_t sb, size_t xb, void* stream) {
+// already checked: 64 tokens by 64 weight columns per workgroup with K split
+// over its waves, or (sx) 64 tokens by 256 weight columns sharing each X tile,
+// which needs 4x as many tokens to fill the CUs.  `path` is NGQ_KERNEL_TILED
+// or NGQ_KERNEL_TILED_SX to force either, anything else to choose.
+int run_tiled(int path, int nsets, int T, int K, int Nout, int Ncols, const Format& f, const void* x,
+              const void* wq, const void* scales, void* y, size_t wb0, size_t wb1, size_t sb, size_t xb,
+              void* stream) {
   dev::TiledArgs a;
   a.x = x; a.wq = wq; a.scales = scales; a.y = y;
   a.T = T; a.K = K; a.Nout = Nout; a.Ncols = Ncols; a.up_off = nsets == 2 ? Nout : 0;
   a.G = K / kGroup;
-  const int ocols = dev::kTiledCols / nsets;
+  const long ttiles = (T + dev::kTiledTok - 1) / dev::kTiledTok;
+  const long sx_tiles = (Nout + dev::kSxCols / nsets - 1) / (dev::kSxCols / nsets) * ttiles;
+  const bool sx = path == NGQ_KERNEL_TILED_SX ||
+                  (path != NGQ_KERNEL_TILED && 10 * sx_tiles >= (long)kSxMinTiles10PerCu * cu_count());
+  const int ocols = (sx ? dev::kSxCols : dev::kTiledCols) / nsets;
   a.tiles_n = (Nout + ocols - 1) / ocols;
-  const long tiles = (long)a.tiles_n * ((T + dev::kTiledTok - 1) / dev::kTiledTok);
+  const long tiles = (long)a.tiles_n * ttiles;
   if (tiles > 0x7FFFFFFFL) return NGQ_ERR_SHAPE;
   a.tiles = (int)tiles;
   a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
   a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
-  const uint32_t lds = dev::tiled_lds_bytes();
-  const hipError_t e = nsets == 1 ? launch_tiled<1>(f, a, lds, (hipStream_t)stream)
-                                  : launch_tiled<2>(f, a, lds, (hipStream_t)stream);
+  hipError_t e;
+  if (sx) {
+    const uint32_t lds = dev::tiled_sx_lds_bytes();
+    e = nsets == 1 ? launch_tiled<1, true>(f, a, lds, (hipStream_t)stream)
+                   : launch_tiled<2, true>(f, a, lds, (hipStream_t)stream);
+  } else {
+    const uint32_t lds = dev::tiled_lds_bytes();
+    e = nsets == 1 ? launch_tiled<1, false>(f, a, lds, (hipStream_t)stream)
+                   : launch_tiled<2, false>(f, a, lds, (hipStream_t)stream);
+  }
   return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
 
@@ -2058,12 +2303,12 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     return NGQ_ERR_UNSUPPORTED;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, wq, wb0 + wb1) || overlaps(y, yb, scales, sb)) return NGQ_ERR_ARG;
   const int forced = kernel_override.load(std::memory_order_relaxed);
-  if (forced == NGQ_KERNEL_TILED)
-    return run_tiled(nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
+  if (forced == NGQ_KERNEL_TILED || forced == NGQ_KERNEL_TILED_SX)
+    return run_tiled(forced, nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
   if (forced == NGQ_KERNEL_WIDE && (T <= NGQ_MAX_T || T > NGQ_MAX_T_VERIFY)) return NGQ_ERR_UNSUPPORTED;
   if (T > NGQ_MAX_T) {
     if (forced != NGQ_KERNEL_WIDE && T >= kTiledFromT)
-      return run_tiled(nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
+      return run_tiled(NGQ_KERNEL_AUTO, nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
     return run_wide(nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
   }
 
@@ -2555,6 +2800,6 @@ extern "C" int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* 
 }
 
 extern "C" int ngq_debug_force_kernel(int path) {
-  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_TILED) return NGQ_ERR_ARG;
+  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_TILED_SX) return NGQ_ERR_ARG;
   return kernel_override.exchange(path);
 }

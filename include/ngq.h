@@ -227,7 +227,8 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
 #define NGQ_KERNEL_XRES14 3         /* X resident in LDS, 14 waves, one pair each */
 #define NGQ_KERNEL_XRES8 4          /* X resident in LDS, 8 waves, two pairs each */
 #define NGQ_KERNEL_WIDE 5           /* 8 < T <= 64: token blocks of 16, X per pair */
-#define NGQ_KERNEL_TILED 6          /* token x column tiles (prefill), any T */
+#define NGQ_KERNEL_TILED 6          /* token x column tiles (prefill), K split over waves, any T */
+#define NGQ_KERNEL_TILED_SX 7       /* token x column tiles, X tile shared by the waves, any T */
 int ngq_debug_force_kernel(int path);
 
 /* Bandwidth calibration: stream `bytes` (a multiple of 16) from device memory

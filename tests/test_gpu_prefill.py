@@ -1,9 +1,10 @@
-"""ngq_gemm and ngq_swiglu_gemm with prefill-size T (> 64 tokens: token x
-column tiles) on the GPU, against the CPU oracle.
+"""ngq_gemm and ngq_swiglu_gemm with prefill-size T (token x column tiles,
+K split over the waves, or the X tile shared by waves that split the columns)
+on the GPU, against the CPU oracle.
 
 Small ragged shapes (a token tail past every 64-token tile, a column tail,
-odd group counts, every bit width and both scale types), the same kernel
-forced at decode and verify T, the full-size projections at T = 1024 and 256
+odd group counts, every bit width and both scale types) for both variants,
+the K-split kernel forced at decode and verify T, the full-size projections at T = 1024 and 256
 on sampled columns, bit-exact cases, guard bands, K = 0, determinism and
 graph replay.
 """
@@ -44,6 +45,13 @@ def forced_tiled(ngq):
     ngq.ngq_debug_force_kernel(prev)
 
 
+@pytest.fixture
+def forced_sx(ngq):
+    prev = ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_TILED_SX)
+    yield
+    ngq.ngq_debug_force_kernel(prev)
+
+
 SMALL = [
     # bits, scale_bf16, T, K, N
     (4, False, 65, 320, 100),    # one past the verify range; 5 groups; column tail
@@ -73,6 +81,25 @@ def test_tiled_kernel_at_small_t(ngq, orc, forced_tiled, bits, sbf16, T):
     run_and_compare(ngq, orc, bits, sbf16, codes, scales, x, what=f"tiled forced b{bits} T{T}")
 
 
+@pytest.mark.parametrize("bits,sbf16,T,K,N", SMALL + [(4, False, 1, 320, 1000), (5, True, 8, 576, 264)])
+def test_shared_x_kernel_small(ngq, orc, forced_sx, bits, sbf16, T, K, N):
+    """The variant whose waves split the columns and share each X tile
+    (large T routes to it) on the same ragged shapes, forced."""
+    _, (codes, scales, x) = make(bits, sbf16, T, K, N, seed=T * 7 + K + N + 1)
+    run_and_compare(ngq, orc, bits, sbf16, codes, scales, x, what=f"sx forced b{bits} T{T} K{K} N{N}")
+
+
+@pytest.mark.parametrize("bits,sbf16,T,K,N_ff", [(4, False, 65, 512, 100), (5, True, 130, 320, 36),
+                                                  (8, False, 70, 256, 200)])
+def test_shared_x_kernel_swiglu(ngq, orc, forced_sx, bits, sbf16, T, K, N_ff):
+    _, (codes, scales, x) = make(bits, sbf16, T, K, 2 * N_ff, seed=K + N_ff + T + 1)
+    packed = ngq.ngq_pack(codes, bits)
+    h = ngq.ngq_swiglu_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits, N_ff)
+    cols = np.arange(N_ff, dtype=np.int32)
+    h64, g, u = swiglu_reference(orc, x, orc.pack(codes, bits), scales, K, N_ff, bits, sbf16, cols)
+    check_swiglu(host_bits(h), h64, g, u, f"sx swiglu b{bits} T{T}")
+
+
 _FULL = {}
 
 
@@ -85,6 +112,7 @@ def full_inputs(name, T):
     return _FULL[key]
 
 
+# qk at T = 1024 runs the shared-X variant, the others the K-split one
 @pytest.mark.parametrize("name,T", [("qk", 1024), ("gv", 256), ("qk8", 130), ("down", 256)])
 def test_prefill_full_size(ngq, orc, name, T):
     w, codes, scales, x = full_inputs(name, T)
@@ -174,9 +202,9 @@ def test_prefill_k_zero_writes_zeros(ngq):
     assert np.all(host_bits(y) == 0)
 
 
-def test_prefill_graph_replay(ngq):
+@pytest.mark.parametrize("T", [256, 1024])  # K-split and shared-X variants
+def test_prefill_graph_replay(ngq, T):
     w = synthetic.WORKLOADS["qk"]
-    T = 256
     _, codes, scales, x = full_inputs("qk", T)
     args = (dev_bf16(x), dev_u8(ngq.ngq_pack(codes, 4)), dev_scales(scales, False), 4, w.N)
     ref = host_bits(ngq.ngq_gemm(*args))
