@@ -1722,6 +1722,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
 // Each wave's sums are whole: outputs go from registers straight to memory.
 
 constexpr int kSxCols = 4 * kTiledCols;            // weight columns per workgroup
+constexpr int kSxBand = 4;                         // token tiles per band of the tile order
 constexpr uint32_t kSxRow = 2u * 64u + 16u;        // LDS bytes per token row of an X tile (padded)
 constexpr uint32_t kSxBuf = (uint32_t)kTiledTok * kSxRow;
 
@@ -1744,10 +1745,16 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, q = lane >> 4;
-  // XCD-aware order, token tile slowest, as in gemm_tiled_kernel
+  // XCD-aware order (each XCD a contiguous range of tiles), the range walked
+  // in bands of kSxBand token tiles, token tile fastest: the workgroups one
+  // XCD runs at a time then share a few token tiles' X and a few column
+  // tiles' weights in its L2, instead of one token tile and every column
+  // tile's weights
   const int b = blockIdx.x, xcd = b & 7, per = a.tiles >> 3, rem = a.tiles & 7;
   const int tile = xcd * per + min(xcd, rem) + (b >> 3);
-  const int tt = tile / a.tiles_n, tn = tile - tt * a.tiles_n;
+  const int tiles_t = a.tiles / a.tiles_n, band = tile / (kSxBand * a.tiles_n);
+  const int in_band = tile - band * (kSxBand * a.tiles_n), bt = min(kSxBand, tiles_t - band * kSxBand);
+  const int tt = band * kSxBand + in_band % bt, tn = in_band / bt;
   const int t0 = tt * kTiledTok;
   const int c0 = tn * OCOLS + wave * (OCOLS / kTiledWaves);  // this wave's first output column
 
