@@ -615,6 +615,31 @@ __device__ __forceinline__ XresLane xres_lane(int T, int K, uint32_t mask_nib, u
   return ln;
 }
 
+// Row and column (tt, kc) of this thread's 16-byte chunks c_j = tid + 64 W j
+// of a [rows][rowch] array of chunks, with one division for the first chunk
+// and none after: a step of 64 W chunks is q0 rows and r0 chunks, r0 <
+// rowch, so each step carries at most one row.  (A division per chunk, of a
+// value known only at run time, costs ~25 VALU instructions.)  rowch <= 0
+// gives zeros.
+template <int XL, int W>
+__device__ __forceinline__ void chunk_coords(int rowch, int (&tt)[XL], int (&kc)[XL]) {
+  constexpr int S = W * 64;
+  const int d = rowch > 0 ? rowch : 1;
+  int t = (int)threadIdx.x / d, k = (int)threadIdx.x - t * d;
+  const int q0 = S / d, r0 = S - q0 * d;
+#pragma unroll
+  for (int j = 0; j < XL; ++j) {
+    tt[j] = t;
+    kc[j] = k;
+    k += r0;
+    t += q0;
+    if (k >= d) {
+      k -= d;
+      ++t;
+    }
+  }
+}
+
 // The X prologue: XL 16-byte chunks of X per thread, loaded before any weight
 // (x_stage writes them to LDS once the first pairs' loads are issued).
 template <int XL, int W>
@@ -635,6 +660,14 @@ template <int XL, int W>
 __device__ __forceinline__ void x_stage(uint8_t* smem, const uint32_t (&xv)[XL][4], int T, int K) {
   const int nch = T * (K >> 3), rowch = K >> 3;
   const uint32_t XROW = XSmem::xrow(K);
+  // the LDS addresses depend on no loaded value: computed first, while the
+  // loads are in flight (the barrier keeps them ahead of the first wait)
+  int tt[XL], kc[XL];
+  chunk_coords<XL, W>(rowch, tt, kc);
+  uint32_t dst[XL];
+#pragma unroll
+  for (int j = 0; j < XL; ++j) dst[j] = XSmem::ZERO + (uint32_t)tt[j] * XROW + (uint32_t)kc[j] * 16u;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
     const int c = threadIdx.x + W * 64 * j;
@@ -643,10 +676,7 @@ __device__ __forceinline__ void x_stage(uint8_t* smem, const uint32_t (&xv)[XL][
     // (it would wait for X before they are issued)
     uint32_t d[4] = {xv[j][0], xv[j][1], xv[j][2], xv[j][3]};
     asm volatile("" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]));
-    if (c < nch) {
-      const int tt = c / rowch, kc = c - tt * rowch;
-      *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(d);
-    }
+    if (c < nch) *reinterpret_cast<u32x4*>(smem + dst[j]) = interleave_x(d);
   }
   if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
   lds_barrier();
@@ -990,7 +1020,12 @@ __device__ __forceinline__ void x_stage_rounds(uint8_t* smem, const void* x, uin
   const uint32_t XROW = XSmem::xrow(K);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(x, x_bytes);
   if (threadIdx.x < XSmem::ZERO / 16) *reinterpret_cast<u32x4*>(smem + 16u * threadIdx.x) = u32x4{0u, 0u, 0u, 0u};
-  for (int base = 0; base < nch; base += XL * W * 64) {
+  // round r's chunk j is chunk r XL + j of the thread's sequence
+  int tt[XL], kc[XL];
+  chunk_coords<XL, W>(rowch, tt, kc);
+  const int RS = XL * W * 64;
+  const int dq = RS / (rowch > 0 ? rowch : 1), dr = RS - dq * (rowch > 0 ? rowch : 1);
+  for (int base = 0; base < nch; base += RS) {
     uint32_t xr[XL][4];
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
@@ -1000,9 +1035,15 @@ __device__ __forceinline__ void x_stage_rounds(uint8_t* smem, const void* x, uin
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
       const int c = base + threadIdx.x + W * 64 * j;
-      if (c < nch) {
-        const int tt = c / rowch, kc = c - tt * rowch;
-        *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt * XROW + (uint32_t)kc * 16u) = interleave_x(xr[j]);
+      if (c < nch)
+        *reinterpret_cast<u32x4*>(smem + XSmem::ZERO + (uint32_t)tt[j] * XROW + (uint32_t)kc[j] * 16u) =
+            interleave_x(xr[j]);
+      // the same chunk of the next round
+      kc[j] += dr;
+      tt[j] += dq;
+      if (kc[j] >= rowch) {
+        kc[j] -= rowch;
+        ++tt[j];
       }
     }
   }
@@ -1138,11 +1179,12 @@ __device__ __forceinline__ void x_load_slice(uint32_t (&xv)[XL][4], const void* 
                                              int k0, int kx) {
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(x, x_bytes);
   const int rowch = kx >> 3, nch = T * rowch;
+  int tt[XL], kc[XL];
+  chunk_coords<XL, W>(rowch, tt, kc);
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
     const int c = threadIdx.x + W * 64 * j;
-    const int tt = c / rowch, kc = c - tt * rowch;
-    const uint32_t off = c < nch ? ((uint32_t)tt * (uint32_t)K + (uint32_t)k0) * 2u + (uint32_t)kc * 16u : kOOB;
+    const uint32_t off = c < nch ? ((uint32_t)tt[j] * (uint32_t)K + (uint32_t)k0) * 2u + (uint32_t)kc[j] * 16u : kOOB;
     load_words<4>(xv[j], rX, off);
   }
 }
