@@ -68,7 +68,7 @@ extern "C" {
 #define NGQ_SCALE_BF16 0x100
 #define NGQ_GROUP 64 /* the only supported group size */
 #define NGQ_MAX_T 8  /* tokens per call: plain decode (1) up to 7 drafts + 1 */
-#define NGQ_MAX_T_VERIFY 64 /* ngq_gemm / ngq_swiglu_gemm: up to 8 requests x 8 tokens */
+#define NGQ_MAX_T_VERIFY 64 /* several requests verified in one call: up to 8 requests x 8 tokens */
 #define NGQ_MAX_T_PREFILL 16384 /* ngq_gemm / ngq_swiglu_gemm: prefill chunks */
 
 /* Bytes of the packed weight buffer (P0, plus P1 for int5) for a K x N
@@ -216,11 +216,14 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
 
 /* Debug export: force the kernel path of ngq_gemm / ngq_swiglu_gemm for every
  * later call in the process (tests use it to run each path on the same
- * shapes).  NGQ_KERNEL_AUTO restores the per-shape choice.  A forced path
- * that cannot serve a shape (X or the partial sums do not fit in LDS, or the
- * 14-wave kernel with the SwiGLU epilogue) makes those calls return
- * NGQ_ERR_UNSUPPORTED.  Returns the previous setting, or NGQ_ERR_ARG for an
- * unknown path.  Not thread-safe with respect to calls that are running. */
+ * shapes).  NGQ_KERNEL_AUTO restores the per-shape choice.  Paths 1..4 are
+ * the T <= 8 kernels (larger T keeps the library's choice under them);
+ * NGQ_KERNEL_WIDE serves 8 < T <= 64; the two token x column paths serve any
+ * T.  A forced path that cannot serve a shape (X or the partial sums do not
+ * fit in LDS, the 14-wave kernel with the SwiGLU epilogue, NGQ_KERNEL_WIDE
+ * outside its T range) makes those calls return NGQ_ERR_UNSUPPORTED.
+ * Returns the previous setting, or NGQ_ERR_ARG for an unknown path.  Not
+ * thread-safe with respect to calls that are running. */
 #define NGQ_KERNEL_AUTO 0
 #define NGQ_KERNEL_PERPAIR_DYN 1    /* X per pair, pairs handed out dynamically */
 #define NGQ_KERNEL_PERPAIR_STATIC 2 /* X per pair, static pair ranges per wave */
