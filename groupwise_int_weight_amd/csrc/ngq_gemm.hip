@@ -185,6 +185,9 @@ struct GemmArgs {
   int pairs;   // ceil(G / 2)
   int ppw;     // pairs per wave
   int ntiles;  // workgroups
+  // X-resident launches (grid-stride over the tiles): ntiles / grid and
+  // ntiles % grid, so that a workgroup's tile count needs no division
+  int tiles_q, tiles_r;
   uint32_t p0_bytes, p1_bytes, s_bytes, x_bytes;
   uint32_t mask_nib, mask_base, mask_hi;  // the unpack constants (UnpackMasks)
 };
@@ -947,7 +950,7 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
   // consecutively, so that one XCD works on neighbouring tiles at a time
   const int G = gridDim.x, b = blockIdx.x, xcd = b & 7;
   const int rank = xcd * (G >> 3) + min(xcd, G & 7) + (b >> 3);
-  const int my_tiles = (a.ntiles - rank + G - 1) / G;
+  const int my_tiles = a.tiles_q + (rank < a.tiles_r ? 1 : 0);  // tiles rank, rank + G, ... < ntiles
 
   // -- prologue: X loads first, then the first pairs' weights; the X wait in
   // x_stage then leaves those weights in flight.
@@ -2415,6 +2418,7 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   a.G = K / kGroup;
   a.pairs = pairs;
   a.ppw = (a.pairs + dev::kWaves - 1) / dev::kWaves;
+  a.tiles_q = a.tiles_r = 0;  // set for the X-resident launch below
   a.ntiles = (Nout + 16 * v - 1) / (16 * v);
   a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
   a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
@@ -2424,6 +2428,8 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     const int per = (a.pairs + xc.W - 1) / xc.W;
     a.ppw = (per + xc.NB - 1) / xc.NB * xc.NB;
     const int grid = std::min(a.ntiles, cus);
+    a.tiles_q = a.ntiles / grid;
+    a.tiles_r = a.ntiles % grid;
     e = nsets == 1 ? launch_xres<1>(f, xc, v, a, grid, lx, st) : launch_xres<2>(f, xc, v, a, grid, lx, st);
     return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
   }
