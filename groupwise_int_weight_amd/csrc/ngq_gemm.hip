@@ -74,8 +74,18 @@ constexpr int kThreads = kWaves * 64;
 constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  // raw buffer (stride 0), 32-bit data format: bounds-checked against `bytes`
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+  // raw buffer (stride 0), 32-bit data format: bounds-checked against `bytes`.
+  // Every descriptor is built from kernel arguments, so it is uniform; saying
+  // so (readfirstlane) keeps it in scalar registers.  Where the compiler lost
+  // track of that it held the descriptor in vector registers and wrapped
+  // every load in a loop over the lanes' distinct descriptors.
+  // (readfirstlane returns a signed int: each half goes through uint32_t, or
+  // the low half would sign-extend into the high one)
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  void* const pu = reinterpret_cast<void*>(((uint64_t)hi << 32) | (uint64_t)lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
 
 template <int NW>
