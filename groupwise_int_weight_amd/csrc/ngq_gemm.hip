@@ -1563,57 +1563,36 @@ struct TiledBuf {
   uint32_t x[4][2][4];                       // [token block][step][dword]
 };
 
-template <int BITS, bool SBF16, int NSETS, int NB>
-__global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs a) {
-  constexpr int W = kTiledWaves, V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
-  constexpr int OCOLS = kTiledCols / NSETS;  // output columns per tile
-  constexpr int E = NSETS * V * 16;           // accumulators per lane (64)
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* const part = reinterpret_cast<float*>(smem);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m = lane & 15, q = lane >> 4;
-  // XCD-aware order: each XCD (block b runs on XCD b % 8) takes a contiguous
-  // range of tiles, token tile slowest, so the workgroups of one XCD share
-  // the X rows of a token tile in its L2
-  const int b = blockIdx.x, xcd = b & 7, per = a.tiles >> 3, rem = a.tiles & 7;
-  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
-  const int tt = tile / a.tiles_n, tn = tile - tt * a.tiles_n;
-  const int t0 = tt * kTiledTok, c0 = tn * OCOLS;
+// The weight side of a wave's 64 columns in the token x column kernels:
+// lane (m, q) loads, per set s and 32-k step, V adjacent P0 words of columns
+// c0 + s up_off + V m .. at 8-k block 8 g + 4 ks + q (two rows for int8),
+// the int5 high-bit words of the same columns, and the 4V scales of columns
+// c0 + s up_off + 4 V q ...  Columns past the matrix read the next row or
+// nothing: only their own (discarded) outputs see them.
+template <int BITS, int NSETS>
+struct TileWeights {
+  static constexpr int V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
+  __amdgpu_buffer_rsrc_t rW, rP1, rS;
+  uint32_t rowb, srow, offA[NSETS], offP1[NSETS], offS[NSETS];
 
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
-  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
-  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
-  uint32_t vbase = a.mask_base;
-  asm volatile("" : "+v"(vbase));
-  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
-
-  // Lane (m, q) supplies, for set s and column i < V, operand row m of the
-  // A block (weight column c0 + s up_off + V m + i) at the 8 k of slot q, and
-  // token 16 tb + m of the B block; its results are rows 4q + r (weight
-  // columns c0 + s up_off + V (4q + r) + i) for token 16 tb + m.  Columns past
-  // the matrix read the next row or nothing: only their own (discarded)
-  // outputs see them.
-  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
-  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];
+  __device__ __forceinline__ TileWeights(const TiledArgs& a, int c0, int m, int q) {
+    rW = make_rsrc(a.wq, a.p0_bytes);
+    rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+    rS = make_rsrc(a.scales, a.s_bytes);
+    rowb = (uint32_t)a.Ncols * 4u;
+    srow = (uint32_t)a.Ncols * 2u;
 #pragma unroll
-  for (int s = 0; s < NSETS; ++s) {
-    const uint32_t col = (uint32_t)(c0 + s * a.up_off + V * m);
-    offA[s] = (uint32_t)q * WPK * rowb + col * 4u;
-    offP1[s] = col * 4u;
-    offS[s] = (uint32_t)(c0 + s * a.up_off + 4 * V * q) * 2u;
-  }
-  uint32_t offX[4];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int t = t0 + 16 * tb + m;
-    offX[tb] = t < a.T ? (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)q * 16u : kOOB;
+    for (int s = 0; s < NSETS; ++s) {
+      const uint32_t col = (uint32_t)(c0 + s * a.up_off + V * m);
+      offA[s] = (uint32_t)q * WPK * rowb + col * 4u;
+      offP1[s] = col * 4u;
+      offS[s] = (uint32_t)(c0 + s * a.up_off + 4 * V * q) * 2u;
+    }
   }
 
-  // loads of group g (g >= G loads nothing)
-  auto issue = [&](TiledBuf<BITS, NSETS>& buf, int g) {
-    const bool valid = g < a.G;
+  // group g's words and scales into `buf` (nothing when !valid)
+  template <class Buf>
+  __device__ __forceinline__ void issue(Buf& buf, int g, bool valid) const {
     const uint32_t ga = valid ? (uint32_t)g * 8u * WPK * rowb : kOOB;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -1632,7 +1611,102 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
     }
 #pragma unroll
     for (int s = 0; s < NSETS; ++s)
-      load_words<2 * V>(&buf.sc[s][0], rS, valid ? (uint32_t)g * (uint32_t)a.Ncols * 2u + offS[s] : kOOB);
+      load_words<2 * V>(&buf.sc[s][0], rS, valid ? (uint32_t)g * srow + offS[s] : kOOB);
+  }
+};
+
+// One group (64 k) of a token x column tile for one wave: the offset chain
+// -(128 + bias) sum_k x per token block, then per weight column the two
+// 32-k steps unpacked once and multiplied with the 4 token blocks' B
+// fragments `bfr`, each group's partial scaled into acc.  Lane (m, q): A row
+// m = weight column V m + i of set s, k-slot q.  `buf` holds the group's
+// P0 words, int5 high-bit words and scales (TiledBuf or SxBuf).
+template <int BITS, bool SBF16, int NSETS, class Buf>
+__device__ __forceinline__ void tile_group(const Buf& buf, const bf16x8 (&bfr)[4][2], const UnpackMasks& mk, int q,
+                                           f32x4 (&acc)[NSETS][4 / NSETS][4]) {
+  constexpr int V = 4 / NSETS;
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+  f32x4 dx[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][0],
+                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][1], dx[tb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      u32x4 av[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (BITS == 4) {
+          av[ks] = nibbles_to_bf16_il(buf.a[s][ks][i], mk);
+        } else if constexpr (BITS == 5) {
+          // k-block 4 ks + q is byte q of the step's 32-k high-bit word
+          const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][ks][i], 8u * (uint32_t)q, 8u);
+          av[ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb, mk);
+        } else {
+          av[ks] = bytes_to_bf16_il(buf.a[s][ks][i], buf.a[s][ks][V + i]);
+        }
+      }
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = V * r + i;
+        sc[r] = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
+      }
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        f32x4 dp =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[0]), bfr[tb][0], dx[tb], 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[1]), bfr[tb][1], dp, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[s][i][tb][r] = __builtin_fmaf(sc[r], dp[r], acc[s][i][tb][r]);
+      }
+    }
+}
+
+template <int BITS, bool SBF16, int NSETS, int NB>
+__global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs a) {
+  constexpr int W = kTiledWaves, V = 4 / NSETS;
+  constexpr int OCOLS = kTiledCols / NSETS;  // output columns per tile
+  constexpr int E = NSETS * V * 16;           // accumulators per lane (64)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* const part = reinterpret_cast<float*>(smem);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, q = lane >> 4;
+  // XCD-aware order: each XCD (block b runs on XCD b % 8) takes a contiguous
+  // range of tiles, token tile slowest, so the workgroups of one XCD share
+  // the X rows of a token tile in its L2
+  const int b = blockIdx.x, xcd = b & 7, per = a.tiles >> 3, rem = a.tiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
+  const int tt = tile / a.tiles_n, tn = tile - tt * a.tiles_n;
+  const int t0 = tt * kTiledTok, c0 = tn * OCOLS;
+
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
+  uint32_t vbase = a.mask_base;
+  asm volatile("" : "+v"(vbase));
+  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
+
+  // Lane (m, q) supplies, for set s and column i < V, operand row m of the
+  // A block (weight column c0 + s up_off + V m + i) at the 8 k of slot q, and
+  // token 16 tb + m of the B block; its results are rows 4q + r (weight
+  // columns c0 + s up_off + V (4q + r) + i) for token 16 tb + m.
+  const TileWeights<BITS, NSETS> tw(a, c0, m, q);
+  uint32_t offX[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = t0 + 16 * tb + m;
+    offX[tb] = t < a.T ? (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)q * 16u : kOOB;
+  }
+
+  // loads of group g (g >= G loads nothing)
+  auto issue = [&](TiledBuf<BITS, NSETS>& buf, int g) {
+    const bool valid = g < a.G;
+    tw.issue(buf, g, valid);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -1647,8 +1721,6 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
     for (int i = 0; i < V; ++i)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[s][i][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
-                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
 
   auto compute = [&](const TiledBuf<BITS, NSETS>& buf) {
     bf16x8 bfr[4][2];
@@ -1656,46 +1728,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) bfr[tb][ks] = __builtin_bit_cast(bf16x8, interleave_x(buf.x[tb][ks]));
-    f32x4 dx[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][0],
-                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][1], dx[tb], 0, 0,
-                                                       0);
-    }
-#pragma unroll
-    for (int s = 0; s < NSETS; ++s)
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        u32x4 av[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if constexpr (BITS == 4) {
-            av[ks] = nibbles_to_bf16_il(buf.a[s][ks][i], mk);
-          } else if constexpr (BITS == 5) {
-            // k-block 4 ks + q is byte q of the step's 32-k high-bit word
-            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][ks][i], 8u * (uint32_t)q, 8u);
-            av[ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb, mk);
-          } else {
-            av[ks] = bytes_to_bf16_il(buf.a[s][ks][i], buf.a[s][ks][V + i]);
-          }
-        }
-        float sc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = V * r + i;
-          sc[r] = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
-        }
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          f32x4 dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[0]), bfr[tb][0], dx[tb], 0,
-                                                             0, 0);
-          dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[1]), bfr[tb][1], dp, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[s][i][tb][r] = __builtin_fmaf(sc[r], dp[r], acc[s][i][tb][r]);
-        }
-      }
+    tile_group<BITS, SBF16, NSETS>(buf, bfr, mk, q, acc);
   };
 
   // NB groups in flight per wave; loads are issued without a branch (a group
@@ -1797,7 +1830,7 @@ struct SxBuf {
 
 template <int BITS, bool SBF16, int NSETS, int NB>
 __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledArgs a) {
-  constexpr int V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
+  constexpr int V = 4 / NSETS;
   constexpr int OCOLS = kSxCols / NSETS;  // output columns per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -1816,24 +1849,13 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
   const int t0 = tt * kTiledTok;
   const int c0 = tn * OCOLS + wave * (OCOLS / kTiledWaves);  // this wave's first output column
 
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
-  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
   uint32_t vbase = a.mask_base;
   asm volatile("" : "+v"(vbase));
   const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
 
   // operand roles of lane (m, q) as in gemm_tiled_kernel, for this wave's columns
-  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
-  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];
-#pragma unroll
-  for (int s = 0; s < NSETS; ++s) {
-    const uint32_t col = (uint32_t)(c0 + s * a.up_off + V * m);
-    offA[s] = (uint32_t)q * WPK * rowb + col * 4u;
-    offP1[s] = col * 4u;
-    offS[s] = (uint32_t)(c0 + s * a.up_off + 4 * V * q) * 2u;
-  }
+  const TileWeights<BITS, NSETS> tw(a, c0, m, q);
   // X tile chunks of this thread: chunk j = tid + 256 u is token row j / 8,
   // 16-byte k chunk j % 8 of the group
   uint32_t offX[2], ldsX[2];
@@ -1848,25 +1870,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
 
   auto issue = [&](SxBuf<BITS, NSETS>& buf, int g) {
     const bool valid = g < a.G;
-    const uint32_t ga = valid ? (uint32_t)g * 8u * WPK * rowb : kOOB;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int s = 0; s < NSETS; ++s) {
-        const uint32_t o = offA[s] + ga + (uint32_t)ks * 4u * WPK * rowb;
-        load_words<V>(&buf.a[s][ks][0], rW, o);
-        if constexpr (BITS == 8) load_words<V>(&buf.a[s][ks][V], rW, o + rowb);
-      }
-    if constexpr (BITS == 5) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int s = 0; s < NSETS; ++s)
-          load_words<V>(&buf.p1[s][ks][0], rP1, valid ? (uint32_t)(2 * g + ks) * rowb + offP1[s] : kOOB);
-    }
-#pragma unroll
-    for (int s = 0; s < NSETS; ++s)
-      load_words<2 * V>(&buf.sc[s][0], rS, valid ? (uint32_t)g * (uint32_t)a.Ncols * 2u + offS[s] : kOOB);
+    tw.issue(buf, g, valid);
 #pragma unroll
     for (int u = 0; u < 2; ++u) load_words<4>(&buf.x[u][0], rX, valid ? offX[u] + (uint32_t)g * 128u : kOOB);
   };
@@ -1878,8 +1882,6 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
     for (int i = 0; i < V; ++i)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[s][i][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
-                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
 
   // group g: its X chunks into LDS buffer g % 2, barrier, then the wave's MFMAs
   auto compute = [&](const SxBuf<BITS, NSETS>& buf, int g) {
@@ -1894,45 +1896,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
       for (int ks = 0; ks < 2; ++ks)
         bfr[tb][ks] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(xb + ldsB + (uint32_t)tb * 16u * kSxRow + (uint32_t)ks * 64u));
-    f32x4 dx[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][0],
-                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      dx[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfr[tb][1], dx[tb], 0, 0,
-                                                       0);
-    }
-#pragma unroll
-    for (int s = 0; s < NSETS; ++s)
-#pragma unroll
-      for (int i = 0; i < V; ++i) {
-        u32x4 av[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if constexpr (BITS == 4) {
-            av[ks] = nibbles_to_bf16_il(buf.a[s][ks][i], mk);
-          } else if constexpr (BITS == 5) {
-            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][ks][i], 8u * (uint32_t)q, 8u);
-            av[ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb, mk);
-          } else {
-            av[ks] = bytes_to_bf16_il(buf.a[s][ks][i], buf.a[s][ks][V + i]);
-          }
-        }
-        float sc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = V * r + i;
-          sc[r] = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
-        }
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          f32x4 dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[0]), bfr[tb][0], dx[tb], 0,
-                                                             0, 0);
-          dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[1]), bfr[tb][1], dp, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[s][i][tb][r] = __builtin_fmaf(sc[r], dp[r], acc[s][i][tb][r]);
-        }
-      }
+    tile_group<BITS, SBF16, NSETS>(buf, bfr, mk, q, acc);
   };
 
   // NB groups in flight; every wave walks every group (the barrier inside
