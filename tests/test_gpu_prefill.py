@@ -100,6 +100,21 @@ def test_shared_x_kernel_swiglu(ngq, orc, forced_sx, bits, sbf16, T, K, N_ff):
     check_swiglu(host_bits(h), h64, g, u, f"sx swiglu b{bits} T{T}")
 
 
+@pytest.mark.parametrize("T,N", [(700, 1000), (1090, 520)])
+def test_shared_x_bands_with_partial_last_band(ngq, orc, forced_sx, T, N):
+    """Token tiles walked in bands of 4: 11 and 18 token tiles leave a last
+    band of 3 and 2, next to a partial last column tile."""
+    _, (codes, scales, x) = make(4, False, T, 256, N, seed=T + N)
+    run_and_compare(ngq, orc, 4, False, codes, scales, x, what=f"sx bands T{T} N{N}")
+
+
+def test_maximum_token_count(ngq, orc):
+    """T = NGQ_MAX_T_PREFILL, the largest T the call takes (256 token tiles)."""
+    T = ngq.NGQ_MAX_T_PREFILL
+    _, (codes, scales, x) = make(5, True, T, 192, 36, seed=11)
+    run_and_compare(ngq, orc, 5, True, codes, scales, x, what=f"max T{T}")
+
+
 _FULL = {}
 
 
