@@ -117,6 +117,28 @@ def time_steps(launch, replicas, steps, warmup):
     return ms
 
 
+def clocks_under_load(launch, ms_per_launch):
+    """GPU clocks as rocm-smi reads them while about 1.5 s of streaming-read
+    launches are queued (read only, nothing set); None where rocm-smi is not
+    available.  A child process, started after the launches are enqueued."""
+    import re
+    import subprocess
+
+    import torch
+
+    n = max(1, int(1500 / max(ms_per_launch, 1e-3)))
+    for _ in range(n):
+        launch()
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(r.stdout[r.stdout.index("{"):]).values()))
+        mhz = {k.split()[0]: int(re.search(r"(\d+)", v).group(1)) for k, v in card.items() if "speed" in k}
+    except Exception:  # no rocm-smi, or an output this parser does not know
+        mhz = None
+    torch.cuda.synchronize()
+    return None if not mhz else {f"{k}_MHz": v for k, v in mhz.items()}
+
+
 def calibrate(ngq):
     """Attainable HBM read rate (own streaming-read kernel) and a torch copy of
     known size (the reference point for the traffic counters)."""
@@ -128,6 +150,7 @@ def calibrate(ngq):
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
     ms = time_steps(lambda i: ngq.ngq_stream_read(buf, sink), 1, 10, 3)
     out["stream_read_GBps"] = nbytes / ms / 1e6
+    out["clocks_under_load"] = clocks_under_load(lambda: ngq.ngq_stream_read(buf, sink), ms)
     del buf
     cb = 1 << 30
     src = torch.zeros(cb, dtype=torch.uint8, device="cuda")
