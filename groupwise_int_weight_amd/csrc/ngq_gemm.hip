@@ -1283,7 +1283,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // ---- many tokens: several requests verified together, 8 < T <= 64 -----------
 //
 // Requests verified together (T = requests x (drafts + 1), up to 64) still
-// stream every weight once.  The tokens run in blocks of 16 as the B
+// stream every weight once.  By default this kernel serves 8 < T <= 32; from
+// 33 tokens the token x column kernels below are faster (it still serves up
+// to 64 when forced).  The tokens run in blocks of 16 as the B
 // operand's 16 columns (no slot sharing), so each MFMA step covers 32 k of
 // one group: step st of a pair reads k-blocks 4 st .. 4 st + 3 (group st / 2),
 // k-slot q of a lane taking k-block 4 st + q.  X is too large for LDS (640 KB
@@ -2209,7 +2211,7 @@ hipError_t launch_wide(const Format& f, int v, int tb, const dev::WideArgs& a, u
                       : launch_wide_b<8, false, NSETS>(v, tb, a, lds, st);
 }
 
-// 8 < T <= 64, arguments already checked: one workgroup per tile of 32
+// 8 < T <= 64 (by default up to 32), arguments already checked: one workgroup per tile of 32
 // columns, or 48 where that gives one tile per CU (plain projections at
 // T <= 32, whose registers allow it); 16 (T <= 16), 32 or 64 token rows per
 // workgroup.
