@@ -58,3 +58,15 @@ def test_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
     d["kernel_sha"] = "0" * 16
     f.write_text(json.dumps(d))
     assert bench.traffic_for("qk", 8) is None
+
+
+def test_kernel_hash_ignores_comments_only(tmp_path, monkeypatch):
+    code = "int f(int a) {\n  return a + 1;  // one more\n}\n"
+    src = tmp_path / "k.hip"
+    src.write_text(code)
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    h = bench.kernel_sha()
+    src.write_text("/* a block\n   comment */\n" + code.replace("// one more", "// a different note") + "\n\n")
+    assert bench.kernel_sha() == h
+    src.write_text(code.replace("a + 1", "a + 2"))
+    assert bench.kernel_sha() != h
