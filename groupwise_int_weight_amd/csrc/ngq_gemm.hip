@@ -1817,22 +1817,82 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
 constexpr int kSxCols = 4 * kTiledCols;            // weight columns per workgroup
 constexpr int kSxBand = 4;                         // token tiles per band of the tile order
 constexpr uint32_t kSxRow = 2u * 64u + 16u;        // LDS bytes per token row of an X tile (padded)
-constexpr uint32_t kSxBuf = (uint32_t)kTiledTok * kSxRow;
+// LDS bytes of one group's X tile of 16 TB token rows
+__host__ __device__ constexpr uint32_t sx_buf_bytes(int tb) { return 16u * (uint32_t)tb * kSxRow; }
 
-__host__ __device__ constexpr uint32_t tiled_sx_lds_bytes() { return 2u * kSxBuf; }
+__host__ __device__ constexpr uint32_t tiled_sx_lds_bytes(int tb) { return 2u * sx_buf_bytes(tb); }
 
-template <int BITS, int NSETS>
+template <int BITS, int NSETS, int TB>
 struct SxBuf {
   static constexpr int V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
   uint32_t a[NSETS][2][V * WPK];             // as TiledBuf
   uint32_t p1[NSETS][2][BITS == 5 ? V : 1];
   uint32_t sc[NSETS][2 * V];
-  uint32_t x[2][4];                          // this thread's two 16-byte chunks of the X tile
+  uint32_t x[TB / 2][4];                     // this thread's 16-byte chunks of the X tile
 };
 
-template <int BITS, bool SBF16, int NSETS, int NB>
-__global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledArgs a) {
+// tile_group with the token blocks outermost, for the 96- and 128-token
+// tiles: the A fragments and scales of all columns first, then per token
+// block its B fragments (read by `rb`), its offset chain and its MFMAs, so
+// that one block's B fragments live at a time and the kernel keeps two waves
+// per SIMD.  The same arithmetic in the same order per output as tile_group.
+template <int BITS, bool SBF16, int NSETS, int TB, class Buf, class ReadB>
+__device__ __forceinline__ void tile_group_tbo(const Buf& buf, ReadB&& rb, const UnpackMasks& mk, int q,
+                                               f32x4 (&acc)[NSETS][4 / NSETS][TB]) {
   constexpr int V = 4 / NSETS;
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+  u32x4 av[NSETS][V][2];
+  float sc[NSETS][V][4];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (BITS == 4) {
+          av[s][i][ks] = nibbles_to_bf16_il(buf.a[s][ks][i], mk);
+        } else if constexpr (BITS == 5) {
+          // k-block 4 ks + q is byte q of the step's 32-k high-bit word
+          const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][ks][i], 8u * (uint32_t)q, 8u);
+          av[s][i][ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb, mk);
+        } else {
+          av[s][i][ks] = bytes_to_bf16_il(buf.a[s][ks][i], buf.a[s][ks][V + i]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = V * r + i;
+        sc[s][i][r] = scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16);
+      }
+    }
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    bf16x8 b[2];
+    rb(b, tb);
+    f32x4 dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), b[0],
+                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), b[1], dx, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        f32x4 dp =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s][i][0]), b[0], dx, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[s][i][1]), b[1], dp, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[s][i][tb][r] = __builtin_fmaf(sc[s][i][r], dp[r], acc[s][i][tb][r]);
+      }
+  }
+}
+
+// TB token blocks of 16 per tile (64, 96 or 128 tokens): more tokens reuse
+// each unpacked weight word for more MFMAs; which size fills the CUs best
+// depends on the shape (chosen on the host).
+template <int BITS, bool SBF16, int NSETS, int NB, int TB>
+__global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledArgs a) {
+  constexpr int V = 4 / NSETS, XC = TB / 2;  // X chunks per thread and group
+  constexpr uint32_t XBUF = sx_buf_bytes(TB);
   constexpr int OCOLS = kSxCols / NSETS;  // output columns per workgroup
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
@@ -1848,7 +1908,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
   const int tiles_t = a.tiles / a.tiles_n, band = tile / (kSxBand * a.tiles_n);
   const int in_band = tile - band * (kSxBand * a.tiles_n), bt = min(kSxBand, tiles_t - band * kSxBand);
   const int tt = band * kSxBand + in_band % bt, tn = in_band / bt;
-  const int t0 = tt * kTiledTok;
+  const int t0 = tt * 16 * TB;
   const int c0 = tn * OCOLS + wave * (OCOLS / kTiledWaves);  // this wave's first output column
 
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
@@ -1860,9 +1920,9 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
   const TileWeights<BITS, NSETS> tw(a, c0, m, q);
   // X tile chunks of this thread: chunk j = tid + 256 u is token row j / 8,
   // 16-byte k chunk j % 8 of the group
-  uint32_t offX[2], ldsX[2];
+  uint32_t offX[XC], ldsX[XC];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < XC; ++u) {
     const int j = (int)threadIdx.x + 256 * u, row = j >> 3, kc = j & 7, t = t0 + row;
     offX[u] = t < a.T ? (uint32_t)t * (uint32_t)a.K * 2u + (uint32_t)kc * 16u : kOOB;
     ldsX[u] = (uint32_t)row * kSxRow + (uint32_t)kc * 16u;
@@ -1870,40 +1930,46 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
   // B fragment of token block tb, step ks: row 16 tb + m, k chunk 4 ks + q
   const uint32_t ldsB = (uint32_t)m * kSxRow + (uint32_t)q * 16u;
 
-  auto issue = [&](SxBuf<BITS, NSETS>& buf, int g) {
+  auto issue = [&](SxBuf<BITS, NSETS, TB>& buf, int g) {
     const bool valid = g < a.G;
     tw.issue(buf, g, valid);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) load_words<4>(&buf.x[u][0], rX, valid ? offX[u] + (uint32_t)g * 128u : kOOB);
+    for (int u = 0; u < XC; ++u) load_words<4>(&buf.x[u][0], rX, valid ? offX[u] + (uint32_t)g * 128u : kOOB);
   };
 
-  f32x4 acc[NSETS][V][4];
+  f32x4 acc[NSETS][V][TB];
 #pragma unroll
   for (int s = 0; s < NSETS; ++s)
 #pragma unroll
     for (int i = 0; i < V; ++i)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) acc[s][i][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tb = 0; tb < TB; ++tb) acc[s][i][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // group g: its X chunks into LDS buffer g % 2, barrier, then the wave's MFMAs
-  auto compute = [&](const SxBuf<BITS, NSETS>& buf, int g) {
-    uint8_t* const xb = smem + (uint32_t)(g & 1) * kSxBuf;
+  auto compute = [&](const SxBuf<BITS, NSETS, TB>& buf, int g) {
+    uint8_t* const xb = smem + (uint32_t)(g & 1) * XBUF;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(xb + ldsX[u]) = interleave_x(buf.x[u]);
+    for (int u = 0; u < XC; ++u) *reinterpret_cast<u32x4*>(xb + ldsX[u]) = interleave_x(buf.x[u]);
     lds_barrier();
-    bf16x8 bfr[4][2];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    auto read_b = [&](bf16x8 (&b)[2], int tb) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        bfr[tb][ks] = __builtin_bit_cast(
+        b[ks] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(xb + ldsB + (uint32_t)tb * 16u * kSxRow + (uint32_t)ks * 64u));
-    tile_group<BITS, SBF16, NSETS>(buf, bfr, mk, q, acc);
+    };
+    if constexpr (TB == 4) {
+      bf16x8 bfr[4][2];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) read_b(bfr[tb], tb);
+      tile_group<BITS, SBF16, NSETS>(buf, bfr, mk, q, acc);
+    } else {
+      tile_group_tbo<BITS, SBF16, NSETS, TB>(buf, read_b, mk, q, acc);
+    }
   };
 
   // NB groups in flight; every wave walks every group (the barrier inside
   // compute is reached the same number of times by all waves)
-  SxBuf<BITS, NSETS> buf[NB];
+  SxBuf<BITS, NSETS, TB> buf[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     issue(buf[u], u);
@@ -1923,7 +1989,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_sx_kernel(TiledAr
   // c0 + V (4q + r) .. per (tb, r)
   uint16_t* const y = static_cast<uint16_t*>(a.y);
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+  for (int tb = 0; tb < TB; ++tb) {
     const int t = t0 + 16 * tb + m;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -2247,24 +2313,52 @@ hipError_t launch_tiled_b(const dev::TiledArgs& a, uint32_t lds, hipStream_t st)
   return hipGetLastError();
 }
 
+// 96- and 128-token tiles for int4 only: the int5 and int8 variants need
+// more than 256 VGPRs there (one wave per SIMD).
 template <int BITS, bool SBF16, int NSETS>
-hipError_t launch_tiled_sx_b(const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((dev::gemm_tiled_sx_kernel<BITS, SBF16, NSETS, kSxNB>), dim3((unsigned)a.tiles),
-                     dim3(dev::kTiledWaves * 64), lds, st, a);
-  return hipGetLastError();
+hipError_t launch_tiled_sx_b(int tb, const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
+  auto one = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.tiles), dim3(dev::kTiledWaves * 64), lds, st, a);
+    return hipGetLastError();
+  };
+  if constexpr (BITS == 4) {
+    if (tb == 8) return one(dev::gemm_tiled_sx_kernel<BITS, SBF16, NSETS, kSxNB, 8>);
+    if (tb == 6) return one(dev::gemm_tiled_sx_kernel<BITS, SBF16, NSETS, kSxNB, 6>);
+  }
+  return one(dev::gemm_tiled_sx_kernel<BITS, SBF16, NSETS, kSxNB, 4>);
+}
+
+// Token tile of the shared-X kernel (token blocks of 16): the one whose tile
+// count best fills rounds of two workgroups per CU, the larger on a tie
+// (measured: QK T = 2048 runs 128-token tiles 8 % faster, down T = 2048
+// 96-token tiles 13 % faster, QK T = 1024 and int8 64-token tiles).
+int sx_token_blocks(int bits, long sx_cols, int T, int cus) {
+  if (bits != 4) return 4;
+  int best = 4;
+  double best_eff = -1.0;
+  for (int tb : {8, 6, 4}) {
+    const long tiles = sx_cols * ((T + 16L * tb - 1) / (16L * tb));
+    const long slots = 2L * cus;
+    const double eff = (double)tiles / (double)(((tiles + slots - 1) / slots) * slots);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = tb;
+    }
+  }
+  return best;
 }
 
 template <int NSETS, bool SX>
-hipError_t launch_tiled(const Format& f, const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
+hipError_t launch_tiled(const Format& f, int tb, const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
   if constexpr (SX) {
     if (f.bits == 4)
-      return f.scale_bf16 ? launch_tiled_sx_b<4, true, NSETS>(a, lds, st)
-                          : launch_tiled_sx_b<4, false, NSETS>(a, lds, st);
+      return f.scale_bf16 ? launch_tiled_sx_b<4, true, NSETS>(tb, a, lds, st)
+                          : launch_tiled_sx_b<4, false, NSETS>(tb, a, lds, st);
     if (f.bits == 5)
-      return f.scale_bf16 ? launch_tiled_sx_b<5, true, NSETS>(a, lds, st)
-                          : launch_tiled_sx_b<5, false, NSETS>(a, lds, st);
-    return f.scale_bf16 ? launch_tiled_sx_b<8, true, NSETS>(a, lds, st)
-                        : launch_tiled_sx_b<8, false, NSETS>(a, lds, st);
+      return f.scale_bf16 ? launch_tiled_sx_b<5, true, NSETS>(tb, a, lds, st)
+                          : launch_tiled_sx_b<5, false, NSETS>(tb, a, lds, st);
+    return f.scale_bf16 ? launch_tiled_sx_b<8, true, NSETS>(tb, a, lds, st)
+                        : launch_tiled_sx_b<8, false, NSETS>(tb, a, lds, st);
   } else {
     if (f.bits == 4)
       return f.scale_bf16 ? launch_tiled_b<4, true, NSETS>(a, lds, st) : launch_tiled_b<4, false, NSETS>(a, lds, st);
@@ -2276,9 +2370,10 @@ hipError_t launch_tiled(const Format& f, const dev::TiledArgs& a, uint32_t lds, 
 
 // Token x column tiles (prefill-size T; any T >= 1 when forced), arguments
 // already checked: 64 tokens by 64 weight columns per workgroup with K split
-// over its waves, or (sx) 64 tokens by 256 weight columns sharing each X tile,
-// which needs 4x as many tokens to fill the CUs.  `path` is NGQ_KERNEL_TILED
-// or NGQ_KERNEL_TILED_SX to force either, anything else to choose.
+// over its waves, or (sx) 64, 96 or 128 tokens by 256 weight columns sharing
+// each X tile, which needs 4x as many tokens to fill the CUs.  `path` is
+// NGQ_KERNEL_TILED or NGQ_KERNEL_TILED_SX (64 tokens), _SX96 or _SX128 (int4)
+// to force one, anything else to choose.
 int run_tiled(int path, int nsets, int T, int K, int Nout, int Ncols, const Format& f, const void* x,
               const void* wq, const void* scales, void* y, size_t wb0, size_t wb1, size_t sb, size_t xb,
               void* stream) {
@@ -2286,10 +2381,17 @@ int run_tiled(int path, int nsets, int T, int K, int Nout, int Ncols, const Form
   a.x = x; a.wq = wq; a.scales = scales; a.y = y;
   a.T = T; a.K = K; a.Nout = Nout; a.Ncols = Ncols; a.up_off = nsets == 2 ? Nout : 0;
   a.G = K / kGroup;
-  const long ttiles = (T + dev::kTiledTok - 1) / dev::kTiledTok;
-  const long sx_tiles = (Nout + dev::kSxCols / nsets - 1) / (dev::kSxCols / nsets) * ttiles;
-  const bool sx = path == NGQ_KERNEL_TILED_SX ||
+  const long sx_cols = (Nout + dev::kSxCols / nsets - 1) / (dev::kSxCols / nsets);
+  const long sx_tiles = sx_cols * ((T + dev::kTiledTok - 1) / dev::kTiledTok);
+  if ((path == NGQ_KERNEL_TILED_SX96 || path == NGQ_KERNEL_TILED_SX128) && f.bits != 4) return NGQ_ERR_UNSUPPORTED;
+  const bool sx = path == NGQ_KERNEL_TILED_SX || path == NGQ_KERNEL_TILED_SX96 || path == NGQ_KERNEL_TILED_SX128 ||
                   (path != NGQ_KERNEL_TILED && 10 * sx_tiles >= (long)kSxMinTiles10PerCu * cu_count());
+  const int tb = !sx                                 ? 4
+                 : path == NGQ_KERNEL_TILED_SX       ? 4
+                 : path == NGQ_KERNEL_TILED_SX96     ? 6
+                 : path == NGQ_KERNEL_TILED_SX128    ? 8
+                                                     : sx_token_blocks(f.bits, sx_cols, T, cu_count());
+  const long ttiles = (T + 16L * tb - 1) / (16L * tb);
   const int ocols = (sx ? dev::kSxCols : dev::kTiledCols) / nsets;
   a.tiles_n = (Nout + ocols - 1) / ocols;
   const long tiles = (long)a.tiles_n * ttiles;
@@ -2299,13 +2401,13 @@ int run_tiled(int path, int nsets, int T, int K, int Nout, int Ncols, const Form
   a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
   hipError_t e;
   if (sx) {
-    const uint32_t lds = dev::tiled_sx_lds_bytes();
-    e = nsets == 1 ? launch_tiled<1, true>(f, a, lds, (hipStream_t)stream)
-                   : launch_tiled<2, true>(f, a, lds, (hipStream_t)stream);
+    const uint32_t lds = dev::tiled_sx_lds_bytes(tb);
+    e = nsets == 1 ? launch_tiled<1, true>(f, tb, a, lds, (hipStream_t)stream)
+                   : launch_tiled<2, true>(f, tb, a, lds, (hipStream_t)stream);
   } else {
     const uint32_t lds = dev::tiled_lds_bytes();
-    e = nsets == 1 ? launch_tiled<1, false>(f, a, lds, (hipStream_t)stream)
-                   : launch_tiled<2, false>(f, a, lds, (hipStream_t)stream);
+    e = nsets == 1 ? launch_tiled<1, false>(f, tb, a, lds, (hipStream_t)stream)
+                   : launch_tiled<2, false>(f, tb, a, lds, (hipStream_t)stream);
   }
   return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
@@ -2334,7 +2436,8 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     return NGQ_ERR_UNSUPPORTED;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, wq, wb0 + wb1) || overlaps(y, yb, scales, sb)) return NGQ_ERR_ARG;
   const int forced = kernel_override.load(std::memory_order_relaxed);
-  if (forced == NGQ_KERNEL_TILED || forced == NGQ_KERNEL_TILED_SX)
+  if (forced == NGQ_KERNEL_TILED || forced == NGQ_KERNEL_TILED_SX || forced == NGQ_KERNEL_TILED_SX96 ||
+      forced == NGQ_KERNEL_TILED_SX128)
     return run_tiled(forced, nsets, T, K, Nout, Ncols, f, x, wq, scales, y, wb0, wb1, sb, xb, stream);
   if (forced == NGQ_KERNEL_WIDE && (T <= NGQ_MAX_T || T > NGQ_MAX_T_VERIFY)) return NGQ_ERR_UNSUPPORTED;
   if (T > NGQ_MAX_T) {
@@ -2834,6 +2937,6 @@ extern "C" int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* 
 }
 
 extern "C" int ngq_debug_force_kernel(int path) {
-  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_TILED_SX) return NGQ_ERR_ARG;
+  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_TILED_SX128) return NGQ_ERR_ARG;
   return kernel_override.exchange(path);
 }

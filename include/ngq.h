@@ -218,8 +218,8 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
  * later call in the process (tests use it to run each path on the same
  * shapes).  NGQ_KERNEL_AUTO restores the per-shape choice.  Paths 1..4 are
  * the T <= 8 kernels (larger T keeps the library's choice under them);
- * NGQ_KERNEL_WIDE serves 8 < T <= 64; the two token x column paths serve any
- * T.  A forced path that cannot serve a shape (X or the partial sums do not
+ * NGQ_KERNEL_WIDE serves 8 < T <= 64; the token x column paths serve any T
+ * (the 96- and 128-token ones int4 only).  A forced path that cannot serve a shape (X or the partial sums do not
  * fit in LDS, the 14-wave kernel with the SwiGLU epilogue, NGQ_KERNEL_WIDE
  * outside its T range) makes those calls return NGQ_ERR_UNSUPPORTED.
  * Returns the previous setting, or NGQ_ERR_ARG for an unknown path.  Not
@@ -232,6 +232,8 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
 #define NGQ_KERNEL_WIDE 5           /* 8 < T <= 64: token blocks of 16, X per pair */
 #define NGQ_KERNEL_TILED 6          /* token x column tiles (prefill), K split over waves, any T */
 #define NGQ_KERNEL_TILED_SX 7       /* token x column tiles, X tile shared by the waves, any T */
+#define NGQ_KERNEL_TILED_SX96 8     /* the same with 96-token tiles (int4 only) */
+#define NGQ_KERNEL_TILED_SX128 9    /* the same with 128-token tiles (int4 only) */
 int ngq_debug_force_kernel(int path);
 
 /* Bandwidth calibration: stream `bytes` (a multiple of 16) from device memory

@@ -89,6 +89,51 @@ def test_shared_x_kernel_small(ngq, orc, forced_sx, bits, sbf16, T, K, N):
     run_and_compare(ngq, orc, bits, sbf16, codes, scales, x, what=f"sx forced b{bits} T{T} K{K} N{N}")
 
 
+INT4_SHAPES = [(sbf16, T, K, N) for bits, sbf16, T, K, N in SMALL if bits == 4] + \
+    [(False, 1, 320, 1000), (True, 97, 576, 264), (False, 250, 1088, 516), (True, 129, 64, 4)]
+
+
+@pytest.mark.parametrize("path_name", ["NGQ_KERNEL_TILED_SX96", "NGQ_KERNEL_TILED_SX128"])
+@pytest.mark.parametrize("sbf16,T,K,N", INT4_SHAPES)
+def test_shared_x_larger_token_tiles(ngq, orc, path_name, sbf16, T, K, N):
+    """The shared-X kernel with 96- and 128-token tiles (int4), forced, on
+    ragged shapes: token tails past a tile, column tails, odd group counts."""
+    _, (codes, scales, x) = make(4, sbf16, T, K, N, seed=T * 5 + K + N)
+    prev = ngq.ngq_debug_force_kernel(getattr(ngq, path_name))
+    try:
+        run_and_compare(ngq, orc, 4, sbf16, codes, scales, x, what=f"{path_name} T{T} K{K} N{N}")
+    finally:
+        ngq.ngq_debug_force_kernel(prev)
+
+
+@pytest.mark.parametrize("path_name", ["NGQ_KERNEL_TILED_SX96", "NGQ_KERNEL_TILED_SX128"])
+def test_shared_x_larger_token_tiles_swiglu(ngq, orc, path_name):
+    T, K, N_ff = 200, 512, 100
+    _, (codes, scales, x) = make(4, False, T, K, 2 * N_ff, seed=41)
+    prev = ngq.ngq_debug_force_kernel(getattr(ngq, path_name))
+    try:
+        h = ngq.ngq_swiglu_gemm(dev_bf16(x), dev_u8(ngq.ngq_pack(codes, 4)), dev_scales(scales, False), 4, N_ff)
+    finally:
+        ngq.ngq_debug_force_kernel(prev)
+    cols = np.arange(N_ff, dtype=np.int32)
+    h64, g, u = swiglu_reference(orc, x, orc.pack(codes, 4), scales, K, N_ff, 4, False, cols)
+    check_swiglu(host_bits(h), h64, g, u, f"{path_name} swiglu")
+
+
+def test_larger_token_tiles_refuse_int5(ngq):
+    x = torch.zeros((128, 64), dtype=torch.bfloat16, device="cuda")
+    wq = torch.zeros(ngq.ngq_packed_bytes(64, 8, 5), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((1, 8), dtype=torch.float16, device="cuda")
+    y = torch.zeros((128, 8), dtype=torch.bfloat16, device="cuda")
+    prev = ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_TILED_SX128)
+    try:
+        st = ngq.lib().ngq_gemm(128, 64, 8, 5, 64, x.data_ptr(), wq.data_ptr(), sc.data_ptr(), y.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+    finally:
+        ngq.ngq_debug_force_kernel(prev)
+    assert st == ngq.NGQ_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("bits,sbf16,T,K,N_ff", [(4, False, 65, 512, 100), (5, True, 130, 320, 36),
                                                   (8, False, 70, 256, 200)])
 def test_shared_x_kernel_swiglu(ngq, orc, forced_sx, bits, sbf16, T, K, N_ff):
@@ -127,8 +172,10 @@ def full_inputs(name, T):
     return _FULL[key]
 
 
-# qk at T = 1024 runs the shared-X variant, the others the K-split one
-@pytest.mark.parametrize("name,T", [("qk", 1024), ("gv", 256), ("qk8", 130), ("down", 256)])
+# qk at T = 1024 runs the shared-X variant with 64-token tiles, qk at 2048
+# with 128, down at 2048 with 96, the others the K-split one
+@pytest.mark.parametrize("name,T", [("qk", 1024), ("gv", 256), ("qk8", 130), ("down", 256), ("qk", 2048),
+                                    ("down", 2048)])
 def test_prefill_full_size(ngq, orc, name, T):
     w, codes, scales, x = full_inputs(name, T)
     cols = sample_cols(w.N, seed=T + 11, n_random=96)
