@@ -1537,7 +1537,10 @@ __global__ __launch_bounds__(kWideWaves * 64) void gemm_wide_kernel(WideArgs a) 
 // with 4 token blocks of 16: 32 MFMAs plus 8 for the -(128 + bias) sum_k x
 // term, then acc += s * partial per group.  Weights, scales and X go from
 // memory straight into registers, NB groups ahead.  The 4 wave sums meet in
-// LDS and are added in wave order (deterministic, no atomics).
+// LDS and are added in wave order (deterministic, no atomics).  Where 64
+// columns per tile leave CUs idle (tens of tokens, or few columns) a plain
+// projection's tiles narrow to 32 or 16 columns (V = 2 or 1 per lane): less
+// unpack and MFMA work per group and wave, more workgroups.
 
 constexpr int kTiledWaves = 4;
 constexpr int kTiledTok = 64;   // tokens per tile: 4 MFMA token blocks
@@ -1554,26 +1557,30 @@ struct TiledArgs {
 };
 
 // LDS of the wave-sum exchange: per wave 64 values per lane
-__host__ __device__ constexpr uint32_t tiled_lds_bytes() { return (uint32_t)kTiledWaves * 64u * 64u * 4u; }
+// (e accumulators per lane: 16 NSETS V, at most 64)
+__host__ __device__ constexpr uint32_t tiled_lds_bytes(int e) {
+  return (uint32_t)kTiledWaves * (uint32_t)e * 64u * 4u;
+}
 
-template <int BITS, int NSETS>
+template <int BITS, int NSETS, int V_ = 4 / NSETS>
 struct TiledBuf {
-  static constexpr int V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
+  static constexpr int V = V_, WPK = BITS == 8 ? 2 : 1;
   uint32_t a[NSETS][2][V * WPK];             // [set][32-k step][word]; int8: row 2kb words, then 2kb+1
   uint32_t p1[NSETS][2][BITS == 5 ? V : 1];  // int5: the step's 32-k high-bit word
   uint32_t sc[NSETS][2 * V];                 // 4V 16-bit scales per set
   uint32_t x[4][2][4];                       // [token block][step][dword]
 };
 
-// The weight side of a wave's 64 columns in the token x column kernels:
+// The weight side of a wave's 16 V NSETS columns (64 unless the K-split
+// kernel narrows its tiles) in the token x column kernels:
 // lane (m, q) loads, per set s and 32-k step, V adjacent P0 words of columns
 // c0 + s up_off + V m .. at 8-k block 8 g + 4 ks + q (two rows for int8),
 // the int5 high-bit words of the same columns, and the 4V scales of columns
 // c0 + s up_off + 4 V q ...  Columns past the matrix read the next row or
 // nothing: only their own (discarded) outputs see them.
-template <int BITS, int NSETS>
+template <int BITS, int NSETS, int V_ = 4 / NSETS>
 struct TileWeights {
-  static constexpr int V = 4 / NSETS, WPK = BITS == 8 ? 2 : 1;
+  static constexpr int V = V_, WPK = BITS == 8 ? 2 : 1;
   __amdgpu_buffer_rsrc_t rW, rP1, rS;
   uint32_t rowb, srow, offA[NSETS], offP1[NSETS], offS[NSETS];
 
@@ -1623,10 +1630,9 @@ struct TileWeights {
 // fragments `bfr`, each group's partial scaled into acc.  Lane (m, q): A row
 // m = weight column V m + i of set s, k-slot q.  `buf` holds the group's
 // P0 words, int5 high-bit words and scales (TiledBuf or SxBuf).
-template <int BITS, bool SBF16, int NSETS, class Buf>
+template <int BITS, bool SBF16, int NSETS, int V, class Buf>
 __device__ __forceinline__ void tile_group(const Buf& buf, const bf16x8 (&bfr)[4][2], const UnpackMasks& mk, int q,
-                                           f32x4 (&acc)[NSETS][4 / NSETS][4]) {
-  constexpr int V = 4 / NSETS;
+                                           f32x4 (&acc)[NSETS][V][4]) {
   const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
                         Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
   f32x4 dx[4];
@@ -1670,11 +1676,12 @@ __device__ __forceinline__ void tile_group(const Buf& buf, const bf16x8 (&bfr)[4
     }
 }
 
-template <int BITS, bool SBF16, int NSETS, int NB>
+template <int BITS, bool SBF16, int NSETS, int NB, int V>
 __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs a) {
-  constexpr int W = kTiledWaves, V = 4 / NSETS;
-  constexpr int OCOLS = kTiledCols / NSETS;  // output columns per tile
-  constexpr int E = NSETS * V * 16;           // accumulators per lane (64)
+  static_assert(NSETS == 2 ? V == 2 : V == 4 || V == 2 || V == 1, "column tile");
+  constexpr int W = kTiledWaves;
+  constexpr int OCOLS = 16 * V;     // output columns per tile
+  constexpr int E = NSETS * V * 16;  // accumulators per lane (16-64)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* const part = reinterpret_cast<float*>(smem);
   const int lane = threadIdx.x & 63;
@@ -1697,7 +1704,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
   // A block (weight column c0 + s up_off + V m + i) at the 8 k of slot q, and
   // token 16 tb + m of the B block; its results are rows 4q + r (weight
   // columns c0 + s up_off + V (4q + r) + i) for token 16 tb + m.
-  const TileWeights<BITS, NSETS> tw(a, c0, m, q);
+  const TileWeights<BITS, NSETS, V> tw(a, c0, m, q);
   uint32_t offX[4];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
@@ -1706,7 +1713,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
   }
 
   // loads of group g (g >= G loads nothing)
-  auto issue = [&](TiledBuf<BITS, NSETS>& buf, int g) {
+  auto issue = [&](TiledBuf<BITS, NSETS, V>& buf, int g) {
     const bool valid = g < a.G;
     tw.issue(buf, g, valid);
 #pragma unroll
@@ -1724,7 +1731,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[s][i][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const TiledBuf<BITS, NSETS>& buf) {
+  auto compute = [&](const TiledBuf<BITS, NSETS, V>& buf) {
     bf16x8 bfr[4][2];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -1736,7 +1743,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
   // NB groups in flight per wave; loads are issued without a branch (a group
   // past the end loads nothing), and the scheduling barriers keep the groups'
   // loads in issue order, so each compute waits for exactly its own group
-  TiledBuf<BITS, NSETS> buf[NB];
+  TiledBuf<BITS, NSETS, V> buf[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     issue(buf[u], wave + W * u);
@@ -1767,7 +1774,8 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
         }
   __syncthreads();
   // wave w finishes token block w: the four wave sums in wave order, then
-  // SwiGLU or plain, V consecutive output columns per store
+  // SwiGLU or plain, V consecutive output columns per store (V even, or a
+  // single column: N % 4 == 0 keeps every store aligned and inside its row)
   const int tb = wave, t = t0 + 16 * tb + m;
   uint16_t* const y = static_cast<uint16_t*>(a.y);
 #pragma unroll
@@ -1785,24 +1793,28 @@ __global__ __launch_bounds__(kTiledWaves * 64) void gemm_tiled_kernel(TiledArgs 
         for (int w = 0; w < W; ++w) sum += part[((uint32_t)w * E + (uint32_t)e) * 64u + (uint32_t)lane];
         v[s][i] = sum;
       }
-    uint32_t pk[V / 2];
+    uint16_t* const dst = y + (size_t)t * a.Nout + col;
+    if constexpr (V == 1) {  // plain projections only
+      *dst = f32_to_bf16_rne(v[0][0]);
+    } else {
+      uint32_t pk[V / 2];
 #pragma unroll
-    for (int i = 0; i < V; i += 2) {
-      float o0, o1;
-      if constexpr (NSETS == 2) {
-        o0 = v[0][i] * v[1][i] / (1.0f + expf(-v[0][i]));  // SiLU(gate) * up
-        o1 = v[0][i + 1] * v[1][i + 1] / (1.0f + expf(-v[0][i + 1]));
-      } else {
-        o0 = v[0][i];
-        o1 = v[0][i + 1];
+      for (int i = 0; i < V; i += 2) {
+        float o0, o1;
+        if constexpr (NSETS == 2) {
+          o0 = v[0][i] * v[1][i] / (1.0f + expf(-v[0][i]));  // SiLU(gate) * up
+          o1 = v[0][i + 1] * v[1][i + 1] / (1.0f + expf(-v[0][i + 1]));
+        } else {
+          o0 = v[0][i];
+          o1 = v[0][i + 1];
+        }
+        pk[i / 2] = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
       }
-      pk[i / 2] = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+      if constexpr (V == 4)
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+      else
+        *reinterpret_cast<uint32_t*>(dst) = pk[0];
     }
-    uint16_t* dst = y + (size_t)t * a.Nout + col;
-    if constexpr (V == 4)
-      *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
-    else
-      *reinterpret_cast<uint32_t*>(dst) = pk[0];
   }
 }
 
@@ -2156,6 +2168,10 @@ constexpr XCfg kX14 = {14, 1, 6}, kX8a = {8, 2, 10}, kX8b = {8, 2, 18};
 // Token x column tiles: groups in flight per wave, and the smallest T routed
 // to them rather than to the 8 < T <= 64 kernel.
 constexpr int kTiledNB = 2, kSxNB = 2;  // 3 in flight measured 2-4 % slower for the shared-X kernel
+// The K-split kernel's plain tiles narrow from 64 to 32 and 16 columns (V =
+// 4, 2, 1) while the wider tiles would leave CUs without a workgroup and
+// the narrower ones fit one round; this is the narrowest allowed.
+constexpr int kTiledMinV = 1;
 // shared-X tiles once there are at least 0.6 per CU (measured crossover:
 // QK at T = 256, 0.5 per CU, is faster K-split; down at T = 512, 0.63 per CU,
 // shared)
@@ -2300,17 +2316,17 @@ int run_wide(int nsets, int T, int K, int Nout, int Ncols, const Format& f, cons
 }
 
 template <int BITS, bool SBF16, int NSETS>
-hipError_t launch_tiled_b(const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
-  auto kern = dev::gemm_tiled_kernel<BITS, SBF16, NSETS, kTiledNB>;
-  static bool raised = false;
-  if (lds > 64u * 1024u && !raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-    if (e != hipSuccess) return e;
-    raised = true;
+hipError_t launch_tiled_b(int v, const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
+  // lds <= 64 KB (tiled_lds_bytes of at most 64 accumulators per lane)
+  auto one = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.tiles), dim3(dev::kTiledWaves * 64), lds, st, a);
+    return hipGetLastError();
+  };
+  if constexpr (NSETS == 1) {
+    if (v == 2) return one(dev::gemm_tiled_kernel<BITS, SBF16, 1, kTiledNB, 2>);
+    if (v == 1) return one(dev::gemm_tiled_kernel<BITS, SBF16, 1, kTiledNB, 1>);
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)a.tiles), dim3(dev::kTiledWaves * 64), lds, st, a);
-  return hipGetLastError();
+  return one(dev::gemm_tiled_kernel<BITS, SBF16, NSETS, kTiledNB, 4 / NSETS>);
 }
 
 // 96- and 128-token tiles for int4 only: the int5 and int8 variants need
@@ -2348,29 +2364,35 @@ int sx_token_blocks(int bits, long sx_cols, int T, int cus) {
   return best;
 }
 
+// sel: token blocks per tile (shared-X kernel) or columns per lane and set,
+// V (K-split kernel)
 template <int NSETS, bool SX>
-hipError_t launch_tiled(const Format& f, int tb, const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
+hipError_t launch_tiled(const Format& f, int sel, const dev::TiledArgs& a, uint32_t lds, hipStream_t st) {
   if constexpr (SX) {
     if (f.bits == 4)
-      return f.scale_bf16 ? launch_tiled_sx_b<4, true, NSETS>(tb, a, lds, st)
-                          : launch_tiled_sx_b<4, false, NSETS>(tb, a, lds, st);
+      return f.scale_bf16 ? launch_tiled_sx_b<4, true, NSETS>(sel, a, lds, st)
+                          : launch_tiled_sx_b<4, false, NSETS>(sel, a, lds, st);
     if (f.bits == 5)
-      return f.scale_bf16 ? launch_tiled_sx_b<5, true, NSETS>(tb, a, lds, st)
-                          : launch_tiled_sx_b<5, false, NSETS>(tb, a, lds, st);
-    return f.scale_bf16 ? launch_tiled_sx_b<8, true, NSETS>(tb, a, lds, st)
-                        : launch_tiled_sx_b<8, false, NSETS>(tb, a, lds, st);
+      return f.scale_bf16 ? launch_tiled_sx_b<5, true, NSETS>(sel, a, lds, st)
+                          : launch_tiled_sx_b<5, false, NSETS>(sel, a, lds, st);
+    return f.scale_bf16 ? launch_tiled_sx_b<8, true, NSETS>(sel, a, lds, st)
+                        : launch_tiled_sx_b<8, false, NSETS>(sel, a, lds, st);
   } else {
     if (f.bits == 4)
-      return f.scale_bf16 ? launch_tiled_b<4, true, NSETS>(a, lds, st) : launch_tiled_b<4, false, NSETS>(a, lds, st);
+      return f.scale_bf16 ? launch_tiled_b<4, true, NSETS>(sel, a, lds, st)
+                          : launch_tiled_b<4, false, NSETS>(sel, a, lds, st);
     if (f.bits == 5)
-      return f.scale_bf16 ? launch_tiled_b<5, true, NSETS>(a, lds, st) : launch_tiled_b<5, false, NSETS>(a, lds, st);
-    return f.scale_bf16 ? launch_tiled_b<8, true, NSETS>(a, lds, st) : launch_tiled_b<8, false, NSETS>(a, lds, st);
+      return f.scale_bf16 ? launch_tiled_b<5, true, NSETS>(sel, a, lds, st)
+                          : launch_tiled_b<5, false, NSETS>(sel, a, lds, st);
+    return f.scale_bf16 ? launch_tiled_b<8, true, NSETS>(sel, a, lds, st)
+                        : launch_tiled_b<8, false, NSETS>(sel, a, lds, st);
   }
 }
 
 // Token x column tiles (prefill-size T; any T >= 1 when forced), arguments
-// already checked: 64 tokens by 64 weight columns per workgroup with K split
-// over its waves, or (sx) 64, 96 or 128 tokens by 256 weight columns sharing
+// already checked: 64 tokens by 64 weight columns per workgroup (32 or 16
+// for a plain projection whose 64-column tiles would leave CUs idle) with K
+// split over its waves, or (sx) 64, 96 or 128 tokens by 256 weight columns sharing
 // each X tile, which needs 4x as many tokens to fill the CUs.  `path` is
 // NGQ_KERNEL_TILED or NGQ_KERNEL_TILED_SX (64 tokens), _SX96 or _SX128 (int4)
 // to force one, anything else to choose.
@@ -2392,7 +2414,16 @@ int run_tiled(int path, int nsets, int T, int K, int Nout, int Ncols, const Form
                  : path == NGQ_KERNEL_TILED_SX128    ? 8
                                                      : sx_token_blocks(f.bits, sx_cols, T, cu_count());
   const long ttiles = (T + 16L * tb - 1) / (16L * tb);
-  const int ocols = (sx ? dev::kSxCols : dev::kTiledCols) / nsets;
+  // K-split tiles of 16 v output columns per set: a plain projection halves
+  // v while its tiles leave CUs without a workgroup and the halved tiles
+  // still fit one round (a CU running two narrow tiles finishes last: QK at
+  // 64 tokens on 32-column tiles, 256 of them, takes 23.2 us against 24.8
+  // on 64; GV on 32, 384 tiles, 47 against 27)
+  const long cus = cu_count();
+  auto ktiles = [&](int vv) { return (long)((Nout + 16 * vv - 1) / (16 * vv)) * ttiles; };
+  int v = 4 / nsets;
+  while (!sx && nsets == 1 && v > kTiledMinV && ktiles(v) < cus && ktiles(v / 2) <= cus) v /= 2;
+  const int ocols = sx ? dev::kSxCols / nsets : 16 * v;
   a.tiles_n = (Nout + ocols - 1) / ocols;
   const long tiles = (long)a.tiles_n * ttiles;
   if (tiles > 0x7FFFFFFFL) return NGQ_ERR_SHAPE;
@@ -2405,9 +2436,9 @@ int run_tiled(int path, int nsets, int T, int K, int Nout, int Ncols, const Form
     e = nsets == 1 ? launch_tiled<1, true>(f, tb, a, lds, (hipStream_t)stream)
                    : launch_tiled<2, true>(f, tb, a, lds, (hipStream_t)stream);
   } else {
-    const uint32_t lds = dev::tiled_lds_bytes();
-    e = nsets == 1 ? launch_tiled<1, false>(f, tb, a, lds, (hipStream_t)stream)
-                   : launch_tiled<2, false>(f, tb, a, lds, (hipStream_t)stream);
+    const uint32_t lds = dev::tiled_lds_bytes(16 * nsets * v);
+    e = nsets == 1 ? launch_tiled<1, false>(f, v, a, lds, (hipStream_t)stream)
+                   : launch_tiled<2, false>(f, v, a, lds, (hipStream_t)stream);
   }
   return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }

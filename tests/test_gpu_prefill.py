@@ -4,8 +4,8 @@ on the GPU, against the CPU oracle.
 
 Small ragged shapes (a token tail past every 64-token tile, a column tail,
 odd group counts, every bit width and both scale types) for both variants,
-the K-split kernel forced at decode and verify T, the full-size projections at T = 1024 and 256
-on sampled columns, bit-exact cases, guard bands, K = 0, determinism and
+the K-split kernel forced at decode and verify T (its 16-, 32- and 64-column
+tiles), the full-size projections at T = 40 to 2048 on sampled columns, bit-exact cases, guard bands, K = 0, determinism and
 graph replay.
 """
 import numpy as np
@@ -63,6 +63,11 @@ SMALL = [
     (4, False, 300, 2048, 4100),
     (5, True, 77, 64, 40),       # a single group (waves 1..3 have none)
     (8, False, 150, 1088, 132),  # 17 groups
+    # on 256 CUs the K-split kernel runs 16-column tiles for most shapes
+    # above and 32-column ones for these two (66 tiles of 64 columns would
+    # leave CUs idle, 264 of 16 two rounds); column tails of 20
+    (5, True, 65, 320, 2100),
+    (8, False, 100, 256, 2100),
 ]
 
 
@@ -173,9 +178,10 @@ def full_inputs(name, T):
 
 
 # qk at T = 1024 runs the shared-X variant with 64-token tiles, qk at 2048
-# with 128, down at 2048 with 96, the others the K-split one
+# with 128, down at 2048 with 96, the others the K-split one (qk at 64 and
+# down at 40 on 32-column tiles, the rest on 64)
 @pytest.mark.parametrize("name,T", [("qk", 1024), ("gv", 256), ("qk8", 130), ("down", 256), ("qk", 2048),
-                                    ("down", 2048)])
+                                    ("down", 2048), ("qk", 64), ("down", 40)])
 def test_prefill_full_size(ngq, orc, name, T):
     w, codes, scales, x = full_inputs(name, T)
     cols = sample_cols(w.N, seed=T + 11, n_random=96)
