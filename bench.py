@@ -122,6 +122,7 @@ def clocks_under_load(launch, ms_per_launch):
     launches are queued (read only, nothing set); None where rocm-smi is not
     available.  A child process, started after the launches are enqueued."""
     import re
+    import shutil
     import subprocess
 
     import torch
@@ -130,7 +131,15 @@ def clocks_under_load(launch, ms_per_launch):
     for _ in range(n):
         launch()
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        # rocm-smi is a Python script: run it with this interpreter rather than
+        # through its `#!/usr/bin/env` line, so that the child does not replace
+        # itself with another program (under a counter-collecting profiler the
+        # preloaded library has already initialised the GPU in that child)
+        smi = shutil.which("rocm-smi")
+        if smi is None:
+            raise FileNotFoundError("rocm-smi")
+        r = subprocess.run([sys.executable, smi, "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=30)
         card = next(iter(json.loads(r.stdout[r.stdout.index("{"):]).values()))
         mhz = {k.split()[0]: int(re.search(r"(\d+)", v).group(1)) for k, v in card.items() if "speed" in k}
     except Exception:  # no rocm-smi, or an output this parser does not know

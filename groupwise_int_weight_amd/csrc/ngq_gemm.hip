@@ -2111,12 +2111,32 @@ std::atomic<int> kernel_override{NGQ_KERNEL_AUTO};
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  static int cache[64] = {0};
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  static std::atomic<int> cache[64];  // zero-initialised (static storage); 0 = not yet read
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (dev >= 0 && dev < 64) cache[dev] = cus;
+  if (cached) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// Raises a kernel's dynamic LDS limit from the default 64 KiB to the 160 KiB
+// of a CDNA4 workgroup on the current device.  A function attribute belongs
+// to a device, so `done` (one per kernel) keeps a bit per device index; two
+// threads that both see the bit clear both make the call, which is
+// idempotent.
+hipError_t raise_lds(const void* kern, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 // Columns per lane V in [vmin, vmax]: the tile count should fill the CUs in
@@ -2141,17 +2161,14 @@ int choose_v(int N, int cus, int vmin, int vmax) {
 }
 
 // One instantiation.  Its LDS (X staging + partial-sum blocks) can exceed the
-// default 64 KiB dynamic limit, so the limit is raised once per kernel to the
-// 160 KiB of a CDNA4 workgroup (idempotent: a race only repeats the call).
+// default 64 KiB dynamic limit, which is then raised (raise_lds).
 template <int BITS, bool SBF16, int V, int NSETS, bool DYN>
 hipError_t launch_one(const dev::GemmArgs& a, uint32_t lds, hipStream_t st) {
   auto kern = dev::gemm_kernel<BITS, SBF16, V, NSETS, DYN>;
-  static bool raised = false;
-  if (lds > 64u * 1024u && !raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  static std::atomic<uint64_t> raised{0};
+  if (lds > 64u * 1024u) {
+    const hipError_t e = raise_lds(reinterpret_cast<const void*>(kern), raised);
     if (e != hipSuccess) return e;
-    raised = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(dev::kThreads), lds, st, a);
   return hipGetLastError();
@@ -2187,12 +2204,10 @@ constexpr int xres_vmax(int bits, int nsets, int xl) {
 template <int BITS, bool SBF16, int V, int NSETS, int W, int NB, int XL>
 hipError_t launch_xres_one(const dev::GemmArgs& a, int grid, uint32_t lds, hipStream_t st) {
   auto kern = dev::gemm_xres_kernel<BITS, SBF16, V, NSETS, W, NB, XL>;
-  static bool raised = false;
-  if (lds > 64u * 1024u && !raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  static std::atomic<uint64_t> raised{0};
+  if (lds > 64u * 1024u) {
+    const hipError_t e = raise_lds(reinterpret_cast<const void*>(kern), raised);
     if (e != hipSuccess) return e;
-    raised = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W * 64), lds, st, a);
   return hipGetLastError();
@@ -2781,16 +2796,10 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
   std::memcpy(a.count, pl->count, sizeof(a.count));
   using Kern = void (*)(dev::MultiArgs);
   static const Kern kernels[2] = {dev::gemm_multi_kernel<false>, dev::gemm_multi_kernel<true>};
-  static std::once_flag raised;
-  static hipError_t raise_err = hipSuccess;
-  std::call_once(raised, [] {
-    for (Kern k : kernels)
-      if (raise_err == hipSuccess)
-        raise_err = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        (int)kMaxLds);
-  });
-  if (raise_err != hipSuccess) return NGQ_ERR_HIP;
+  static std::atomic<uint64_t> raised[2] = {{0}, {0}};
   const bool big_x = (long)T * (K / 8) > (long)dev::kMultiXL * dev::kMultiW * 64;
+  if (raise_lds(reinterpret_cast<const void*>(kernels[big_x ? 1 : 0]), raised[big_x ? 1 : 0]) != hipSuccess)
+    return NGQ_ERR_HIP;
   hipLaunchKernelGGL(kernels[big_x ? 1 : 0], dim3((unsigned)pl->grid), dim3(dev::kMultiW * 64), lds,
                      (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
@@ -2821,12 +2830,10 @@ int choose_splits(int T, int K, int pairs, int ntiles, int cus) {
 template <int BITS, bool SBF16>
 hipError_t launch_splitk_b(int xl, const dev::SplitArgs& a, int grid, uint32_t lds, hipStream_t st) {
   auto one = [&](auto kern) {
-    static bool raised = false;
-    if (lds > 64u * 1024u && !raised) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    static std::atomic<uint64_t> raised{0};  // one per instantiation of this lambda, i.e. per kernel
+    if (lds > 64u * 1024u) {
+      const hipError_t e = raise_lds(reinterpret_cast<const void*>(kern), raised);
       if (e != hipSuccess) return e;
-      raised = true;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(dev::kSplitWaves * 64), lds, st, a);
     return hipGetLastError();
