@@ -146,6 +146,38 @@ def _dev_ptr(t, what):
     return t.data_ptr()
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_operands(where, x, wq, scales, outs, K: int, ncols: int, bits: int, group: int):
+    """Shapes, sizes, dtypes and devices of a projection's tensors, checked
+    before the library is called: the library sizes its reads from K and N, so
+    a buffer that is too small would be read or written past its end.
+      wq     : ngq_packed_bytes(K, ncols, bits) bytes (nothing is read when K = 0)
+      scales : (K / group) * ncols elements, float16 or bfloat16
+      outs   : (tensor, rows, cols) triples, each bfloat16 of exactly that shape
+    Every tensor must be on x's device."""
+    import torch
+
+    if K > 0:
+        need = ngq_packed_bytes(K, ncols, int(bits) & 0xFF, group)
+        if need == 0:
+            raise ValueError(f"{where}: K={K}, columns={ncols}, bits={bits} is not a valid shape")
+        if _nbytes(wq) != need:
+            raise ValueError(f"{where}: wq holds {_nbytes(wq)} bytes, the packed {K} x {ncols} matrix {need}")
+        if scales.numel() != (K // group) * ncols:
+            raise ValueError(f"{where}: scales hold {scales.numel()} values, expected {(K // group) * ncols}")
+    for t, rows, cols in outs:
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{where}: outputs must be bfloat16")
+        if tuple(t.shape) != (rows, cols):
+            raise ValueError(f"{where}: output shape {tuple(t.shape)}, expected {(rows, cols)}")
+    for t in [wq, scales] + [o[0] for o in outs]:
+        if t is not None and t.device != x.device:
+            raise ValueError(f"{where}: every tensor must be on {x.device}, found one on {t.device}")
+
+
 def _format_bits(bits: int, scales) -> int:
     import torch
 
@@ -166,6 +198,7 @@ def ngq_gemm(x, wq, scales, bits: int, N: int, y=None, group: int = NGQ_GROUP, s
         raise TypeError("x must be bfloat16")
     if y is None:
         y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check_operands("ngq_gemm", x, wq, scales, [(y, T, N)], K, N, bits, group)
     st = lib().ngq_gemm(T, K, N, _format_bits(bits, scales), group, _dev_ptr(x, "x"), _dev_ptr(wq, "wq"),
                         _dev_ptr(scales, "scales"), _dev_ptr(y, "y"), _stream(stream))
     _check(st, "ngq_gemm")
@@ -182,6 +215,7 @@ def ngq_swiglu_gemm(x, wq_gate_up, scales_gate_up, bits: int, N_ff: int, h=None,
         raise TypeError("x must be bfloat16")
     if h is None:
         h = torch.empty((T, N_ff), dtype=torch.bfloat16, device=x.device)
+    _check_operands("ngq_swiglu_gemm", x, wq_gate_up, scales_gate_up, [(h, T, N_ff)], K, 2 * N_ff, bits, group)
     st = lib().ngq_swiglu_gemm(T, K, N_ff, _format_bits(bits, scales_gate_up), group, _dev_ptr(x, "x"),
                                _dev_ptr(wq_gate_up, "wq_gate_up"), _dev_ptr(scales_gate_up, "scales_gate_up"),
                                _dev_ptr(h, "h"), _stream(stream))
@@ -207,6 +241,9 @@ def ngq_gemm_splitk(x, wq, scales, bits: int, N: int, y=None, workspace=None, gr
     if workspace is None:
         workspace = torch.empty(max(16, ngq_splitk_workspace_bytes(K, N, bits, group)), dtype=torch.uint8,
                                 device=x.device)
+    _check_operands("ngq_gemm_splitk", x, wq, scales, [(y, T, N)], K, N, bits, group)
+    if workspace.device != x.device:
+        raise ValueError("ngq_gemm_splitk: the workspace must be on x's device")
     st = lib().ngq_gemm_splitk(T, K, N, _format_bits(bits, scales), group, _dev_ptr(x, "x"), _dev_ptr(wq, "wq"),
                                _dev_ptr(scales, "scales"), _dev_ptr(y, "y"), _dev_ptr(workspace, "workspace"),
                                workspace.numel() * workspace.element_size(), _stream(stream))
@@ -231,6 +268,11 @@ def ngq_multi_gemm(x, projs, group: int = NGQ_GROUP, stream=None):
         if y is None:
             y = torch.empty((T, int(p["n"])), dtype=torch.bfloat16, device=x.device)
         outs.append(y)
+        n = int(p["n"])
+        nsets = 2 if p.get("swiglu", False) else 1
+        _check_operands(f"ngq_multi_gemm projection {i}", x, p["wq"], p["scales"], [(y, T, n)], K, nsets * n,
+                        p["bits"], group)
+    for i, (p, y) in enumerate(zip(projs, outs)):
         arr[i] = NgqProj(_format_bits(p["bits"], p["scales"]), int(p["n"]), int(bool(p.get("swiglu", False))), 0,
                          _dev_ptr(p["wq"], "wq"), _dev_ptr(p["scales"], "scales"), _dev_ptr(y, "y"))
     _check(lib().ngq_multi_gemm(T, K, group, _dev_ptr(x, "x"), arr, len(projs), _stream(stream)), "ngq_multi_gemm")
@@ -246,6 +288,7 @@ def ngq_rms_rescale(z, x=None, stream=None):
         raise TypeError("z must be bfloat16")
     if x is None:
         x = torch.empty_like(z)
+    _check_operands("ngq_rms_rescale", z, None, None, [(x, T, N)], 0, N, NGQ_INT4, NGQ_GROUP)
     _check(lib().ngq_rms_rescale(T, N, _dev_ptr(z, "z"), _dev_ptr(x, "x"), _stream(stream)), "ngq_rms_rescale")
     return x
 
@@ -266,6 +309,9 @@ def ngq_gemm_rescale(x, wq, scales, bits: int, N: int, y=None, x_next=None, work
     if workspace is None:
         workspace = torch.empty(max(16, ngq_splitk_workspace_bytes(K, N, bits, group)), dtype=torch.uint8,
                                 device=x.device)
+    _check_operands("ngq_gemm_rescale", x, wq, scales, [(y, T, N), (x_next, T, N)], K, N, bits, group)
+    if workspace.device != x.device:
+        raise ValueError("ngq_gemm_rescale: the workspace must be on x's device")
     st = lib().ngq_gemm_rescale(T, K, N, _format_bits(bits, scales), group, _dev_ptr(x, "x"), _dev_ptr(wq, "wq"),
                                 _dev_ptr(scales, "scales"), _dev_ptr(y, "y"), _dev_ptr(x_next, "x_next"),
                                 _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
@@ -278,6 +324,8 @@ def ngq_unpack_codes(wq, K: int, N: int, bits: int, group: int = NGQ_GROUP, stre
     import torch
 
     codes = torch.empty((K, N), dtype=torch.int8, device=wq.device)
+    if K > 0 and _nbytes(wq) != ngq_packed_bytes(K, N, int(bits) & 0xFF, group):
+        raise ValueError("ngq_unpack_codes: wq does not hold the packed K x N matrix")
     _check(lib().ngq_unpack_codes(K, N, int(bits) & 0xFF, group, _dev_ptr(wq, "wq"), _dev_ptr(codes, "codes"),
                                   _stream(stream)), "ngq_unpack_codes")
     return codes
@@ -287,6 +335,9 @@ def ngq_dequant_f32(wq, scales, K: int, N: int, bits: int, group: int = NGQ_GROU
     import torch
 
     w = torch.empty((K, N), dtype=torch.float32, device=wq.device)
+    if K > 0 and (_nbytes(wq) != ngq_packed_bytes(K, N, int(bits) & 0xFF, group) or
+                  scales.numel() != (K // group) * N or scales.device != wq.device):
+        raise ValueError("ngq_dequant_f32: wq or scales do not match the K x N matrix")
     _check(lib().ngq_dequant_f32(K, N, _format_bits(bits, scales), group, _dev_ptr(wq, "wq"),
                                  _dev_ptr(scales, "scales"), _dev_ptr(w, "w"), _stream(stream)),
            "ngq_dequant_f32")
@@ -294,6 +345,8 @@ def ngq_dequant_f32(wq, scales, K: int, N: int, bits: int, group: int = NGQ_GROU
 
 
 def ngq_stream_read(buf, sink, stream=None):
+    if _nbytes(sink) < 16384 or sink.device != buf.device:
+        raise ValueError("ngq_stream_read: sink must hold 16384 bytes on the buffer's device")
     _check(lib().ngq_stream_read(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(), _dev_ptr(sink, "sink"),
                                  _stream(stream)), "ngq_stream_read")
 

@@ -2600,6 +2600,9 @@ int run_unpack(int K, int N, int bits, int group, const void* wq, const void* sc
 
 // ---- several projections of one X in one launch (host) ----
 
+// Shapes whose plans are kept; the oldest is dropped beyond that.
+constexpr size_t kPlanCacheSize = 16;
+
 // Tiles per projection and workgroup for one shape (see gemm_multi_kernel).
 struct MultiPlan {
   int key[3 + 2 * dev::kMultiMaxProj];  // grid bound, K, nproj, then (kind, Nout) per projection
@@ -2668,8 +2671,12 @@ bool make_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, M
   return true;
 }
 
-// The plan of a shape, computed once and kept (a few shapes per process).
-const MultiPlan* get_plan(int K, int nproj, const int* kind, const int* nout, int wg_max) {
+// The plan of a shape, computed once and kept (a few shapes per process),
+// copied into the launch arguments while the cache's lock is held: a plan
+// may be evicted (and freed) by another thread as soon as the lock is
+// released, so no pointer into the cache leaves this function.  Returns the
+// grid, or -1 when the shape has no plan.
+int load_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, dev::MultiArgs& a) {
   static std::mutex mu;
   static std::deque<MultiPlan> plans;
   int key[3 + 2 * dev::kMultiMaxProj] = {wg_max, K, nproj};
@@ -2678,14 +2685,22 @@ const MultiPlan* get_plan(int K, int nproj, const int* kind, const int* nout, in
     key[4 + 2 * p] = nout[p];
   }
   std::lock_guard<std::mutex> lock(mu);
+  const MultiPlan* found = nullptr;
   for (const MultiPlan& pl : plans)
-    if (std::memcmp(pl.key, key, sizeof(key)) == 0) return &pl;
-  MultiPlan pl;
-  std::memcpy(pl.key, key, sizeof(key));
-  if (!make_plan(K, nproj, kind, nout, wg_max, pl)) return nullptr;
-  if (plans.size() == 16) plans.pop_front();
-  plans.push_back(pl);
-  return &plans.back();
+    if (std::memcmp(pl.key, key, sizeof(key)) == 0) found = &pl;
+  if (found == nullptr) {
+    MultiPlan pl;
+    std::memcpy(pl.key, key, sizeof(key));
+    if (!make_plan(K, nproj, kind, nout, wg_max, pl)) return -1;
+    if (plans.size() == kPlanCacheSize) plans.pop_front();
+    plans.push_back(pl);
+    found = &plans.back();
+  }
+  static_assert(sizeof(a.first) == sizeof(found->first) && sizeof(a.count) == sizeof(found->count),
+                "plan tables and launch arguments differ");
+  std::memcpy(a.first, found->first, sizeof(a.first));
+  std::memcpy(a.count, found->count, sizeof(a.count));
+  return found->grid;
 }
 
 int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int nproj, void* stream) {
@@ -2779,8 +2794,8 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
       nout[i] = no[i];
     }
   }
-  const MultiPlan* pl = get_plan(K, n, kind, nout, std::min(cu_count(), dev::kMultiMaxWg));
-  if (pl == nullptr) return NGQ_ERR_UNSUPPORTED;
+  const int grid = load_plan(K, n, kind, nout, std::min(cu_count(), dev::kMultiMaxWg), a);
+  if (grid < 0) return NGQ_ERR_UNSUPPORTED;
   a.x = x;
   a.x_bytes = (uint32_t)xb;
   a.T = T;
@@ -2792,15 +2807,14 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
   a.mask_nib = dev::kMasks.nib;
   a.mask_base = dev::kMasks.base;
   a.mask_hi = dev::kMasks.hi;
-  std::memcpy(a.first, pl->first, sizeof(a.first));
-  std::memcpy(a.count, pl->count, sizeof(a.count));
   using Kern = void (*)(dev::MultiArgs);
   static const Kern kernels[2] = {dev::gemm_multi_kernel<false>, dev::gemm_multi_kernel<true>};
   static std::atomic<uint64_t> raised[2] = {{0}, {0}};
   const bool big_x = (long)T * (K / 8) > (long)dev::kMultiXL * dev::kMultiW * 64;
   if (raise_lds(reinterpret_cast<const void*>(kernels[big_x ? 1 : 0]), raised[big_x ? 1 : 0]) != hipSuccess)
     return NGQ_ERR_HIP;
-  hipLaunchKernelGGL(kernels[big_x ? 1 : 0], dim3((unsigned)pl->grid), dim3(dev::kMultiW * 64), lds,
+  if (grid == 0) return NGQ_OK;
+  hipLaunchKernelGGL(kernels[big_x ? 1 : 0], dim3((unsigned)grid), dim3(dev::kMultiW * 64), lds,
                      (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
@@ -2827,19 +2841,24 @@ int choose_splits(int T, int K, int pairs, int ntiles, int cus) {
   return kSplitMax;
 }
 
+// One split-K kernel; the flag that its LDS limit was raised is a static of
+// this instantiation, so every kernel (each XL) has its own.
+template <int BITS, bool SBF16, int XL>
+hipError_t launch_splitk_xl(const dev::SplitArgs& a, int grid, uint32_t lds, hipStream_t st) {
+  auto kern = dev::gemm_splitk_kernel<BITS, SBF16, XL>;
+  static std::atomic<uint64_t> raised{0};
+  if (lds > 64u * 1024u) {
+    const hipError_t e = raise_lds(reinterpret_cast<const void*>(kern), raised);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(dev::kSplitWaves * 64), lds, st, a);
+  return hipGetLastError();
+}
+
 template <int BITS, bool SBF16>
 hipError_t launch_splitk_b(int xl, const dev::SplitArgs& a, int grid, uint32_t lds, hipStream_t st) {
-  auto one = [&](auto kern) {
-    static std::atomic<uint64_t> raised{0};  // one per instantiation of this lambda, i.e. per kernel
-    if (lds > 64u * 1024u) {
-      const hipError_t e = raise_lds(reinterpret_cast<const void*>(kern), raised);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(dev::kSplitWaves * 64), lds, st, a);
-    return hipGetLastError();
-  };
-  if (xl <= 7) return one(dev::gemm_splitk_kernel<BITS, SBF16, 7>);
-  return one(dev::gemm_splitk_kernel<BITS, SBF16, 18>);
+  if (xl <= 7) return launch_splitk_xl<BITS, SBF16, 7>(a, grid, lds, st);
+  return launch_splitk_xl<BITS, SBF16, 18>(a, grid, lds, st);
 }
 
 // x_next == nullptr: ngq_gemm_splitk.  Otherwise ngq_gemm_rescale: the same

@@ -282,5 +282,79 @@ def test_debug_exports_reject_bad_arguments(ngq):
 def test_binding_refuses_host_tensors(ngq):
     torch = pytest.importorskip("torch")
     x = torch.zeros((1, 64), dtype=torch.bfloat16)
+    # operands of the right sizes, but in host memory
     with pytest.raises(TypeError):
-        ngq.ngq_gemm(x, torch.zeros(32, dtype=torch.uint8), torch.zeros((1, 4), dtype=torch.float16), 4, 4)
+        ngq.ngq_gemm(x, torch.zeros(128, dtype=torch.uint8), torch.zeros((1, 4), dtype=torch.float16), 4, 4)
+
+
+def test_binding_checks_sizes_before_any_call(ngq):
+    """The library sizes its reads and writes from K and N, so the binding
+    refuses tensors that do not hold what those sizes imply, before calling it
+    (host tensors here: the size checks come before the device check)."""
+    torch = pytest.importorskip("torch")
+    bf, f16, u8 = torch.bfloat16, torch.float16, torch.uint8
+    T, K, N = 2, 128, 8
+    x = torch.zeros((T, K), dtype=bf)
+    wq = torch.zeros(ngq.ngq_packed_bytes(K, N, 4), dtype=u8)  # 512 bytes
+    sc = torch.zeros((K // 64, N), dtype=f16)
+    y = torch.zeros((T, N), dtype=bf)
+    with pytest.raises(ValueError, match="wq holds"):
+        ngq.ngq_gemm(x, wq[:-16], sc, 4, N, y=y)
+    with pytest.raises(ValueError, match="wq holds"):
+        ngq.ngq_gemm(x, wq, sc, 5, N, y=y)  # an int4 buffer read as int5 (P1 missing)
+    with pytest.raises(ValueError, match="scales hold"):
+        ngq.ngq_gemm(x, wq, sc[:1], 4, N, y=y)
+    with pytest.raises(ValueError, match="output shape"):
+        ngq.ngq_gemm(x, wq, sc, 4, N, y=torch.zeros((T, N - 4), dtype=bf))
+    with pytest.raises(TypeError, match="bfloat16"):
+        ngq.ngq_gemm(x, wq, sc, 4, N, y=torch.zeros((T, N), dtype=f16))
+    # SwiGLU: wq and scales cover 2 N_ff columns
+    with pytest.raises(ValueError, match="wq holds"):
+        ngq.ngq_swiglu_gemm(x, wq, sc, 4, N)
+    with pytest.raises(ValueError, match="output shape"):
+        ngq.ngq_swiglu_gemm(x, wq, sc, 4, N // 2, h=torch.zeros((T + 1, N // 2), dtype=bf))
+    with pytest.raises(ValueError, match="output shape"):
+        ngq.ngq_gemm_splitk(x, wq, sc, 4, N, y=torch.zeros((T, N), dtype=bf).t(), workspace=wq)
+    with pytest.raises(ValueError, match="output shape"):
+        ngq.ngq_gemm_rescale(x, wq, sc, 4, N, y=y, x_next=torch.zeros((1, N), dtype=bf), workspace=wq)
+    with pytest.raises(ValueError, match="projection 1"):
+        ngq.ngq_multi_gemm(x, [dict(wq=wq, scales=sc, bits=4, n=N, y=y),
+                               dict(wq=wq, scales=sc, bits=4, n=N, swiglu=True)])
+    with pytest.raises(ValueError, match="output shape"):
+        ngq.ngq_rms_rescale(y, x=torch.zeros((T, N + 4), dtype=bf))
+    with pytest.raises(ValueError):
+        ngq.ngq_unpack_codes(wq[:64], K, N, 4)
+    with pytest.raises(ValueError):
+        ngq.ngq_stream_read(wq, torch.zeros(16, dtype=torch.int32))
+
+
+def test_multi_plan_cache_under_concurrent_eviction(ngq):
+    """ngq_multi_gemm plans its tile split per shape and keeps the last 16
+    plans.  Two threads asking for 40 distinct shapes each keep evicting
+    plans the other is using; every call must still finish with the same
+    status (no device here: planning succeeds, the launch reports the missing
+    device), and a plan is never read after its eviction (it is copied into
+    the launch arguments under the cache's lock)."""
+    import threading
+
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("host-only check: with a device these fake pointers would be launched")
+    L = ngq.lib()
+    results = []
+
+    def worker(base):
+        out = []
+        for i in range(40):
+            n = 64 + 4 * (base + i)
+            arr = (ngq.NgqProj * 2)(ngq.NgqProj(4, n, 0, 0, W, S, Y), ngq.NgqProj(5, 2 * n, 0, 0, W + 0x40000, S, Y + 0x8000))
+            out.append(L.ngq_multi_gemm(8, 1024, 64, X, arr, 2, None))
+        results.append(out)
+
+    th = [threading.Thread(target=worker, args=(b,)) for b in (0, 17)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    statuses = {st for out in results for st in out}
+    assert len(results) == 2 and len(statuses) == 1 and statuses.pop() in (ngq.NGQ_ERR_HIP,), statuses

@@ -12,7 +12,7 @@ import pytest
 
 import synthetic
 from tests.parity import assert_parity, compare
-from tests.test_gpu_parity import (check_swiglu, dev_bf16, dev_scales, dev_u8, host_bits, sample_cols,
+from tests.test_gpu_parity import (ORACLE_THREADS, check_swiglu, dev_bf16, dev_scales, dev_u8, host_bits,
                                    swiglu_reference)
 
 pytestmark = pytest.mark.gpu
@@ -61,7 +61,7 @@ def single(ngq, x, p):
         ngq.ngq_debug_force_kernel(prev)
 
 
-def run_case(ngq, orc, T, K, specs, seed, full_cols_below=2048):
+def run_case(ngq, orc, T, K, specs, seed):
     g = np.random.default_rng(seed)
     x = synthetic.f32_to_bf16_bits(g.standard_normal((T, K)).astype(np.float32))
     xd = dev_bf16(x)
@@ -85,12 +85,13 @@ def run_case(ngq, orc, T, K, specs, seed, full_cols_below=2048):
         if ref is not None:
             assert np.array_equal(yb, host_bits(ref)), what + ": differs from the single-projection kernel"
         codes, scales, packed_o = host[i]
-        cols = np.arange(n, dtype=np.int32) if n < full_cols_below else sample_cols(n, seed=seed + i)
+        cols = np.arange(n, dtype=np.int32)
         if swiglu:
             h64, gg, u = swiglu_reference(orc, x, packed_o, scales, K, n, bits, sbf16, cols)
             check_swiglu(yb[:, cols], h64, gg, u, what)
         else:
-            y64, axw, axs = orc.gemm(x, packed_o, scales, K, n, bits, sbf16, cols=cols, nthreads=8, with_bounds=True)
+            y64, axw, axs = orc.gemm(x, packed_o, scales, K, n, bits, sbf16, cols=cols, nthreads=ORACLE_THREADS,
+                                     with_bounds=True)
             assert_parity(compare(yb[:, cols], y64, axw, axs, K, bits), what)
     return outs
 

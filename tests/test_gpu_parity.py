@@ -3,9 +3,11 @@
 Every case draws seeded inputs from `synthetic`, packs them with the library's
 packer (and, independently, with the oracle's), runs the HIP kernels and
 compares element by element with the oracle (gates in tests/parity.py).
-Full-size workloads are checked on sampled columns the oracle computes one by
-one, plus whole-output properties.
+Full-size workloads are checked on every output column (the oracle computes a
+whole T=8 projection in well under a second on the host's cores), plus
+whole-output properties.
 """
+import os
 import math
 
 import numpy as np
@@ -59,6 +61,10 @@ def make(bits, sbf16, T, K, N, seed, lo=1e-3, hi=2e-2, config_id=50):
     return w, synthetic.make_inputs(w, T, seed=seed)
 
 
+# host threads for the oracle on full-size cases
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def run_and_compare(ngq, orc, bits, sbf16, codes, scales, x, cols=None, what=""):
     K, N = codes.shape
     packed = ngq.ngq_pack(codes, bits)
@@ -66,7 +72,8 @@ def run_and_compare(ngq, orc, bits, sbf16, codes, scales, x, cols=None, what="")
     assert np.array_equal(packed, packed_o)
     y = ngq.ngq_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits, N)
     yb = host_bits(y)
-    y64, axw, axs = orc.gemm(x, packed_o, scales, K, N, bits, sbf16, cols=cols, nthreads=8, with_bounds=True)
+    y64, axw, axs = orc.gemm(x, packed_o, scales, K, N, bits, sbf16, cols=cols, nthreads=ORACLE_THREADS,
+                             with_bounds=True)
     sub = yb if cols is None else yb[:, cols]
     rep = compare(sub, y64, axw, axs, K, bits)
     assert_parity(rep, what)
@@ -125,9 +132,11 @@ def test_gemm_every_t(ngq, orc, T):
     run_and_compare(ngq, orc, 4, False, codes, scales, x, what=f"T{T}")
 
 
-# ---- full-size workloads on sampled columns ------------------------------------
+# ---- full-size workloads, every output column ------------------------------------
 
 def sample_cols(N, seed, n_random=192):
+    """Columns for cases too large for the oracle to compute whole in seconds
+    (prefill-size T): both edges and random columns in between."""
     g = np.random.default_rng(seed)
     cols = np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N), g.integers(0, N, n_random)]))
     return cols.astype(np.int32)
@@ -151,13 +160,13 @@ def closed_form_rms(w):
     return math.sqrt(w.K * ec2 * es2)
 
 
-@pytest.mark.parametrize("name,T", [("qk", 8), ("qk", 1), ("qk", 2), ("qk", 4),
-                                    ("gv", 8), ("gv", 1), ("gv", 2), ("gv", 4), ("qk8", 8), ("qk8", 1)])
+# every T of one request's decode or verify step: each T has its own X layout
+# in the kernels (T = 6 is the ninfer-ext README's recommended five drafts + 1)
+@pytest.mark.parametrize("name,T", [("qk", t) for t in range(1, 9)] + [("gv", t) for t in range(1, 9)] +
+                         [("qk8", 1), ("qk8", 8)])
 def test_gemm_full_size(ngq, orc, name, T):
     w, codes, scales, x = full_inputs(name)
-    cols = sample_cols(w.N, seed=T)
-    yb, rep = run_and_compare(ngq, orc, w.bits, w.scale_bf16, codes, scales, x[:T], cols=cols,
-                              what=f"{name} T{T}")
+    yb, rep = run_and_compare(ngq, orc, w.bits, w.scale_bf16, codes, scales, x[:T], what=f"{name} T{T}")
     y = bf16_bits_to_f64(yb)
     assert np.all(np.isfinite(y))
     assert abs(math.sqrt(np.mean(y ** 2)) / closed_form_rms(w) - 1) < 0.03
@@ -165,7 +174,7 @@ def test_gemm_full_size(ngq, orc, name, T):
 
 def swiglu_reference(orc, x, packed_o, scales, K, N_ff, bits, sbf16, cols):
     both = np.concatenate([cols, cols + N_ff]).astype(np.int32)
-    y64, axw, axs = orc.gemm(x, packed_o, scales, K, 2 * N_ff, bits, sbf16, cols=both, nthreads=8,
+    y64, axw, axs = orc.gemm(x, packed_o, scales, K, 2 * N_ff, bits, sbf16, cols=both, nthreads=ORACLE_THREADS,
                              with_bounds=True)
     n = cols.size
     g, u = y64[:, :n], y64[:, n:]
@@ -198,9 +207,9 @@ def test_swiglu_and_down_full_size(ngq, orc, T):
     assert np.array_equal(packed, packed_o)
     h = ngq.ngq_swiglu_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, False), 4, N_ff)
     hb = host_bits(h)
-    cols = sample_cols(N_ff, seed=10 + T)
+    cols = np.arange(N_ff, dtype=np.int32)
     h64, g, u = swiglu_reference(orc, x, packed_o, scales, wgu.K, N_ff, 4, False, cols)
-    check_swiglu(hb[:, cols], h64, g, u, f"swiglu T{T}")
+    check_swiglu(hb, h64, g, u, f"swiglu T{T}")
     del codes, packed, packed_o
     # down projection: K = N_ff, its activations drawn by the generator (the
     # oracle never takes a GPU result as input)
@@ -208,10 +217,9 @@ def test_swiglu_and_down_full_size(ngq, orc, T):
     dpacked = ngq.ngq_pack(dcodes, 4)
     y = ngq.ngq_gemm(dev_bf16(dx), dev_u8(dpacked), dev_scales(dscales, False), 4, wdn.N)
     yb = host_bits(y)
-    dcols = sample_cols(wdn.N, seed=20 + T)
-    y64, axw, axs = orc.gemm(dx, orc.pack(dcodes, 4), dscales, wdn.K, wdn.N, 4, False, cols=dcols, nthreads=8,
+    y64, axw, axs = orc.gemm(dx, orc.pack(dcodes, 4), dscales, wdn.K, wdn.N, 4, False, nthreads=ORACLE_THREADS,
                              with_bounds=True)
-    assert_parity(compare(yb[:, dcols], y64, axw, axs, wdn.K, 4), f"down T{T}")
+    assert_parity(compare(yb, y64, axw, axs, wdn.K, 4), f"down T{T}")
 
 
 @pytest.mark.parametrize("bits,sbf16,T,K,N_ff", [(4, False, 8, 512, 100), (5, True, 3, 320, 36),

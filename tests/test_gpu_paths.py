@@ -4,9 +4,10 @@ The library picks a kernel per shape (per-pair X with dynamic or static pair
 assignment, X resident in LDS with 14 or 8 waves).  Here each path is forced
 through the debug export and run on the same ragged shapes: odd group counts
 (the last group pair has one group), N not a multiple of the tile, several
-tiles per workgroup, long K, every bit width and both scale types.  A path
-that cannot serve a shape reports NGQ_ERR_UNSUPPORTED and the case is
-skipped.
+tiles per workgroup, long K, every bit width and both scale types.  The
+(path, case) pairs a path does not serve are listed in UNSUPPORTED with the
+reason; for them the call must refuse with NGQ_ERR_UNSUPPORTED, and a refusal
+anywhere else fails the test.
 """
 import numpy as np
 import pytest
@@ -46,15 +47,25 @@ def forced(ngq, request):
     ngq.ngq_debug_force_kernel(prev)
 
 
-def run_or_skip(fn):
+# (path, entry point, case) pairs that a forced path does not serve, with the
+# reason; a case of None stands for every case of that entry point
+UNSUPPORTED = {
+    ("xres14", "swiglu", None): "the 14-wave X-resident kernel has no SwiGLU epilogue",
+    ("perpair_dyn", "gemm", (4, True, 2, 17408, 64)):
+        "one partial-sum block per pair (136 pairs at K = 17408) does not fit in LDS",
+}
+
+
+def run_checked(fn, path, entry, case):
+    """The call's result, or None after checking that a listed pair refuses."""
     import groupwise_int_weight_amd as g
 
-    try:
-        return fn()
-    except g.NgqError as e:
-        if e.status == g.NGQ_ERR_UNSUPPORTED:
-            pytest.skip("path does not serve this shape")
-        raise
+    if (path, entry, None) in UNSUPPORTED or (path, entry, case) in UNSUPPORTED:
+        with pytest.raises(g.NgqError) as e:
+            fn()
+        assert e.value.status == g.NGQ_ERR_UNSUPPORTED
+        return None
+    return fn()
 
 
 GEMM_CASES = [
@@ -76,9 +87,13 @@ GEMM_CASES = [
 def test_gemm_path(ngq, orc, forced, bits, sbf16, T, K, N):
     _, (codes, scales, x) = make(bits, sbf16, T, K, N, seed=K + N + T)
     packed = ngq.ngq_pack(codes, bits)
-    y = run_or_skip(lambda: ngq.ngq_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits, N))
+    y = run_checked(lambda: ngq.ngq_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits, N),
+                    PATHS[forced], "gemm", (bits, sbf16, T, K, N))
+    if y is None:
+        return
     yb = host_bits(y)
-    y64, axw, axs = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, sbf16, nthreads=8, with_bounds=True)
+    y64, axw, axs = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, sbf16, nthreads=8,
+                             with_bounds=True)
     assert_parity(compare(yb, y64, axw, axs, K, bits), f"{PATHS[forced]} b{bits} T{T} K{K} N{N}")
 
 
@@ -97,8 +112,10 @@ def test_swiglu_path(ngq, orc, forced, bits, sbf16, T, K, N_ff):
 
     _, (codes, scales, x) = make(bits, sbf16, T, K, 2 * N_ff, seed=K + N_ff)
     packed = ngq.ngq_pack(codes, bits)
-    h = run_or_skip(lambda: ngq.ngq_swiglu_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits,
-                                                N_ff))
+    h = run_checked(lambda: ngq.ngq_swiglu_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits,
+                                                N_ff), PATHS[forced], "swiglu", (bits, sbf16, T, K, N_ff))
+    if h is None:
+        return
     cols = np.arange(N_ff, dtype=np.int32)
     h64, g, u = swiglu_reference(orc, x, orc.pack(codes, bits), scales, K, N_ff, bits, sbf16, cols)
     check_swiglu(host_bits(h), h64, g, u, f"{PATHS[forced]} swiglu b{bits} T{T}")
@@ -116,7 +133,10 @@ def test_identity_scales_integer_x_bit_exact_per_path(ngq, orc, forced, bits):
     scales = np.full((K // 64, N), 0x3C00, np.uint16)  # fp16 1.0
     x = synthetic.f32_to_bf16_bits(g.integers(-3, 4, size=(T, K)).astype(np.float32))
     packed = ngq.ngq_pack(codes, bits)
-    y = run_or_skip(lambda: ngq.ngq_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, False), bits, N))
+    y = run_checked(lambda: ngq.ngq_gemm(dev_bf16(x), dev_u8(packed), dev_scales(scales, False), bits, N),
+                    PATHS[forced], "gemm", (bits, False, T, K, N))
+    if y is None:
+        return
     y64 = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, False)
     assert np.array_equal(host_bits(y), orc.round_bf16_array(y64)), PATHS[forced]
 

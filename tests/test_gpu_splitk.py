@@ -13,7 +13,7 @@ import pytest
 
 import synthetic
 from tests.parity import assert_parity, compare
-from tests.test_gpu_parity import dev_bf16, dev_scales, dev_u8, host_bits, make, sample_cols
+from tests.test_gpu_parity import ORACLE_THREADS, dev_bf16, dev_scales, dev_u8, host_bits, make
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -43,7 +43,7 @@ def run(ngq, orc, bits, sbf16, T, K, N, seed, cols=None):
     y = torch.full((T, N), -7.0, dtype=torch.bfloat16, device="cuda")
     ngq.ngq_gemm_splitk(dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits, N, y=y)
     yb = host_bits(y)
-    y64, axw, axs = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, sbf16, cols=cols, nthreads=8,
+    y64, axw, axs = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, sbf16, cols=cols, nthreads=ORACLE_THREADS,
                              with_bounds=True)
     sub = yb if cols is None else yb[:, cols]
     assert_parity(compare(sub, y64, axw, axs, K, bits), f"splitk b{bits} T{T} K{K} N{N}")
@@ -69,10 +69,9 @@ def test_splitk_down_shape(ngq, orc, T):
     packed = ngq.ngq_pack(codes, 4)
     xd, wd, sd = dev_bf16(x), dev_u8(packed), dev_scales(scales, False)
     y = host_bits(ngq.ngq_gemm_splitk(xd, wd, sd, 4, w.N))
-    cols = sample_cols(w.N, seed=60 + T)
-    y64, axw, axs = orc.gemm(x, orc.pack(codes, 4), scales, w.K, w.N, 4, False, cols=cols, nthreads=8,
+    y64, axw, axs = orc.gemm(x, orc.pack(codes, 4), scales, w.K, w.N, 4, False, nthreads=ORACLE_THREADS,
                              with_bounds=True)
-    assert_parity(compare(y[:, cols], y64, axw, axs, w.K, 4), f"splitk down T{T}")
+    assert_parity(compare(y, y64, axw, axs, w.K, 4), f"splitk down T{T}")
     # deterministic, and a captured graph replays to the same bits
     assert np.array_equal(y, host_bits(ngq.ngq_gemm_splitk(xd, wd, sd, 4, w.N)))
     ws = torch.empty(ngq.ngq_splitk_workspace_bytes(w.K, w.N, 4), dtype=torch.uint8, device="cuda")

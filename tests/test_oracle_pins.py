@@ -272,6 +272,56 @@ def test_projection_brute_force_fractions(oracle_lib, bits, scale_bf16, K, N, T)
             assert abs(Fraction(y64[t, n]) - exact[t][n]) <= Fraction(1, 2 ** 40) * (1 + abs(exact[t][n]))
 
 
+def exact_magnitudes(codes, scale_bits, x_bits, scale_bf16):
+    """Brute force with exact rationals of the two magnitude sums the oracle
+    returns beside y: A = sum_k |x c s| and B = sum_k |x| s, per output."""
+    K, N = codes.shape
+    T = x_bits.shape[0]
+    dec = bf16_ref if scale_bf16 else f16_ref
+    S = [[Fraction(dec(scale_bits[g, n])) for n in range(N)] for g in range(K // 64)]
+    X = [[Fraction(bf16_ref(x_bits[t, k])) for k in range(K)] for t in range(T)]
+    A = [[sum(abs(X[t][k] * int(codes[k, n]) * S[k // 64][n]) for k in range(K)) for n in range(N)]
+         for t in range(T)]
+    B = [[sum(abs(X[t][k]) * S[k // 64][n] for k in range(K)) for n in range(N)] for t in range(T)]
+    return A, B
+
+
+@pytest.mark.parametrize("bits,scale_bf16,K,N,T", [(4, False, 192, 5, 2), (5, True, 128, 4, 3),
+                                                    (8, False, 128, 3, 2)])
+def test_magnitude_sums_brute_force_fractions(oracle_lib, bits, scale_bf16, K, N, T):
+    """The magnitudes sum|x w| and sum|x| s size the tie exemption of the parity
+    gate, so they are pinned like y: against exact rational sums.  Every group
+    has its own scales (U[1e-3, 2e-2]), so a wrong group index, a dropped or
+    squared scale, or |x| c s in place of |x| s changes them by far more than
+    the fp64 summation error (at most K 2^-53 relative)."""
+    w = synthetic.Workload("t", K, N, bits, scale_bf16, 1e-3, 2e-2, 91)
+    codes, scales, x = synthetic.make_inputs(w, T, seed=4)
+    assert len({int(v) for v in scales[:, 0]}) == K // 64  # distinct per group
+    y64, axw, axs = oracle_lib.gemm(x, oracle_lib.pack(codes, bits), scales, K, N, bits, scale_bf16,
+                                    with_bounds=True)
+    A, B = exact_magnitudes(codes, scales, x, scale_bf16)
+    tol = Fraction(K, 2 ** 52)
+    for t in range(T):
+        for n in range(N):
+            assert abs(Fraction(axw[t, n]) - A[t][n]) <= tol * A[t][n], (t, n)
+            assert abs(Fraction(axs[t, n]) - B[t][n]) <= tol * B[t][n], (t, n)
+            # triangle inequality and |c| <= 2^(bits-1): |y| <= A <= 2^(bits-1) B
+            assert abs(y64[t, n]) <= axw[t, n] <= 2 ** (bits - 1) * axs[t, n]
+
+
+def test_magnitude_sums_worked_example(oracle_lib):
+    """Hand-worked: K=64, one column, codes k-8 on k<16 and 0 elsewhere
+    (worked example W1's words), s = 0.5, x = 1 on k<16:
+    sum|x c s| = 0.5 (8+7+...+1 + 0+1+...+7) = 0.5 * 64 = 32,
+    sum|x| s = 16 * 0.5 = 8."""
+    case = next(c for c in load_cases() if c["bits"] == 4 and c["x"]["kind"] == "indicator_below")
+    packed = words_to_bytes(case["p0_words"])
+    scales = np.array([int(s, 16) for s in case["scales"]], dtype=np.uint16).reshape(1, 1)
+    assert scales[0, 0] == 0x3800
+    y, axw, axs = oracle_lib.gemm(case_x(case), packed, scales, 64, 1, 4, False, with_bounds=True)
+    assert (y[0, 0], axw[0, 0], axs[0, 0]) == (-4.0, 32.0, 8.0)
+
+
 def numpy_projection(codes, scale_bits, x_bits, scale_bf16):
     K, N = codes.shape
     if scale_bf16:
