@@ -154,13 +154,16 @@ def _check_operands(where, x, wq, scales, outs, K: int, ncols: int, bits: int, g
     """Shapes, sizes, dtypes and devices of a projection's tensors, checked
     before the library is called: the library sizes its reads from K and N, so
     a buffer that is too small would be read or written past its end.
-      wq     : ngq_packed_bytes(K, ncols, bits) bytes (nothing is read when K = 0)
+      wq     : ngq_packed_bytes(K, ncols, bits) bytes (nothing is read when K or ncols is 0)
       scales : (K / group) * ncols elements, float16 or bfloat16
       outs   : (tensor, rows, cols) triples, each bfloat16 of exactly that shape
-    Every tensor must be on x's device."""
+    Every tensor must be on x's device.  With no token rows the call is a
+    no-op that touches no buffer, so nothing is checked."""
     import torch
 
-    if K > 0:
+    if x.shape[0] == 0:
+        return
+    if K > 0 and ncols > 0:
         need = ngq_packed_bytes(K, ncols, int(bits) & 0xFF, group)
         if need == 0:
             raise ValueError(f"{where}: K={K}, columns={ncols}, bits={bits} is not a valid shape")
