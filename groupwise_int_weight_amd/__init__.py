@@ -31,6 +31,7 @@ NGQ_MAX_T = 8
 NGQ_MAX_T_VERIFY = 64  # several requests' verify rounds in one call
 NGQ_MAX_T_PREFILL = 16384  # ngq_gemm / ngq_swiglu_gemm
 NGQ_MAX_PROJ = 4
+NGQ_STATIC_SCRATCH_BYTES = 4 << 20  # ngq_gemm_splitk_static's partial-sum array per device
 NGQ_KERNEL_AUTO, NGQ_KERNEL_PERPAIR_DYN, NGQ_KERNEL_PERPAIR_STATIC, NGQ_KERNEL_XRES14, NGQ_KERNEL_XRES8 = 0, 1, 2, 3, 4
 NGQ_KERNEL_WIDE, NGQ_KERNEL_TILED, NGQ_KERNEL_TILED_SX, NGQ_KERNEL_TILED_SX96, NGQ_KERNEL_TILED_SX128 = 5, 6, 7, 8, 9
 
@@ -57,6 +58,7 @@ SIGNATURES = {
     "ngq_multi_gemm": (_INT, [_INT, _INT, _INT, _PTR, ctypes.POINTER(NgqProj), _INT, _PTR]),
     "ngq_splitk_workspace_bytes": (_SIZE, [_INT, _INT, _INT, _INT]),
     "ngq_gemm_splitk": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR, _SIZE, _PTR]),
+    "ngq_gemm_splitk_static": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR]),
     "ngq_rms_rescale": (_INT, [_INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_gemm_rescale": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR, _PTR, _SIZE, _PTR]),
     "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
@@ -254,6 +256,25 @@ def ngq_gemm_splitk(x, wq, scales, bits: int, N: int, y=None, workspace=None, gr
     return y
 
 
+def ngq_gemm_splitk_static(x, wq, scales, bits: int, N: int, y=None, group: int = NGQ_GROUP, stream=None):
+    """ngq_gemm_splitk with the partial sums in the library's fixed device
+    array (no allocation by the library; calls on one device must not
+    overlap).  `y` is allocated here when not given."""
+    import torch
+
+    T, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _check_operands("ngq_gemm_splitk_static", x, wq, scales, [(y, T, N)], K, N, bits, group)
+    st = lib().ngq_gemm_splitk_static(T, K, N, _format_bits(bits, scales), group, _dev_ptr(x, "x"),
+                                      _dev_ptr(wq, "wq"), _dev_ptr(scales, "scales"), _dev_ptr(y, "y"),
+                                      _stream(stream))
+    _check(st, "ngq_gemm_splitk_static")
+    return y
+
+
 def ngq_multi_gemm(x, projs, group: int = NGQ_GROUP, stream=None):
     """Several projections of the same x in one launch.  `projs` is a list of
     dicts with keys wq, scales, bits, n and optionally swiglu (False) and y;
@@ -365,6 +386,7 @@ def ngq_debug_force_kernel(path: int) -> int:
 
 __all__ = [
     "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_gemm_splitk", "ngq_splitk_workspace_bytes",
+    "ngq_gemm_splitk_static",
     "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
     "ngq_debug_force_kernel",
     "ngq_packed_bytes", "ngq_scale_bytes", "ngq_strerror", "ngq_version", "NgqError", "NgqLibraryMissing",

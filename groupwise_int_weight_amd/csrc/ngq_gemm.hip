@@ -2096,6 +2096,13 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0];
 }
 
+// The partial-sum area of ngq_gemm_splitk_static: a fixed array in device
+// memory (each device the library runs on holds its own copy for the life of
+// the process), for callers that cannot allocate.  Host code never passes its
+// name to a kernel: the device address comes from hipGetSymbolAddress.
+constexpr size_t kStaticScratchBytes = NGQ_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 }  // namespace dev
 
 // ---- host side: configuration and launch ------------------------------------
@@ -2932,6 +2939,55 @@ int run_splitk(int T, int K, int N, int bits, int group, const void* x, const vo
   return fuse ? ngq_rms_rescale(T, N, y, x_next, stream) : NGQ_OK;
 }
 
+// Device address of the static scratch array on the current device, looked up
+// once per device (with that device current) and kept; nullptr and the HIP
+// status on failure.
+void* static_scratch(hipError_t& err) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  err = hipGetDevice(&dev);
+  if (err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = ptrs[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(dev::scratch));
+    if (err != hipSuccess) return nullptr;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+int run_splitk_static(int T, int K, int N, int bits, int group, const void* x, const void* wq, const void* scales,
+                      void* y, void* stream) {
+  Format f;
+  int rc = parse_format(bits, group, &f);
+  if (rc != NGQ_OK) return rc;
+  if (T < 0 || T > NGQ_MAX_T) return NGQ_ERR_SHAPE;
+  if ((rc = check_kn(K, N)) != NGQ_OK) return rc;
+  if (T == 0 || N == 0) return NGQ_OK;
+  // the same split as ngq_gemm_splitk; the partial sums must fit the array
+  const int pairs = (K / kGroup + 1) / 2, ntiles = (N + 31) / 32;
+  const int S = choose_splits(T, K, pairs, ntiles, cu_count());
+  const size_t need = S > 1 ? (size_t)S * T * N * 4u : 0;
+  if (need > dev::kStaticScratchBytes) return NGQ_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (S > 1) {
+    hipError_t e;
+    ws = static_scratch(e);
+    if (ws == nullptr) return NGQ_ERR_HIP;
+  }
+  return run_splitk(T, K, N, bits, group, x, wq, scales, y, nullptr, ws, S > 1 ? dev::kStaticScratchBytes : 0,
+                    stream);
+}
+
 }  // namespace
 }  // namespace ngq
 
@@ -2961,6 +3017,11 @@ extern "C" size_t ngq_splitk_workspace_bytes(int K, int N, int bits, int group) 
 extern "C" int ngq_gemm_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq,
                                const void* scales, void* y, void* workspace, size_t workspace_bytes, void* stream) {
   return run_splitk(T, K, N, bits, group, x, wq, scales, y, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int ngq_gemm_splitk_static(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                                      const void* scales, void* y, void* stream) {
+  return run_splitk_static(T, K, N, bits, group, x, wq, scales, y, stream);
 }
 
 extern "C" int ngq_gemm_rescale(int T, int K, int N, int bits, int group, const void* x, const void* wq,

@@ -143,6 +143,27 @@ size_t ngq_splitk_workspace_bytes(int K, int N, int bits, int group);
 int ngq_gemm_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq,
                     const void* scales, void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ngq_gemm_splitk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, split and result bit for bit, with the fp32 partial sums
+ * in a fixed array of NGQ_STATIC_SCRATCH_BYTES in device memory that the
+ * library holds on each device it runs on until the process ends.  The call
+ * allocates nothing; the caller passes inputs and outputs as for
+ * ngq_gemm_splitk.
+ *  - The array's device address is looked up on a device's first call (a
+ *    HIP runtime query, no allocation).
+ *  - Where K is split, the partial sums take 8 * T * N * 4 bytes; beyond
+ *    NGQ_STATIC_SCRATCH_BYTES (T * N > 131072) the call returns
+ *    NGQ_ERR_UNSUPPORTED before any launch.  Unsplit calls need no scratch.
+ *  - Every call on one device shares that device's array: calls that may run
+ *    at the same time on one device (other streams, other threads) race and
+ *    must be ordered by the caller.  Nothing in the array needs to start at
+ *    zero: the split kernels write every partial sum they read.
+ * Shapes, formats and other status codes as ngq_gemm_splitk. */
+#define NGQ_STATIC_SCRATCH_BYTES (4u << 20)
+int ngq_gemm_splitk_static(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                           const void* scales, void* y, void* stream);
+
 /* Several projections of the same activations in one launch.  The
  * projections of a layer that read one x (in the stacked sweep: QK,
  * gate/value and the gate/up pair) are computed as one persistent kernel, so
