@@ -88,22 +88,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
 }
 
-template <int NW>
+// Cache policy of a buffer load (the instruction's aux bits): 0 default, or
+// kNT, the nontemporal hint, for data read once (weights and scales).  On
+// MI355X a weights-only stream of the QK tile pattern took 5.76 instead of
+// 6.02 us per 22 MB launch with it, the gate/value pattern 9.81 instead of
+// 10.06; the coherence-scope bits changed nothing.
+constexpr int kNT = 2;
+
+template <int NW, int AUX = 0>
 __device__ __forceinline__ void load_words(uint32_t* d, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (NW == 1) {
-    d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
   } else if constexpr (NW == 2) {
-    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
     d[0] = v[0]; d[1] = v[1];
   } else if constexpr (NW == 3) {
-    u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, AUX);
     d[0] = v[0]; d[1] = v[1]; d[2] = v[2];
   } else if constexpr (NW == 4) {
-    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
     d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
   } else {
-    load_words<4>(d, r, off);
-    load_words<NW - 4>(d + 4, r, off + 16u);
+    load_words<4, AUX>(d, r, off);
+    load_words<NW - 4, AUX>(d + 4, r, off + 16u);
   }
 }
 
@@ -977,6 +984,263 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
       pv, sh, ln, smem, rank, G, my_tiles, buf, false, [&]() { x_stage<XL, W>(smem, xv, a.T, a.K); },
       [](WBuf<BITS, V, NSETS>&, int) {},
       [&](const float* part, int c0) { finish_outputs<V, NSETS, W>(part, pv, a.T, c0); });
+}
+
+// ---- one round of tiles: each wave streams its own pairs ------------------------
+//
+// For shapes whose column tiles fill the CUs once (the QK projection: 256
+// tiles of 32 columns), a workgroup owns one tile and every group pair of it
+// is read by exactly one wave, so X needs no sharing between waves: wave w
+// takes pairs w, w + W, ... and loads each pair's X band (T rows of 128 k)
+// with the pair's weights and scales.  No workgroup-wide X prologue or
+// barrier stands before the weight stream, which starts with the kernel's
+// first loads.
+//
+// One pair is in flight per wave, and the next is requested as soon as the
+// current one has landed, before it is computed, so the compute of a pair
+// overlaps the next pair's round trip.  Measured on MI355X with the loads
+// alone, about 20-32 KB in flight per CU streams fastest (W = 10 pairs of
+// QK, 8 of gate/value; more in flight was slower), so the wave count, not a
+// deeper per-wave pipeline, sets the depth.  Weights and scales are read
+// with the nontemporal hint.
+//
+// X bands are loaded with as few lanes and bytes as T needs (each load's
+// lanes return data through the same path whether in range or not, and in
+// a load-only probe every X load added to the launch: 0.45 us for a single
+// 16-lane load per pair at T = 1):
+//   T = 1: one dword per lane (k 2l, 2l + 1 of the band);
+//   T = 2: two dwords per lane (token l / 32, k 4 (l % 32) .. + 3);
+//   T = 3, 4: one 16-byte load (token l / 16, k-block l % 16);
+//   T > 4: two 16-byte loads.
+// The band is written to a per-wave LDS slot in the interleaved k order of
+// the unpack: 16-bit stores to their places for T <= 2, one permute per
+// 4 bytes and 16-byte stores otherwise.
+template <int BITS, int V>
+struct StreamBuf {
+  static constexpr int WPK = BITS == 8 ? 2 : 1;
+  uint32_t a[4][V * WPK];             // [step][word]; int8: V words of row 2kb, then 2kb+1
+  uint32_t p1[2][BITS == 5 ? V : 1];  // int5 high-bit words, one per group of the pair
+  uint32_t sc[2 * V];                 // 4V scales (16-bit)
+  uint32_t x[2][4];                   // the pair's X band
+};
+
+// LDS of the streaming kernel: one X staging slot per wave (gemm_kernel's
+// layout), then one partial-sum block per wave.
+template <int W>
+struct StreamSmem {
+  static __host__ __device__ constexpr uint32_t bytes(int tile) {
+    return (uint32_t)W * Smem::XSLOT + (uint32_t)W * Smem::block_floats(1, tile) * 4u;
+  }
+};
+
+// LDS byte offset of element k (0..127) of a band's token row in the
+// interleaved order: each 8-k block holds k = 0, 4, 1, 5, 2, 6, 3, 7.
+__device__ __forceinline__ uint32_t il_offset(uint32_t k) {
+  return (k >> 3) * 16u + (2u * (k & 3u) + ((k >> 2) & 1u)) * 2u;
+}
+
+// XM: the X load class, 1 (T = 1), 2 (T = 2), 4 (T = 3, 4) or 8 (T > 4); a
+// template parameter so that no load sits under a branch (where the compiler
+// waits for it, and with it every older load, before the join)
+template <int BITS, bool SBF16, int V, int W, int XM>
+__global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
+  constexpr int WPK = BITS == 8 ? 2 : 1;
+  constexpr int TILE = 16 * V;
+  constexpr uint32_t XROW = Smem::XROW, XZERO = Smem::XZERO;
+  constexpr uint32_t BLK = Smem::block_floats(1, TILE);
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* const part = reinterpret_cast<float*>(smem + (uint32_t)W * Smem::XSLOT);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, q = lane >> 4;
+  const int t = m & 7, h = m >> 3;  // B slot m: token t of group half h
+
+  // consecutive tiles on one XCD (workgroup b runs on XCD b % 8)
+  const int b = blockIdx.x;
+  const int xcd = b & 7, per = a.ntiles >> 3, rem = a.ntiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
+  const uint32_t c0 = (uint32_t)(tile * TILE);
+
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  uint32_t vbase = a.mask_base;
+  asm volatile("" : "+v"(vbase));
+  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
+
+  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
+  // k-slot q of step st reads k-block 2 st + (q & 1) of group (q >> 1)
+  const uint32_t lane_kb = 8u * (uint32_t)(q >> 1) + (uint32_t)(q & 1);
+  const uint32_t col = c0 + (uint32_t)(V * m);
+  const uint32_t offA = lane_kb * WPK * rowb + col * 4u;
+  const uint32_t offP1 = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
+  // result rows 4q..4q+3 of every MFMA -> columns c0 + 4Vq + [0, 4V)
+  const uint32_t offS = (uint32_t)h * (uint32_t)a.Ncols * 2u + (c0 + (uint32_t)(4 * V * q)) * 2u;
+
+  // This lane's share of a band: token row xt, first element xk (of the
+  // band's 128), xe elements; chunk loads (T > 2) take 8 elements from rows
+  // xt and xt + 4.
+  const int T = a.T;
+  constexpr int xmode = XM;
+  const int xt = xmode == 1 ? 0 : (xmode == 2 ? lane >> 5 : lane >> 4);
+  const int xk = xmode == 1 ? 2 * lane : (xmode == 2 ? 4 * (lane & 31) : 8 * (lane & 15));
+  const uint32_t offX = (uint32_t)xt * (uint32_t)a.K * 2u + (uint32_t)xk * 2u;
+  const uint32_t rowX4 = 4u * (uint32_t)a.K * 2u;
+  const bool x0_on = xt < T, x1_on = xt + 4 < T;
+  uint8_t* const xslot = smem + (uint32_t)wave * Smem::XSLOT;
+  const uint32_t xdst = (uint32_t)xt * XROW + il_offset((uint32_t)xk);  // T <= 2: first element
+  // B fragment source in the slot: this lane's token row at its k-slot, or
+  // the zero block
+  const bool b_on = (q >> 1) == h;
+  const uint32_t bsrc = b_on ? (uint32_t)t * XROW + lane_kb * 16u : 8u * XROW;
+  if (lane < XZERO / 16) *reinterpret_cast<u32x4*>(xslot + 8 * XROW + 16u * (uint32_t)lane) = u32x4{0u, 0u, 0u, 0u};
+  // rows t >= T of the slot are read by the lanes of those tokens and must
+  // hold zeros; rows no load covers (T <= 2: rows T..7, T <= 4: rows 4..7)
+  // are cleared once here, the others are written with every band
+  if constexpr (xmode <= 4) {
+    for (int r = T; r < 8; ++r) *reinterpret_cast<uint32_t*>(xslot + (uint32_t)r * XROW + 4u * (uint32_t)lane) = 0u;
+  }
+
+  auto pair_of = [&](int i) { return wave + W * i; };
+
+  // the loads of pair p (p >= pairs: out of range, nothing moves); flags are
+  // combined bitwise so that no lane-divergent branch appears
+  auto issue = [&](StreamBuf<BITS, V>& buf, int p) {
+    const bool valid = p < a.pairs;
+    const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb : kOOB;
+    const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb : kOOB;
+    const uint32_t ps = valid ? (uint32_t)p * rowb : kOOB;  // two scale rows of 2-byte entries
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint32_t o = offA + pa + (uint32_t)st * 2u * WPK * rowb;
+      load_words<V, kNT>(&buf.a[st][0], rW, o);
+      if constexpr (BITS == 8) load_words<V, kNT>(&buf.a[st][V], rW, o + rowb);
+    }
+    if constexpr (BITS == 5) {
+      load_words<V, kNT>(&buf.p1[0][0], rP1, offP1 + pp1);
+      load_words<V, kNT>(&buf.p1[1][0], rP1, offP1 + pp1 + rowb);
+    }
+    load_words<2 * V, kNT>(&buf.sc[0], rS, offS + ps);
+    // the band: the second group of the last pair of an odd group count
+    // does not exist (elements 64..127 of its band read nothing)
+    const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
+    const bool xin = valid & !(half & (xk >= 64));
+    const uint32_t px0 = (xin & x0_on) ? (uint32_t)p * 256u + offX : kOOB;
+    if constexpr (xmode == 1) {
+      load_words<1>(&buf.x[0][0], rX, px0);
+    } else if constexpr (xmode == 2) {
+      load_words<2>(&buf.x[0][0], rX, px0);
+    } else {
+      load_words<4>(&buf.x[0][0], rX, px0);
+      if constexpr (xmode == 8)
+        load_words<4>(&buf.x[1][0], rX, (xin & x1_on) ? (uint32_t)p * 256u + offX + rowX4 : kOOB);
+    }
+  };
+
+  // the landed band of a pair into the slot (the previous pair's B fragments
+  // have been read: LDS is in order within a wave)
+  auto stage_x = [&](const StreamBuf<BITS, V>& buf) {
+    if constexpr (xmode <= 2) {
+      uint16_t* const d = reinterpret_cast<uint16_t*>(xslot + xdst);
+      // element xk + e sits il_offset(xk + e) - il_offset(xk) bytes on: xk is
+      // a multiple of 2 (T = 1) or 4 (T = 2) within an 8-k block
+      d[0] = (uint16_t)buf.x[0][0];
+      d[2] = (uint16_t)(buf.x[0][0] >> 16);
+      if constexpr (xmode == 2) {
+        d[4] = (uint16_t)buf.x[0][1];
+        d[6] = (uint16_t)(buf.x[0][1] >> 16);
+      }
+    } else {
+      *reinterpret_cast<u32x4*>(xslot + (uint32_t)xt * XROW + (uint32_t)(xk >> 3) * 16u) = interleave_x(buf.x[0]);
+      if constexpr (xmode == 8)
+        *reinterpret_cast<u32x4*>(xslot + (uint32_t)(xt + 4) * XROW + (uint32_t)(xk >> 3) * 16u) =
+            interleave_x(buf.x[1]);
+    }
+  };
+
+  f32x4 acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
+                        Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
+
+  // one pair: its B fragments from the slot, multiply, scale into the
+  // accumulators
+  auto compute = [&](const StreamBuf<BITS, V>& buf) {
+    bf16x8 bfrag[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      bfrag[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xslot + bsrc + (uint32_t)st * 32u));
+    f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfrag[st], dx, 0, 0, 0);
+    f32x4 dp[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) dp[i] = dx;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        u32x4 av;
+        if constexpr (BITS == 4) {
+          av = nibbles_to_bf16_il(buf.a[st][i], mk);
+        } else if constexpr (BITS == 5) {
+          const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[st >> 1][i], 16u * (uint32_t)(st & 1) +
+                                                                           8u * (uint32_t)(q & 1), 8u);
+          av = nibbles5_to_bf16_il(buf.a[st][i], hb, mk);
+        } else {
+          av = bytes_to_bf16_il(buf.a[st][i], buf.a[st][V + i]);
+        }
+        dp[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag[st], dp[i], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = V * r + i;
+        acc[i][r] = __builtin_fmaf(scale_to_f32(buf.sc[e >> 1], e & 1, SBF16), dp[i][r], acc[i][r]);
+      }
+  };
+
+  // Pair slot i of this wave is pair wave + W i.  Two buffers: once slot i
+  // has landed, slot i + 1 is requested, then slot i is computed.  A slot
+  // past the last pair loads nothing and is not computed.
+  StreamBuf<BITS, V> buf[2];
+  issue(buf[0], pair_of(0));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < a.ppw; i += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    stage_x(buf[0]);
+    issue(buf[1], pair_of(i + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if (pair_of(i) < a.pairs) compute(buf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    stage_x(buf[1]);
+    issue(buf[0], pair_of(i + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    if (pair_of(i + 1) < a.pairs) compute(buf[1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // the two group halves of each token (slots j, j + 8), then the wave
+  // blocks summed in wave order
+  f32x4 accs[1][V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) accs[0][i] = acc[i];
+  XresLane ln;
+  ln.t = t;
+  ln.q = q;
+  ln.h = h;
+  store_partials<V, 1>(accs, ln, part + (uint32_t)wave * BLK);
+  lds_barrier();
+  const ProjView pv{a.wq, a.scales, a.y, a.p0_bytes, a.p1_bytes, a.s_bytes, a.Nout, a.Ncols, a.up_off};
+  finish_outputs<V, 1, W>(part, pv, a.T, (int)c0);
 }
 
 // ---- several projections of one X in one launch ----------------------------
@@ -2285,6 +2549,36 @@ hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, uint32_t l
   return f.scale_bf16 ? launch_v<8, true, NSETS, DYN>(v, a, lds, st) : launch_v<8, false, NSETS, DYN>(v, a, lds, st);
 }
 
+// The streaming single-round kernel: 10 waves, 32-column tiles (16 where N
+// is narrower), one workgroup per tile (LDS under 64 KiB); the X load class
+// follows T.
+constexpr int kStreamW = 10;
+template <int BITS, bool SBF16, int V>
+hipError_t launch_stream_v(const dev::GemmArgs& a, hipStream_t st) {
+  auto one = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(kStreamW * 64), dev::StreamSmem<kStreamW>::bytes(16 * V),
+                       st, a);
+    return hipGetLastError();
+  };
+  if (a.T == 1) return one(dev::gemm_stream_kernel<BITS, SBF16, V, kStreamW, 1>);
+  if (a.T == 2) return one(dev::gemm_stream_kernel<BITS, SBF16, V, kStreamW, 2>);
+  if (a.T <= 4) return one(dev::gemm_stream_kernel<BITS, SBF16, V, kStreamW, 4>);
+  return one(dev::gemm_stream_kernel<BITS, SBF16, V, kStreamW, 8>);
+}
+static_assert(dev::StreamSmem<kStreamW>::bytes(32) <= 64u * 1024u,
+              "the streaming kernel's LDS stays under the default 64 KiB limit");
+
+template <int BITS, bool SBF16>
+hipError_t launch_stream_b(int v, const dev::GemmArgs& a, hipStream_t st) {
+  return v >= 2 ? launch_stream_v<BITS, SBF16, 2>(a, st) : launch_stream_v<BITS, SBF16, 1>(a, st);
+}
+
+hipError_t launch_stream(const Format& f, int v, const dev::GemmArgs& a, hipStream_t st) {
+  if (f.bits == 4) return f.scale_bf16 ? launch_stream_b<4, true>(v, a, st) : launch_stream_b<4, false>(v, a, st);
+  if (f.bits == 5) return f.scale_bf16 ? launch_stream_b<5, true>(v, a, st) : launch_stream_b<5, false>(v, a, st);
+  return f.scale_bf16 ? launch_stream_b<8, true>(v, a, st) : launch_stream_b<8, false>(v, a, st);
+}
+
 // Shared validation and launch of ngq_gemm (nsets 1) and ngq_swiglu_gemm (2).
 // ---- many tokens (host) ----
 
@@ -2520,9 +2814,12 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   };
   const XCfg x8 = xchunks <= (long)kX8a.XL * kX8a.W * 64 ? kX8a : kX8b;
   // Kernel choice (measured on MI355X):
-  //  - one round of tiles, one output set and the per-pair-X kernel's blocks
-  //    fit in LDS: per-pair X with dynamic pair assignment, except for
-  //    32-column tiles, where 14 waves of the X-resident kernel are faster;
+  //  - one round of 32-column tiles and one output set: the streaming
+  //    kernel for int4 and int5 (QK, T = 1..8: 6.5-7.4 us against 7.4-7.9
+  //    for the 14-wave X-resident kernel), the X-resident kernel for int8
+  //    (equal times); other one-round shapes: per-pair X with dynamic pair
+  //    assignment (gate/value: 48-column tiles, where the streaming kernel's
+  //    int5 unpack did not keep up);
   //  - otherwise the X-resident kernel with 8 waves when X fits in LDS;
   //  - otherwise per-pair X (dynamic, or static ranges for very long K).
   int path = forced;
@@ -2531,7 +2828,9 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   uint32_t lx = 0;
   if (path == NGQ_KERNEL_AUTO) {
     const bool one_round = nsets == 1 && tiles_pp <= cus && pp_dyn_fits;
-    if (one_round && v_pp == 2 && xres_fits(kX14, vx, lx))
+    if (one_round && v_pp == 2 && f.bits != 8 && K > 0)
+      path = NGQ_KERNEL_STREAM;
+    else if (one_round && v_pp == 2 && xres_fits(kX14, vx, lx))
       path = NGQ_KERNEL_XRES14;
     else if (!one_round && xres_fits(x8, vx, lx))
       path = NGQ_KERNEL_XRES8;
@@ -2541,6 +2840,8 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     if (!xres_fits(path == NGQ_KERNEL_XRES14 ? kX14 : x8, vx, lx)) return NGQ_ERR_UNSUPPORTED;
   } else if (path == NGQ_KERNEL_PERPAIR_DYN && !pp_dyn_fits) {
     return NGQ_ERR_UNSUPPORTED;
+  } else if (path == NGQ_KERNEL_STREAM && nsets != 1) {
+    return NGQ_ERR_UNSUPPORTED;  // no SwiGLU epilogue
   }
   const bool xres = path == NGQ_KERNEL_XRES14 || path == NGQ_KERNEL_XRES8;
   if (xres) {
@@ -2559,6 +2860,13 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
+  if (path == NGQ_KERNEL_STREAM) {
+    const int vs = Nout >= 32 ? 2 : 1;
+    a.ntiles = (Nout + 16 * vs - 1) / (16 * vs);
+    a.ppw = (a.pairs + kStreamW - 1) / kStreamW;
+    e = launch_stream(f, vs, a, st);
+    return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+  }
   if (xres) {
     const int per = (a.pairs + xc.W - 1) / xc.W;
     a.ppw = (per + xc.NB - 1) / xc.NB * xc.NB;
@@ -3055,6 +3363,6 @@ extern "C" int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* 
 }
 
 extern "C" int ngq_debug_force_kernel(int path) {
-  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_TILED_SX128) return NGQ_ERR_ARG;
+  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_STREAM) return NGQ_ERR_ARG;
   return kernel_override.exchange(path);
 }

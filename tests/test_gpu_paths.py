@@ -19,7 +19,7 @@ from tests.test_gpu_parity import dev_bf16, dev_scales, dev_u8, host_bits, make
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-PATHS = {1: "perpair_dyn", 2: "perpair_static", 3: "xres14", 4: "xres8"}
+PATHS = {1: "perpair_dyn", 2: "perpair_static", 3: "xres14", 4: "xres8", 10: "stream"}
 
 
 @pytest.fixture(scope="module")
@@ -51,8 +51,13 @@ def forced(ngq, request):
 # reason; a case of None stands for every case of that entry point
 UNSUPPORTED = {
     ("xres14", "swiglu", None): "the 14-wave X-resident kernel has no SwiGLU epilogue",
+    ("stream", "swiglu", None): "the streaming kernel has no SwiGLU epilogue",
     ("perpair_dyn", "gemm", (4, True, 2, 17408, 64)):
         "one partial-sum block per pair (136 pairs at K = 17408) does not fit in LDS",
+    ("perpair_dyn", "gemm", (8, False, 8, 17408, 96)): "the same",
+    ("xres14", "gemm", (4, False, 8, 9216, 64)): "X exceeds the 14-wave kernel's prologue (6 chunks a thread)",
+    ("xres14", "gemm", (8, False, 8, 17408, 96)): "the same",
+    ("xres8", "gemm", (8, False, 8, 17408, 96)): "X (278 KB at T = 8) does not fit in LDS",
 }
 
 
@@ -79,6 +84,8 @@ GEMM_CASES = [
     (4, True, 2, 17408, 64),     # long K
     (4, False, 8, 192, 520),
     (5, True, 7, 256, 16416),    # 513 tiles of 32 columns: several tiles per workgroup
+    (4, False, 8, 9216, 64),     # X just fits in LDS: resident X staged in two rounds (streaming kernel)
+    (8, False, 8, 17408, 96),    # X does not fit in LDS: X per pair (streaming kernel)
 ]
 
 
