@@ -34,7 +34,7 @@ NGQ_MAX_PROJ = 4
 NGQ_STATIC_SCRATCH_BYTES = 4 << 20  # ngq_gemm_splitk_static's partial-sum array per device
 NGQ_KERNEL_AUTO, NGQ_KERNEL_PERPAIR_DYN, NGQ_KERNEL_PERPAIR_STATIC, NGQ_KERNEL_XRES14, NGQ_KERNEL_XRES8 = 0, 1, 2, 3, 4
 NGQ_KERNEL_WIDE, NGQ_KERNEL_TILED, NGQ_KERNEL_TILED_SX, NGQ_KERNEL_TILED_SX96, NGQ_KERNEL_TILED_SX128 = 5, 6, 7, 8, 9
-NGQ_KERNEL_STREAM = 10
+NGQ_KERNEL_STREAM, NGQ_KERNEL_DOT = 10, 11
 
 # Every function the header declares, with its ctypes signature.
 _SIZE = ctypes.c_size_t

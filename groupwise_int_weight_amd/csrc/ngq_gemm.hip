@@ -58,6 +58,7 @@ namespace ngq {
 namespace dev {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
@@ -172,6 +173,10 @@ __device__ __forceinline__ u32x4 interleave_x(const uint32_t (&d)[4]) {
   return u32x4{__builtin_amdgcn_perm(d[2], d[0], 0x05040100u), __builtin_amdgcn_perm(d[2], d[0], 0x07060302u),
                __builtin_amdgcn_perm(d[3], d[1], 0x05040100u), __builtin_amdgcn_perm(d[3], d[1], 0x07060302u)};
 }
+
+// Two bf16 in a dword.  Taken by value: hipcc turned __builtin_bit_cast of a
+// vector element (v[j] of an ext_vector) into a read of element 0.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 
 template <int BITS>
 struct Code {
@@ -1241,6 +1246,237 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
   lds_barrier();
   const ProjView pv{a.wq, a.scales, a.y, a.p0_bytes, a.p1_bytes, a.s_bytes, a.Nout, a.Ncols, a.up_off};
   finish_outputs<V, 1, W>(part, pv, a.T, (int)c0);
+}
+
+// ---- the same stream with a VALU inner step ---------------------------------
+//
+// gemm_dot_kernel is gemm_stream_kernel's pipeline (one 32-column tile per
+// workgroup, pair w + W i on wave w, one pair in flight per wave, X band per
+// pair) with the multiply-add on the vector ALU instead of the matrix cores:
+// lane (c, g) owns column c0 + c and group g of every pair, unpacks its 8
+// words per pair into bf16 pairs (the value 128 + u) and accumulates
+// v_dot2_f32_bf16 products against X read from LDS (one address per half
+// wave: a broadcast).  The offset (128 + bias) sum x of each group and token
+// is reduced from the pair's X band across the lanes that hold it (DPP row
+// shifts) and subtracted before scaling.  It exists to measure the VALU
+// against the MFMA inner step per bit width and T.
+template <int W>
+struct DotSmem {
+  static constexpr uint32_t SX = 16u * 4u;  // per wave: sums of x per (token, group) or per 16-lane row
+  static __host__ __device__ constexpr uint32_t sx_off() { return (uint32_t)W * Smem::XSLOT; }
+  static __host__ __device__ constexpr uint32_t part_off() { return sx_off() + (uint32_t)W * SX; }
+  static __host__ __device__ constexpr uint32_t bytes() { return part_off() + (uint32_t)W * 2u * 8u * 32u * 4u; }
+};
+
+template <int BITS>
+struct DotBuf {
+  static constexpr int WPK = BITS == 8 ? 2 : 1;
+  uint32_t a[8 * WPK];  // one word per k-block of the lane's group (int8: two)
+  uint32_t p1[BITS == 5 ? 2 : 1];
+  uint32_t sc;          // the lane's scale (16-bit)
+  uint32_t x[2][4];     // the pair's X band (the streaming kernel's load classes)
+};
+
+template <int BITS, bool SBF16, int W, int XM>
+__global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
+  constexpr int WPK = BITS == 8 ? 2 : 1;
+  constexpr uint32_t XROW = Smem::XROW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 31, g = lane >> 5;  // column of the tile, group of the pair
+
+  const int b = blockIdx.x;
+  const int xcd = b & 7, per = a.ntiles >> 3, rem = a.ntiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
+  const uint32_t c0 = (uint32_t)(tile * 32);
+
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  uint32_t vbase = a.mask_base;
+  asm volatile("" : "+v"(vbase));
+  const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
+
+  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
+  const uint32_t colb = (c0 + (uint32_t)c) * 4u;
+  const uint32_t offW = 8u * (uint32_t)g * WPK * rowb + colb;      // k-block 0 of the lane's group
+  const uint32_t offP1 = 2u * (uint32_t)g * rowb + colb;
+  const uint32_t offS = (uint32_t)g * (uint32_t)a.Ncols * 2u + (c0 + (uint32_t)c) * 2u;
+
+  // the X band, as in gemm_stream_kernel
+  const int T = a.T;
+  constexpr int xmode = XM;
+  const int xt = xmode == 1 ? 0 : (xmode == 2 ? lane >> 5 : lane >> 4);
+  const int xk = xmode == 1 ? 2 * lane : (xmode == 2 ? 4 * (lane & 31) : 8 * (lane & 15));
+  const uint32_t offX = (uint32_t)xt * (uint32_t)a.K * 2u + (uint32_t)xk * 2u;
+  const uint32_t rowX4 = 4u * (uint32_t)a.K * 2u;
+  const bool x0_on = xt < T, x1_on = xt + 4 < T;
+  uint8_t* const xslot = smem + (uint32_t)wave * Smem::XSLOT;
+  float* const sxw = reinterpret_cast<float*>(smem + DotSmem<W>::sx_off() + (uint32_t)wave * DotSmem<W>::SX);
+  const uint32_t xdst = (uint32_t)xt * XROW + il_offset((uint32_t)xk);
+
+  auto pair_of = [&](int i) { return wave + W * i; };
+
+  auto issue = [&](DotBuf<BITS>& buf, int p) {
+    const bool valid = p < a.pairs;
+    const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
+    const bool gin = valid & !(half & (g == 1));  // the lane's group exists
+    const uint32_t pa = gin ? (uint32_t)p * 16u * WPK * rowb + offW : kOOB;
+#pragma unroll
+    for (int kb = 0; kb < 8 * WPK; ++kb) load_words<1, kNT>(&buf.a[kb], rW, pa + (uint32_t)kb * rowb);
+    if constexpr (BITS == 5) {
+      const uint32_t pp1 = gin ? (uint32_t)p * 4u * rowb + offP1 : kOOB;
+      load_words<1, kNT>(&buf.p1[0], rP1, pp1);
+      load_words<1, kNT>(&buf.p1[1], rP1, pp1 + rowb);
+    }
+    buf.sc = __builtin_amdgcn_raw_buffer_load_b16(rS, gin ? (uint32_t)p * rowb + offS : kOOB, 0, kNT);
+    const bool xin = valid & !(half & (xk >= 64));
+    const uint32_t px0 = (xin & x0_on) ? (uint32_t)p * 256u + offX : kOOB;
+    if constexpr (xmode == 1) {
+      load_words<1>(&buf.x[0][0], rX, px0);
+    } else if constexpr (xmode == 2) {
+      load_words<2>(&buf.x[0][0], rX, px0);
+    } else {
+      load_words<4>(&buf.x[0][0], rX, px0);
+      if constexpr (xmode == 8)
+        load_words<4>(&buf.x[1][0], rX, (xin & x1_on) ? (uint32_t)p * 256u + offX + rowX4 : kOOB);
+    }
+  };
+
+  // the landed band into the slot, and the sums of x per (token, group):
+  // each lane's share, then a segmented sum over the lanes of one (token,
+  // group) with DPP row shifts (8 lanes a segment for 16-byte chunks, 16 for
+  // T = 2; for T = 1 the two 16-lane rows of a group are added by the reader)
+  const uint32_t ones = 0x3F803F80u;  // bf16 (1, 1)
+  auto stage_x = [&](const DotBuf<BITS>& buf) {
+    float s0 = 0.f, s1 = 0.f;
+    if constexpr (xmode <= 2) {
+      uint16_t* const d = reinterpret_cast<uint16_t*>(xslot + xdst);
+      d[0] = (uint16_t)buf.x[0][0];
+      d[2] = (uint16_t)(buf.x[0][0] >> 16);
+      s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(buf.x[0][0]),
+                                            as_bf16x2(ones), 0.f, false);
+      if constexpr (xmode == 2) {
+        d[4] = (uint16_t)buf.x[0][1];
+        d[6] = (uint16_t)(buf.x[0][1] >> 16);
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(buf.x[0][1]),
+                                              as_bf16x2(ones), s0, false);
+      }
+    } else {
+      *reinterpret_cast<u32x4*>(xslot + (uint32_t)xt * XROW + (uint32_t)(xk >> 3) * 16u) = interleave_x(buf.x[0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(buf.x[0][j]),
+                                              as_bf16x2(ones), s0, false);
+      if constexpr (xmode == 8) {
+        *reinterpret_cast<u32x4*>(xslot + (uint32_t)(xt + 4) * XROW + (uint32_t)(xk >> 3) * 16u) =
+            interleave_x(buf.x[1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(buf.x[1][j]),
+                                                as_bf16x2(ones), s1, false);
+      }
+    }
+    constexpr int seg = xmode >= 4 ? 8 : 16;
+    // row_shr:1, 2, 4 (and 8): lane i then holds the sum of lanes i - seg + 1 .. i of its row
+    s0 += __builtin_amdgcn_update_dpp(0.f, s0, 0x111, 0xF, 0xF, true);
+    s0 += __builtin_amdgcn_update_dpp(0.f, s0, 0x112, 0xF, 0xF, true);
+    s0 += __builtin_amdgcn_update_dpp(0.f, s0, 0x114, 0xF, 0xF, true);
+    if constexpr (seg == 16) s0 += __builtin_amdgcn_update_dpp(0.f, s0, 0x118, 0xF, 0xF, true);
+    if constexpr (xmode == 8) {
+      s1 += __builtin_amdgcn_update_dpp(0.f, s1, 0x111, 0xF, 0xF, true);
+      s1 += __builtin_amdgcn_update_dpp(0.f, s1, 0x112, 0xF, 0xF, true);
+      s1 += __builtin_amdgcn_update_dpp(0.f, s1, 0x114, 0xF, 0xF, true);
+    }
+    if ((lane & (seg - 1)) == seg - 1) {
+      if constexpr (xmode >= 4) {
+        const int gg = (lane >> 3) & 1;  // lanes 0..7 of a row: group 0
+        sxw[xt * 2 + gg] = s0;
+        if constexpr (xmode == 8) sxw[(xt + 4) * 2 + gg] = s1;
+      } else {
+        sxw[lane >> 4] = s0;  // row r: T = 2 token r / 2, group r % 2; T = 1 group r / 2
+      }
+    }
+  };
+  auto sum_x = [&](int t) -> float {
+    if constexpr (xmode == 1) return sxw[2 * g] + sxw[2 * g + 1];
+    return sxw[t * 2 + g];
+  };
+
+  float acc[XM];
+#pragma unroll
+  for (int t = 0; t < XM; ++t) acc[t] = 0.f;
+
+  auto compute = [&](const DotBuf<BITS>& buf) {
+    float pacc[XM];
+#pragma unroll
+    for (int t = 0; t < XM; ++t) pacc[t] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      u32x4 w;
+      if constexpr (BITS == 4) {
+        w = nibbles_to_bf16_il(buf.a[kb], mk);
+      } else if constexpr (BITS == 5) {
+        w = nibbles5_to_bf16_il(buf.a[kb], __builtin_amdgcn_ubfe(buf.p1[kb >> 2], 8u * (uint32_t)(kb & 3), 8u), mk);
+      } else {
+        w = bytes_to_bf16_il(buf.a[2 * kb], buf.a[2 * kb + 1]);
+      }
+#pragma unroll
+      for (int t = 0; t < XM; ++t) {
+        if (t < T) {
+          const u32x4 xr = *reinterpret_cast<const u32x4*>(xslot + (uint32_t)t * XROW + (uint32_t)(8 * g + kb) * 16u);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pacc[t] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[j]), as_bf16x2(xr[j]), pacc[t], false);
+        }
+      }
+    }
+    const float sc = scale_to_f32(buf.sc, 0, SBF16);
+#pragma unroll
+    for (int t = 0; t < XM; ++t)
+      if (t < T) acc[t] = __builtin_fmaf(sc, pacc[t] - (float)Code<BITS>::offset * sum_x(t), acc[t]);
+  };
+
+  DotBuf<BITS> buf[2];
+  issue(buf[0], pair_of(0));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < a.ppw; i += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    stage_x(buf[0]);
+    issue(buf[1], pair_of(i + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if (pair_of(i) < a.pairs) compute(buf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    stage_x(buf[1]);
+    issue(buf[0], pair_of(i + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    if (pair_of(i + 1) < a.pairs) compute(buf[1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // partial sums [wave][group][token][column], added in wave then group
+  // order
+  float* const part = reinterpret_cast<float*>(smem + DotSmem<W>::part_off());
+#pragma unroll
+  for (int t = 0; t < XM; ++t)
+    if (t < T) part[(((uint32_t)wave * 2u + (uint32_t)g) * 8u + (uint32_t)t) * 32u + (uint32_t)c] = acc[t];
+  lds_barrier();
+  uint16_t* y = static_cast<uint16_t*>(a.y);
+  for (int idx = threadIdx.x; idx < 8 * 32; idx += W * 64) {
+    const int tt = idx >> 5, cc = idx & 31;
+    if (tt >= T || c0 + (uint32_t)cc >= (uint32_t)a.Nout) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      sum += part[(((uint32_t)w * 2u) * 8u + (uint32_t)tt) * 32u + (uint32_t)cc];
+      sum += part[(((uint32_t)w * 2u + 1u) * 8u + (uint32_t)tt) * 32u + (uint32_t)cc];
+    }
+    y[(size_t)tt * a.Nout + c0 + cc] = f32_to_bf16_rne(sum);
+  }
 }
 
 // ---- several projections of one X in one launch ----------------------------
@@ -2579,6 +2815,27 @@ hipError_t launch_stream(const Format& f, int v, const dev::GemmArgs& a, hipStre
   return f.scale_bf16 ? launch_stream_b<8, true>(v, a, st) : launch_stream_b<8, false>(v, a, st);
 }
 
+// The VALU-inner-step kernel (measurement path): the streaming kernel's
+// pipeline and tiles (32 columns, 10 waves).
+template <int BITS, bool SBF16>
+hipError_t launch_dot_b(const dev::GemmArgs& a, hipStream_t st) {
+  auto one = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(kStreamW * 64), dev::DotSmem<kStreamW>::bytes(), st, a);
+    return hipGetLastError();
+  };
+  if (a.T == 1) return one(dev::gemm_dot_kernel<BITS, SBF16, kStreamW, 1>);
+  if (a.T == 2) return one(dev::gemm_dot_kernel<BITS, SBF16, kStreamW, 2>);
+  if (a.T <= 4) return one(dev::gemm_dot_kernel<BITS, SBF16, kStreamW, 4>);
+  return one(dev::gemm_dot_kernel<BITS, SBF16, kStreamW, 8>);
+}
+static_assert(dev::DotSmem<kStreamW>::bytes() <= 64u * 1024u, "the VALU kernel's LDS stays under 64 KiB");
+
+hipError_t launch_dot(const Format& f, const dev::GemmArgs& a, hipStream_t st) {
+  if (f.bits == 4) return f.scale_bf16 ? launch_dot_b<4, true>(a, st) : launch_dot_b<4, false>(a, st);
+  if (f.bits == 5) return f.scale_bf16 ? launch_dot_b<5, true>(a, st) : launch_dot_b<5, false>(a, st);
+  return f.scale_bf16 ? launch_dot_b<8, true>(a, st) : launch_dot_b<8, false>(a, st);
+}
+
 // Shared validation and launch of ngq_gemm (nsets 1) and ngq_swiglu_gemm (2).
 // ---- many tokens (host) ----
 
@@ -2814,10 +3071,13 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   };
   const XCfg x8 = xchunks <= (long)kX8a.XL * kX8a.W * 64 ? kX8a : kX8b;
   // Kernel choice (measured on MI355X):
-  //  - one round of 32-column tiles and one output set: the streaming
-  //    kernel for int4 and int5 (QK, T = 1..8: 6.5-7.4 us against 7.4-7.9
-  //    for the 14-wave X-resident kernel), the X-resident kernel for int8
-  //    (equal times); other one-round shapes: per-pair X with dynamic pair
+  //  - one round of 32-column tiles and one output set: at T = 1 the VALU
+  //    inner step for int4 and int8 (QK shape: 6.39 against 6.52 us with the
+  //    MFMA step, int8 10.71 against 10.92; from T = 2 the MFMA step wins,
+  //    by 27 % at T = 2 and 2.7x at T = 8), otherwise the streaming kernel
+  //    for int4 and int5 (QK, T = 2..8: 6.5-7.4 us against 7.4-7.9 for the
+  //    14-wave X-resident kernel) and the X-resident kernel for int8 (equal
+  //    times); other one-round shapes: per-pair X with dynamic pair
   //    assignment (gate/value: 48-column tiles, where the streaming kernel's
   //    int5 unpack did not keep up);
   //  - otherwise the X-resident kernel with 8 waves when X fits in LDS;
@@ -2828,7 +3088,9 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   uint32_t lx = 0;
   if (path == NGQ_KERNEL_AUTO) {
     const bool one_round = nsets == 1 && tiles_pp <= cus && pp_dyn_fits;
-    if (one_round && v_pp == 2 && f.bits != 8 && K > 0)
+    if (one_round && v_pp == 2 && T == 1 && f.bits != 5 && K > 0)
+      path = NGQ_KERNEL_DOT;
+    else if (one_round && v_pp == 2 && f.bits != 8 && K > 0)
       path = NGQ_KERNEL_STREAM;
     else if (one_round && v_pp == 2 && xres_fits(kX14, vx, lx))
       path = NGQ_KERNEL_XRES14;
@@ -2840,7 +3102,7 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     if (!xres_fits(path == NGQ_KERNEL_XRES14 ? kX14 : x8, vx, lx)) return NGQ_ERR_UNSUPPORTED;
   } else if (path == NGQ_KERNEL_PERPAIR_DYN && !pp_dyn_fits) {
     return NGQ_ERR_UNSUPPORTED;
-  } else if (path == NGQ_KERNEL_STREAM && nsets != 1) {
+  } else if ((path == NGQ_KERNEL_STREAM || path == NGQ_KERNEL_DOT) && nsets != 1) {
     return NGQ_ERR_UNSUPPORTED;  // no SwiGLU epilogue
   }
   const bool xres = path == NGQ_KERNEL_XRES14 || path == NGQ_KERNEL_XRES8;
@@ -2860,6 +3122,12 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
+  if (path == NGQ_KERNEL_DOT) {
+    a.ntiles = (Nout + 31) / 32;
+    a.ppw = (a.pairs + kStreamW - 1) / kStreamW;
+    e = launch_dot(f, a, st);
+    return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+  }
   if (path == NGQ_KERNEL_STREAM) {
     const int vs = Nout >= 32 ? 2 : 1;
     a.ntiles = (Nout + 16 * vs - 1) / (16 * vs);
@@ -3363,6 +3631,6 @@ extern "C" int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* 
 }
 
 extern "C" int ngq_debug_force_kernel(int path) {
-  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_STREAM) return NGQ_ERR_ARG;
+  if (path < NGQ_KERNEL_AUTO || path > NGQ_KERNEL_DOT) return NGQ_ERR_ARG;
   return kernel_override.exchange(path);
 }

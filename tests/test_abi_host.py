@@ -265,7 +265,7 @@ def test_force_kernel_roundtrip(ngq):
     """The kernel-path override is host state only: set, read back, reject."""
     prev = ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_XRES8)
     assert ngq.ngq_debug_force_kernel(prev) == ngq.NGQ_KERNEL_XRES8
-    assert ngq.lib().ngq_debug_force_kernel(11) == ngq.NGQ_ERR_ARG
+    assert ngq.lib().ngq_debug_force_kernel(12) == ngq.NGQ_ERR_ARG
     assert ngq.lib().ngq_debug_force_kernel(-1) == ngq.NGQ_ERR_ARG
     assert ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_AUTO) == prev
 

@@ -19,7 +19,7 @@ from tests.test_gpu_parity import dev_bf16, dev_scales, dev_u8, host_bits, make
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-PATHS = {1: "perpair_dyn", 2: "perpair_static", 3: "xres14", 4: "xres8", 10: "stream"}
+PATHS = {1: "perpair_dyn", 2: "perpair_static", 3: "xres14", 4: "xres8", 10: "stream", 11: "dot"}
 
 
 @pytest.fixture(scope="module")
@@ -52,6 +52,7 @@ def forced(ngq, request):
 UNSUPPORTED = {
     ("xres14", "swiglu", None): "the 14-wave X-resident kernel has no SwiGLU epilogue",
     ("stream", "swiglu", None): "the streaming kernel has no SwiGLU epilogue",
+    ("dot", "swiglu", None): "the VALU kernel has no SwiGLU epilogue",
     ("perpair_dyn", "gemm", (4, True, 2, 17408, 64)):
         "one partial-sum block per pair (136 pairs at K = 17408) does not fit in LDS",
     ("perpair_dyn", "gemm", (8, False, 8, 17408, 96)): "the same",
