@@ -93,7 +93,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // kNT, the nontemporal hint, for data read once (weights and scales).  On
 // MI355X a weights-only stream of the QK tile pattern took 5.76 instead of
 // 6.02 us per 22 MB launch with it, the gate/value pattern 9.81 instead of
-// 10.06; the coherence-scope bits changed nothing.
+// 10.06; the coherence-scope bits changed nothing.  In the decode kernels
+// (T <= 8) it took 1-7 % off every projection (gate/up + SwiGLU T = 8:
+// 26.7 against 27.6 us, split-K down 16.7 against 17.9, the fused launch
+// 36.7 against 38.0).
 constexpr int kNT = 2;
 
 template <int NW, int AUX = 0>
@@ -337,8 +340,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int s = 0; s < NSETS; ++s) {
         const uint32_t o = offA[s] + pa + (uint32_t)st * 2u * WPK * rowb;
-        load_words<V>(&buf.a[s][st][0], rW, o);
-        if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
+        load_words<V, kNT>(&buf.a[s][st][0], rW, o);
+        if constexpr (BITS == 8) load_words<V, kNT>(&buf.a[s][st][V], rW, o + rowb);
       }
     }
     load_words<4>(&buf.x[0][0], rX, px0);
@@ -346,12 +349,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
     if constexpr (BITS == 5) {
 #pragma unroll
       for (int s = 0; s < NSETS; ++s) {
-        load_words<V>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
-        load_words<V>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
+        load_words<V, kNT>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
+        load_words<V, kNT>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
       }
     }
 #pragma unroll
-    for (int s = 0; s < NSETS; ++s) load_words<2 * V>(&buf.sc[s][0], rS, offS[s] + ps);
+    for (int s = 0; s < NSETS; ++s) load_words<2 * V, kNT>(&buf.sc[s][0], rS, offS[s] + ps);
   };
 
   f32x4 acc[NSETS][V];
@@ -746,19 +749,19 @@ struct PairLoads {
 #pragma unroll
       for (int s = 0; s < NSETS; ++s) {
         const uint32_t o = offA[s] + pa + (uint32_t)st * 2u * WPK * rowb;
-        load_words<V>(&buf.a[s][st][0], rW, o);
-        if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
+        load_words<V, kNT>(&buf.a[s][st][0], rW, o);
+        if constexpr (BITS == 8) load_words<V, kNT>(&buf.a[s][st][V], rW, o + rowb);
       }
     }
     if constexpr (BITS == 5) {
 #pragma unroll
       for (int s = 0; s < NSETS; ++s) {
-        load_words<V>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
-        load_words<V>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
+        load_words<V, kNT>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
+        load_words<V, kNT>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
       }
     }
 #pragma unroll
-    for (int s = 0; s < NSETS; ++s) load_words<2 * V>(&buf.sc[s][0], rS, offS[s] + ps);
+    for (int s = 0; s < NSETS; ++s) load_words<2 * V, kNT>(&buf.sc[s][0], rS, offS[s] + ps);
   }
 };
 
@@ -1883,8 +1886,8 @@ __global__ __launch_bounds__(kWideWaves * 64) void gemm_wide_kernel(WideArgs a) 
 #pragma unroll
       for (int s = 0; s < NSETS; ++s) {
         const uint32_t o = offA[s] + pa + (uint32_t)st * 4u * WPK * rowb;
-        load_words<V>(&buf.a[s][st][0], rW, o);
-        if constexpr (BITS == 8) load_words<V>(&buf.a[s][st][V], rW, o + rowb);
+        load_words<V, kNT>(&buf.a[s][st][0], rW, o);
+        if constexpr (BITS == 8) load_words<V, kNT>(&buf.a[s][st][V], rW, o + rowb);
       }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
