@@ -58,6 +58,10 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill-size T sweep")
     p.add_argument("--prefill-t", type=int, nargs="*", default=[128, 256, 512, 1024, 2048],
                    help="token counts of the prefill sweep")
+    p.add_argument("--no-cpu-configs", action="store_true",
+                   help="skip the oracle's CPU time per workload and T (the headline's CPU baseline stays)")
+    p.add_argument("--summarize-trace", metavar="CSV",
+                   help="print per-kernel duration percentiles of a rocprofv3 kernel-trace CSV and exit (no GPU)")
     return p.parse_args()
 
 
@@ -86,13 +90,20 @@ class Rotation:
         self.cold_bytes = self.replicas * per
 
 
+# GPU clock cycles of the spin kernel queued ahead of a timed replay (~0.4 ms)
+LEAD_CYCLES = 1_000_000
+
+
 def time_steps(launch, replicas, steps, warmup):
     """Average GPU time of one launch: `warmup` eager launches, then exactly
     `steps` launches (rotating through the replicas) captured in one HIP graph,
     replayed twice untimed and once between two events on the capturing
-    stream.  The graph
-    removes the host's per-launch cost (~10 us through Python), so the events
-    bracket back-to-back kernels, as a serving loop would replay them."""
+    stream.  The graph removes the host's per-launch cost (~10 us through
+    Python), so the events bracket back-to-back kernels, as a serving loop
+    would replay them.  A spin kernel queued ahead of the start event keeps
+    the GPU busy while the host submits the replay, so that the submission's
+    host latency does not fall between the start event and the first launch
+    (with 20 launches it added 0.3-0.5 us to each)."""
     import torch
 
     for i in range(warmup):
@@ -107,6 +118,7 @@ def time_steps(launch, replicas, steps, warmup):
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(LEAD_CYCLES)
     start.record()
     g.replay()
     end.record()
@@ -274,6 +286,116 @@ def run_prefill(ngq, Ts, steps):
     return out
 
 
+ATTAINABLE = {"qk": 32, "gv": 48, "qk8": 32}  # tile columns of the streaming pattern per workload
+
+
+def run_attainable(ngq, steps):
+    """The weight stream alone in the streaming kernel's access pattern
+    (ngq_stream_tiles: same tiles, waves, pair order and loads; no X, no
+    compute), per workload, cold: what a launch of these weight bytes can
+    attain in that pattern."""
+    import torch
+
+    import synthetic
+
+    out = {}
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    for name, cols in ATTAINABLE.items():
+        w = synthetic.WORKLOADS[name]
+        rot = Rotation(ngq, w, 1)
+        ms = time_steps(lambda i: ngq.ngq_stream_tiles(rot.wq[i], rot.s[i], w.K, w.N, w.bits, cols, sink),
+                        rot.replicas, steps, 10)
+        b = packed_bytes(ngq, w) + ngq.ngq_scale_bytes(w.K, w.N, w.bits)
+        out[name] = {"us": ms * 1e3, "weight_bytes": b, "GBps": b / ms / 1e6, "pct_peak": 100 * b / ms / 1e6 / PEAK_GBS,
+                     "pattern": f"{cols}-column tiles, {10 if cols == 32 else 8} waves, one pair in flight per wave"}
+        del rot
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_tiny(ngq, steps):
+    """The tiny int4 GEMV (T=1, K=256, N=256; 32 KB of weights): latency bound,
+    reported in microseconds; its replicas are L2/MALL resident (labelled)."""
+    import torch
+
+    import synthetic
+
+    w = synthetic.WORKLOADS["tiny"]
+    nb = packed_bytes(ngq, w)
+    wq, sc, x = synthetic.device_replicas(w, 1, steps, nb, seed=0)
+    y = torch.empty((1, w.N), dtype=torch.bfloat16, device="cuda")
+    ms = time_steps(lambda i: ngq.ngq_gemm(x, wq[i], sc[i], 4, w.N, y=y), steps, steps, 10)
+    return {"workload": "tiny int4 GEMV T=1 K=256 N=256", "us": ms * 1e3,
+            "cache": f"{steps} replicas of {nb + ngq.ngq_scale_bytes(w.K, w.N, 4)} B (cache resident: latency bound)"}
+
+
+def cpu_configs(ngq, threads):
+    """The oracle's CPU time per workload and T on `threads` host threads (one
+    run each; random packed bytes, scales and x of the workload's shape), and
+    the stacked layer (QK, gate/value, gate/up + SwiGLU, down, rescale) times
+    64, labelled extrapolated."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    def inputs(w, T, seed):
+        g = np.random.default_rng(seed)
+        nb = packed_bytes(ngq, w)
+        packed = synthetic.random_words(nb, g)
+        scales = synthetic.draw_scales(w.K, w.N, w.scale_lo, w.scale_hi, w.scale_bf16, g)
+        return synthetic.draw_x(T, w.K, g), packed, scales
+
+    rows, layer = [], {}
+    for name, Ts in (("tiny", (1,)), ("qk", (1, 2, 4, 8)), ("gv", (1, 2, 4, 8)), ("gate_up", (1, 2, 4, 8)),
+                     ("down", (1, 2, 4, 8))):
+        w = synthetic.WORKLOADS[name]
+        x8, packed, scales = inputs(w, max(Ts), 11)
+        for T in Ts:
+            x = x8[:T]
+            t0 = time.perf_counter()
+            y64 = oracle.gemm(x, packed, scales, w.K, w.N, w.bits, w.scale_bf16, nthreads=threads)
+            if name == "gate_up":
+                oracle.swiglu(y64[:, :synthetic.N_FF], y64[:, synthetic.N_FF:])
+            dt = time.perf_counter() - t0
+            n_out = synthetic.N_FF if name == "gate_up" else w.N
+            b = algorithmic_bytes(ngq, w, T, n_out=n_out)
+            rows.append({"workload": name, "T": T, "us": dt * 1e6, "GBps": b / dt / 1e9})
+            if name != "tiny":
+                layer.setdefault(T, 0.0)
+                layer[T] += dt
+    # the rescale of the layer's down output (T x 5120)
+    g = np.random.default_rng(12)
+    stack = []
+    for T, dt in sorted(layer.items()):
+        z = synthetic.draw_x(T, synthetic.HIDDEN, g)
+        t0 = time.perf_counter()
+        oracle.rms_rescale(z)
+        dt += time.perf_counter() - t0
+        stack.append({"T": T, "us_per_layer": dt * 1e6, "ms_per_64_layers_extrapolated": 64 * dt * 1e3})
+    return {"threads": threads, "runs": "one each", "projections": rows, "stack_64_layers_extrapolated": stack}
+
+
+def summarize_trace(path):
+    """Per-kernel duration percentiles of a rocprofv3 kernel-trace CSV."""
+    import csv
+    import statistics
+
+    durs = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name", "")
+            d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            durs.setdefault(name, []).append(d / 1e3)
+    out = []
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        q = lambda f: v[min(len(v) - 1, int(f * (len(v) - 1) + 0.5))]
+        out.append({"kernel": name[:160], "calls": len(v), "median_us": statistics.median(v), "p10_us": q(0.1),
+                    "p90_us": q(0.9), "mean_us": sum(v) / len(v)})
+    return out
+
+
 def gpu_output(ngq, rot, y_dev):
     """Recompute replica 0 on the GPU; host copies of its inputs and output."""
     import numpy as np
@@ -318,6 +440,7 @@ def run_stack(ngq, layers, passes, Ts=(1, 2, 4, 8), side=True):
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(LEAD_CYCLES)
         e0.record()
         for _ in range(passes):
             g.replay()
@@ -400,6 +523,7 @@ def run_fused(ngq, Ts, steps, sets=8):
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(LEAD_CYCLES)
         e0.record()
         g.replay()
         e1.record()
@@ -507,6 +631,10 @@ def traffic_for(name, T):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        for row in summarize_trace(args.summarize_trace):
+            print(json.dumps(row))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path is not sharded "
               f"across GPUs)", file=sys.stderr)
@@ -564,6 +692,16 @@ def main():
             del r
             torch.cuda.empty_cache()
 
+    attainable = run_attainable(ngq, args.sweep_steps)
+    names_pct = {f"{n} int{synthetic.WORKLOADS[n].bits} K={synthetic.WORKLOADS[n].K} N={synthetic.WORKLOADS[n].N}": n
+                 for n in ("qk", "gv")}
+    names_pct["qk-shaped int8 K=5120 N=8192"] = "qk8"
+    for row in sweep:
+        base = names_pct.get(row["workload"])
+        if base is not None and row["T"] <= 8:
+            row["pct_of_attainable"] = 100 * attainable[base]["us"] / row["us"]
+    tiny = run_tiny(ngq, args.sweep_steps)
+
     prefill = None if args.no_prefill else run_prefill(ngq, tuple(args.prefill_t), min(args.sweep_steps, 20))
 
     stack = None if args.no_stack else run_stack(ngq, args.stack_layers, args.stack_passes, tuple(args.stack_t),
@@ -574,6 +712,8 @@ def main():
 
     cpu, parity = (None, {"oracle": "not run (--no-cpu-baseline)"}) if args.no_cpu_baseline else \
         cpu_baseline(w, T, host, nbytes)
+    if cpu is not None and not args.no_cpu_configs:
+        cpu["per_workload"] = cpu_configs(ngq, host_threads())
     parity["graph_replay_matches_eager"] = graph_ok
 
     traffic = traffic_for(args.workload, T)
@@ -601,6 +741,9 @@ def main():
         },
         "us_per_projection": ms * 1e3,
         "pct_of_peak": 100 * gbps / PEAK_GBS,
+        "pct_of_attainable": 100 * attainable[args.workload]["us"] / (ms * 1e3) if args.workload in attainable else None,
+        "attainable": attainable,
+        "tiny": tiny,
         "roofline": {
             "bound": "hbm",
             "achieved": gbps,

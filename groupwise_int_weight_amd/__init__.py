@@ -63,6 +63,7 @@ SIGNATURES = {
     "ngq_rms_rescale": (_INT, [_INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_gemm_rescale": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR, _PTR, _SIZE, _PTR]),
     "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
+    "ngq_stream_tiles": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR]),
     "ngq_debug_force_kernel": (_INT, [_INT]),
     "ngq_strerror": (ctypes.c_char_p, [_INT]),
     "ngq_version": (_INT, []),
@@ -376,6 +377,18 @@ def ngq_stream_read(buf, sink, stream=None):
                                  _stream(stream)), "ngq_stream_read")
 
 
+def ngq_stream_tiles(wq, scales, K: int, N: int, bits: int, cols: int, sink, group: int = NGQ_GROUP, stream=None):
+    """The weight stream of the streaming decode kernel alone (calibration);
+    sink (device, >= 16384 bytes) receives per-tile checksums."""
+    if K > 0 and _nbytes(wq) != ngq_packed_bytes(K, N, int(bits) & 0xFF, group):
+        raise ValueError("ngq_stream_tiles: wq does not hold the packed K x N matrix")
+    if _nbytes(sink) < 16384:
+        raise ValueError("ngq_stream_tiles: sink must hold 16384 bytes")
+    _check(lib().ngq_stream_tiles(K, N, _format_bits(bits, scales), group, cols, _dev_ptr(wq, "wq"),
+                                  _dev_ptr(scales, "scales"), _dev_ptr(sink, "sink"), _stream(stream)),
+           "ngq_stream_tiles")
+
+
 def ngq_debug_force_kernel(path: int) -> int:
     """Force a kernel path for later calls (NGQ_KERNEL_AUTO restores the
     per-shape choice); returns the previous setting."""
@@ -388,7 +401,7 @@ def ngq_debug_force_kernel(path: int) -> int:
 __all__ = [
     "ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_gemm_splitk", "ngq_splitk_workspace_bytes",
     "ngq_gemm_splitk_static",
-    "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read",
+    "ngq_rms_rescale", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_stream_read", "ngq_stream_tiles",
     "ngq_debug_force_kernel",
     "ngq_packed_bytes", "ngq_scale_bytes", "ngq_strerror", "ngq_version", "NgqError", "NgqLibraryMissing",
     "lib", "SIGNATURES", "NgqProj",

@@ -2606,6 +2606,109 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 constexpr size_t kStaticScratchBytes = NGQ_STATIC_SCRATCH_BYTES;
 __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
+// The weight stream of gemm_stream_kernel alone: the same tiles, waves, pair
+// order and loads (weights, int5 high bits, scales; nontemporal), one pair in
+// flight per wave and the next requested as soon as it lands, but no X, no
+// compute and no output beyond a checksum.  Its time per launch is the
+// attainable time of the projection's weight stream in this access pattern,
+// which the bench reports beside the 8 TB/s peak.  sink[block] = XOR of the
+// packed P0 words the workgroup read (each read once);
+// sink[gridDim + block] = a sum over the other words (keeps their loads).
+template <int BITS, int V, int W>
+__global__ __launch_bounds__(W * 64) void stream_tiles_kernel(GemmArgs a, uint32_t* sink) {
+  constexpr int WPK = BITS == 8 ? 2 : 1;
+  constexpr int TILE = 16 * V;
+  __shared__ uint32_t red[2][W];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15, q = lane >> 4, h = m >> 3;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, per = a.ntiles >> 3, rem = a.ntiles & 7;
+  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
+  const uint32_t c0 = (uint32_t)(tile * TILE);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
+  const __amdgpu_buffer_rsrc_t rP1 = make_rsrc(static_cast<const char*>(a.wq) + a.p0_bytes, a.p1_bytes);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.scales, a.s_bytes);
+  const uint32_t rowb = (uint32_t)a.Ncols * 4u;
+  const uint32_t lane_kb = 8u * (uint32_t)(q >> 1) + (uint32_t)(q & 1);
+  const uint32_t col = c0 + (uint32_t)(V * m);
+  const uint32_t offA = lane_kb * WPK * rowb + col * 4u;
+  const uint32_t offP1 = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
+  const uint32_t offS = (uint32_t)h * (uint32_t)a.Ncols * 2u + (c0 + (uint32_t)(4 * V * q)) * 2u;
+  struct Buf {
+    uint32_t a[4][V * WPK];
+    uint32_t p1[2][BITS == 5 ? V : 1];
+    uint32_t sc[2 * V];
+  };
+  auto issue = [&](Buf& buf, int p) {
+    const bool valid = p < a.pairs;
+    const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb : kOOB;
+    const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb : kOOB;
+    const uint32_t ps = valid ? (uint32_t)p * rowb : kOOB;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint32_t o = offA + pa + (uint32_t)st * 2u * WPK * rowb;
+      load_words<V, kNT>(&buf.a[st][0], rW, o);
+      if constexpr (BITS == 8) load_words<V, kNT>(&buf.a[st][V], rW, o + rowb);
+    }
+    if constexpr (BITS == 5) {
+      load_words<V, kNT>(&buf.p1[0][0], rP1, offP1 + pp1);
+      load_words<V, kNT>(&buf.p1[1][0], rP1, offP1 + pp1 + rowb);
+    }
+    load_words<2 * V, kNT>(&buf.sc[0], rS, offS + ps);
+  };
+  uint32_t x = 0, other = 0;
+  auto consume = [&](const Buf& buf) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < V * WPK; ++i) x ^= buf.a[st][i];
+    if constexpr (BITS == 5) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) other += buf.p1[0][i] + buf.p1[1][i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * V; ++i) other += buf.sc[i];
+  };
+  Buf buf[2];
+  auto pair_of = [&](int i) { return wave + W * i; };
+  issue(buf[0], pair_of(0));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < a.ppw; i += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue(buf[1], pair_of(i + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    consume(buf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue(buf[0], pair_of(i + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    consume(buf[1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // lanes, then waves (an out-of-range pair loaded zeros: no effect)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    x ^= __shfl_xor(x, off);
+    other += __shfl_xor(other, off);
+  }
+  if (lane == 0) {
+    red[0][wave] = x;
+    red[1][wave] = other;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t rx = 0, ro = 0;
+    for (int w = 0; w < W; ++w) {
+      rx ^= red[0][w];
+      ro += red[1][w];
+    }
+    sink[blockIdx.x] = rx;
+    sink[gridDim.x + blockIdx.x] = ro;
+  }
+}
+
 }  // namespace dev
 
 // ---- host side: configuration and launch ------------------------------------
@@ -3631,6 +3734,42 @@ extern "C" int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* 
   hipLaunchKernelGGL(dev::stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      static_cast<const dev::u32x4*>(buf), n16, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
+extern "C" int ngq_stream_tiles(int K, int N, int bits, int group, int cols, const void* wq, const void* scales,
+                                void* sink, void* stream) {
+  Format f;
+  int rc = parse_format(bits, group, &f);
+  if (rc != NGQ_OK) return rc;
+  if ((rc = check_kn(K, N)) != NGQ_OK) return rc;
+  if (cols != 32 && cols != 48) return NGQ_ERR_UNSUPPORTED;
+  if (N % cols != 0) return NGQ_ERR_SHAPE;  // whole tiles only
+  if (K == 0 || N == 0) return NGQ_OK;
+  if ((rc = check_ptr(wq)) != NGQ_OK || (rc = check_ptr(scales)) != NGQ_OK || (rc = check_ptr(sink)) != NGQ_OK)
+    return rc;
+  const size_t wb0 = p0_bytes(K, N, f.bits), wb1 = p1_bytes(K, N, f.bits), sb = (size_t)(K / kGroup) * N * 2;
+  if (wb0 + wb1 >= kMaxBuffer || sb >= kMaxBuffer) return NGQ_ERR_UNSUPPORTED;
+  const int ntiles = (N + cols - 1) / cols;
+  if (ntiles > 2048) return NGQ_ERR_SHAPE;  // the sink holds two words per workgroup
+  dev::GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.wq = wq; a.scales = scales;
+  a.K = K; a.Nout = N; a.Ncols = N;
+  a.G = K / kGroup;
+  a.pairs = (a.G + 1) / 2;
+  a.ntiles = ntiles;
+  a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb;
+  const int W = cols == 32 ? 10 : 8;
+  a.ppw = (a.pairs + W - 1) / W;
+  uint32_t* sk = static_cast<uint32_t*>(sink);
+  hipStream_t st = (hipStream_t)stream;
+  auto go = [&](auto kern, int w) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(w * 64), 0, st, a, sk);
+    return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+  };
+  if (f.bits == 4) return cols == 32 ? go(dev::stream_tiles_kernel<4, 2, 10>, 10) : go(dev::stream_tiles_kernel<4, 3, 8>, 8);
+  if (f.bits == 5) return cols == 32 ? go(dev::stream_tiles_kernel<5, 2, 10>, 10) : go(dev::stream_tiles_kernel<5, 3, 8>, 8);
+  return cols == 32 ? go(dev::stream_tiles_kernel<8, 2, 10>, 10) : go(dev::stream_tiles_kernel<8, 3, 8>, 8);
 }
 
 extern "C" int ngq_debug_force_kernel(int path) {

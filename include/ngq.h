@@ -267,6 +267,23 @@ int ngq_debug_force_kernel(int path);
  * bench to measure the attainable HBM read rate of the device. */
 int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
 
+/* Calibration: the weight stream of a K x N projection in the access pattern
+ * of the streaming decode kernel (NGQ_KERNEL_STREAM), alone: the same column
+ * tiles (cols = 32, 10 waves; or 48, 8 waves), pair order and loads of the
+ * packed words and scales, with no X, no arithmetic and no output.  Its
+ * launch time is what this pattern can attain for the projection's weight
+ * bytes, which the bench reports beside the HBM peak.
+ *   wq, scales : device, as for ngq_gemm
+ *   sink       : device, at least 16384 bytes; word b (b < number of tiles)
+ *                receives the XOR of the packed P0 words tile b read (each
+ *                once; a check of the pattern), word tiles + b a sum of the
+ *                other words it read
+ * Status codes as ngq_gemm; cols other than 32 or 48: NGQ_ERR_UNSUPPORTED;
+ * N not a multiple of cols (whole tiles only) or more than 2048 tiles:
+ * NGQ_ERR_SHAPE. */
+int ngq_stream_tiles(int K, int N, int bits, int group, int cols, const void* wq, const void* scales, void* sink,
+                     void* stream);
+
 /* Static description of a status code. */
 const char* ngq_strerror(int status);
 

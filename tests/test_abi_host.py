@@ -277,6 +277,9 @@ def test_debug_exports_reject_bad_arguments(ngq):
     assert L.ngq_unpack_codes(64, 4, 4, 64, W + 4, Y, None) == -4
     assert L.ngq_dequant_f32(64, 4, 4, 64, W, None, Y, None) == -1
     assert L.ngq_stream_read(X, 24, Y, None) == -2
+    assert L.ngq_stream_tiles(64, 200, 4, 64, 32, W, S, Y, None) == -2   # ragged tiles
+    assert L.ngq_stream_tiles(64, 192, 4, 64, 40, W, S, Y, None) == -3   # tile width
+    assert L.ngq_stream_tiles(64, 192, 4, 64, 32, None, S, Y, None) == -1
 
 
 def test_binding_refuses_host_tensors(ngq):

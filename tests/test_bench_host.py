@@ -70,3 +70,20 @@ def test_kernel_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.kernel_sha() == h
     src.write_text(code.replace("a + 1", "a + 2"))
     assert bench.kernel_sha() != h
+
+
+def test_summarize_trace_percentiles(tmp_path):
+    """bench.py --summarize-trace: per-kernel median, p10 and p90 of a
+    rocprofv3 kernel-trace CSV (durations from the timestamps, in us)."""
+    import bench
+
+    p = tmp_path / "kernel_trace.csv"
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    for i in range(11):  # durations 1..11 us
+        rows.append(f"gemm_a,{1000 * i},{1000 * i + 1000 * (i + 1)}")
+    rows.append("other,0,500")
+    p.write_text("\n".join(rows) + "\n")
+    out = {r["kernel"]: r for r in bench.summarize_trace(str(p))}
+    a = out["gemm_a"]
+    assert a["calls"] == 11 and a["median_us"] == 6.0 and a["p10_us"] == 2.0 and a["p90_us"] == 10.0
+    assert out["other"]["calls"] == 1 and out["other"]["median_us"] == 0.5

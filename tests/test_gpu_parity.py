@@ -335,3 +335,24 @@ def test_stream_read_checksum(ngq):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(words)
+
+
+@pytest.mark.parametrize("bits,cols", [(4, 32), (5, 48), (8, 32), (5, 32)])
+def test_stream_tiles_reads_every_word_once(ngq, bits, cols):
+    """The calibration stream reads each packed P0 word of its tiles once:
+    the per-tile XOR checksums equal the host's (as a multiset: workgroups
+    take tiles in an XCD-grouped order)."""
+    K, N = 1088, 192  # 17 groups (a half pair at the end); whole tiles of 32 or 48 columns
+    g = np.random.default_rng(bits + cols)
+    nb = ngq.ngq_packed_bytes(K, N, bits)
+    packed = g.integers(0, 256, size=nb, dtype=np.uint8)
+    scales = (g.uniform(1e-3, 2e-2, size=(K // 64, N))).astype(np.float16).view(np.uint16)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    ngq.ngq_stream_tiles(dev_u8(packed), dev_scales(scales, False), K, N, bits, cols, sink)
+    torch.cuda.synchronize()
+    rows = K // (4 if bits == 8 else 8)
+    p0 = packed[: rows * N * 4].view("<u4").reshape(rows, N)
+    ntiles = (N + cols - 1) // cols
+    want = sorted(int(np.bitwise_xor.reduce(p0[:, t * cols:(t + 1) * cols], axis=None)) for t in range(ntiles))
+    got = sorted(int(v) for v in sink.cpu().numpy().view(np.uint32)[:ntiles])
+    assert got == want
