@@ -195,6 +195,22 @@ def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return h
 
 
+def add_residual(y64: np.ndarray, r_bits: np.ndarray, axw: np.ndarray | None = None):
+    """The residual connection closing a stacked layer (harness, not a step the
+    pages describe): y + r in fp64, with r given as bf16 bit patterns and
+    decoded exactly, so the sum is the exact value the closing epilogue rounds
+    once.  With ``axw`` (the projection's sum |x w|) also returns the
+    magnitude |x w| summed with |r|, which bounds the rounding error of an
+    fp32 evaluation of the same sum."""
+    y64 = np.asarray(y64, dtype=np.float64)
+    r = bf16_bits_to_f64(r_bits)
+    if r.shape != y64.shape:
+        raise OracleError("the residual must have the projection's shape")
+    if axw is None:
+        return y64 + r
+    return y64 + r, np.asarray(axw, dtype=np.float64) + np.abs(r)
+
+
 def rms_rescale(z_bits: np.ndarray) -> np.ndarray:
     z = np.ascontiguousarray(z_bits, dtype=np.uint16)
     T, N = z.shape

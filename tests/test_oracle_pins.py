@@ -322,6 +322,35 @@ def test_magnitude_sums_worked_example(oracle_lib):
     assert (y[0, 0], axw[0, 0], axs[0, 0]) == (-4.0, 32.0, 8.0)
 
 
+def test_residual_worked_example(oracle_lib):
+    """Hand-worked: worked example W1 (y = -4.0, sum|x w| = 32) plus a
+    residual of bf16 0x3FC0 = 1.5 gives y = -2.5 and the bound 33.5; the
+    residual 0xBE80 = -0.25 gives -4.25 and 32.25.  (Read as fp16, 0x3FC0 would
+    be 1.9375: a decode slip shows.)"""
+    case = next(c for c in load_cases() if c["bits"] == 4 and c["x"]["kind"] == "indicator_below")
+    packed = words_to_bytes(case["p0_words"])
+    scales = np.array([int(s, 16) for s in case["scales"]], dtype=np.uint16).reshape(1, 1)
+    y, axw, _ = oracle_lib.gemm(case_x(case), packed, scales, 64, 1, 4, False, with_bounds=True)
+    for r_bits, want, bound in ((0x3FC0, -2.5, 33.5), (0xBE80, -4.25, 32.25), (0x0000, -4.0, 32.0)):
+        yr, ar = oracle_lib.add_residual(y, np.array([[r_bits]], dtype=np.uint16), axw)
+        assert (yr[0, 0], ar[0, 0]) == (want, bound), hex(r_bits)
+    assert oracle_lib.add_residual(y, np.array([[0x3FC0]], dtype=np.uint16))[0, 0] == -2.5
+
+
+def test_residual_zero_weights_give_the_residual(oracle_lib):
+    """With every code 0 the projection is exactly 0, so y + r is r itself,
+    decoded as bf16 (checked against the standard library's float decode)."""
+    g = np.random.default_rng(11)
+    T, K, N = 3, 128, 8
+    codes = np.zeros((K, N), dtype=np.int8)
+    scales = synthetic.draw_scales(K, N, 1e-3, 2e-2, False, g)
+    x = synthetic.f32_to_bf16_bits(g.standard_normal((T, K)).astype(np.float32))
+    r = synthetic.f32_to_bf16_bits(g.standard_normal((T, N)).astype(np.float32))
+    y = oracle_lib.gemm(x, oracle_lib.pack(codes, 4), scales, K, N, 4, False)
+    yr = oracle_lib.add_residual(y, r)
+    assert all(yr[t, n] == bf16_ref(r[t, n]) for t in range(T) for n in range(N))
+
+
 def numpy_projection(codes, scale_bits, x_bits, scale_bf16):
     K, N = codes.shape
     if scale_bf16:
