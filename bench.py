@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--no-stack-side", action="store_true", help="skip the side-stream comparison graph")
     p.add_argument("--fused", type=int, default=0, metavar="T",
                    help="time only the fused qk + gv + gate/up launch at T tokens (for profiling) and exit")
+    p.add_argument("--valu-vs-mfma", action="store_true",
+                   help="only the A/B of the streaming kernel's MFMA and VALU inner steps per bit width and T")
+    p.add_argument("--ab-reps", type=int, default=5, help="interleaved repetitions of each A/B candidate")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill-size T sweep")
     p.add_argument("--prefill-t", type=int, nargs="*", default=[128, 256, 512, 1024, 2048],
                    help="token counts of the prefill sweep")
@@ -230,9 +233,13 @@ def run_swiglu(ngq, T, steps, warmup):
     ms_dr = time_steps(two_calls, rd.replicas, steps, warmup)
     ms_fr = time_steps(lambda i: ngq.ngq_gemm_rescale(h, rd.wq[i], rd.s[i], 4, wdn.N, y=y, x_next=xn, workspace=ws),
                        rd.replicas, steps, warmup)
+    # the residual: the layer's input x (T x 5120), read once more
+    ms_rr = time_steps(lambda i: ngq.ngq_gemm_residual_rescale(h, rd.wq[i], rd.s[i], 4, wdn.N, rg.x, y=y, x_next=xn,
+                                                               workspace=ws), rd.replicas, steps, warmup)
     b_gu = algorithmic_bytes(ngq, wgu, T, n_out=n_ff)
     b_dn = algorithmic_bytes(ngq, wdn, T)
     b_dr = b_dn + 2 * T * wdn.N  # and the rescaled rows written
+    b_rr = b_dr + 2 * T * wdn.N  # and the residual read
     del rg, rd
     torch.cuda.empty_cache()
     return [
@@ -246,6 +253,8 @@ def run_swiglu(ngq, T, steps, warmup):
          "GBps": b_dr / ms_dr / 1e6, "pct_peak": 100 * b_dr / ms_dr / 1e6 / PEAK_GBS},
         {"workload": "down + RMS rescale, ngq_gemm_rescale (split K, fused closing kernel)", "T": T,
          "us": ms_fr * 1e3, "GBps": b_dr / ms_fr / 1e6, "pct_peak": 100 * b_dr / ms_fr / 1e6 / PEAK_GBS},
+        {"workload": "down + residual + RMS rescale, ngq_gemm_residual_rescale (split K, fused closing kernel)",
+         "T": T, "us": ms_rr * 1e3, "GBps": b_rr / ms_rr / 1e6, "pct_peak": 100 * b_rr / ms_rr / 1e6 / PEAK_GBS},
     ]
 
 
@@ -542,6 +551,68 @@ def run_fused(ngq, Ts, steps, sets=8):
     return out
 
 
+def run_valu_vs_mfma(ngq, steps, reps, Ts=(1, 2, 4, 8)):
+    """The streaming pipeline with its two inner steps, forced on the same
+    shapes: v_mfma (NGQ_KERNEL_STREAM) against v_dot2 on the VALU
+    (NGQ_KERNEL_DOT), 32-column tiles, for int4 (QK shape), int5 (gate/value
+    shape) and int8 (QK shape) at each T.  The candidates are timed
+    alternately, `reps` graphs each (median reported), on the same cold
+    replicas, each taking every place in the order in turn; the library's
+    own choice is timed beside them.  Each
+    candidate's output must match the library's within 4e-3 relative L2 (the
+    two sum in different orders, so bit equality is not expected)."""
+    import statistics
+
+    import torch
+
+    import synthetic
+
+    rows = []
+    names = {ngq.NGQ_KERNEL_STREAM: "mfma", ngq.NGQ_KERNEL_DOT: "valu"}
+    for name in ("qk", "gv", "qk8"):
+        w = synthetic.WORKLOADS[name]
+        for T in Ts:
+            rot = Rotation(ngq, w, T)
+            y = torch.empty((T, w.N), dtype=torch.bfloat16, device="cuda")
+            ref = ngq.ngq_gemm(rot.x, rot.wq[0], rot.s[0], w.bits, w.N).float()
+            times = {p: [] for p in names}
+            times[ngq.NGQ_KERNEL_AUTO] = []
+            order = list(times)
+            for rep in range(reps):
+                # each candidate takes every place in the order in turn
+                for path in order[rep % 3:] + order[:rep % 3]:
+                    prev = ngq.ngq_debug_force_kernel(path)
+                    try:
+                        times[path].append(1e3 * time_steps(
+                            lambda i: ngq.ngq_gemm(rot.x, rot.wq[i], rot.s[i], w.bits, w.N, y=y),
+                            rot.replicas, steps, 5))
+                    finally:
+                        ngq.ngq_debug_force_kernel(prev)
+            rel = {}
+            for path in names:
+                prev = ngq.ngq_debug_force_kernel(path)
+                try:
+                    out = ngq.ngq_gemm(rot.x, rot.wq[0], rot.s[0], w.bits, w.N).float()
+                finally:
+                    ngq.ngq_debug_force_kernel(prev)
+                rel[names[path]] = float(torch.linalg.vector_norm(out - ref) / torch.linalg.vector_norm(ref))
+                assert rel[names[path]] < 4e-3, (name, T, names[path], rel[names[path]])
+            med = {k: statistics.median(v) for k, v in times.items()}
+            b = algorithmic_bytes(ngq, w, T)
+            row = {"workload": f"{name} int{w.bits} K={w.K} N={w.N}", "T": T,
+                   "mfma_us": med[ngq.NGQ_KERNEL_STREAM], "valu_us": med[ngq.NGQ_KERNEL_DOT],
+                   "library_us": med[ngq.NGQ_KERNEL_AUTO],
+                   "faster": "valu" if med[ngq.NGQ_KERNEL_DOT] < med[ngq.NGQ_KERNEL_STREAM] else "mfma",
+                   "valu_over_mfma": med[ngq.NGQ_KERNEL_DOT] / med[ngq.NGQ_KERNEL_STREAM],
+                   "library_pct_peak": 100 * b / (med[ngq.NGQ_KERNEL_AUTO] * 1e3) / PEAK_GBS,
+                   "rel_l2_vs_library": rel}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+            del rot, y, ref
+            torch.cuda.empty_cache()
+    return rows
+
+
 def host_threads() -> int:
     """The logical cores this process may run on (its CPU affinity, which a
     container's CPU share narrows), not the machine's total."""
@@ -649,6 +720,9 @@ def main():
     ngq.lib()
     if args.fused:
         print(json.dumps({"fused": run_fused(ngq, (args.fused,), args.sweep_steps)}), flush=True)
+        return
+    if args.valu_vs_mfma:
+        print(json.dumps({"valu_vs_mfma": run_valu_vs_mfma(ngq, args.sweep_steps, args.ab_reps)}), flush=True)
         return
 
     w = synthetic.WORKLOADS[args.workload]

@@ -62,6 +62,8 @@ SIGNATURES = {
     "ngq_gemm_splitk_static": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR]),
     "ngq_rms_rescale": (_INT, [_INT, _INT, _PTR, _PTR, _PTR]),
     "ngq_gemm_rescale": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR, _PTR, _SIZE, _PTR]),
+    "ngq_gemm_residual_rescale": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR, _PTR, _PTR, _PTR,
+                                         _SIZE, _PTR]),
     "ngq_stream_read": (_INT, [_PTR, _SIZE, _PTR, _PTR]),
     "ngq_stream_tiles": (_INT, [_INT, _INT, _INT, _INT, _INT, _PTR, _PTR, _PTR, _PTR]),
     "ngq_debug_force_kernel": (_INT, [_INT]),
@@ -343,6 +345,39 @@ def ngq_gemm_rescale(x, wq, scales, bits: int, N: int, y=None, x_next=None, work
                                 _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                 _stream(stream))
     _check(st, "ngq_gemm_rescale")
+    return y, x_next
+
+
+def ngq_gemm_residual_rescale(x, wq, scales, bits: int, N: int, residual, y=None, x_next=None, workspace=None,
+                              group: int = NGQ_GROUP, stream=None):
+    """y = x . W + residual, rounded once to bf16, and x_next = the RMS rescale
+    of y, in one call (K split, the residual added by the closing kernel);
+    returns (y, x_next)."""
+    import torch
+
+    T, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if x_next is None:
+        x_next = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(16, ngq_splitk_workspace_bytes(K, N, bits, group)), dtype=torch.uint8,
+                                device=x.device)
+    _check_operands("ngq_gemm_residual_rescale", x, wq, scales, [(y, T, N), (x_next, T, N)], K, N, bits, group)
+    if residual.dtype != torch.bfloat16 or tuple(residual.shape) != (T, N):
+        raise ValueError(f"ngq_gemm_residual_rescale: the residual must be bfloat16 of shape ({T}, {N}), "
+                         f"not {residual.dtype} {tuple(residual.shape)}")
+    for what, t in (("residual", residual), ("workspace", workspace)):
+        if t.device != x.device:
+            raise ValueError(f"ngq_gemm_residual_rescale: the {what} must be on x's device")
+    st = lib().ngq_gemm_residual_rescale(T, K, N, _format_bits(bits, scales), group, _dev_ptr(x, "x"),
+                                         _dev_ptr(wq, "wq"), _dev_ptr(scales, "scales"),
+                                         _dev_ptr(residual, "residual"), _dev_ptr(y, "y"),
+                                         _dev_ptr(x_next, "x_next"), _dev_ptr(workspace, "workspace"),
+                                         workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "ngq_gemm_residual_rescale")
     return y, x_next
 
 

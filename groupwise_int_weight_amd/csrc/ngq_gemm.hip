@@ -1261,8 +1261,11 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
 // v_dot2_f32_bf16 products against X read from LDS (one address per half
 // wave: a broadcast).  The offset (128 + bias) sum x of each group and token
 // is reduced from the pair's X band across the lanes that hold it (DPP row
-// shifts) and subtracted before scaling.  It exists to measure the VALU
-// against the MFMA inner step per bit width and T.
+// shifts) and subtracted before scaling.  Measured against the MFMA step on
+// the same pipeline, it is the faster of the two only at T = 1 for int4 and
+// int8 (the projection's rows then cost one dot2 per two weights; from T = 2
+// the VALU issue grows with T while the MFMA step's does not), where the
+// library routes to it.
 template <int W>
 struct DotSmem {
   static constexpr uint32_t SX = 16u * 4u;  // per wave: sums of x per (token, group) or per 16-lane row
@@ -1766,8 +1769,11 @@ __global__ __launch_bounds__(kSplitWaves * 64) void gemm_splitk_kernel(SplitArgs
 
 // y[e] = bf16(partial[0][e] + partial[1][e] + ... + partial[S-1][e]), in slice
 // order; e runs over the T N outputs, four per thread (N % 4 == 0).
+// With a residual r (bf16, same layout as y), r[e] is added last, before the
+// rounding.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int S, int TN,
-                                                            uint16_t* __restrict__ y) {
+                                                            uint16_t* __restrict__ y,
+                                                            const uint16_t* __restrict__ res) {
   const int e = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (e >= TN) return;
   float4 acc = *reinterpret_cast<const float4*>(partial + e);
@@ -1777,6 +1783,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     acc.y += v.y;
     acc.z += v.z;
     acc.w += v.w;
+  }
+  if (res != nullptr) {
+    const u32x2 r = *reinterpret_cast<const u32x2*>(res + e);
+    acc.x += __uint_as_float(r[0] << 16);
+    acc.y += __uint_as_float(r[0] & 0xFFFF0000u);
+    acc.z += __uint_as_float(r[1] << 16);
+    acc.w += __uint_as_float(r[1] & 0xFFFF0000u);
   }
   const uint32_t lo = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
   const uint32_t hi = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
@@ -3553,27 +3566,42 @@ hipError_t launch_splitk_b(int xl, const dev::SplitArgs& a, int grid, uint32_t l
 // x_next == nullptr: ngq_gemm_splitk.  Otherwise ngq_gemm_rescale: the same
 // projection, then x_next = the RMS rescale of y.  Its split is taken at every
 // T where the tiles leave CUs idle: the closing kernel then also does the
-// rescale, so the split's second launch replaces the rescale's own.
+// rescale, so the split's second launch replaces the rescale's own.  With a
+// residual (ngq_gemm_residual_rescale) K is always split, into as many
+// slices (at most 8) as leave every slice at least 8 pairs, or one slice, so
+// that the residual meets the fp32 sum in the closing kernel and y is
+// rounded once.
 int run_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq, const void* scales, void* y,
-               void* x_next, void* workspace, size_t workspace_bytes, void* stream) {
+               void* x_next, const void* residual, void* workspace, size_t workspace_bytes, void* stream) {
   Format f;
   int rc = parse_format(bits, group, &f);
   if (rc != NGQ_OK) return rc;
   if (T < 0 || T > NGQ_MAX_T) return NGQ_ERR_SHAPE;
   if ((rc = check_kn(K, N)) != NGQ_OK) return rc;
-  const bool fuse = x_next != nullptr;
+  const bool fuse = x_next != nullptr, res = residual != nullptr;
+  if (res && !fuse) return NGQ_ERR_ARG;
   const int pairs = (K / kGroup + 1) / 2, ntiles = (N + 31) / 32, cus = cu_count();
-  const int S = fuse ? (ntiles < cus && pairs >= kSplitMax * 8 ? kSplitMax : 1) : choose_splits(T, K, pairs, ntiles, cus);
+  const int S = res    ? std::max(1, std::min(kSplitMax, pairs / 8))
+                : fuse ? (ntiles < cus && pairs >= kSplitMax * 8 ? kSplitMax : 1)
+                       : choose_splits(T, K, pairs, ntiles, cus);
+  const bool split = S > 1 || res;  // the split kernel and a closing kernel
   const size_t xb = (size_t)T * K * 2, yb = (size_t)T * N * 2;
   const size_t wb0 = p0_bytes(K, N, f.bits), wb1 = p1_bytes(K, N, f.bits), sb = (size_t)(K / kGroup) * N * 2;
   if (fuse && T > 0 && N > 0) {
     if ((rc = check_ptr(x_next)) != NGQ_OK) return rc;
     if (yb >= kMaxBuffer) return NGQ_ERR_UNSUPPORTED;
     if (overlaps(x_next, yb, x, xb) || overlaps(x_next, yb, wq, wb0 + wb1) || overlaps(x_next, yb, scales, sb) ||
-        overlaps(x_next, yb, y, yb) || (S > 1 && overlaps(x_next, yb, workspace, (size_t)S * T * N * 4)))
+        overlaps(x_next, yb, y, yb) || (split && overlaps(x_next, yb, workspace, (size_t)S * T * N * 4)))
       return NGQ_ERR_ARG;
   }
-  if (S == 1) {
+  if (res && T > 0 && N > 0) {
+    // read while other workgroups write y and x_next: no overlap with either
+    if ((rc = check_ptr(residual)) != NGQ_OK) return rc;
+    if (overlaps(residual, yb, y, yb) || overlaps(residual, yb, x_next, yb) ||
+        overlaps(residual, yb, workspace, (size_t)S * T * N * 4))
+      return NGQ_ERR_ARG;
+  }
+  if (!split) {
     rc = run_gemm(1, T, K, N, bits, group, x, wq, scales, y, stream);
     if (rc != NGQ_OK || !fuse) return rc;
     return ngq_rms_rescale(T, N, y, x_next, stream);
@@ -3613,10 +3641,11 @@ int run_splitk(int T, int K, int N, int bits, int group, const void* x, const vo
     e = f.scale_bf16 ? launch_splitk_b<8, true>(xl, a, grid, lds, st) : launch_splitk_b<8, false>(xl, a, grid, lds, st);
   if (e != hipSuccess) return NGQ_ERR_HIP;
   if (fuse && reduce_rescale_fits(N))
-    return launch_reduce_rescale(static_cast<const float*>(workspace), S, T, N, y, x_next, stream);
+    return launch_reduce_rescale(static_cast<const float*>(workspace), S, T, N, y, x_next, residual, stream);
   const int TN = T * N;
   hipLaunchKernelGGL(dev::splitk_reduce_kernel, dim3((unsigned)((TN / 4 + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const float*>(workspace), S, TN, static_cast<uint16_t*>(y));
+                     static_cast<const float*>(workspace), S, TN, static_cast<uint16_t*>(y),
+                     static_cast<const uint16_t*>(residual));
   if (hipGetLastError() != hipSuccess) return NGQ_ERR_HIP;
   return fuse ? ngq_rms_rescale(T, N, y, x_next, stream) : NGQ_OK;
 }
@@ -3666,8 +3695,8 @@ int run_splitk_static(int T, int K, int N, int bits, int group, const void* x, c
     ws = static_scratch(e);
     if (ws == nullptr) return NGQ_ERR_HIP;
   }
-  return run_splitk(T, K, N, bits, group, x, wq, scales, y, nullptr, ws, S > 1 ? dev::kStaticScratchBytes : 0,
-                    stream);
+  return run_splitk(T, K, N, bits, group, x, wq, scales, y, nullptr, nullptr, ws,
+                    S > 1 ? dev::kStaticScratchBytes : 0, stream);
 }
 
 }  // namespace
@@ -3698,7 +3727,7 @@ extern "C" size_t ngq_splitk_workspace_bytes(int K, int N, int bits, int group) 
 
 extern "C" int ngq_gemm_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq,
                                const void* scales, void* y, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_splitk(T, K, N, bits, group, x, wq, scales, y, nullptr, workspace, workspace_bytes, stream);
+  return run_splitk(T, K, N, bits, group, x, wq, scales, y, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 extern "C" int ngq_gemm_splitk_static(int T, int K, int N, int bits, int group, const void* x, const void* wq,
@@ -3710,7 +3739,14 @@ extern "C" int ngq_gemm_rescale(int T, int K, int N, int bits, int group, const 
                                 const void* scales, void* y, void* x_next, void* workspace, size_t workspace_bytes,
                                 void* stream) {
   if (x_next == nullptr) return NGQ_ERR_ARG;
-  return run_splitk(T, K, N, bits, group, x, wq, scales, y, x_next, workspace, workspace_bytes, stream);
+  return run_splitk(T, K, N, bits, group, x, wq, scales, y, x_next, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int ngq_gemm_residual_rescale(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                                         const void* scales, const void* residual, void* y, void* x_next,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (x_next == nullptr || residual == nullptr) return NGQ_ERR_ARG;
+  return run_splitk(T, K, N, bits, group, x, wq, scales, y, x_next, residual, workspace, workspace_bytes, stream);
 }
 
 extern "C" int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream) {

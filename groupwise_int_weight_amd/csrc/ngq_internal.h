@@ -33,11 +33,13 @@ int check_ptr(const void* p);
 bool overlaps(const void* a, size_t na, const void* b, size_t nb);
 
 // The split-K closing kernel of ngq_gemm_rescale (ngq_rescale.hip): y = the
-// slice-order sum of the S fp32 slice sums partial[S][T][N] rounded to bf16,
-// and x = the RMS rescale of y, bit for bit as ngq_rms_rescale(T, N, y, x).
-// Only for S == 8 and rows that reduce_rescale_fits (else
-// NGQ_ERR_UNSUPPORTED); arguments are not checked further.
+// slice-order sum of the S fp32 slice sums partial[S][T][N] (then + res, the
+// bf16 residual [T][N], when res is not null) rounded to bf16, and x = the
+// RMS rescale of y, bit for bit as ngq_rms_rescale(T, N, y, x).  Only for
+// 1 <= S <= 8 and rows that reduce_rescale_fits (else NGQ_ERR_UNSUPPORTED);
+// arguments are not checked further.
 bool reduce_rescale_fits(int N);
-int launch_reduce_rescale(const float* partial, int S, int T, int N, void* y, void* x, void* stream);
+int launch_reduce_rescale(const float* partial, int S, int T, int N, void* y, void* x, const void* res,
+                          void* stream);
 
 }  // namespace ngq

@@ -148,8 +148,11 @@ __global__ __launch_bounds__(kSplitRowThreads) void rms_rescale_split_kernel(con
 // partial fp32 [S][T][N] -> y = bf16(partial[0] + ... + partial[S-1]) (slice
 // order, as the split-K reduction) and x = the rescale of y; N % 8 == 0; 2 N
 // bytes of dynamic LDS.  All S loads of a chunk are issued before the adds.
-template <int S>
-__global__ __launch_bounds__(kSplitRowThreads) void reduce_rescale_kernel(const float* __restrict__ partial, int T,
+// RES: the residual r (bf16 [T][N]) is added to the fp32 sum last, before its
+// one rounding: y = bf16(partial[0] + ... + partial[S-1] + r).
+template <int S, bool RES>
+__global__ __launch_bounds__(kSplitRowThreads) void reduce_rescale_kernel(const float* __restrict__ partial,
+                                                                          const uint16_t* __restrict__ res, int T,
                                                                           int N, uint16_t* y, uint16_t* x) {
   extern __shared__ r32x4 zrow[];
   const size_t row = (size_t)blockIdx.y * (size_t)N, TN = (size_t)T * (size_t)N;
@@ -163,11 +166,20 @@ __global__ __launch_bounds__(kSplitRowThreads) void reduce_rescale_kernel(const 
       lo[ks] = p4[ks * (TN / 4) + 2 * c];
       hi[ks] = p4[ks * (TN / 4) + 2 * c + 1];
     }
+    r32x4 rv = {0u, 0u, 0u, 0u};
+    if constexpr (RES) rv = reinterpret_cast<const r32x4*>(res + row)[c];
     float4 a = lo[0], b = hi[0];
 #pragma unroll
     for (int ks = 1; ks < S; ++ks) {
       a.x += lo[ks].x; a.y += lo[ks].y; a.z += lo[ks].z; a.w += lo[ks].w;
       b.x += hi[ks].x; b.y += hi[ks].y; b.z += hi[ks].z; b.w += hi[ks].w;
+    }
+    if constexpr (RES) {
+      // a bf16 value is the upper half of its fp32 value
+      a.x += __uint_as_float(rv[0] << 16); a.y += __uint_as_float(rv[0] & 0xFFFF0000u);
+      a.z += __uint_as_float(rv[1] << 16); a.w += __uint_as_float(rv[1] & 0xFFFF0000u);
+      b.x += __uint_as_float(rv[2] << 16); b.y += __uint_as_float(rv[2] & 0xFFFF0000u);
+      b.z += __uint_as_float(rv[3] << 16); b.w += __uint_as_float(rv[3] & 0xFFFF0000u);
     }
     r32x4 w;
     w[0] = f32_to_bf16_rne(a.x) | ((uint32_t)f32_to_bf16_rne(a.y) << 16);
@@ -194,11 +206,34 @@ static bool split_rows(int N) { return N % 8 == 0 && N >= 4096 && N <= 30720; }
 
 bool reduce_rescale_fits(int N) { return split_rows(N); }
 
-int launch_reduce_rescale(const float* partial, int S, int T, int N, void* y, void* x, void* stream) {
-  if (S != 8 || !split_rows(N)) return NGQ_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(dev::reduce_rescale_kernel<8>, dim3((unsigned)dev::kRowParts, (unsigned)T),
-                     dim3(dev::kSplitRowThreads), (uint32_t)N * 2u, (hipStream_t)stream, partial, T, N,
-                     static_cast<uint16_t*>(y), static_cast<uint16_t*>(x));
+template <int S>
+static void launch_rr(const float* partial, const void* res, int T, int N, void* y, void* x, hipStream_t st) {
+  const dim3 grid((unsigned)dev::kRowParts, (unsigned)T), block(dev::kSplitRowThreads);
+  const uint32_t lds = (uint32_t)N * 2u;
+  const uint16_t* r = static_cast<const uint16_t*>(res);
+  uint16_t* yy = static_cast<uint16_t*>(y);
+  uint16_t* xx = static_cast<uint16_t*>(x);
+  if (res != nullptr)
+    hipLaunchKernelGGL((dev::reduce_rescale_kernel<S, true>), grid, block, lds, st, partial, r, T, N, yy, xx);
+  else
+    hipLaunchKernelGGL((dev::reduce_rescale_kernel<S, false>), grid, block, lds, st, partial, r, T, N, yy, xx);
+}
+
+int launch_reduce_rescale(const float* partial, int S, int T, int N, void* y, void* x, const void* res,
+                          void* stream) {
+  if (!split_rows(N)) return NGQ_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  switch (S) {
+    case 1: launch_rr<1>(partial, res, T, N, y, x, st); break;
+    case 2: launch_rr<2>(partial, res, T, N, y, x, st); break;
+    case 3: launch_rr<3>(partial, res, T, N, y, x, st); break;
+    case 4: launch_rr<4>(partial, res, T, N, y, x, st); break;
+    case 5: launch_rr<5>(partial, res, T, N, y, x, st); break;
+    case 6: launch_rr<6>(partial, res, T, N, y, x, st); break;
+    case 7: launch_rr<7>(partial, res, T, N, y, x, st); break;
+    case 8: launch_rr<8>(partial, res, T, N, y, x, st); break;
+    default: return NGQ_ERR_UNSUPPORTED;
+  }
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
 

@@ -226,6 +226,29 @@ int ngq_gemm_rescale(int T, int K, int N, int bits, int group, const void* x, co
                      const void* scales, void* y, void* x_next, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* The same closing step with the residual connection added in the epilogue
+ * (not a step the pages describe: the residual stream of the stacked layer,
+ * added where the last projection's sums are closed, so that the block
+ * needs no separate pass):
+ *   y      = bf16( X . dequant(Wq) + residual ): the residual (bf16) is added
+ *            to the projection's fp32 sum, which is rounded once
+ *   x_next = the per-token RMS rescale of y, as ngq_rms_rescale(T, N, y, x_next)
+ * K is always split here (S = min(8, pairs / 8) slices of whole group pairs,
+ * at least one, pairs = ceil(K / 128)), and the kernel that adds the slices'
+ * fp32 sums in slice order adds the residual last; the sums are therefore
+ * grouped as in ngq_gemm_rescale only where both take 8 slices (K >= 8192),
+ * and y can differ from ngq_gemm_rescale's y + residual in the last bit.
+ *   residual : device bf16 [T][N]; must not overlap y, x_next or the
+ *              workspace (NGQ_ERR_ARG: other workgroups write those while it
+ *              is read); null: NGQ_ERR_ARG
+ *   workspace: device, at least ngq_splitk_workspace_bytes(K, N, bits, group)
+ *              bytes, for every T (it is always used)
+ * Other arguments, shapes and status codes as ngq_gemm_rescale; a K slice of
+ * X that does not fit in LDS gives NGQ_ERR_UNSUPPORTED. */
+int ngq_gemm_residual_rescale(int T, int K, int N, int bits, int group, const void* x, const void* wq,
+                              const void* scales, const void* residual, void* y, void* x_next, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Debug export: the signed codes as the GEMM kernels unpack them.
  *   wq : device, ngq_pack layout;  codes : device int8 [K][N], overwritten. */
 int ngq_unpack_codes(int K, int N, int bits, int group, const void* wq, int8_t* codes, void* stream);

@@ -35,7 +35,7 @@ def header_functions():
 def test_header_declares_the_boundary():
     names = header_functions()
     for required in ["ngq_pack", "ngq_gemm", "ngq_swiglu_gemm", "ngq_multi_gemm", "ngq_gemm_splitk", "ngq_gemm_rescale",
-                     "ngq_packed_bytes",
+                     "ngq_gemm_residual_rescale", "ngq_packed_bytes",
                      "ngq_scale_bytes", "ngq_unpack_codes", "ngq_dequant_f32", "ngq_rms_rescale", "ngq_strerror"]:
         assert required in names
 
@@ -214,15 +214,24 @@ def test_multi_empty_calls_are_no_ops(ngq):
     assert ngq.lib().ngq_multi_gemm(1, 64, 64, X, None, 1, None) == -1
 
 
+# Long-K calls (the down projection: 44.5 MB of packed weights) get addresses
+# 256 MB apart, so that no buffer overlaps another unless a case says so and
+# each case fails for the reason it names.
+XL, WL, SL, YL, WSL, XNL, RL = (i << 28 for i in range(1, 8))
+DOWN = (17408, 5120, 4, 64)
+
+
 @pytest.mark.parametrize("args,status", [
-    ((9, 17408, 5120, 4, 64, X, W, S, Y, 0x500000, 1 << 21), -2),          # T > 8
-    ((8, 17400, 5120, 4, 64, X, W, S, Y, 0x500000, 1 << 21), -2),          # K % 64
-    ((8, 17408, 5120, 7, 64, X, W, S, Y, 0x500000, 1 << 21), -3),          # bits
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, None, 1 << 21), -1),              # null workspace
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, 0x500008, 1 << 21), -4),          # misaligned workspace
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, 0x500000, 1 << 16), -1),          # workspace too small
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, Y + 64, 1 << 21), -1),            # workspace overlaps y
-    ((8, 17408, 5120, 4, 64, X, W, S, X, 0x500000, 1 << 21), -1),          # y overlaps x
+    ((9, *DOWN, XL, WL, SL, YL, WSL, 1 << 21), -2),                   # T > 8
+    ((8, 17400, 5120, 4, 64, XL, WL, SL, YL, WSL, 1 << 21), -2),      # K % 64
+    ((8, 17408, 5120, 7, 64, XL, WL, SL, YL, WSL, 1 << 21), -3),      # bits
+    ((8, *DOWN, XL, WL, SL, YL, None, 1 << 21), -1),                  # null workspace
+    ((8, *DOWN, XL, WL, SL, YL, WSL + 8, 1 << 21), -4),               # misaligned workspace
+    ((8, *DOWN, XL, WL, SL, YL, WSL, 1 << 16), -1),                   # workspace too small
+    ((8, *DOWN, XL, WL, SL, YL, YL + 64, 1 << 21), -1),               # workspace overlaps y
+    ((8, *DOWN, XL, WL, SL, XL, WSL, 1 << 21), -1),                   # y overlaps x
+    ((8, *DOWN, XL, WL, SL, WL + 4096, WSL, 1 << 21), -1),            # y overlaps wq
+    ((8, *DOWN, XL, WL, SL, YL, XL + 64, 1 << 21), -1),               # workspace overlaps x
 ])
 def test_splitk_rejects_bad_arguments(ngq, args, status):
     assert ngq.lib().ngq_gemm_splitk(*args, None) == status
@@ -237,19 +246,16 @@ def test_splitk_workspace_and_empty_calls(ngq):
     assert L.ngq_gemm_splitk(0, 17408, 5120, 4, 64, None, None, None, None, None, 0, None) == 0
 
 
-XN = 0x700000  # a next-activation buffer clear of the others
-
-
 @pytest.mark.parametrize("args,status", [
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, None, 0x500000, 1 << 21), -1),        # null x_next
-    ((9, 17408, 5120, 4, 64, X, W, S, Y, XN, 0x500000, 1 << 21), -2),          # T > 8
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, XN + 8, 0x500000, 1 << 21), -4),      # misaligned x_next
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, Y + 64, 0x500000, 1 << 21), -1),      # x_next overlaps y
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, X, 0x500000, 1 << 21), -1),           # x_next overlaps x
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, W + 4096, 0x500000, 1 << 21), -1),    # x_next overlaps wq
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, 0x510000, 0x500000, 1 << 21), -1),    # x_next overlaps the workspace
-    ((1, 17408, 5120, 4, 64, X, W, S, Y, XN, 0x500000, 1 << 16), -1),          # workspace too small (split at T = 1)
-    ((8, 17408, 5120, 4, 64, X, W, S, Y, XN, None, 1 << 21), -1),              # null workspace
+    ((8, *DOWN, XL, WL, SL, YL, None, WSL, 1 << 21), -1),             # null x_next
+    ((9, *DOWN, XL, WL, SL, YL, XNL, WSL, 1 << 21), -2),              # T > 8
+    ((8, *DOWN, XL, WL, SL, YL, XNL + 8, WSL, 1 << 21), -4),          # misaligned x_next
+    ((8, *DOWN, XL, WL, SL, YL, YL + 64, WSL, 1 << 21), -1),          # x_next overlaps y
+    ((8, *DOWN, XL, WL, SL, YL, XL, WSL, 1 << 21), -1),               # x_next overlaps x
+    ((8, *DOWN, XL, WL, SL, YL, WL + 4096, WSL, 1 << 21), -1),        # x_next overlaps wq
+    ((8, *DOWN, XL, WL, SL, YL, WSL + 0x10000, WSL, 1 << 21), -1),    # x_next overlaps the workspace
+    ((1, *DOWN, XL, WL, SL, YL, XNL, WSL, 1 << 16), -1),              # workspace too small (split at T = 1)
+    ((8, *DOWN, XL, WL, SL, YL, XNL, None, 1 << 21), -1),             # null workspace
 ])
 def test_gemm_rescale_rejects_bad_arguments(ngq, args, status):
     assert ngq.lib().ngq_gemm_rescale(*args, None) == status
@@ -257,8 +263,34 @@ def test_gemm_rescale_rejects_bad_arguments(ngq, args, status):
 
 def test_gemm_rescale_empty_calls(ngq):
     L = ngq.lib()
-    assert L.ngq_gemm_rescale(0, 17408, 5120, 4, 64, None, None, None, None, XN, None, 0, None) == 0
+    assert L.ngq_gemm_rescale(0, 17408, 5120, 4, 64, None, None, None, None, XNL, None, 0, None) == 0
     assert L.ngq_gemm_rescale(0, 17408, 5120, 4, 64, None, None, None, None, None, None, 0, None) == -1
+
+
+@pytest.mark.parametrize("args,status", [
+    ((8, *DOWN, XL, WL, SL, None, YL, XNL, WSL, 1 << 21), -1),        # null residual
+    ((8, *DOWN, XL, WL, SL, RL, YL, None, WSL, 1 << 21), -1),         # null x_next
+    ((9, *DOWN, XL, WL, SL, RL, YL, XNL, WSL, 1 << 21), -2),          # T > 8
+    ((8, *DOWN, XL, WL, SL, RL + 8, YL, XNL, WSL, 1 << 21), -4),      # misaligned residual
+    ((8, *DOWN, XL, WL, SL, YL + 64, YL, XNL, WSL, 1 << 21), -1),     # residual overlaps y
+    ((8, *DOWN, XL, WL, SL, XNL, YL, XNL, WSL, 1 << 21), -1),         # residual is x_next
+    ((8, *DOWN, XL, WL, SL, WSL + 64, YL, XNL, WSL, 1 << 21), -1),    # residual overlaps the workspace
+    ((8, *DOWN, XL, WL, SL, RL, YL, XNL, WSL, 1 << 16), -1),          # workspace too small
+    ((8, *DOWN, XL, WL, SL, RL, YL, XNL, None, 1 << 21), -1),         # null workspace
+    ((8, *DOWN, XL, WL, SL, RL, YL, YL, WSL, 1 << 21), -1),           # x_next is y
+    # the residual is always split: even K = 64 (one slice) needs the workspace
+    ((1, 64, 5120, 4, 64, XL, WL, SL, RL, YL, XNL, None, 0), -1),
+])
+def test_gemm_residual_rescale_rejects_bad_arguments(ngq, args, status):
+    assert ngq.lib().ngq_gemm_residual_rescale(*args, None) == status
+
+
+def test_gemm_residual_rescale_empty_calls(ngq):
+    L = ngq.lib()
+    # T == 0 touches nothing; the two pointers that define the call are still required
+    assert L.ngq_gemm_residual_rescale(0, *DOWN, None, None, None, RL, None, XNL, None, 0, None) == 0
+    assert L.ngq_gemm_residual_rescale(0, *DOWN, None, None, None, None, None, XNL, None, 0, None) == -1
+    assert L.ngq_gemm_residual_rescale(0, *DOWN, None, None, None, RL, None, None, None, 0, None) == -1
 
 
 def test_force_kernel_roundtrip(ngq):
@@ -320,6 +352,10 @@ def test_binding_checks_sizes_before_any_call(ngq):
         ngq.ngq_gemm_splitk(x, wq, sc, 4, N, y=torch.zeros((T, N), dtype=bf).t(), workspace=wq)
     with pytest.raises(ValueError, match="output shape"):
         ngq.ngq_gemm_rescale(x, wq, sc, 4, N, y=y, x_next=torch.zeros((1, N), dtype=bf), workspace=wq)
+    with pytest.raises(ValueError, match="residual must be"):
+        ngq.ngq_gemm_residual_rescale(x, wq, sc, 4, N, torch.zeros((T, N + 4), dtype=bf), y=y, workspace=wq)
+    with pytest.raises(ValueError, match="residual must be"):
+        ngq.ngq_gemm_residual_rescale(x, wq, sc, 4, N, torch.zeros((T, N), dtype=f16), y=y, workspace=wq)
     with pytest.raises(ValueError, match="projection 1"):
         ngq.ngq_multi_gemm(x, [dict(wq=wq, scales=sc, bits=4, n=N, y=y),
                                dict(wq=wq, scales=sc, bits=4, n=N, swiglu=True)])

@@ -15,7 +15,7 @@ import pytest
 
 import synthetic
 from tests.parity import assert_parity, bf16_bits_to_f64, compare
-from tests.test_gpu_parity import check_swiglu, dev_bf16, host_bits, sample_cols, swiglu_reference
+from tests.test_gpu_parity import ORACLE_THREADS, check_swiglu, dev_bf16, host_bits, sample_cols, swiglu_reference
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -101,8 +101,8 @@ def gemm_rescale_case(ngq, orc, bits, sbf16, codes, scales, x, cols, what):
     args = (dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits, N)
     y, xn = ngq.ngq_gemm_rescale(*args)
     yb, xb = host_bits(y), host_bits(xn)
-    y64, axw, axs = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, sbf16, cols=cols, nthreads=8,
-                             with_bounds=True)
+    y64, axw, axs = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, sbf16, cols=cols,
+                             nthreads=ORACLE_THREADS, with_bounds=True)
     assert_parity(compare(yb if cols is None else yb[:, cols], y64, axw, axs, K, bits), what)
     assert np.array_equal(xb, host_bits(ngq.ngq_rms_rescale(y)))
     rescale_check(yb, xb, orc)
@@ -118,8 +118,7 @@ def test_gemm_rescale_down_shape(ngq, orc, T):
         mags = np.array([1.0, 1e-30, 3e20, 1e-3, 17.0, 0.0, 2.0 ** 60, 0.5], np.float32)
         xf = (bf16_bits_to_f64(x) * mags[:, None]).astype(np.float32)
         x = synthetic.f32_to_bf16_bits(xf)
-    args, yb, xb = gemm_rescale_case(ngq, orc, 4, False, codes, scales, x, sample_cols(w.N, seed=80 + T),
-                                     f"gemm_rescale down T{T}")
+    args, yb, xb = gemm_rescale_case(ngq, orc, 4, False, codes, scales, x, None, f"gemm_rescale down T{T}")
     if T == 8:
         assert np.all(yb[5] == 0) and np.all(xb[5] == 0)
         # at T >= 5 the split is ngq_gemm_splitk's: the same y bits
@@ -159,10 +158,105 @@ def test_gemm_rescale_ragged(ngq, orc, bits, sbf16, T, K, N):
     from tests.test_gpu_parity import make
 
     _, (codes, scales, x) = make(bits, sbf16, T, K, N, seed=K + N)
-    cols = None if N <= 512 else sample_cols(N, seed=90)
-    args, yb, _ = gemm_rescale_case(ngq, orc, bits, sbf16, codes, scales, x, cols, f"gemm_rescale b{bits} T{T} N{N}")
+    args, yb, _ = gemm_rescale_case(ngq, orc, bits, sbf16, codes, scales, x, None, f"gemm_rescale b{bits} T{T} N{N}")
     if K == 4096:
         assert np.array_equal(yb, host_bits(ngq.ngq_gemm(*args)))
+
+
+# ---- the same with the residual added in the epilogue (ngq_gemm_residual_rescale) ------
+
+def draw_residual(T, N, seed, scale=4.0):
+    g = np.random.default_rng(seed)
+    return synthetic.f32_to_bf16_bits((g.standard_normal((T, N)) * scale).astype(np.float32))
+
+
+def residual_case(ngq, orc, bits, sbf16, codes, scales, x, r, what):
+    """y = x W + r against the oracle (every column; the residual's magnitude
+    joins the rounding bound), x_next bit for bit against ngq_rms_rescale(y)
+    and against the oracle's rescale of the GPU's own y."""
+    from tests.test_gpu_parity import dev_scales, dev_u8
+
+    K, N = codes.shape
+    packed = ngq.ngq_pack(codes, bits)
+    args = (dev_bf16(x), dev_u8(packed), dev_scales(scales, sbf16), bits, N)
+    rd = dev_bf16(r)
+    y, xn = ngq.ngq_gemm_residual_rescale(*args, rd)
+    yb, xb = host_bits(y), host_bits(xn)
+    y64, axw, axs = orc.gemm(x, orc.pack(codes, bits), scales, K, N, bits, sbf16, nthreads=ORACLE_THREADS,
+                             with_bounds=True)
+    y64r, axwr = orc.add_residual(y64, r, axw)
+    assert_parity(compare(yb, y64r, axwr, axs, K, bits), what)
+    assert np.array_equal(xb, host_bits(ngq.ngq_rms_rescale(y)))
+    rescale_check(yb, xb, orc)
+    return args, rd, yb, xb
+
+
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_gemm_residual_rescale_down_shape(ngq, orc, T):
+    w = synthetic.WORKLOADS["down"]
+    codes, scales, x = synthetic.make_inputs(w, T, seed=5)
+    r = draw_residual(T, w.N, seed=60 + T)
+    if T == 8:
+        # a zero row of x and of r: y = 0 and x_next = 0
+        x[5] = 0
+        r[5] = 0
+    args, rd, yb, xb = residual_case(ngq, orc, 4, False, codes, scales, x, r, f"residual down T{T}")
+    if T == 8:
+        assert np.all(yb[5] == 0) and np.all(xb[5] == 0)
+    # a zero residual: the same slices (8) and sums as ngq_gemm_rescale, so the
+    # same y (as values: an fp32 sum of -0 plus +0 is +0)
+    y0, _ = ngq.ngq_gemm_residual_rescale(*args, torch.zeros_like(rd))
+    yr, _ = ngq.ngq_gemm_rescale(*args)
+    assert torch.equal(y0.float(), yr.float())
+    # deterministic, and a captured graph replays to the same bits
+    ws = torch.empty(ngq.ngq_splitk_workspace_bytes(w.K, w.N, 4), dtype=torch.uint8, device="cuda")
+    yg = torch.empty((T, w.N), dtype=torch.bfloat16, device="cuda")
+    xg = torch.empty((T, w.N), dtype=torch.bfloat16, device="cuda")
+    ngq.ngq_gemm_residual_rescale(*args, rd, y=yg, x_next=xg, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(yg), yb) and np.array_equal(host_bits(xg), xb)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ngq.ngq_gemm_residual_rescale(*args, rd, y=yg, x_next=xg, workspace=ws)
+    for rep in range(3):
+        yg.fill_(1.0)
+        xg.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(yg), yb), rep
+        assert np.array_equal(host_bits(xg), xb), rep
+        ngq.ngq_rms_rescale(yg, x=xg)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("bits,sbf16,T,K,N", [
+    (4, False, 3, 12352, 100),  # 8 slices (97 pairs, the last one group), N % 8 != 0: plain reduction + rescale
+    (5, True, 6, 16384, 4104),  # 8 slices, 129 tiles, the fused closing kernel
+    (8, False, 2, 20480, 8),    # 8 slices, one tile
+    (4, True, 4, 4096, 64),     # 32 pairs: 4 slices, plain reduction
+    (5, False, 5, 5120, 4096),  # 40 pairs: 5 slices, the fused closing kernel
+    (4, False, 8, 640, 5120),   # 5 pairs: one slice, the fused closing kernel
+    (8, True, 7, 64, 4096),     # one group
+])
+def test_gemm_residual_rescale_ragged(ngq, orc, bits, sbf16, T, K, N):
+    from tests.test_gpu_parity import make
+
+    _, (codes, scales, x) = make(bits, sbf16, T, K, N, seed=K + N + 1)
+    r = draw_residual(T, N, seed=K + N, scale=0.05)
+    residual_case(ngq, orc, bits, sbf16, codes, scales, x, r, f"residual b{bits} T{T} K{K} N{N}")
+
+
+def test_gemm_residual_rescale_zero_weights(ngq, orc):
+    """Every code 0: the projection is 0, so y is the residual (up to the
+    offset term's fp32 cancellation, which the parity bound covers) and
+    x_next its rescale."""
+    T, K, N = 8, 17408, 5120
+    codes = np.zeros((K, N), dtype=np.int8)
+    scales = synthetic.draw_scales(K, N, 1e-3, 2e-2, False, np.random.default_rng(2))
+    x = synthetic.f32_to_bf16_bits(np.random.default_rng(3).standard_normal((T, K)).astype(np.float32))
+    r = draw_residual(T, N, seed=4)
+    residual_case(ngq, orc, 4, False, codes, scales, x, r, "residual, zero weights")
 
 
 # ---- stacked layers -------------------------------------------------------------------
