@@ -93,43 +93,75 @@ class Rotation:
         self.cold_bytes = self.replicas * per
 
 
-# GPU clock cycles of the spin kernel queued ahead of a timed replay (~0.4 ms)
+# GPU clock cycles of the spin kernel queued ahead of the timed launches (at
+# least ~0.4 ms), and the cycles per microsecond it is sized with
 LEAD_CYCLES = 1_000_000
+SPIN_CYCLES_PER_US = 2400
 
 
 def time_steps(launch, replicas, steps, warmup):
-    """Average GPU time of one launch: `warmup` eager launches, then exactly
-    `steps` launches (rotating through the replicas) captured in one HIP graph,
-    replayed twice untimed and once between two events on the capturing
-    stream.  The graph removes the host's per-launch cost (~10 us through
-    Python), so the events bracket back-to-back kernels, as a serving loop
-    would replay them.  A spin kernel queued ahead of the start event keeps
-    the GPU busy while the host submits the replay, so that the submission's
-    host latency does not fall between the start event and the first launch
-    (with 20 launches it added 0.3-0.5 us to each)."""
+    """Average GPU time of one launch: `warmup` eager launches (untimed; they
+    also give the host's cost per launch), then exactly `steps` launches,
+    rotating through the replicas, enqueued between two events on the
+    launching stream behind a spin kernel that outlasts their submission (after
+    one untimed pass of the same launches), so that the GPU runs them back to
+    back with no host latency between them
+    (checked: the host must have enqueued the last launch before the spin
+    ended, else the spin is lengthened and the measurement taken again).
+    Measured on MI355X (QK, T = 8): 20 such launches take 7.44 us each, the
+    same 20 as one HIP graph replay 7.65 us (a replay adds ~9 us of its own:
+    15.8 us for a graph of one launch); at 200 launches 7.43 eager and 7.22
+    in a graph."""
     import torch
 
+    t0 = time.perf_counter()
     for i in range(warmup):
         launch(i % replicas)
+    host_us = (time.perf_counter() - t0) * 1e6 / max(1, warmup)
+    # one untimed pass of the same launches settles the clocks (the first
+    # timed pass of a process otherwise ran ~10 % slow)
+    for i in range(steps):
+        launch(i % replicas)
     torch.cuda.synchronize()
+    spin = max(LEAD_CYCLES, int(4 * steps * host_us * SPIN_CYCLES_PER_US))
+    for _ in range(3):
+        e_spin = torch.cuda.Event(enable_timing=True)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        e_spin.record()
+        torch.cuda._sleep(spin)
+        start.record()
+        for i in range(steps):
+            launch(i % replicas)
+        h1 = time.perf_counter()
+        end.record()
+        end.synchronize()
+        if (h1 - h0) * 1e3 < e_spin.elapsed_time(start):
+            break
+        spin *= 4
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def graph_matches_eager(launch, replicas, steps=3):
+    """A captured graph of `steps` launches replays to what the same last
+    launch gives eagerly (returns the graph's output check)."""
+    import torch
+
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
             launch(i % replicas)
-    g.replay()  # untimed: the first replay uploads the graph
-    g.replay()  # untimed: settles clocks after the preceding work
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(LEAD_CYCLES)
-    start.record()
+    out = launch.output
     g.replay()
-    end.record()
-    end.synchronize()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    y_graph = out.clone()
+    out.fill_(0)
+    launch((steps - 1) % replicas)
+    torch.cuda.synchronize()
     del g
-    return ms
+    return bool(torch.equal(y_graph, out))
 
 
 def clocks_under_load(launch, ms_per_launch):
@@ -202,9 +234,10 @@ def run_projection(ngq, w, T, steps, warmup):
         st = lib.ngq_gemm(T, w.K, w.N, bits, 64, xp, wp[i], sp[i], yp, torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise ngq.NgqError(st, "ngq_gemm")
+    launch.output = y
 
     ms = time_steps(launch, rot.replicas, steps, warmup)
-    return ms, rot, y
+    return ms, rot, y, launch
 
 
 def run_swiglu(ngq, T, steps, warmup):
@@ -278,7 +311,7 @@ def run_prefill(ngq, Ts, steps):
     for T in Ts:
         for name in ("qk", "gv", "down"):
             w = synthetic.WORKLOADS[name]
-            ms, rot, _ = run_projection(ngq, w, T, steps, 3)
+            ms, rot, _, _ = run_projection(ngq, w, T, steps, 3)
             record(f"{name} int{w.bits} K={w.K} N={w.N}", w, T, ms, w.N)
             del rot
             torch.cuda.empty_cache()
@@ -727,15 +760,11 @@ def main():
 
     w = synthetic.WORKLOADS[args.workload]
     T = args.T
-    ms, rot, y = run_projection(ngq, w, T, args.steps, args.warmup)
+    ms, rot, y, launch = run_projection(ngq, w, T, args.steps, args.warmup)
     nbytes = algorithmic_bytes(ngq, w, T)
     gbps = nbytes / ms / 1e6
-    # the graph's last launch must equal an eager launch on the same replica
-    last = (args.steps - 1) % rot.replicas
-    y_graph = y.clone()
-    ngq.ngq_gemm(rot.x, rot.wq[last], rot.s[last], w.bits, w.N, y=y)
-    torch.cuda.synchronize()
-    graph_ok = bool(torch.equal(y_graph, y))
+    # the launch replays from a captured graph to the eager result
+    graph_ok = graph_matches_eager(launch, rot.replicas)
     host = gpu_output(ngq, rot, y)
     cold = rot.cold_bytes
     replicas = rot.replicas
@@ -748,7 +777,7 @@ def main():
             wl = synthetic.WORKLOADS[name]
             # T > 8: the verify rounds of several requests in one call
             for t in (1, 2, 4, 8, 16, 32, 64):
-                ms_t, r, _ = run_projection(ngq, wl, t, args.sweep_steps, 10)
+                ms_t, r, _, _ = run_projection(ngq, wl, t, args.sweep_steps, 10)
                 b = algorithmic_bytes(ngq, wl, t)
                 sweep.append({"workload": f"{name} int{wl.bits} K={wl.K} N={wl.N}", "T": t, "us": ms_t * 1e3,
                               "GBps": b / ms_t / 1e6, "pct_peak": 100 * b / ms_t / 1e6 / PEAK_GBS})
@@ -759,7 +788,7 @@ def main():
         sweep.extend(run_fused(ngq, (1, 8), args.sweep_steps))
         wl = synthetic.WORKLOADS["qk8"]  # int8: reported, not part of the metric
         for t in (1, 8):
-            ms_t, r, _ = run_projection(ngq, wl, t, args.sweep_steps, 10)
+            ms_t, r, _, _ = run_projection(ngq, wl, t, args.sweep_steps, 10)
             b = algorithmic_bytes(ngq, wl, t)
             sweep.append({"workload": f"qk-shaped int8 K={wl.K} N={wl.N}", "T": t, "us": ms_t * 1e3,
                           "GBps": b / ms_t / 1e6, "pct_peak": 100 * b / ms_t / 1e6 / PEAK_GBS})
