@@ -349,7 +349,8 @@ def run_attainable(ngq, steps):
                         rot.replicas, steps, 10)
         b = packed_bytes(ngq, w) + ngq.ngq_scale_bytes(w.K, w.N, w.bits)
         out[name] = {"us": ms * 1e3, "weight_bytes": b, "GBps": b / ms / 1e6, "pct_peak": 100 * b / ms / 1e6 / PEAK_GBS,
-                     "pattern": f"{cols}-column tiles, {10 if cols == 32 else 8} waves, one pair in flight per wave"}
+                     "pattern": f"{cols}-column tiles, {(5 if w.bits == 8 else 10) if cols == 32 else 8} waves, "
+                                "one pair in flight per wave"}
         del rot
         torch.cuda.empty_cache()
     return out

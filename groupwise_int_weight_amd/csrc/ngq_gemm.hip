@@ -2904,23 +2904,37 @@ hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, uint32_t l
   return f.scale_bf16 ? launch_v<8, true, NSETS, DYN>(v, a, lds, st) : launch_v<8, false, NSETS, DYN>(v, a, lds, st);
 }
 
-// The streaming single-round kernel: 10 waves, 32-column tiles (16 where N
-// is narrower), one workgroup per tile (LDS under 64 KiB); the X load class
-// follows T.
+// The streaming single-round kernels: one workgroup per tile of 32 columns
+// (16 where N is narrower), LDS under 64 KiB, the X load class following T.
+// Waves per workgroup: 10 for int4 and int5; for int8, whose pair of a
+// 32-column tile is twice as large, 5 (MFMA step) and 8 (VALU step).  A
+// weights-only stream of the int8 QK-shape tiles took 9.78 us with 5 waves,
+// 10.11 with 6, 10.28 with 8 and 10.32 with 10 (int4: 10 waves best, 6.08 us
+// against 6.52 with 12 and 6.66 with 8); in an interleaved A/B of the whole
+// kernels, int8 with 5 streaming waves took 10.41, 10.31, 10.90 us at T = 2,
+// 4, 8 against 10.66, 10.70, 11.13 for the 14-wave X-resident kernel, and
+// the VALU step with 8 waves 10.26 at T = 1 against 10.77 with 10.
 constexpr int kStreamW = 10;
+constexpr int kStreamW8 = 5;
+constexpr int kDotW8 = 8;
+// int8 at T >= 2 on the streaming kernel (else the 14-wave X-resident one)
+constexpr bool kInt8Stream = true;
+constexpr int stream_waves(int bits) { return bits == 8 ? kStreamW8 : kStreamW; }
+constexpr int dot_waves(int bits) { return bits == 8 ? kDotW8 : kStreamW; }
+
 template <int BITS, bool SBF16, int V>
 hipError_t launch_stream_v(const dev::GemmArgs& a, hipStream_t st) {
+  constexpr int W = stream_waves(BITS);
   auto one = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(kStreamW * 64), dev::StreamSmem<kStreamW>::bytes(16 * V),
-                       st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(W * 64), dev::StreamSmem<W>::bytes(16 * V), st, a);
     return hipGetLastError();
   };
-  if (a.T == 1) return one(dev::gemm_stream_kernel<BITS, SBF16, V, kStreamW, 1>);
-  if (a.T == 2) return one(dev::gemm_stream_kernel<BITS, SBF16, V, kStreamW, 2>);
-  if (a.T <= 4) return one(dev::gemm_stream_kernel<BITS, SBF16, V, kStreamW, 4>);
-  return one(dev::gemm_stream_kernel<BITS, SBF16, V, kStreamW, 8>);
+  if (a.T == 1) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 1>);
+  if (a.T == 2) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 2>);
+  if (a.T <= 4) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 4>);
+  return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 8>);
 }
-static_assert(dev::StreamSmem<kStreamW>::bytes(32) <= 64u * 1024u,
+static_assert(dev::StreamSmem<kStreamW>::bytes(32) <= 64u * 1024u && dev::StreamSmem<kStreamW8>::bytes(32) <= 64u * 1024u,
               "the streaming kernel's LDS stays under the default 64 KiB limit");
 
 template <int BITS, bool SBF16>
@@ -2938,16 +2952,18 @@ hipError_t launch_stream(const Format& f, int v, const dev::GemmArgs& a, hipStre
 // pipeline and tiles (32 columns, 10 waves).
 template <int BITS, bool SBF16>
 hipError_t launch_dot_b(const dev::GemmArgs& a, hipStream_t st) {
+  constexpr int W = dot_waves(BITS);
   auto one = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(kStreamW * 64), dev::DotSmem<kStreamW>::bytes(), st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(W * 64), dev::DotSmem<W>::bytes(), st, a);
     return hipGetLastError();
   };
-  if (a.T == 1) return one(dev::gemm_dot_kernel<BITS, SBF16, kStreamW, 1>);
-  if (a.T == 2) return one(dev::gemm_dot_kernel<BITS, SBF16, kStreamW, 2>);
-  if (a.T <= 4) return one(dev::gemm_dot_kernel<BITS, SBF16, kStreamW, 4>);
-  return one(dev::gemm_dot_kernel<BITS, SBF16, kStreamW, 8>);
+  if (a.T == 1) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 1>);
+  if (a.T == 2) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 2>);
+  if (a.T <= 4) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 4>);
+  return one(dev::gemm_dot_kernel<BITS, SBF16, W, 8>);
 }
-static_assert(dev::DotSmem<kStreamW>::bytes() <= 64u * 1024u, "the VALU kernel's LDS stays under 64 KiB");
+static_assert(dev::DotSmem<kStreamW>::bytes() <= 64u * 1024u && dev::DotSmem<kDotW8>::bytes() <= 64u * 1024u,
+              "the VALU kernel's LDS stays under 64 KiB");
 
 hipError_t launch_dot(const Format& f, const dev::GemmArgs& a, hipStream_t st) {
   if (f.bits == 4) return f.scale_bf16 ? launch_dot_b<4, true>(a, st) : launch_dot_b<4, false>(a, st);
@@ -3193,10 +3209,10 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   //  - one round of 32-column tiles and one output set: at T = 1 the VALU
   //    inner step for int4 and int8 (QK shape: 6.39 against 6.52 us with the
   //    MFMA step, int8 10.71 against 10.92; from T = 2 the MFMA step wins,
-  //    by 27 % at T = 2 and 2.7x at T = 8), otherwise the streaming kernel
-  //    for int4 and int5 (QK, T = 2..8: 6.5-7.4 us against 7.4-7.9 for the
-  //    14-wave X-resident kernel) and the X-resident kernel for int8 (equal
-  //    times); other one-round shapes: per-pair X with dynamic pair
+  //    by 12-22 % at T = 2 and 2-2.7x at T = 8), otherwise the streaming
+  //    kernel (QK, T = 2..8: 6.5-7.4 us against 7.4-7.9 for the 14-wave
+  //    X-resident kernel; int8 with 5 waves, 2-4 % ahead of the X-resident
+  //    kernel); other one-round shapes: per-pair X with dynamic pair
   //    assignment (gate/value: 48-column tiles, where the streaming kernel's
   //    int5 unpack did not keep up);
   //  - otherwise the X-resident kernel with 8 waves when X fits in LDS;
@@ -3209,7 +3225,7 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     const bool one_round = nsets == 1 && tiles_pp <= cus && pp_dyn_fits;
     if (one_round && v_pp == 2 && T == 1 && f.bits != 5 && K > 0)
       path = NGQ_KERNEL_DOT;
-    else if (one_round && v_pp == 2 && f.bits != 8 && K > 0)
+    else if (one_round && v_pp == 2 && (f.bits != 8 || kInt8Stream) && K > 0)
       path = NGQ_KERNEL_STREAM;
     else if (one_round && v_pp == 2 && xres_fits(kX14, vx, lx))
       path = NGQ_KERNEL_XRES14;
@@ -3243,14 +3259,14 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   hipError_t e;
   if (path == NGQ_KERNEL_DOT) {
     a.ntiles = (Nout + 31) / 32;
-    a.ppw = (a.pairs + kStreamW - 1) / kStreamW;
+    a.ppw = (a.pairs + dot_waves(f.bits) - 1) / dot_waves(f.bits);
     e = launch_dot(f, a, st);
     return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
   }
   if (path == NGQ_KERNEL_STREAM) {
     const int vs = Nout >= 32 ? 2 : 1;
     a.ntiles = (Nout + 16 * vs - 1) / (16 * vs);
-    a.ppw = (a.pairs + kStreamW - 1) / kStreamW;
+    a.ppw = (a.pairs + stream_waves(f.bits) - 1) / stream_waves(f.bits);
     e = launch_stream(f, vs, a, st);
     return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
   }
@@ -3795,7 +3811,7 @@ extern "C" int ngq_stream_tiles(int K, int N, int bits, int group, int cols, con
   a.pairs = (a.G + 1) / 2;
   a.ntiles = ntiles;
   a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb;
-  const int W = cols == 32 ? 10 : 8;
+  const int W = cols == 32 ? stream_waves(f.bits) : 8;
   a.ppw = (a.pairs + W - 1) / W;
   uint32_t* sk = static_cast<uint32_t*>(sink);
   hipStream_t st = (hipStream_t)stream;
@@ -3805,7 +3821,7 @@ extern "C" int ngq_stream_tiles(int K, int N, int bits, int group, int cols, con
   };
   if (f.bits == 4) return cols == 32 ? go(dev::stream_tiles_kernel<4, 2, 10>, 10) : go(dev::stream_tiles_kernel<4, 3, 8>, 8);
   if (f.bits == 5) return cols == 32 ? go(dev::stream_tiles_kernel<5, 2, 10>, 10) : go(dev::stream_tiles_kernel<5, 3, 8>, 8);
-  return cols == 32 ? go(dev::stream_tiles_kernel<8, 2, 10>, 10) : go(dev::stream_tiles_kernel<8, 3, 8>, 8);
+  return cols == 32 ? go(dev::stream_tiles_kernel<8, 2, kStreamW8>, kStreamW8) : go(dev::stream_tiles_kernel<8, 3, 8>, 8);
 }
 
 extern "C" int ngq_debug_force_kernel(int path) {

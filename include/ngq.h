@@ -280,8 +280,9 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
 #define NGQ_KERNEL_TILED_SX128 9    /* the same with 128-token tiles (int4 only) */
 #define NGQ_KERNEL_STREAM 10        /* T <= 8, one workgroup per column tile, each wave streams its
                                        pairs with their X band (plain projections only) */
-#define NGQ_KERNEL_DOT 11           /* the same pipeline with the multiply-add on the VALU (bf16 dot2),
-                                       for measuring against the MFMA step (plain projections only) */
+#define NGQ_KERNEL_DOT 11           /* the same pipeline with the multiply-add on the VALU (bf16 dot2);
+                                       the library's choice at T = 1 for int4 and int8 (plain
+                                       projections only) */
 int ngq_debug_force_kernel(int path);
 
 /* Bandwidth calibration: stream `bytes` (a multiple of 16) from device memory
@@ -292,7 +293,8 @@ int ngq_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
 
 /* Calibration: the weight stream of a K x N projection in the access pattern
  * of the streaming decode kernel (NGQ_KERNEL_STREAM), alone: the same column
- * tiles (cols = 32, 10 waves; or 48, 8 waves), pair order and loads of the
+ * tiles (cols = 32 with that kernel's waves per workgroup: 10, or 5 for
+ * int8; or cols = 48, 8 waves), pair order and loads of the
  * packed words and scales, with no X, no arithmetic and no output.  Its
  * launch time is what this pattern can attain for the projection's weight
  * bytes, which the bench reports beside the HBM peak.
