@@ -3222,10 +3222,16 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   int v = v_pp, vx = 0;
   uint32_t lx = 0;
   if (path == NGQ_KERNEL_AUTO) {
-    const bool one_round = nsets == 1 && tiles_pp <= cus && pp_dyn_fits;
-    if (one_round && v_pp == 2 && T == 1 && f.bits != 5 && K > 0)
+    const bool one_round_tiles = nsets == 1 && tiles_pp <= cus;
+    const bool one_round = one_round_tiles && pp_dyn_fits;
+    // the streaming kernels need no per-pair LDS blocks: long K (the down
+    // projection, 160 tiles) takes them too up to T = 4 (measured there:
+    // T = 1 VALU step 14.2 us against 15.3 X-resident, T = 2 and 4 MFMA step
+    // 2 % ahead; at T = 8 the per-pair kernel stays 2 % ahead)
+    const bool streams = one_round_tiles && v_pp == 2 && K > 0 && (pp_dyn_fits || T <= 4);
+    if (streams && T == 1 && f.bits != 5)
       path = NGQ_KERNEL_DOT;
-    else if (one_round && v_pp == 2 && (f.bits != 8 || kInt8Stream) && K > 0)
+    else if (streams && (f.bits != 8 || kInt8Stream))
       path = NGQ_KERNEL_STREAM;
     else if (one_round && v_pp == 2 && xres_fits(kX14, vx, lx))
       path = NGQ_KERNEL_XRES14;
