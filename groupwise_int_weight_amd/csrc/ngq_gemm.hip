@@ -1023,21 +1023,21 @@ __global__ __launch_bounds__(W * 64) void gemm_xres_kernel(GemmArgs a) {
 // The band is written to a per-wave LDS slot in the interleaved k order of
 // the unpack: 16-bit stores to their places for T <= 2, one permute per
 // 4 bytes and 16-byte stores otherwise.
-template <int BITS, int V>
+template <int BITS, int V, int NSETS>
 struct StreamBuf {
   static constexpr int WPK = BITS == 8 ? 2 : 1;
-  uint32_t a[4][V * WPK];             // [step][word]; int8: V words of row 2kb, then 2kb+1
-  uint32_t p1[2][BITS == 5 ? V : 1];  // int5 high-bit words, one per group of the pair
-  uint32_t sc[2 * V];                 // 4V scales (16-bit)
-  uint32_t x[2][4];                   // the pair's X band
+  uint32_t a[NSETS][4][V * WPK];             // [set][step][word]; int8: V words of row 2kb, then 2kb+1
+  uint32_t p1[NSETS][2][BITS == 5 ? V : 1];  // int5 high-bit words, one per group of the pair
+  uint32_t sc[NSETS][2 * V];                 // 4V scales (16-bit)
+  uint32_t x[2][4];                          // the pair's X band
 };
 
 // LDS of the streaming kernel: one X staging slot per wave (gemm_kernel's
 // layout), then one partial-sum block per wave.
 template <int W>
 struct StreamSmem {
-  static __host__ __device__ constexpr uint32_t bytes(int tile) {
-    return (uint32_t)W * Smem::XSLOT + (uint32_t)W * Smem::block_floats(1, tile) * 4u;
+  static __host__ __device__ constexpr uint32_t bytes(int tile, int nsets = 1) {
+    return (uint32_t)W * Smem::XSLOT + (uint32_t)W * Smem::block_floats(nsets, tile) * 4u;
   }
 };
 
@@ -1050,12 +1050,14 @@ __device__ __forceinline__ uint32_t il_offset(uint32_t k) {
 // XM: the X load class, 1 (T = 1), 2 (T = 2), 4 (T = 3, 4) or 8 (T > 4); a
 // template parameter so that no load sits under a branch (where the compiler
 // waits for it, and with it every older load, before the join)
-template <int BITS, bool SBF16, int V, int W, int XM>
+// NSETS = 2: the SwiGLU gate/up projection, the tile's columns of both
+// halves (gate at c, up at up_off + c) in each pair.
+template <int BITS, bool SBF16, int V, int W, int XM, int NSETS>
 __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
   constexpr int WPK = BITS == 8 ? 2 : 1;
   constexpr int TILE = 16 * V;
   constexpr uint32_t XROW = Smem::XROW, XZERO = Smem::XZERO;
-  constexpr uint32_t BLK = Smem::block_floats(1, TILE);
+  constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* const part = reinterpret_cast<float*>(smem + (uint32_t)W * Smem::XSLOT);
 
@@ -1081,11 +1083,16 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
   const uint32_t rowb = (uint32_t)a.Ncols * 4u;
   // k-slot q of step st reads k-block 2 st + (q & 1) of group (q >> 1)
   const uint32_t lane_kb = 8u * (uint32_t)(q >> 1) + (uint32_t)(q & 1);
-  const uint32_t col = c0 + (uint32_t)(V * m);
-  const uint32_t offA = lane_kb * WPK * rowb + col * 4u;
-  const uint32_t offP1 = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
-  // result rows 4q..4q+3 of every MFMA -> columns c0 + 4Vq + [0, 4V)
-  const uint32_t offS = (uint32_t)h * (uint32_t)a.Ncols * 2u + (c0 + (uint32_t)(4 * V * q)) * 2u;
+  uint32_t offA[NSETS], offP1[NSETS], offS[NSETS];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s) {
+    const uint32_t cs = c0 + (uint32_t)(s * a.up_off);
+    const uint32_t col = cs + (uint32_t)(V * m);
+    offA[s] = lane_kb * WPK * rowb + col * 4u;
+    offP1[s] = 2u * (uint32_t)(q >> 1) * rowb + col * 4u;
+    // result rows 4q..4q+3 of every MFMA -> columns c0 + 4Vq + [0, 4V)
+    offS[s] = (uint32_t)h * (uint32_t)a.Ncols * 2u + (cs + (uint32_t)(4 * V * q)) * 2u;
+  }
 
   // This lane's share of a band: token row xt, first element xk (of the
   // band's 128), xe elements; chunk loads (T > 2) take 8 elements from rows
@@ -1115,22 +1122,28 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
 
   // the loads of pair p (p >= pairs: out of range, nothing moves); flags are
   // combined bitwise so that no lane-divergent branch appears
-  auto issue = [&](StreamBuf<BITS, V>& buf, int p) {
+  auto issue = [&](StreamBuf<BITS, V, NSETS>& buf, int p) {
     const bool valid = p < a.pairs;
     const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb : kOOB;
     const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb : kOOB;
     const uint32_t ps = valid ? (uint32_t)p * rowb : kOOB;  // two scale rows of 2-byte entries
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const uint32_t o = offA + pa + (uint32_t)st * 2u * WPK * rowb;
-      load_words<V, kNT>(&buf.a[st][0], rW, o);
-      if constexpr (BITS == 8) load_words<V, kNT>(&buf.a[st][V], rW, o + rowb);
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        const uint32_t o = offA[s] + pa + (uint32_t)st * 2u * WPK * rowb;
+        load_words<V, kNT>(&buf.a[s][st][0], rW, o);
+        if constexpr (BITS == 8) load_words<V, kNT>(&buf.a[s][st][V], rW, o + rowb);
+      }
     }
-    if constexpr (BITS == 5) {
-      load_words<V, kNT>(&buf.p1[0][0], rP1, offP1 + pp1);
-      load_words<V, kNT>(&buf.p1[1][0], rP1, offP1 + pp1 + rowb);
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) {
+      if constexpr (BITS == 5) {
+        load_words<V, kNT>(&buf.p1[s][0][0], rP1, offP1[s] + pp1);
+        load_words<V, kNT>(&buf.p1[s][1][0], rP1, offP1[s] + pp1 + rowb);
+      }
+      load_words<2 * V, kNT>(&buf.sc[s][0], rS, offS[s] + ps);
     }
-    load_words<2 * V, kNT>(&buf.sc[0], rS, offS + ps);
     // the band: the second group of the last pair of an odd group count
     // does not exist (elements 64..127 of its band read nothing)
     const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
@@ -1149,7 +1162,7 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
 
   // the landed band of a pair into the slot (the previous pair's B fragments
   // have been read: LDS is in order within a wave)
-  auto stage_x = [&](const StreamBuf<BITS, V>& buf) {
+  auto stage_x = [&](const StreamBuf<BITS, V, NSETS>& buf) {
     if constexpr (xmode <= 2) {
       uint16_t* const d = reinterpret_cast<uint16_t*>(xslot + xdst);
       // element xk + e sits il_offset(xk + e) - il_offset(xk) bytes on: xk is
@@ -1168,15 +1181,17 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
     }
   };
 
-  f32x4 acc[V];
+  f32x4 acc[NSETS][V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4 negoff = {Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u,
                         Code<BITS>::neg_offset_bf16 * 0x10001u, Code<BITS>::neg_offset_bf16 * 0x10001u};
 
   // one pair: its B fragments from the slot, multiply, scale into the
   // accumulators
-  auto compute = [&](const StreamBuf<BITS, V>& buf) {
+  auto compute = [&](const StreamBuf<BITS, V, NSETS>& buf) {
     bf16x8 bfrag[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -1185,39 +1200,47 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
     for (int st = 0; st < 4; ++st)
       dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, negoff), bfrag[st], dx, 0, 0, 0);
-    f32x4 dp[V];
+    f32x4 dp[NSETS][V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) dp[i] = dx;
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < V; ++i) dp[s][i] = dx;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        u32x4 av;
-        if constexpr (BITS == 4) {
-          av = nibbles_to_bf16_il(buf.a[st][i], mk);
-        } else if constexpr (BITS == 5) {
-          const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[st >> 1][i], 16u * (uint32_t)(st & 1) +
-                                                                           8u * (uint32_t)(q & 1), 8u);
-          av = nibbles5_to_bf16_il(buf.a[st][i], hb, mk);
-        } else {
-          av = bytes_to_bf16_il(buf.a[st][i], buf.a[st][V + i]);
+      for (int s = 0; s < NSETS; ++s) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          u32x4 av;
+          if constexpr (BITS == 4) {
+            av = nibbles_to_bf16_il(buf.a[s][st][i], mk);
+          } else if constexpr (BITS == 5) {
+            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
+                                                                                 8u * (uint32_t)(q & 1), 8u);
+            av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, mk);
+          } else {
+            av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
+          }
+          dp[s][i] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag[st], dp[s][i], 0, 0, 0);
         }
-        dp[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bfrag[st], dp[i], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int i = 0; i < V; ++i)
+    for (int s = 0; s < NSETS; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = V * r + i;
-        acc[i][r] = __builtin_fmaf(scale_to_f32(buf.sc[e >> 1], e & 1, SBF16), dp[i][r], acc[i][r]);
-      }
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = V * r + i;
+          acc[s][i][r] = __builtin_fmaf(scale_to_f32(buf.sc[s][e >> 1], e & 1, SBF16), dp[s][i][r], acc[s][i][r]);
+        }
   };
 
   // Pair slot i of this wave is pair wave + W i.  Two buffers: once slot i
   // has landed, slot i + 1 is requested, then slot i is computed.  A slot
   // past the last pair loads nothing and is not computed.
-  StreamBuf<BITS, V> buf[2];
+  StreamBuf<BITS, V, NSETS> buf[2];
   issue(buf[0], pair_of(0));
   __builtin_amdgcn_sched_barrier(0);
   for (int i = 0; i < a.ppw; i += 2) {
@@ -1238,17 +1261,14 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
 
   // the two group halves of each token (slots j, j + 8), then the wave
   // blocks summed in wave order
-  f32x4 accs[1][V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) accs[0][i] = acc[i];
   XresLane ln;
   ln.t = t;
   ln.q = q;
   ln.h = h;
-  store_partials<V, 1>(accs, ln, part + (uint32_t)wave * BLK);
+  store_partials<V, NSETS>(acc, ln, part + (uint32_t)wave * BLK);
   lds_barrier();
   const ProjView pv{a.wq, a.scales, a.y, a.p0_bytes, a.p1_bytes, a.s_bytes, a.Nout, a.Ncols, a.up_off};
-  finish_outputs<V, 1, W>(part, pv, a.T, (int)c0);
+  finish_outputs<V, NSETS, W>(part, pv, a.T, (int)c0);
 }
 
 // ---- the same stream with a VALU inner step ---------------------------------
@@ -2916,36 +2936,45 @@ hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, uint32_t l
 // the VALU step with 8 waves 10.26 at T = 1 against 10.77 with 10.
 constexpr int kStreamW = 10;
 constexpr int kStreamW8 = 5;
+constexpr int kStreamW2 = 5;  // SwiGLU (two output sets), whose pairs are twice as large
+constexpr int kStreamSwigluMaxT = 4;
 constexpr int kDotW8 = 8;
 // int8 at T >= 2 on the streaming kernel (else the 14-wave X-resident one)
 constexpr bool kInt8Stream = true;
-constexpr int stream_waves(int bits) { return bits == 8 ? kStreamW8 : kStreamW; }
+constexpr int stream_waves(int bits, int nsets = 1) {
+  return nsets == 2 ? kStreamW2 : (bits == 8 ? kStreamW8 : kStreamW);
+}
 constexpr int dot_waves(int bits) { return bits == 8 ? kDotW8 : kStreamW; }
 
-template <int BITS, bool SBF16, int V>
+template <int BITS, bool SBF16, int V, int NSETS>
 hipError_t launch_stream_v(const dev::GemmArgs& a, hipStream_t st) {
-  constexpr int W = stream_waves(BITS);
+  constexpr int W = stream_waves(BITS, NSETS);
   auto one = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(W * 64), dev::StreamSmem<W>::bytes(16 * V), st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(W * 64), dev::StreamSmem<W>::bytes(16 * V, NSETS), st,
+                       a);
     return hipGetLastError();
   };
-  if (a.T == 1) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 1>);
-  if (a.T == 2) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 2>);
-  if (a.T <= 4) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 4>);
-  return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 8>);
+  if (a.T == 1) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 1, NSETS>);
+  if (a.T == 2) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 2, NSETS>);
+  if (a.T <= 4) return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 4, NSETS>);
+  return one(dev::gemm_stream_kernel<BITS, SBF16, V, W, 8, NSETS>);
 }
-static_assert(dev::StreamSmem<kStreamW>::bytes(32) <= 64u * 1024u && dev::StreamSmem<kStreamW8>::bytes(32) <= 64u * 1024u,
+static_assert(dev::StreamSmem<kStreamW>::bytes(32) <= 64u * 1024u && dev::StreamSmem<kStreamW8>::bytes(32) <= 64u * 1024u &&
+                  dev::StreamSmem<kStreamW2>::bytes(32, 2) <= 64u * 1024u,
               "the streaming kernel's LDS stays under the default 64 KiB limit");
 
-template <int BITS, bool SBF16>
+template <int BITS, bool SBF16, int NSETS>
 hipError_t launch_stream_b(int v, const dev::GemmArgs& a, hipStream_t st) {
-  return v >= 2 ? launch_stream_v<BITS, SBF16, 2>(a, st) : launch_stream_v<BITS, SBF16, 1>(a, st);
+  return v >= 2 ? launch_stream_v<BITS, SBF16, 2, NSETS>(a, st) : launch_stream_v<BITS, SBF16, 1, NSETS>(a, st);
 }
 
+template <int NSETS>
 hipError_t launch_stream(const Format& f, int v, const dev::GemmArgs& a, hipStream_t st) {
-  if (f.bits == 4) return f.scale_bf16 ? launch_stream_b<4, true>(v, a, st) : launch_stream_b<4, false>(v, a, st);
-  if (f.bits == 5) return f.scale_bf16 ? launch_stream_b<5, true>(v, a, st) : launch_stream_b<5, false>(v, a, st);
-  return f.scale_bf16 ? launch_stream_b<8, true>(v, a, st) : launch_stream_b<8, false>(v, a, st);
+  if (f.bits == 4)
+    return f.scale_bf16 ? launch_stream_b<4, true, NSETS>(v, a, st) : launch_stream_b<4, false, NSETS>(v, a, st);
+  if (f.bits == 5)
+    return f.scale_bf16 ? launch_stream_b<5, true, NSETS>(v, a, st) : launch_stream_b<5, false, NSETS>(v, a, st);
+  return f.scale_bf16 ? launch_stream_b<8, true, NSETS>(v, a, st) : launch_stream_b<8, false, NSETS>(v, a, st);
 }
 
 // The VALU-inner-step kernel (measurement path): the streaming kernel's
@@ -3215,6 +3244,11 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   //    kernel); other one-round shapes: per-pair X with dynamic pair
   //    assignment (gate/value: 48-column tiles, where the streaming kernel's
   //    int5 unpack did not keep up);
+  //  - SwiGLU at T <= 4: the streaming kernel with 5 waves and one
+  //    workgroup per 32-column tile (gate/up, 544 tiles: 23.5 us against 27.0
+  //    for the persistent X-resident kernel, whose 2.125 rounds of tiles end
+  //    in a round on 32 CUs; 3, 4, 6, 8 waves: 24.7-27.3; at T = 8 the X
+  //    bands make it 3 % slower than the X-resident kernel);
   //  - otherwise the X-resident kernel with 8 waves when X fits in LDS;
   //  - otherwise per-pair X (dynamic, or static ranges for very long K).
   int path = forced;
@@ -3233,6 +3267,8 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
       path = NGQ_KERNEL_DOT;
     else if (streams && (f.bits != 8 || kInt8Stream))
       path = NGQ_KERNEL_STREAM;
+    else if (nsets == 2 && T <= kStreamSwigluMaxT && f.bits != 8 && K > 0)
+      path = NGQ_KERNEL_STREAM;
     else if (one_round && v_pp == 2 && xres_fits(kX14, vx, lx))
       path = NGQ_KERNEL_XRES14;
     else if (!one_round && xres_fits(x8, vx, lx))
@@ -3243,7 +3279,7 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     if (!xres_fits(path == NGQ_KERNEL_XRES14 ? kX14 : x8, vx, lx)) return NGQ_ERR_UNSUPPORTED;
   } else if (path == NGQ_KERNEL_PERPAIR_DYN && !pp_dyn_fits) {
     return NGQ_ERR_UNSUPPORTED;
-  } else if ((path == NGQ_KERNEL_STREAM || path == NGQ_KERNEL_DOT) && nsets != 1) {
+  } else if (path == NGQ_KERNEL_DOT && nsets != 1) {
     return NGQ_ERR_UNSUPPORTED;  // no SwiGLU epilogue
   }
   const bool xres = path == NGQ_KERNEL_XRES14 || path == NGQ_KERNEL_XRES8;
@@ -3272,8 +3308,9 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   if (path == NGQ_KERNEL_STREAM) {
     const int vs = Nout >= 32 ? 2 : 1;
     a.ntiles = (Nout + 16 * vs - 1) / (16 * vs);
-    a.ppw = (a.pairs + stream_waves(f.bits) - 1) / stream_waves(f.bits);
-    e = launch_stream(f, vs, a, st);
+    const int ws = stream_waves(f.bits, nsets);
+    a.ppw = (a.pairs + ws - 1) / ws;
+    e = nsets == 1 ? launch_stream<1>(f, vs, a, st) : launch_stream<2>(f, vs, a, st);
     return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
   }
   if (xres) {

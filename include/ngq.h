@@ -264,7 +264,7 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
  * and 11 are the T <= 8 kernels (larger T keeps the library's choice under them);
  * NGQ_KERNEL_WIDE serves 8 < T <= 64; the token x column paths serve any T
  * (the 96- and 128-token ones int4 only).  A forced path that cannot serve a shape (X or the partial sums do not
- * fit in LDS, the 14-wave, streaming and VALU kernels with the SwiGLU epilogue, NGQ_KERNEL_WIDE
+ * fit in LDS, the 14-wave and VALU kernels with the SwiGLU epilogue, NGQ_KERNEL_WIDE
  * outside its T range) makes those calls return NGQ_ERR_UNSUPPORTED.
  * Returns the previous setting, or NGQ_ERR_ARG for an unknown path.  Not
  * thread-safe with respect to calls that are running. */
@@ -279,7 +279,7 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
 #define NGQ_KERNEL_TILED_SX96 8     /* the same with 96-token tiles (int4 only) */
 #define NGQ_KERNEL_TILED_SX128 9    /* the same with 128-token tiles (int4 only) */
 #define NGQ_KERNEL_STREAM 10        /* T <= 8, one workgroup per column tile, each wave streams its
-                                       pairs with their X band (plain projections only) */
+                                       pairs with their X band (plain or SwiGLU) */
 #define NGQ_KERNEL_DOT 11           /* the same pipeline with the multiply-add on the VALU (bf16 dot2);
                                        the library's choice at T = 1 for int4 and int8 (plain
                                        projections only) */
