@@ -94,8 +94,10 @@ class Rotation:
 
 
 # GPU clock cycles of the spin kernel queued ahead of the timed launches (at
-# least ~0.4 ms), and the cycles per microsecond it is sized with
-LEAD_CYCLES = 1_000_000
+# least ~2 ms: with ~0.4 ms, 20 QK launches timed 7.66 us each against 7.49,
+# and varied more; 200 launches were unaffected), and the cycles per
+# microsecond it is sized with
+LEAD_CYCLES = 5_000_000
 SPIN_CYCLES_PER_US = 2400
 
 
