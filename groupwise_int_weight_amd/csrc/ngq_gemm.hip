@@ -1285,28 +1285,36 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
 // the same pipeline, it is the faster of the two only at T = 1 for int4 and
 // int8 (the projection's rows then cost one dot2 per two weights; from T = 2
 // the VALU issue grows with T while the MFMA step's does not), where the
-// library routes to it.
-template <int W>
+// library routes to it, and for the int4 SwiGLU projection at T = 1.
+// NSETS = 2: the SwiGLU gate/up projection; the lane also owns column
+// up_off + c0 + c (the up half), and each X element read from LDS serves
+// both columns.
+template <int W, int XM, int NSETS>
 struct DotSmem {
+  static constexpr uint32_t SLOT = (uint32_t)XM * Smem::XROW;  // per wave: the pair's X band, XM token rows
   static constexpr uint32_t SX = 16u * 4u;  // per wave: sums of x per (token, group) or per 16-lane row
-  static __host__ __device__ constexpr uint32_t sx_off() { return (uint32_t)W * Smem::XSLOT; }
+  static __host__ __device__ constexpr uint32_t sx_off() { return (uint32_t)W * SLOT; }
   static __host__ __device__ constexpr uint32_t part_off() { return sx_off() + (uint32_t)W * SX; }
-  static __host__ __device__ constexpr uint32_t bytes() { return part_off() + (uint32_t)W * 2u * 8u * 32u * 4u; }
+  // partial sums [wave][set][group][token][column]
+  static __host__ __device__ constexpr uint32_t bytes() {
+    return part_off() + (uint32_t)W * (uint32_t)NSETS * 2u * (uint32_t)XM * 32u * 4u;
+  }
 };
 
-template <int BITS>
+template <int BITS, int NSETS>
 struct DotBuf {
   static constexpr int WPK = BITS == 8 ? 2 : 1;
-  uint32_t a[8 * WPK];  // one word per k-block of the lane's group (int8: two)
-  uint32_t p1[BITS == 5 ? 2 : 1];
-  uint32_t sc;          // the lane's scale (16-bit)
-  uint32_t x[2][4];     // the pair's X band (the streaming kernel's load classes)
+  uint32_t a[NSETS][8 * WPK];  // one word per k-block of the lane's group (int8: two)
+  uint32_t p1[NSETS][BITS == 5 ? 2 : 1];
+  uint32_t sc[NSETS];          // the lane's scales (16-bit)
+  uint32_t x[2][4];            // the pair's X band (the streaming kernel's load classes)
 };
 
-template <int BITS, bool SBF16, int W, int XM>
+template <int BITS, bool SBF16, int W, int XM, int NSETS>
 __global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
   constexpr int WPK = BITS == 8 ? 2 : 1;
   constexpr uint32_t XROW = Smem::XROW;
+  using Lds = DotSmem<W, XM, NSETS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1326,10 +1334,14 @@ __global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
   const UnpackMasks mk{a.mask_nib, vbase, a.mask_hi};
 
   const uint32_t rowb = (uint32_t)a.Ncols * 4u;
-  const uint32_t colb = (c0 + (uint32_t)c) * 4u;
-  const uint32_t offW = 8u * (uint32_t)g * WPK * rowb + colb;      // k-block 0 of the lane's group
-  const uint32_t offP1 = 2u * (uint32_t)g * rowb + colb;
-  const uint32_t offS = (uint32_t)g * (uint32_t)a.Ncols * 2u + (c0 + (uint32_t)c) * 2u;
+  uint32_t offW[NSETS], offP1[NSETS], offS[NSETS];
+#pragma unroll
+  for (int s = 0; s < NSETS; ++s) {
+    const uint32_t col = c0 + (uint32_t)(s * a.up_off) + (uint32_t)c;
+    offW[s] = 8u * (uint32_t)g * WPK * rowb + col * 4u;  // k-block 0 of the lane's group
+    offP1[s] = 2u * (uint32_t)g * rowb + col * 4u;
+    offS[s] = (uint32_t)g * (uint32_t)a.Ncols * 2u + col * 2u;
+  }
 
   // the X band, as in gemm_stream_kernel
   const int T = a.T;
@@ -1339,25 +1351,28 @@ __global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
   const uint32_t offX = (uint32_t)xt * (uint32_t)a.K * 2u + (uint32_t)xk * 2u;
   const uint32_t rowX4 = 4u * (uint32_t)a.K * 2u;
   const bool x0_on = xt < T, x1_on = xt + 4 < T;
-  uint8_t* const xslot = smem + (uint32_t)wave * Smem::XSLOT;
-  float* const sxw = reinterpret_cast<float*>(smem + DotSmem<W>::sx_off() + (uint32_t)wave * DotSmem<W>::SX);
+  uint8_t* const xslot = smem + (uint32_t)wave * Lds::SLOT;
+  float* const sxw = reinterpret_cast<float*>(smem + Lds::sx_off() + (uint32_t)wave * Lds::SX);
   const uint32_t xdst = (uint32_t)xt * XROW + il_offset((uint32_t)xk);
 
   auto pair_of = [&](int i) { return wave + W * i; };
 
-  auto issue = [&](DotBuf<BITS>& buf, int p) {
+  auto issue = [&](DotBuf<BITS, NSETS>& buf, int p) {
     const bool valid = p < a.pairs;
     const bool half = (p == a.pairs - 1) & ((a.G & 1) != 0);
     const bool gin = valid & !(half & (g == 1));  // the lane's group exists
-    const uint32_t pa = gin ? (uint32_t)p * 16u * WPK * rowb + offW : kOOB;
 #pragma unroll
-    for (int kb = 0; kb < 8 * WPK; ++kb) load_words<1, kNT>(&buf.a[kb], rW, pa + (uint32_t)kb * rowb);
-    if constexpr (BITS == 5) {
-      const uint32_t pp1 = gin ? (uint32_t)p * 4u * rowb + offP1 : kOOB;
-      load_words<1, kNT>(&buf.p1[0], rP1, pp1);
-      load_words<1, kNT>(&buf.p1[1], rP1, pp1 + rowb);
+    for (int s = 0; s < NSETS; ++s) {
+      const uint32_t pa = gin ? (uint32_t)p * 16u * WPK * rowb + offW[s] : kOOB;
+#pragma unroll
+      for (int kb = 0; kb < 8 * WPK; ++kb) load_words<1, kNT>(&buf.a[s][kb], rW, pa + (uint32_t)kb * rowb);
+      if constexpr (BITS == 5) {
+        const uint32_t pp1 = gin ? (uint32_t)p * 4u * rowb + offP1[s] : kOOB;
+        load_words<1, kNT>(&buf.p1[s][0], rP1, pp1);
+        load_words<1, kNT>(&buf.p1[s][1], rP1, pp1 + rowb);
+      }
+      buf.sc[s] = __builtin_amdgcn_raw_buffer_load_b16(rS, gin ? (uint32_t)p * rowb + offS[s] : kOOB, 0, kNT);
     }
-    buf.sc = __builtin_amdgcn_raw_buffer_load_b16(rS, gin ? (uint32_t)p * rowb + offS : kOOB, 0, kNT);
     const bool xin = valid & !(half & (xk >= 64));
     const uint32_t px0 = (xin & x0_on) ? (uint32_t)p * 256u + offX : kOOB;
     if constexpr (xmode == 1) {
@@ -1376,7 +1391,7 @@ __global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
   // group) with DPP row shifts (8 lanes a segment for 16-byte chunks, 16 for
   // T = 2; for T = 1 the two 16-lane rows of a group are added by the reader)
   const uint32_t ones = 0x3F803F80u;  // bf16 (1, 1)
-  auto stage_x = [&](const DotBuf<BITS>& buf) {
+  auto stage_x = [&](const DotBuf<BITS, NSETS>& buf) {
     float s0 = 0.f, s1 = 0.f;
     if constexpr (xmode <= 2) {
       uint16_t* const d = reinterpret_cast<uint16_t*>(xslot + xdst);
@@ -1431,41 +1446,54 @@ __global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
     return sxw[t * 2 + g];
   };
 
-  float acc[XM];
+  float acc[NSETS][XM];
 #pragma unroll
-  for (int t = 0; t < XM; ++t) acc[t] = 0.f;
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int t = 0; t < XM; ++t) acc[s][t] = 0.f;
 
-  auto compute = [&](const DotBuf<BITS>& buf) {
-    float pacc[XM];
+  auto compute = [&](const DotBuf<BITS, NSETS>& buf) {
+    float pacc[NSETS][XM];
 #pragma unroll
-    for (int t = 0; t < XM; ++t) pacc[t] = 0.f;
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int t = 0; t < XM; ++t) pacc[s][t] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      u32x4 w;
-      if constexpr (BITS == 4) {
-        w = nibbles_to_bf16_il(buf.a[kb], mk);
-      } else if constexpr (BITS == 5) {
-        w = nibbles5_to_bf16_il(buf.a[kb], __builtin_amdgcn_ubfe(buf.p1[kb >> 2], 8u * (uint32_t)(kb & 3), 8u), mk);
-      } else {
-        w = bytes_to_bf16_il(buf.a[2 * kb], buf.a[2 * kb + 1]);
+      u32x4 w[NSETS];
+#pragma unroll
+      for (int s = 0; s < NSETS; ++s) {
+        if constexpr (BITS == 4) {
+          w[s] = nibbles_to_bf16_il(buf.a[s][kb], mk);
+        } else if constexpr (BITS == 5) {
+          w[s] = nibbles5_to_bf16_il(buf.a[s][kb], __builtin_amdgcn_ubfe(buf.p1[s][kb >> 2], 8u * (uint32_t)(kb & 3), 8u),
+                                     mk);
+        } else {
+          w[s] = bytes_to_bf16_il(buf.a[s][2 * kb], buf.a[s][2 * kb + 1]);
+        }
       }
 #pragma unroll
       for (int t = 0; t < XM; ++t) {
         if (t < T) {
           const u32x4 xr = *reinterpret_cast<const u32x4*>(xslot + (uint32_t)t * XROW + (uint32_t)(8 * g + kb) * 16u);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            pacc[t] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[j]), as_bf16x2(xr[j]), pacc[t], false);
+          for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              pacc[s][t] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w[s][j]), as_bf16x2(xr[j]), pacc[s][t], false);
         }
       }
     }
-    const float sc = scale_to_f32(buf.sc, 0, SBF16);
 #pragma unroll
-    for (int t = 0; t < XM; ++t)
-      if (t < T) acc[t] = __builtin_fmaf(sc, pacc[t] - (float)Code<BITS>::offset * sum_x(t), acc[t]);
+    for (int s = 0; s < NSETS; ++s) {
+      const float sc = scale_to_f32(buf.sc[s], 0, SBF16);
+#pragma unroll
+      for (int t = 0; t < XM; ++t)
+        if (t < T) acc[s][t] = __builtin_fmaf(sc, pacc[s][t] - (float)Code<BITS>::offset * sum_x(t), acc[s][t]);
+    }
   };
 
-  DotBuf<BITS> buf[2];
+  DotBuf<BITS, NSETS> buf[2];
   issue(buf[0], pair_of(0));
   __builtin_amdgcn_sched_barrier(0);
   for (int i = 0; i < a.ppw; i += 2) {
@@ -1484,24 +1512,40 @@ __global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // partial sums [wave][group][token][column], added in wave then group
-  // order
-  float* const part = reinterpret_cast<float*>(smem + DotSmem<W>::part_off());
+  // partial sums [wave][set][group][token][column], added in wave then group
+  // order; SwiGLU as in finish_outputs
+  float* const part = reinterpret_cast<float*>(smem + Lds::part_off());
+  auto slot = [](int w, int s, int gg, int t, int cc) -> uint32_t {
+    return (((((uint32_t)w * NSETS + (uint32_t)s) * 2u + (uint32_t)gg) * XM + (uint32_t)t) * 32u) + (uint32_t)cc;
+  };
 #pragma unroll
-  for (int t = 0; t < XM; ++t)
-    if (t < T) part[(((uint32_t)wave * 2u + (uint32_t)g) * 8u + (uint32_t)t) * 32u + (uint32_t)c] = acc[t];
+  for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+    for (int t = 0; t < XM; ++t)
+      if (t < T) part[slot(wave, s, g, t, c)] = acc[s][t];
   lds_barrier();
   uint16_t* y = static_cast<uint16_t*>(a.y);
-  for (int idx = threadIdx.x; idx < 8 * 32; idx += W * 64) {
+  for (int idx = threadIdx.x; idx < XM * 32; idx += W * 64) {
     const int tt = idx >> 5, cc = idx & 31;
     if (tt >= T || c0 + (uint32_t)cc >= (uint32_t)a.Nout) continue;
-    float sum = 0.f;
+    float v[NSETS];
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      sum += part[(((uint32_t)w * 2u) * 8u + (uint32_t)tt) * 32u + (uint32_t)cc];
-      sum += part[(((uint32_t)w * 2u + 1u) * 8u + (uint32_t)tt) * 32u + (uint32_t)cc];
+    for (int s = 0; s < NSETS; ++s) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        sum += part[slot(w, s, 0, tt, cc)];
+        sum += part[slot(w, s, 1, tt, cc)];
+      }
+      v[s] = sum;
     }
-    y[(size_t)tt * a.Nout + c0 + cc] = f32_to_bf16_rne(sum);
+    float out;
+    if constexpr (NSETS == 2) {
+      out = v[0] * v[1] / (1.0f + expf(-v[0]));  // SiLU(gate) * up
+    } else {
+      out = v[0];
+    }
+    y[(size_t)tt * a.Nout + c0 + cc] = f32_to_bf16_rne(out);
   }
 }
 
@@ -1702,7 +1746,7 @@ __global__ __launch_bounds__(kMultiW * 64) void gemm_multi_kernel(MultiArgs a) {
 // caller's workspace, and a second kernel adds the S partials of every output
 // in slice order and rounds to bf16, so the result is deterministic.
 
-constexpr int kSplitWaves = 5, kSplitNB = 4;
+constexpr int kSplitWaves = 5, kSplitNB = 3;
 
 struct SplitArgs {
   const void* x;
@@ -2939,12 +2983,13 @@ constexpr int kStreamW8 = 5;
 constexpr int kStreamW2 = 5;  // SwiGLU (two output sets), whose pairs are twice as large
 constexpr int kStreamSwigluMaxT = 4;
 constexpr int kDotW8 = 8;
+constexpr int kDotW2 = 7;  // SwiGLU (two output sets): three workgroups a CU at 81 VGPRs
 // int8 at T >= 2 on the streaming kernel (else the 14-wave X-resident one)
 constexpr bool kInt8Stream = true;
 constexpr int stream_waves(int bits, int nsets = 1) {
   return nsets == 2 ? kStreamW2 : (bits == 8 ? kStreamW8 : kStreamW);
 }
-constexpr int dot_waves(int bits) { return bits == 8 ? kDotW8 : kStreamW; }
+constexpr int dot_waves(int bits, int nsets = 1) { return nsets == 2 ? kDotW2 : (bits == 8 ? kDotW8 : kStreamW); }
 
 template <int BITS, bool SBF16, int V, int NSETS>
 hipError_t launch_stream_v(const dev::GemmArgs& a, hipStream_t st) {
@@ -2977,27 +3022,29 @@ hipError_t launch_stream(const Format& f, int v, const dev::GemmArgs& a, hipStre
   return f.scale_bf16 ? launch_stream_b<8, true, NSETS>(v, a, st) : launch_stream_b<8, false, NSETS>(v, a, st);
 }
 
-// The VALU-inner-step kernel (measurement path): the streaming kernel's
-// pipeline and tiles (32 columns, 10 waves).
-template <int BITS, bool SBF16>
+// The VALU-inner-step kernel: the streaming kernel's pipeline and tiles (32
+// columns; 10 waves, 8 for int8).
+template <int BITS, bool SBF16, int NSETS>
 hipError_t launch_dot_b(const dev::GemmArgs& a, hipStream_t st) {
-  constexpr int W = dot_waves(BITS);
-  auto one = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(W * 64), dev::DotSmem<W>::bytes(), st, a);
+  constexpr int W = dot_waves(BITS, NSETS);
+  auto one = [&](auto kern, uint32_t lds) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.ntiles), dim3(W * 64), lds, st, a);
     return hipGetLastError();
   };
-  if (a.T == 1) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 1>);
-  if (a.T == 2) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 2>);
-  if (a.T <= 4) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 4>);
-  return one(dev::gemm_dot_kernel<BITS, SBF16, W, 8>);
+  if (a.T == 1) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 1, NSETS>, dev::DotSmem<W, 1, NSETS>::bytes());
+  if (a.T == 2) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 2, NSETS>, dev::DotSmem<W, 2, NSETS>::bytes());
+  if (a.T <= 4) return one(dev::gemm_dot_kernel<BITS, SBF16, W, 4, NSETS>, dev::DotSmem<W, 4, NSETS>::bytes());
+  return one(dev::gemm_dot_kernel<BITS, SBF16, W, 8, NSETS>, dev::DotSmem<W, 8, NSETS>::bytes());
 }
-static_assert(dev::DotSmem<kStreamW>::bytes() <= 64u * 1024u && dev::DotSmem<kDotW8>::bytes() <= 64u * 1024u,
+static_assert(dev::DotSmem<kStreamW, 8, 1>::bytes() <= 64u * 1024u && dev::DotSmem<kDotW8, 8, 1>::bytes() <= 64u * 1024u &&
+                  dev::DotSmem<kDotW2, 8, 2>::bytes() <= 64u * 1024u,
               "the VALU kernel's LDS stays under 64 KiB");
 
+template <int NSETS>
 hipError_t launch_dot(const Format& f, const dev::GemmArgs& a, hipStream_t st) {
-  if (f.bits == 4) return f.scale_bf16 ? launch_dot_b<4, true>(a, st) : launch_dot_b<4, false>(a, st);
-  if (f.bits == 5) return f.scale_bf16 ? launch_dot_b<5, true>(a, st) : launch_dot_b<5, false>(a, st);
-  return f.scale_bf16 ? launch_dot_b<8, true>(a, st) : launch_dot_b<8, false>(a, st);
+  if (f.bits == 4) return f.scale_bf16 ? launch_dot_b<4, true, NSETS>(a, st) : launch_dot_b<4, false, NSETS>(a, st);
+  if (f.bits == 5) return f.scale_bf16 ? launch_dot_b<5, true, NSETS>(a, st) : launch_dot_b<5, false, NSETS>(a, st);
+  return f.scale_bf16 ? launch_dot_b<8, true, NSETS>(a, st) : launch_dot_b<8, false, NSETS>(a, st);
 }
 
 // Shared validation and launch of ngq_gemm (nsets 1) and ngq_swiglu_gemm (2).
@@ -3244,7 +3291,11 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   //    kernel); other one-round shapes: per-pair X with dynamic pair
   //    assignment (gate/value: 48-column tiles, where the streaming kernel's
   //    int5 unpack did not keep up);
-  //  - SwiGLU at T <= 4: the streaming kernel with 5 waves and one
+  //  - SwiGLU at T = 1, int4: the VALU step with 7 waves, one workgroup
+  //    per 32-column tile (gate/up, 544 tiles: 21.0 us against 23.1 for the
+  //    streaming kernel; three of its workgroups fit on a CU, so all 544 are
+  //    resident at once: with 9 or 10 waves only two fit, and 25.7 / 23.9);
+  //  - SwiGLU at T <= 4 otherwise: the streaming kernel with 5 waves and one
   //    workgroup per 32-column tile (gate/up, 544 tiles: 23.5 us against 27.0
   //    for the persistent X-resident kernel, whose 2.125 rounds of tiles end
   //    in a round on 32 CUs; 3, 4, 6, 8 waves: 24.7-27.3; at T = 8 the X
@@ -3267,6 +3318,8 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
       path = NGQ_KERNEL_DOT;
     else if (streams && (f.bits != 8 || kInt8Stream))
       path = NGQ_KERNEL_STREAM;
+    else if (nsets == 2 && T == 1 && f.bits == 4 && K > 0)
+      path = NGQ_KERNEL_DOT;
     else if (nsets == 2 && T <= kStreamSwigluMaxT && f.bits != 8 && K > 0)
       path = NGQ_KERNEL_STREAM;
     else if (one_round && v_pp == 2 && xres_fits(kX14, vx, lx))
@@ -3279,8 +3332,6 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
     if (!xres_fits(path == NGQ_KERNEL_XRES14 ? kX14 : x8, vx, lx)) return NGQ_ERR_UNSUPPORTED;
   } else if (path == NGQ_KERNEL_PERPAIR_DYN && !pp_dyn_fits) {
     return NGQ_ERR_UNSUPPORTED;
-  } else if (path == NGQ_KERNEL_DOT && nsets != 1) {
-    return NGQ_ERR_UNSUPPORTED;  // no SwiGLU epilogue
   }
   const bool xres = path == NGQ_KERNEL_XRES14 || path == NGQ_KERNEL_XRES8;
   if (xres) {
@@ -3301,8 +3352,8 @@ int run_gemm(int nsets, int T, int K, int Nout, int bits, int group, const void*
   hipError_t e;
   if (path == NGQ_KERNEL_DOT) {
     a.ntiles = (Nout + 31) / 32;
-    a.ppw = (a.pairs + dot_waves(f.bits) - 1) / dot_waves(f.bits);
-    e = launch_dot(f, a, st);
+    a.ppw = (a.pairs + dot_waves(f.bits, nsets) - 1) / dot_waves(f.bits, nsets);
+    e = nsets == 1 ? launch_dot<1>(f, a, st) : launch_dot<2>(f, a, st);
     return e == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
   }
   if (path == NGQ_KERNEL_STREAM) {

@@ -264,7 +264,7 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
  * and 11 are the T <= 8 kernels (larger T keeps the library's choice under them);
  * NGQ_KERNEL_WIDE serves 8 < T <= 64; the token x column paths serve any T
  * (the 96- and 128-token ones int4 only).  A forced path that cannot serve a shape (X or the partial sums do not
- * fit in LDS, the 14-wave and VALU kernels with the SwiGLU epilogue, NGQ_KERNEL_WIDE
+ * fit in LDS, the 14-wave kernel with the SwiGLU epilogue, NGQ_KERNEL_WIDE
  * outside its T range) makes those calls return NGQ_ERR_UNSUPPORTED.
  * Returns the previous setting, or NGQ_ERR_ARG for an unknown path.  Not
  * thread-safe with respect to calls that are running. */
@@ -282,7 +282,7 @@ int ngq_dequant_f32(int K, int N, int bits, int group, const void* wq, const voi
                                        pairs with their X band (plain or SwiGLU) */
 #define NGQ_KERNEL_DOT 11           /* the same pipeline with the multiply-add on the VALU (bf16 dot2);
                                        the library's choice at T = 1 for int4 and int8 (plain
-                                       projections only) */
+                                       or SwiGLU int4) */
 int ngq_debug_force_kernel(int path);
 
 /* Bandwidth calibration: stream `bytes` (a multiple of 16) from device memory

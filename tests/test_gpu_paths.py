@@ -51,7 +51,6 @@ def forced(ngq, request):
 # reason; a case of None stands for every case of that entry point
 UNSUPPORTED = {
     ("xres14", "swiglu", None): "the 14-wave X-resident kernel has no SwiGLU epilogue",
-    ("dot", "swiglu", None): "the VALU kernel has no SwiGLU epilogue",
     ("perpair_dyn", "gemm", (4, True, 2, 17408, 64)):
         "one partial-sum block per pair (136 pairs at K = 17408) does not fit in LDS",
     ("perpair_dyn", "gemm", (8, False, 8, 17408, 96)): "the same",
