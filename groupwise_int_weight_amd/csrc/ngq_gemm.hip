@@ -1310,19 +1310,23 @@ struct DotBuf {
   uint32_t x[2][4];            // the pair's X band (the streaming kernel's load classes)
 };
 
+// Workgroup b of a launch over ntiles tiles takes this tile: consecutive
+// tiles on one XCD (workgroup b runs on XCD b % 8).
+__device__ __forceinline__ int xcd_tile(int b, int ntiles) {
+  const int xcd = b & 7, per = ntiles >> 3, rem = ntiles & 7;
+  return xcd * per + min(xcd, rem) + (b >> 3);
+}
+
+// One 32-column tile of one projection (the body of gemm_dot_kernel, also
+// run by gemm_multi_dot_kernel).
 template <int BITS, bool SBF16, int W, int XM, int NSETS>
-__global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
+__device__ __forceinline__ void dot_tile(const GemmArgs& a, int tile, uint8_t* smem) {
   constexpr int WPK = BITS == 8 ? 2 : 1;
   constexpr uint32_t XROW = Smem::XROW;
   using Lds = DotSmem<W, XM, NSETS>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31, g = lane >> 5;  // column of the tile, group of the pair
-
-  const int b = blockIdx.x;
-  const int xcd = b & 7, per = a.ntiles >> 3, rem = a.ntiles & 7;
-  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
   const uint32_t c0 = (uint32_t)(tile * 32);
 
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
@@ -1549,6 +1553,12 @@ __global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
   }
 }
 
+template <int BITS, bool SBF16, int W, int XM, int NSETS>
+__global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  dot_tile<BITS, SBF16, W, XM, NSETS>(a, xcd_tile(blockIdx.x, a.ntiles), smem);
+}
+
 // ---- several projections of one X in one launch ----------------------------
 //
 // The projections of a layer that read the same activations (QK, gate/value
@@ -1729,6 +1739,53 @@ __global__ __launch_bounds__(kMultiW * 64) void gemm_multi_kernel(MultiArgs a) {
       default:
         break;
     }
+  }
+}
+
+// ---- several projections at T = 1: the VALU step, one tile per workgroup ----
+//
+// At T = 1 the projections of one x run as one launch of independent
+// workgroups, one per 32-column tile of any projection, each running the
+// VALU-step tile of gemm_dot_kernel with kMultiDotW waves.  Segment p of the
+// grid holds projection p's tiles (the heaviest tiles first, so the light
+// ones fill the end); three workgroups share a CU, and the hardware hands out
+// the rest as workgroups finish, which evens out the unequal tiles with no
+// plan.  The kinds it serves are those whose tile fits the register budget of
+// three workgroups a CU (int4 with or without SwiGLU, int5 and int8 plain).
+constexpr int kMultiDotW = 7;
+
+struct MultiDotArgs {
+  GemmArgs proj[kMultiMaxProj];
+  int end[kMultiMaxProj];   // one past projection p's last workgroup
+  int kind[kMultiMaxProj];  // multi_kind of projection p
+};
+
+__host__ __device__ constexpr bool multi_dot_kind(int kind) {
+  return kind == multi_kind(4, false, 1) || kind == multi_kind(4, true, 1) || kind == multi_kind(4, false, 2) ||
+         kind == multi_kind(4, true, 2) || kind == multi_kind(5, false, 1) || kind == multi_kind(5, true, 1) ||
+         kind == multi_kind(8, false, 1) || kind == multi_kind(8, true, 1);
+}
+
+__global__ __launch_bounds__(kMultiDotW * 64) void gemm_multi_dot_kernel(MultiDotArgs m) {
+  constexpr int W = kMultiDotW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int b = blockIdx.x;
+  int p = 0;
+#pragma unroll
+  for (int i = 0; i < kMultiMaxProj - 1; ++i) p += b >= m.end[i] ? 1 : 0;
+  const int b0 = p == 0 ? 0 : m.end[p - 1];
+  const int tile = xcd_tile(b - b0, m.end[p] - b0);
+  const GemmArgs& a = m.proj[p];
+  switch (m.kind[p]) {
+    case multi_kind(4, false, 1): dot_tile<4, false, W, 1, 1>(a, tile, smem); break;
+    case multi_kind(4, true, 1): dot_tile<4, true, W, 1, 1>(a, tile, smem); break;
+    case multi_kind(4, false, 2): dot_tile<4, false, W, 1, 2>(a, tile, smem); break;
+    case multi_kind(4, true, 2): dot_tile<4, true, W, 1, 2>(a, tile, smem); break;
+    case multi_kind(5, false, 1): dot_tile<5, false, W, 1, 1>(a, tile, smem); break;
+    case multi_kind(5, true, 1): dot_tile<5, true, W, 1, 1>(a, tile, smem); break;
+    case multi_kind(8, false, 1): dot_tile<8, false, W, 1, 1>(a, tile, smem); break;
+    case multi_kind(8, true, 1): dot_tile<8, true, W, 1, 1>(a, tile, smem); break;
+    default: break;
   }
 }
 
@@ -3515,6 +3572,45 @@ int load_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, de
   return found->grid;
 }
 
+// ngq_multi_gemm at T = 1 on gemm_multi_dot_kernel: the validated projections
+// (descriptors in a.proj, kinds in kind) as segments of one grid, the
+// heaviest tiles (weight and scale bytes per tile) first.
+int run_multi_dot(int K, const void* x, size_t xb, const dev::MultiArgs& a, const int* kind, int n, void* stream) {
+  int order[NGQ_MAX_PROJ];
+  long tile_bytes[NGQ_MAX_PROJ];
+  for (int i = 0; i < n; ++i) {
+    const dev::MultiProj& mp = a.proj[i];
+    tile_bytes[i] = ((long)mp.p0_bytes + mp.p1_bytes + mp.s_bytes) / ((mp.Nout + 31) / 32);
+    order[i] = i;
+  }
+  std::stable_sort(order, order + n, [&](int i, int j) { return tile_bytes[i] > tile_bytes[j]; });
+  dev::MultiDotArgs m;
+  std::memset(&m, 0, sizeof(m));
+  const int G = K / kGroup, pairs = (G + 1) / 2;
+  long grid = 0;
+  for (int i = 0; i < dev::kMultiMaxProj; ++i) m.end[i] = INT32_MAX;
+  for (int i = 0; i < n; ++i) {
+    const dev::MultiProj& mp = a.proj[order[i]];
+    dev::GemmArgs& g = m.proj[i];
+    g.x = x; g.wq = mp.wq; g.scales = mp.scales; g.y = mp.y;
+    g.T = 1; g.K = K; g.Nout = mp.Nout; g.Ncols = mp.Ncols; g.up_off = mp.up_off;
+    g.G = G; g.pairs = pairs;
+    g.ppw = (pairs + dev::kMultiDotW - 1) / dev::kMultiDotW;
+    g.ntiles = (mp.Nout + 31) / 32;
+    g.p0_bytes = mp.p0_bytes; g.p1_bytes = mp.p1_bytes; g.s_bytes = mp.s_bytes; g.x_bytes = (uint32_t)xb;
+    g.mask_nib = dev::kMasks.nib; g.mask_base = dev::kMasks.base; g.mask_hi = dev::kMasks.hi;
+    g.tiles_q = g.tiles_r = 0;
+    grid += g.ntiles;
+    m.end[i] = (int)grid;
+    m.kind[i] = kind[order[i]];
+  }
+  if (grid > INT32_MAX / 2) return NGQ_ERR_UNSUPPORTED;
+  const uint32_t lds = dev::DotSmem<dev::kMultiDotW, 1, 2>::bytes();
+  hipLaunchKernelGGL(dev::gemm_multi_dot_kernel, dim3((unsigned)grid), dim3(dev::kMultiDotW * 64), lds,
+                     (hipStream_t)stream, m);
+  return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
+}
+
 int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int nproj, void* stream) {
   if (projs == nullptr || nproj < 1 || nproj > NGQ_MAX_PROJ) return NGQ_ERR_ARG;
   if (T < 0 || T > NGQ_MAX_T) return NGQ_ERR_SHAPE;
@@ -3580,10 +3676,12 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
       if (j != i && overlaps(live[i]->y, ybytes[i], live[j]->y, ybytes[j])) return NGQ_ERR_ARG;
     }
   }
+  if (n == 0) return NGQ_OK;
+  if (T == 1 && K > 0 && std::all_of(kind, kind + n, [](int k) { return dev::multi_dot_kind(k); }))
+    return run_multi_dot(K, x, xb, a, kind, n, stream);
   const uint32_t lds = dev::XSmem::bytes(T, K, dev::kMultiW, 1, 0) +
                        (uint32_t)dev::kMultiW * dev::Smem::block_floats(nsets_max, 16 * v_max) * 4u;
   if (lds > kMaxLds) return NGQ_ERR_UNSUPPORTED;
-  if (n == 0) return NGQ_OK;
   // The projection with the most tiles first: every workgroup has tiles of it
   // (when any projection has as many tiles as workgroups), so each one finds
   // its first segment without scanning.

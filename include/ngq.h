@@ -185,7 +185,11 @@ int ngq_gemm_splitk_static(int T, int K, int N, int bits, int group, const void*
  * K % 64 == 0; T == 0 is a no-op.  X and the partial sums must fit in the
  * workgroup's LDS (T * (2 K + 16) + 128 bytes for X: K up to ~9000 at T = 8),
  * otherwise NGQ_ERR_UNSUPPORTED.  Any mix of bit widths, scale types and
- * plain / SwiGLU projections may share a call. */
+ * plain / SwiGLU projections may share a call.  At T = 1, when every
+ * projection is int4 (plain or SwiGLU) or plain int5 / int8, the call runs
+ * instead one workgroup per 32-column tile of any projection (the VALU step
+ * of ngq_gemm at T = 1, 7 waves; the hardware spreads the unequal tiles), with
+ * no LDS limit on K. */
 #define NGQ_MAX_PROJ 4
 typedef struct ngq_proj {
   int bits;

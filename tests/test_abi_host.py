@@ -207,6 +207,23 @@ def test_multi_rejects_bad_arguments(ngq, T, K, projs, nproj, status):
     assert multi_call(ngq, T, K, projs, nproj=nproj) == status
 
 
+def test_multi_t1_takes_the_tile_kernel_without_lds_limit(ngq):
+    """At T = 1 with int4 / plain int5 / plain int8 projections the fused call
+    runs one workgroup per tile with X per pair: a K whose X exceeds the
+    persistent kernel's LDS is served (no device here: the launch reports
+    the missing device); with an int5 SwiGLU projection it is refused."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("host-only check: with a device these fake pointers would be launched")
+    K = 131072  # X alone is 256 KB at T = 1
+    p4 = (4, 64, 0, 0, 0x1000000, 0x2000000, 0x3000000)
+    p5 = (5, 64, 0, 0, 0x4000000, 0x5000000, 0x3001000)
+    p5s = (5, 64, 1, 0, 0x4000000, 0x5000000, 0x3001000)
+    assert multi_call(ngq, 1, K, [p4, p5]) == ngq.NGQ_ERR_HIP
+    assert multi_call(ngq, 1, K, [p4, p5s]) == ngq.NGQ_ERR_UNSUPPORTED
+    assert multi_call(ngq, 2, K, [p4, p5]) == ngq.NGQ_ERR_UNSUPPORTED
+
+
 def test_multi_empty_calls_are_no_ops(ngq):
     """T == 0, or every projection zero-width, returns OK without a HIP call."""
     assert multi_call(ngq, 0, 64, [P_OK], x=None) == 0

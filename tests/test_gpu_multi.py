@@ -1,11 +1,18 @@
 """ngq_multi_gemm, several projections of one x in one launch, on the GPU.
 
-Each projection of a fused call is checked against the oracle (sampled
-columns at full size, every column on small shapes), and bit for bit against
-the single-projection call forced to the X-resident kernel with 8 waves: the
-fused kernel runs the same tile loop (wave w takes pairs w, w + 8, ...; the
-wave partials are summed in wave order), so the two must agree exactly,
-whatever the tile width and the tile-to-workgroup assignment.
+Each projection of a fused call is checked against the oracle (every
+column), and bit for bit against a single-projection call that runs the same
+tile code:
+- the persistent fused kernel runs the tile loop of the X-resident kernel
+  with 8 waves (wave w takes pairs w, w + 8, ...; the wave partials are
+  summed in wave order), so each projection must equal the single call
+  forced to that kernel, whatever the tile width and the tile-to-workgroup
+  assignment;
+- at T = 1, when every projection is int4, or int5 / int8 without SwiGLU,
+  the call runs the VALU-step tiles with 7 waves instead: its SwiGLU
+  projections must equal ngq_swiglu_gemm forced to the VALU kernel (7 waves
+  too); its plain projections, which the single call runs with 10 or 8
+  waves (another order of the same sums), are held to the oracle only.
 """
 import numpy as np
 import pytest
@@ -45,10 +52,16 @@ def draw(bits, sbf16, K, ncols, seed):
     return codes, scales
 
 
-def single(ngq, x, p):
-    """The same projection through ngq_gemm / ngq_swiglu_gemm on the 8-wave
-    X-resident kernel, or None when that kernel cannot serve the shape."""
-    prev = ngq.ngq_debug_force_kernel(ngq.NGQ_KERNEL_XRES8)
+def fused_dot(T, K, specs):
+    """Whether ngq_multi_gemm runs these projections on the VALU-step tiles."""
+    live = [(bits, swiglu) for bits, _, n, swiglu in specs if n > 0]
+    return T == 1 and K > 0 and all(bits == 4 or not swiglu for bits, swiglu in live)
+
+
+def single(ngq, x, p, path):
+    """The same projection through ngq_gemm / ngq_swiglu_gemm on a forced
+    kernel, or None when that kernel cannot serve the shape."""
+    prev = ngq.ngq_debug_force_kernel(path)
     try:
         if p["swiglu"]:
             return ngq.ngq_swiglu_gemm(x, p["wq"], p["scales"], p["bits"], p["n"])
@@ -76,12 +89,19 @@ def run_case(ngq, orc, T, K, specs, seed):
         projs.append(dict(wq=dev_u8(packed), scales=dev_scales(scales, sbf16), bits=bits, n=n, swiglu=swiglu, y=y))
     outs = ngq.ngq_multi_gemm(xd, projs)
     torch.cuda.synchronize()
+    dot = fused_dot(T, K, specs)
     for i, ((bits, sbf16, n, swiglu), p, out) in enumerate(zip(specs, projs, outs)):
         what = f"T{T} K{K} proj{i} b{bits} n{n}{' swiglu' if swiglu else ''}"
         yb = host_bits(out)
         if n == 0:
             continue
-        ref = single(ngq, xd, p)
+        if not dot:
+            ref = single(ngq, xd, p, ngq.NGQ_KERNEL_XRES8)
+        elif swiglu:
+            ref = single(ngq, xd, p, ngq.NGQ_KERNEL_DOT)
+            assert ref is not None, what
+        else:
+            ref = None
         if ref is not None:
             assert np.array_equal(yb, host_bits(ref)), what + ": differs from the single-projection kernel"
         codes, scales, packed_o = host[i]
@@ -106,6 +126,12 @@ CASES = [
     (7, 256, [(4, False, 16416, False), (5, True, 8224, True)]),                        # many tiles per workgroup
     (4, 17408, [(4, False, 520, False)]),                                               # X staged in two rounds
     (8, 9216, [(4, False, 260, False), (5, True, 64, False)]),                          # two rounds at T = 8
+    # T = 1: the VALU-step tiles, unless a projection is int5 or int8 with SwiGLU
+    (1, 1088, [(4, False, 96, False), (5, True, 100, False), (4, False, 36, True)]),   # odd group count
+    (1, 448, [(8, False, 64, False), (8, True, 100, False), (4, True, 40, True), (5, False, 4, False)]),
+    (1, 64, [(5, True, 260, False), (4, False, 0, False), (4, False, 1028, True)]),     # one group; n = 0
+    (1, 256, [(4, False, 16416, False), (4, True, 8224, True)]),                        # many tiles
+    (1, 320, [(4, True, 64, False), (4, False, 20, True), (5, False, 36, True)]),       # int5 SwiGLU: persistent
 ]
 
 
@@ -136,12 +162,14 @@ def test_multi_k_zero_and_t_zero(ngq):
     assert torch.all(p["y"] == 5.0)  # T = 0: nothing written
 
 
-def test_multi_deterministic_and_graph_replay(ngq):
-    T, K = 8, 1024
+@pytest.mark.parametrize("T,specs", [(8, [(4, False, 4096, False), (5, True, 2048, True)]),
+                                     (1, [(4, False, 4096, False), (5, True, 2048, False), (4, False, 2048, True)])])
+def test_multi_deterministic_and_graph_replay(ngq, T, specs):
+    K = 1024
     g = np.random.default_rng(3)
     x = dev_bf16(synthetic.f32_to_bf16_bits(g.standard_normal((T, K)).astype(np.float32)))
     projs = []
-    for i, (bits, sbf16, n, swiglu) in enumerate([(4, False, 4096, False), (5, True, 2048, True)]):
+    for i, (bits, sbf16, n, swiglu) in enumerate(specs):
         codes, scales = draw(bits, sbf16, K, 2 * n if swiglu else n, 50 + i)
         projs.append(dict(wq=dev_u8(ngq.ngq_pack(codes, bits)), scales=dev_scales(scales, sbf16), bits=bits, n=n,
                           swiglu=swiglu, y=torch.empty((T, n), dtype=torch.bfloat16, device="cuda")))
