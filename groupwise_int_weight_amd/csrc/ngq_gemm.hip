@@ -1041,6 +1041,13 @@ struct StreamSmem {
   }
 };
 
+// Workgroup b of a launch over ntiles tiles takes this tile: consecutive
+// tiles on one XCD (workgroup b runs on XCD b % 8).
+__device__ __forceinline__ int xcd_tile(int b, int ntiles) {
+  const int xcd = b & 7, per = ntiles >> 3, rem = ntiles & 7;
+  return xcd * per + min(xcd, rem) + (b >> 3);
+}
+
 // LDS byte offset of element k (0..127) of a band's token row in the
 // interleaved order: each 8-k block holds k = 0, 4, 1, 5, 2, 6, 3, 7.
 __device__ __forceinline__ uint32_t il_offset(uint32_t k) {
@@ -1053,23 +1060,17 @@ __device__ __forceinline__ uint32_t il_offset(uint32_t k) {
 // NSETS = 2: the SwiGLU gate/up projection, the tile's columns of both
 // halves (gate at c, up at up_off + c) in each pair.
 template <int BITS, bool SBF16, int V, int W, int XM, int NSETS>
-__global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
+__device__ __forceinline__ void stream_tile(const GemmArgs& a, int tile, uint8_t* smem) {
   constexpr int WPK = BITS == 8 ? 2 : 1;
   constexpr int TILE = 16 * V;
   constexpr uint32_t XROW = Smem::XROW, XZERO = Smem::XZERO;
   constexpr uint32_t BLK = Smem::block_floats(NSETS, TILE);
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* const part = reinterpret_cast<float*>(smem + (uint32_t)W * Smem::XSLOT);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, q = lane >> 4;
   const int t = m & 7, h = m >> 3;  // B slot m: token t of group half h
-
-  // consecutive tiles on one XCD (workgroup b runs on XCD b % 8)
-  const int b = blockIdx.x;
-  const int xcd = b & 7, per = a.ntiles >> 3, rem = a.ntiles & 7;
-  const int tile = xcd * per + min(xcd, rem) + (b >> 3);
   const uint32_t c0 = (uint32_t)(tile * TILE);
 
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(a.wq, a.p0_bytes);
@@ -1271,6 +1272,12 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
   finish_outputs<V, NSETS, W>(part, pv, a.T, (int)c0);
 }
 
+template <int BITS, bool SBF16, int V, int W, int XM, int NSETS>
+__global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  stream_tile<BITS, SBF16, V, W, XM, NSETS>(a, xcd_tile(blockIdx.x, a.ntiles), smem);
+}
+
 // ---- the same stream with a VALU inner step ---------------------------------
 //
 // gemm_dot_kernel is gemm_stream_kernel's pipeline (one 32-column tile per
@@ -1309,13 +1316,6 @@ struct DotBuf {
   uint32_t sc[NSETS];          // the lane's scales (16-bit)
   uint32_t x[2][4];            // the pair's X band (the streaming kernel's load classes)
 };
-
-// Workgroup b of a launch over ntiles tiles takes this tile: consecutive
-// tiles on one XCD (workgroup b runs on XCD b % 8).
-__device__ __forceinline__ int xcd_tile(int b, int ntiles) {
-  const int xcd = b & 7, per = ntiles >> 3, rem = ntiles & 7;
-  return xcd * per + min(xcd, rem) + (b >> 3);
-}
 
 // One 32-column tile of one projection (the body of gemm_dot_kernel, also
 // run by gemm_multi_dot_kernel).
@@ -1742,31 +1742,32 @@ __global__ __launch_bounds__(kMultiW * 64) void gemm_multi_kernel(MultiArgs a) {
   }
 }
 
-// ---- several projections at T = 1: the VALU step, one tile per workgroup ----
+// ---- several projections, one tile per workgroup -----------------------------
 //
-// At T = 1 the projections of one x run as one launch of independent
-// workgroups, one per 32-column tile of any projection, each running the
-// VALU-step tile of gemm_dot_kernel with kMultiDotW waves.  Segment p of the
-// grid holds projection p's tiles (the heaviest tiles first, so the light
-// ones fill the end); three workgroups share a CU, and the hardware hands out
-// the rest as workgroups finish, which evens out the unequal tiles with no
-// plan.  The kinds it serves are those whose tile fits the register budget of
-// three workgroups a CU (int4 with or without SwiGLU, int5 and int8 plain).
+// The projections of one x run as one launch of independent workgroups, one
+// per 32-column tile of any projection: at T = 1 each runs the VALU-step tile
+// of gemm_dot_kernel with kMultiDotW waves (three workgroups a CU), at T =
+// 2..8 the MFMA-step tile of gemm_stream_kernel with kMultiStreamW waves (four
+// a CU).  Segment p of the grid holds projection p's tiles (the heaviest
+// tiles first, so the light ones fill the end), and the hardware hands out
+// workgroups as others finish, which evens out the unequal tiles with no
+// plan.  The kinds served are those whose tile keeps that many workgroups on
+// a CU (int4 with or without SwiGLU, int5 and int8 plain).
 constexpr int kMultiDotW = 7;
 
-struct MultiDotArgs {
+struct MultiTileArgs {
   GemmArgs proj[kMultiMaxProj];
   int end[kMultiMaxProj];   // one past projection p's last workgroup
   int kind[kMultiMaxProj];  // multi_kind of projection p
 };
 
-__host__ __device__ constexpr bool multi_dot_kind(int kind) {
+__host__ __device__ constexpr bool multi_tile_kind(int kind) {
   return kind == multi_kind(4, false, 1) || kind == multi_kind(4, true, 1) || kind == multi_kind(4, false, 2) ||
          kind == multi_kind(4, true, 2) || kind == multi_kind(5, false, 1) || kind == multi_kind(5, true, 1) ||
          kind == multi_kind(8, false, 1) || kind == multi_kind(8, true, 1);
 }
 
-__global__ __launch_bounds__(kMultiDotW * 64) void gemm_multi_dot_kernel(MultiDotArgs m) {
+__global__ __launch_bounds__(kMultiDotW * 64) void gemm_multi_dot_kernel(MultiTileArgs m) {
   constexpr int W = kMultiDotW;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int b = blockIdx.x;
@@ -1785,6 +1786,32 @@ __global__ __launch_bounds__(kMultiDotW * 64) void gemm_multi_dot_kernel(MultiDo
     case multi_kind(5, true, 1): dot_tile<5, true, W, 1, 1>(a, tile, smem); break;
     case multi_kind(8, false, 1): dot_tile<8, false, W, 1, 1>(a, tile, smem); break;
     case multi_kind(8, true, 1): dot_tile<8, true, W, 1, 1>(a, tile, smem); break;
+    default: break;
+  }
+}
+
+constexpr int kMultiStreamW = 4;
+
+template <int XM>
+__global__ __launch_bounds__(kMultiStreamW * 64) void gemm_multi_stream_kernel(MultiTileArgs m) {
+  constexpr int W = kMultiStreamW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int b = blockIdx.x;
+  int p = 0;
+#pragma unroll
+  for (int i = 0; i < kMultiMaxProj - 1; ++i) p += b >= m.end[i] ? 1 : 0;
+  const int b0 = p == 0 ? 0 : m.end[p - 1];
+  const int tile = xcd_tile(b - b0, m.end[p] - b0);
+  const GemmArgs& a = m.proj[p];
+  switch (m.kind[p]) {
+    case multi_kind(4, false, 1): stream_tile<4, false, 2, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(4, true, 1): stream_tile<4, true, 2, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(4, false, 2): stream_tile<4, false, 2, W, XM, 2>(a, tile, smem); break;
+    case multi_kind(4, true, 2): stream_tile<4, true, 2, W, XM, 2>(a, tile, smem); break;
+    case multi_kind(5, false, 1): stream_tile<5, false, 2, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(5, true, 1): stream_tile<5, true, 2, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(8, false, 1): stream_tile<8, false, 2, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(8, true, 1): stream_tile<8, true, 2, W, XM, 1>(a, tile, smem); break;
     default: break;
   }
 }
@@ -3572,10 +3599,18 @@ int load_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, de
   return found->grid;
 }
 
-// ngq_multi_gemm at T = 1 on gemm_multi_dot_kernel: the validated projections
-// (descriptors in a.proj, kinds in kind) as segments of one grid, the
-// heaviest tiles (weight and scale bytes per tile) first.
-int run_multi_dot(int K, const void* x, size_t xb, const dev::MultiArgs& a, const int* kind, int n, void* stream) {
+// ngq_multi_gemm as one workgroup per tile (gemm_multi_dot_kernel at T = 1,
+// gemm_multi_stream_kernel above): the validated projections (descriptors in
+// a.proj, kinds in kind) as segments of one grid, the heaviest tiles (weight
+// and scale bytes per tile) first.  Measured against the persistent kernel
+// (QK + gate/value + gate/up): T = 1 32.7 against 37.8 us, T = 2 32.7
+// against 37.2-38.2, T = 4 33.5 against 37.4-37.9, T = 8 37.2-37.4 against
+// 37.9-39.0; with 2, 3, 5, 6 or 8 waves a tile at T >= 2: 2-10 % slower
+// than 4.
+constexpr int kMultiStreamMaxT = 8;
+
+int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs& a, const int* kind, int n,
+                  void* stream) {
   int order[NGQ_MAX_PROJ];
   long tile_bytes[NGQ_MAX_PROJ];
   for (int i = 0; i < n; ++i) {
@@ -3584,7 +3619,7 @@ int run_multi_dot(int K, const void* x, size_t xb, const dev::MultiArgs& a, cons
     order[i] = i;
   }
   std::stable_sort(order, order + n, [&](int i, int j) { return tile_bytes[i] > tile_bytes[j]; });
-  dev::MultiDotArgs m;
+  dev::MultiTileArgs m;
   std::memset(&m, 0, sizeof(m));
   const int G = K / kGroup, pairs = (G + 1) / 2;
   long grid = 0;
@@ -3593,9 +3628,10 @@ int run_multi_dot(int K, const void* x, size_t xb, const dev::MultiArgs& a, cons
     const dev::MultiProj& mp = a.proj[order[i]];
     dev::GemmArgs& g = m.proj[i];
     g.x = x; g.wq = mp.wq; g.scales = mp.scales; g.y = mp.y;
-    g.T = 1; g.K = K; g.Nout = mp.Nout; g.Ncols = mp.Ncols; g.up_off = mp.up_off;
+    const int w = T == 1 ? dev::kMultiDotW : dev::kMultiStreamW;
+    g.T = T; g.K = K; g.Nout = mp.Nout; g.Ncols = mp.Ncols; g.up_off = mp.up_off;
     g.G = G; g.pairs = pairs;
-    g.ppw = (pairs + dev::kMultiDotW - 1) / dev::kMultiDotW;
+    g.ppw = (pairs + w - 1) / w;
     g.ntiles = (mp.Nout + 31) / 32;
     g.p0_bytes = mp.p0_bytes; g.p1_bytes = mp.p1_bytes; g.s_bytes = mp.s_bytes; g.x_bytes = (uint32_t)xb;
     g.mask_nib = dev::kMasks.nib; g.mask_base = dev::kMasks.base; g.mask_hi = dev::kMasks.hi;
@@ -3605,9 +3641,20 @@ int run_multi_dot(int K, const void* x, size_t xb, const dev::MultiArgs& a, cons
     m.kind[i] = kind[order[i]];
   }
   if (grid > INT32_MAX / 2) return NGQ_ERR_UNSUPPORTED;
-  const uint32_t lds = dev::DotSmem<dev::kMultiDotW, 1, 2>::bytes();
-  hipLaunchKernelGGL(dev::gemm_multi_dot_kernel, dim3((unsigned)grid), dim3(dev::kMultiDotW * 64), lds,
-                     (hipStream_t)stream, m);
+  hipStream_t st = (hipStream_t)stream;
+  if (T == 1) {
+    const uint32_t lds = dev::DotSmem<dev::kMultiDotW, 1, 2>::bytes();
+    hipLaunchKernelGGL(dev::gemm_multi_dot_kernel, dim3((unsigned)grid), dim3(dev::kMultiDotW * 64), lds, st, m);
+  } else {
+    const uint32_t lds = dev::StreamSmem<dev::kMultiStreamW>::bytes(32, 2);
+    const dim3 g((unsigned)grid), blk(dev::kMultiStreamW * 64);
+    if (T == 2)
+      hipLaunchKernelGGL(dev::gemm_multi_stream_kernel<2>, g, blk, lds, st, m);
+    else if (T <= 4)
+      hipLaunchKernelGGL(dev::gemm_multi_stream_kernel<4>, g, blk, lds, st, m);
+    else
+      hipLaunchKernelGGL(dev::gemm_multi_stream_kernel<8>, g, blk, lds, st, m);
+  }
   return hipGetLastError() == hipSuccess ? NGQ_OK : NGQ_ERR_HIP;
 }
 
@@ -3677,8 +3724,8 @@ int run_multi(int T, int K, int group, const void* x, const ngq_proj* projs, int
     }
   }
   if (n == 0) return NGQ_OK;
-  if (T == 1 && K > 0 && std::all_of(kind, kind + n, [](int k) { return dev::multi_dot_kind(k); }))
-    return run_multi_dot(K, x, xb, a, kind, n, stream);
+  if (T <= kMultiStreamMaxT && K > 0 && std::all_of(kind, kind + n, [](int k) { return dev::multi_tile_kind(k); }))
+    return run_multi_tiles(T, K, x, xb, a, kind, n, stream);
   const uint32_t lds = dev::XSmem::bytes(T, K, dev::kMultiW, 1, 0) +
                        (uint32_t)dev::kMultiW * dev::Smem::block_floats(nsets_max, 16 * v_max) * 4u;
   if (lds > kMaxLds) return NGQ_ERR_UNSUPPORTED;

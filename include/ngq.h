@@ -166,8 +166,8 @@ int ngq_gemm_splitk_static(int T, int K, int N, int bits, int group, const void*
 
 /* Several projections of the same activations in one launch.  The
  * projections of a layer that read one x (in the stacked sweep: QK,
- * gate/value and the gate/up pair) are computed as one persistent kernel, so
- * X is staged once and the tiles of all of them are balanced over the CUs
+ * gate/value and the gate/up pair) are computed as one kernel, so the launch
+ * is paid once and the tiles of all of them are spread over the CUs
  * together.  Each projection computes exactly what ngq_gemm (swiglu = 0) or
  * ngq_swiglu_gemm (swiglu = 1) computes for it: the same formula, fp32
  * accumulation and bf16 rounding.
@@ -185,11 +185,11 @@ int ngq_gemm_splitk_static(int T, int K, int N, int bits, int group, const void*
  * K % 64 == 0; T == 0 is a no-op.  X and the partial sums must fit in the
  * workgroup's LDS (T * (2 K + 16) + 128 bytes for X: K up to ~9000 at T = 8),
  * otherwise NGQ_ERR_UNSUPPORTED.  Any mix of bit widths, scale types and
- * plain / SwiGLU projections may share a call.  At T = 1, when every
- * projection is int4 (plain or SwiGLU) or plain int5 / int8, the call runs
- * instead one workgroup per 32-column tile of any projection (the VALU step
- * of ngq_gemm at T = 1, 7 waves; the hardware spreads the unequal tiles), with
- * no LDS limit on K. */
+ * plain / SwiGLU projections may share a call.  When every projection is
+ * int4 (plain or SwiGLU) or plain int5 / int8, the call runs instead one
+ * workgroup per 32-column tile of any projection (the VALU step with 7 waves
+ * at T = 1, the MFMA step with 4 waves above; the hardware spreads the
+ * unequal tiles), with no LDS limit on K. */
 #define NGQ_MAX_PROJ 4
 typedef struct ngq_proj {
   int bits;

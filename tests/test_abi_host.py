@@ -201,17 +201,17 @@ P_OK = (4, 64, 0, 0, W, S, Y)
     (1, 64, [(4, 64, 0, 0, W, S, X)], None, -1),                   # output overlaps x
     (1, 64, [P_OK, (5, 64, 0, 0, W + 4096, S, W + 16)], None, -1),  # output overlaps another wq
     (1, 64, [P_OK, (4, 64, 0, 0, W, S, Y + 64)], None, -1),        # two outputs overlap
-    (8, 65536, [P_OK], None, -3),                                  # X does not fit in LDS
+    (8, 65536, [(5, 64, 1, 0, 0x1000000, 0x2000000, 0x3000000)], None, -3),  # int5 SwiGLU: X does not fit in LDS
 ])
 def test_multi_rejects_bad_arguments(ngq, T, K, projs, nproj, status):
     assert multi_call(ngq, T, K, projs, nproj=nproj) == status
 
 
-def test_multi_t1_takes_the_tile_kernel_without_lds_limit(ngq):
-    """At T = 1 with int4 / plain int5 / plain int8 projections the fused call
-    runs one workgroup per tile with X per pair: a K whose X exceeds the
-    persistent kernel's LDS is served (no device here: the launch reports
-    the missing device); with an int5 SwiGLU projection it is refused."""
+def test_multi_tile_kernels_have_no_lds_limit(ngq):
+    """With int4 / plain int5 / plain int8 projections the fused call runs one
+    workgroup per tile with X per pair: a K whose X exceeds the persistent
+    kernel's LDS is served (no device here: the launch reports the missing
+    device); with an int5 SwiGLU projection it is refused."""
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
         pytest.skip("host-only check: with a device these fake pointers would be launched")
@@ -219,9 +219,9 @@ def test_multi_t1_takes_the_tile_kernel_without_lds_limit(ngq):
     p4 = (4, 64, 0, 0, 0x1000000, 0x2000000, 0x3000000)
     p5 = (5, 64, 0, 0, 0x4000000, 0x5000000, 0x3001000)
     p5s = (5, 64, 1, 0, 0x4000000, 0x5000000, 0x3001000)
-    assert multi_call(ngq, 1, K, [p4, p5]) == ngq.NGQ_ERR_HIP
-    assert multi_call(ngq, 1, K, [p4, p5s]) == ngq.NGQ_ERR_UNSUPPORTED
-    assert multi_call(ngq, 2, K, [p4, p5]) == ngq.NGQ_ERR_UNSUPPORTED
+    for T in (1, 2, 8):
+        assert multi_call(ngq, T, K, [p4, p5]) == ngq.NGQ_ERR_HIP, T
+        assert multi_call(ngq, T, K, [p4, p5s]) == ngq.NGQ_ERR_UNSUPPORTED, T
 
 
 def test_multi_empty_calls_are_no_ops(ngq):

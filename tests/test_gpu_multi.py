@@ -1,18 +1,19 @@
 """ngq_multi_gemm, several projections of one x in one launch, on the GPU.
 
 Each projection of a fused call is checked against the oracle (every
-column), and bit for bit against a single-projection call that runs the same
-tile code:
-- the persistent fused kernel runs the tile loop of the X-resident kernel
-  with 8 waves (wave w takes pairs w, w + 8, ...; the wave partials are
-  summed in wave order), so each projection must equal the single call
+column), and bit for bit against a single-projection call where one runs the
+same tile code:
+- when every projection is int4, or int5 / int8 without SwiGLU, the call
+  runs one workgroup per tile: at T = 1 the VALU-step tile with 7 waves, so
+  its SwiGLU projections must equal ngq_swiglu_gemm forced to the VALU kernel
+  (7 waves too); its plain projections, and every projection at T >= 2 (the
+  MFMA-step tile with 4 waves), have no single call with the same wave count
+  (another order of the same sums) and are held to the oracle only;
+- otherwise the persistent fused kernel runs the tile loop of the X-resident
+  kernel with 8 waves (wave w takes pairs w, w + 8, ...; the wave partials
+  are summed in wave order), so each projection must equal the single call
   forced to that kernel, whatever the tile width and the tile-to-workgroup
-  assignment;
-- at T = 1, when every projection is int4, or int5 / int8 without SwiGLU,
-  the call runs the VALU-step tiles with 7 waves instead: its SwiGLU
-  projections must equal ngq_swiglu_gemm forced to the VALU kernel (7 waves
-  too); its plain projections, which the single call runs with 10 or 8
-  waves (another order of the same sums), are held to the oracle only.
+  assignment.
 """
 import numpy as np
 import pytest
@@ -52,10 +53,10 @@ def draw(bits, sbf16, K, ncols, seed):
     return codes, scales
 
 
-def fused_dot(T, K, specs):
-    """Whether ngq_multi_gemm runs these projections on the VALU-step tiles."""
+def fused_tiles(K, specs):
+    """Whether ngq_multi_gemm runs these projections as one workgroup per tile."""
     live = [(bits, swiglu) for bits, _, n, swiglu in specs if n > 0]
-    return T == 1 and K > 0 and all(bits == 4 or not swiglu for bits, swiglu in live)
+    return K > 0 and all(bits == 4 or not swiglu for bits, swiglu in live)
 
 
 def single(ngq, x, p, path):
@@ -89,15 +90,15 @@ def run_case(ngq, orc, T, K, specs, seed):
         projs.append(dict(wq=dev_u8(packed), scales=dev_scales(scales, sbf16), bits=bits, n=n, swiglu=swiglu, y=y))
     outs = ngq.ngq_multi_gemm(xd, projs)
     torch.cuda.synchronize()
-    dot = fused_dot(T, K, specs)
+    tiles = fused_tiles(K, specs)
     for i, ((bits, sbf16, n, swiglu), p, out) in enumerate(zip(specs, projs, outs)):
         what = f"T{T} K{K} proj{i} b{bits} n{n}{' swiglu' if swiglu else ''}"
         yb = host_bits(out)
         if n == 0:
             continue
-        if not dot:
+        if not tiles:
             ref = single(ngq, xd, p, ngq.NGQ_KERNEL_XRES8)
-        elif swiglu:
+        elif T == 1 and swiglu:
             ref = single(ngq, xd, p, ngq.NGQ_KERNEL_DOT)
             assert ref is not None, what
         else:
@@ -124,8 +125,11 @@ CASES = [
     (5, 512, [(4, False, 4, False)]),                                                   # one narrow tile
     (2, 64, [(5, True, 260, False), (4, False, 0, False), (4, False, 1028, True)]),     # one group; n = 0
     (7, 256, [(4, False, 16416, False), (5, True, 8224, True)]),                        # many tiles per workgroup
-    (4, 17408, [(4, False, 520, False)]),                                               # X staged in two rounds
-    (8, 9216, [(4, False, 260, False), (5, True, 64, False)]),                          # two rounds at T = 8
+    (4, 17408, [(4, False, 520, False)]),                                               # long K, X per pair
+    (8, 9216, [(4, False, 260, False), (5, True, 64, False)]),
+    (4, 17408, [(8, True, 8, True), (8, False, 40, True)]),  # persistent: X staged in two rounds
+    (3, 192, [(4, False, 72, False), (4, True, 36, True)]),                             # tiles, T = 3
+    (7, 640, [(5, True, 96, False), (4, False, 44, True), (8, False, 28, False)]),      # tiles, T = 7
     # T = 1: the VALU-step tiles, unless a projection is int5 or int8 with SwiGLU
     (1, 1088, [(4, False, 96, False), (5, True, 100, False), (4, False, 36, True)]),   # odd group count
     (1, 448, [(8, False, 64, False), (8, True, 100, False), (4, True, 40, True), (5, False, 4, False)]),
@@ -140,7 +144,7 @@ def test_multi_small(ngq, orc, T, K, specs):
     run_case(ngq, orc, T, K, specs, seed=T * 100 + K)
 
 
-@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("T", [1, 4, 8])
 def test_multi_layer_shapes(ngq, orc, T):
     """The three projections of a stacked layer (QK int4, gate/value int5 with
     bf16 scales, gate/up int4 with the SwiGLU epilogue) in one call."""
@@ -163,7 +167,8 @@ def test_multi_k_zero_and_t_zero(ngq):
 
 
 @pytest.mark.parametrize("T,specs", [(8, [(4, False, 4096, False), (5, True, 2048, True)]),
-                                     (1, [(4, False, 4096, False), (5, True, 2048, False), (4, False, 2048, True)])])
+                                     (1, [(4, False, 4096, False), (5, True, 2048, False), (4, False, 2048, True)]),
+                                     (4, [(4, False, 4096, False), (5, True, 2048, False), (4, False, 2048, True)])])
 def test_multi_deterministic_and_graph_replay(ngq, T, specs):
     K = 1024
     g = np.random.default_rng(3)
