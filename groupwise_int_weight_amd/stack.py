@@ -45,16 +45,16 @@ class Stack:
     and the work buffers of one token count T.
 
     By default every call runs in order on the main stream.  With `fused` the
-    QK, gate/value and gate/up projections are one ngq_multi_gemm launch (X
-    staged once, the tiles of all three balanced over the CUs) and the down
+    QK, gate/value and gate/up projections are one ngq_multi_gemm launch (one
+    launch cost, the tiles of all three spread over the CUs together) and the down
     projection with the rescale is ngq_gemm_rescale (K split, since its 160
     column tiles alone leave CUs idle, and the rescale done by the kernel
     that adds the slices).  With `concurrent`
     the QK and gate/value projections, which only read x, run on two side
     streams beside the gate/up and down projections, and the main stream waits
-    for them before the rescale overwrites x.  On MI355X that is slower: each
-    projection kernel keeps one persistent workgroup per CU, and a kernel
-    running beside it delays the workgroups that own its tiles."""
+    for them before the rescale overwrites x.  On MI355X that is slower
+    (measured): a kernel running beside another delays the workgroups that
+    own its tiles, and the launch that finishes last sets the layer's time."""
 
     def __init__(self, layers, T: int, device="cuda", concurrent: bool = False, fused: bool = False):
         import torch
