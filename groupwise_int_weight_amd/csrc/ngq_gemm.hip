@@ -3061,12 +3061,13 @@ hipError_t launch_fmt(const Format& f, int v, const dev::GemmArgs& a, uint32_t l
 // against 6.52 with 12 and 6.66 with 8); in an interleaved A/B of the whole
 // kernels, int8 with 5 streaming waves took 10.41, 10.31, 10.90 us at T = 2,
 // 4, 8 against 10.66, 10.70, 11.13 for the 14-wave X-resident kernel, and
-// the VALU step with 8 waves 10.26 at T = 1 against 10.77 with 10.
+// the VALU step with 7 waves 10.00 at T = 1 against 10.23-10.26 with 8, 10.24
+// with 6, 10.75 with 9 and 10.77 with 10.
 constexpr int kStreamW = 10;
 constexpr int kStreamW8 = 5;
 constexpr int kStreamW2 = 5;  // SwiGLU (two output sets), whose pairs are twice as large
 constexpr int kStreamSwigluMaxT = 4;
-constexpr int kDotW8 = 8;
+constexpr int kDotW8 = 7;
 constexpr int kDotW2 = 7;  // SwiGLU (two output sets): three workgroups a CU at 81 VGPRs
 // int8 at T >= 2 on the streaming kernel (else the 14-wave X-resident one)
 constexpr bool kInt8Stream = true;
@@ -3107,7 +3108,7 @@ hipError_t launch_stream(const Format& f, int v, const dev::GemmArgs& a, hipStre
 }
 
 // The VALU-inner-step kernel: the streaming kernel's pipeline and tiles (32
-// columns; 10 waves, 8 for int8).
+// columns; 10 waves, 7 for int8 and for SwiGLU).
 template <int BITS, bool SBF16, int NSETS>
 hipError_t launch_dot_b(const dev::GemmArgs& a, hipStream_t st) {
   constexpr int W = dot_waves(BITS, NSETS);

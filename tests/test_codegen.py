@@ -56,10 +56,29 @@ def waterfall_blocks(lines):
 def test_every_gemm_kernel_is_present(asm):
     found = {re.match(r"_ZN3ngq3dev\d+(gemm\w*?kernel)", k).group(1) for k, _ in kernels(asm)}
     for fam in ("gemm_xres_kernel", "gemm_kernel", "gemm_multi_kernel", "gemm_splitk_kernel", "gemm_wide_kernel",
-                "gemm_tiled_kernel", "gemm_tiled_sx_kernel"):
+                "gemm_tiled_kernel", "gemm_tiled_sx_kernel", "gemm_stream_kernel", "gemm_dot_kernel",
+                "gemm_multi_dot_kernel", "gemm_multi_stream_kernel"):
         assert fam in found, (fam, sorted(found))
 
 
 def test_no_load_waits_on_a_descriptor_loop(asm):
     bad = {name: n for name, lines in kernels(asm) if (n := waterfall_blocks(lines))}
+    assert not bad, bad
+
+
+def test_decode_kernels_use_no_scratch(asm):
+    """The streaming, VALU-step and one-tile-per-workgroup fused kernels keep
+    everything in registers: no spills, and no private copy of the argument
+    block (the fused kernels index their projection descriptors with a
+    workgroup-uniform value)."""
+    meta = {}
+    for m in re.finditer(r"\.name:\s+(_ZN3ngq3dev\d+(gemm_(?:multi_dot|multi_stream|stream|dot)_kernel)\S*)", asm):
+        start = asm.rfind("\n  - ", 0, m.start())
+        end = asm.find("\n  - ", m.end())
+        block = asm[start:end if end > 0 else len(asm)]
+        fields = dict(re.findall(r"\.(private_segment_fixed_size|vgpr_spill_count):\s+(\d+)", block))
+        meta[m.group(1)] = fields
+    assert {re.match(r"_ZN3ngq3dev\d+(\w+?kernel)", k).group(1) for k in meta} == {
+        "gemm_multi_dot_kernel", "gemm_multi_stream_kernel", "gemm_stream_kernel", "gemm_dot_kernel"}
+    bad = {k: v for k, v in meta.items() if v.get("private_segment_fixed_size") != "0" or v.get("vgpr_spill_count") != "0"}
     assert not bad, bad
