@@ -1792,9 +1792,16 @@ __global__ __launch_bounds__(kMultiDotW * 64) void gemm_multi_dot_kernel(MultiTi
 
 constexpr int kMultiStreamW = 4;
 
+// Columns of a plain (one output set) tile in gemm_multi_stream_kernel: 64 at
+// T >= 5, where a tile's X bands (80 KB per workgroup at T = 8) are worth
+// sharing over more columns (T = 8: 36.1 against 37.4 us; at T <= 4 no
+// gain), else 32.  SwiGLU tiles keep 32 columns of each half.
+__host__ __device__ constexpr int multi_tile_cols(int T, int nsets) { return nsets == 1 && T >= 5 ? 64 : 32; }
+
 template <int XM>
 __global__ __launch_bounds__(kMultiStreamW * 64) void gemm_multi_stream_kernel(MultiTileArgs m) {
   constexpr int W = kMultiStreamW;
+  constexpr int VP = multi_tile_cols(XM, 1) / 16;  // plain tiles; XM = 8 stands for T = 5..8
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int b = blockIdx.x;
   int p = 0;
@@ -1804,14 +1811,14 @@ __global__ __launch_bounds__(kMultiStreamW * 64) void gemm_multi_stream_kernel(M
   const int tile = xcd_tile(b - b0, m.end[p] - b0);
   const GemmArgs& a = m.proj[p];
   switch (m.kind[p]) {
-    case multi_kind(4, false, 1): stream_tile<4, false, 2, W, XM, 1>(a, tile, smem); break;
-    case multi_kind(4, true, 1): stream_tile<4, true, 2, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(4, false, 1): stream_tile<4, false, VP, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(4, true, 1): stream_tile<4, true, VP, W, XM, 1>(a, tile, smem); break;
     case multi_kind(4, false, 2): stream_tile<4, false, 2, W, XM, 2>(a, tile, smem); break;
     case multi_kind(4, true, 2): stream_tile<4, true, 2, W, XM, 2>(a, tile, smem); break;
-    case multi_kind(5, false, 1): stream_tile<5, false, 2, W, XM, 1>(a, tile, smem); break;
-    case multi_kind(5, true, 1): stream_tile<5, true, 2, W, XM, 1>(a, tile, smem); break;
-    case multi_kind(8, false, 1): stream_tile<8, false, 2, W, XM, 1>(a, tile, smem); break;
-    case multi_kind(8, true, 1): stream_tile<8, true, 2, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(5, false, 1): stream_tile<5, false, VP, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(5, true, 1): stream_tile<5, true, VP, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(8, false, 1): stream_tile<8, false, VP, W, XM, 1>(a, tile, smem); break;
+    case multi_kind(8, true, 1): stream_tile<8, true, VP, W, XM, 1>(a, tile, smem); break;
     default: break;
   }
 }
@@ -3605,9 +3612,9 @@ int load_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, de
 // a.proj, kinds in kind) as segments of one grid, the heaviest tiles (weight
 // and scale bytes per tile) first.  Measured against the persistent kernel
 // (QK + gate/value + gate/up): T = 1 32.7 against 37.8 us, T = 2 32.7
-// against 37.2-38.2, T = 4 33.5 against 37.4-37.9, T = 8 37.2-37.4 against
-// 37.9-39.0; with 2, 3, 5, 6 or 8 waves a tile at T >= 2: 2-10 % slower
-// than 4.
+// against 37.2-38.2, T = 4 33.5 against 37.4-37.9, T = 8 36.1 (37.2-37.4
+// with 32-column plain tiles) against 37.9-39.0; with 2, 3, 5, 6 or 8 waves
+// a tile at T >= 2: 2-10 % slower than 4.
 constexpr int kMultiStreamMaxT = 8;
 
 int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs& a, const int* kind, int n,
@@ -3616,7 +3623,8 @@ int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs
   long tile_bytes[NGQ_MAX_PROJ];
   for (int i = 0; i < n; ++i) {
     const dev::MultiProj& mp = a.proj[i];
-    tile_bytes[i] = ((long)mp.p0_bytes + mp.p1_bytes + mp.s_bytes) / ((mp.Nout + 31) / 32);
+    const int tc = dev::multi_tile_cols(T, mp.Ncols / mp.Nout);
+    tile_bytes[i] = ((long)mp.p0_bytes + mp.p1_bytes + mp.s_bytes) / ((mp.Nout + tc - 1) / tc);
     order[i] = i;
   }
   std::stable_sort(order, order + n, [&](int i, int j) { return tile_bytes[i] > tile_bytes[j]; });
@@ -3633,7 +3641,8 @@ int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs
     g.T = T; g.K = K; g.Nout = mp.Nout; g.Ncols = mp.Ncols; g.up_off = mp.up_off;
     g.G = G; g.pairs = pairs;
     g.ppw = (pairs + w - 1) / w;
-    g.ntiles = (mp.Nout + 31) / 32;
+    const int tc = dev::multi_tile_cols(T, mp.Ncols / mp.Nout);
+    g.ntiles = (mp.Nout + tc - 1) / tc;
     g.p0_bytes = mp.p0_bytes; g.p1_bytes = mp.p1_bytes; g.s_bytes = mp.s_bytes; g.x_bytes = (uint32_t)xb;
     g.mask_nib = dev::kMasks.nib; g.mask_base = dev::kMasks.base; g.mask_hi = dev::kMasks.hi;
     g.tiles_q = g.tiles_r = 0;
@@ -3647,7 +3656,8 @@ int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs
     const uint32_t lds = dev::DotSmem<dev::kMultiDotW, 1, 2>::bytes();
     hipLaunchKernelGGL(dev::gemm_multi_dot_kernel, dim3((unsigned)grid), dim3(dev::kMultiDotW * 64), lds, st, m);
   } else {
-    const uint32_t lds = dev::StreamSmem<dev::kMultiStreamW>::bytes(32, 2);
+    const uint32_t lds = std::max(dev::StreamSmem<dev::kMultiStreamW>::bytes(32, 2),
+                                  dev::StreamSmem<dev::kMultiStreamW>::bytes(64, 1));
     const dim3 g((unsigned)grid), blk(dev::kMultiStreamW * 64);
     if (T == 2)
       hipLaunchKernelGGL(dev::gemm_multi_stream_kernel<2>, g, blk, lds, st, m);
