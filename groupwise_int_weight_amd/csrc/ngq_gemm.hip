@@ -143,11 +143,23 @@ __device__ __forceinline__ u32x4 nibbles_to_bf16_il(uint32_t w, const UnpackMask
   return r;
 }
 
+// The 5th bits of k-block b of a high-bit word p1 (its byte b, bit i for
+// k = i) spread for nibbles5_to_bf16_il with one byte permute: byte 0 of the
+// result is byte b of p1s = p1 << 4 (the block's k 0..3 bits at 4..7), byte 2
+// is byte b of p1 (k 4..7 at bits 4..7 of it, so 20..23); bits 0..3 and
+// 16..19 carry neighbouring bits that the unpack never reads.  p1s is shared
+// by the four blocks of the word; hb_select(b) is the permute's selector.
+__host__ __device__ constexpr uint32_t hb_select(uint32_t b) { return b | 0x0C00u | ((4u + b) << 16) | 0x0C000000u; }
+__device__ __forceinline__ uint32_t hb_spread(uint32_t p1, uint32_t p1s, uint32_t sel) {
+  return __builtin_amdgcn_perm(p1, p1s, sel);
+}
+
 // int5: the high bits are first merged into the base pattern, then the
 // nibbles; each merge is one three-input bitwise op ((a & b) | c, truth
-// table 0xEA), so an output register costs two shifts and two ops.
-__device__ __forceinline__ u32x4 nibbles5_to_bf16_il(uint32_t w, uint32_t hb, const UnpackMasks& mk) {
-  const uint32_t hs = ((hb & 0x0Fu) << 4) | ((hb & 0xF0u) << 16);
+// table 0xEA), so an output register costs two shifts and two ops.  hs holds
+// the block's eight 5th bits spread: k 0..3 at bits 4..7, k 4..7 at bits
+// 20..23 (hb_spread); no other bit of it is read.
+__device__ __forceinline__ u32x4 nibbles5_to_bf16_il(uint32_t w, uint32_t hs, const UnpackMasks& mk) {
   u32x4 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -426,9 +438,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
             av = nibbles_to_bf16_il(buf.a[s][st][i], mk);
           } else if constexpr (BITS == 5) {
             // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
-            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
-                                                                                 8u * (uint32_t)(q & 1), 8u);
-            av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, mk);
+            const uint32_t p1 = buf.p1[s][st >> 1][i];
+            const uint32_t hs = hb_spread(p1, p1 << 4, hb_select(2u * (uint32_t)(st & 1) + (uint32_t)(q & 1)));
+            av = nibbles5_to_bf16_il(buf.a[s][st][i], hs, mk);
           } else {
             av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
           }
@@ -801,9 +813,9 @@ __device__ __forceinline__ void pair_partials(const Buf& buf, int p, const XresS
           av = nibbles_to_bf16_il(buf.a[s][st][i], ln.mk);
         } else if constexpr (BITS == 5) {
           // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
-          const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
-                                                                               8u * (uint32_t)(ln.q & 1), 8u);
-          av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, ln.mk);
+          const uint32_t p1 = buf.p1[s][st >> 1][i];
+          const uint32_t hs = hb_spread(p1, p1 << 4, hb_select(2u * (uint32_t)(st & 1) + (uint32_t)(ln.q & 1)));
+          av = nibbles5_to_bf16_il(buf.a[s][st][i], hs, ln.mk);
         } else {
           av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
         }
@@ -1216,9 +1228,10 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int tile, uint8_t
           if constexpr (BITS == 4) {
             av = nibbles_to_bf16_il(buf.a[s][st][i], mk);
           } else if constexpr (BITS == 5) {
-            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st >> 1][i], 16u * (uint32_t)(st & 1) +
-                                                                                 8u * (uint32_t)(q & 1), 8u);
-            av = nibbles5_to_bf16_il(buf.a[s][st][i], hb, mk);
+            // k-block 2 st + (q & 1) of a 32-k P1 word group: byte 2 (st & 1) + (q & 1)
+            const uint32_t p1 = buf.p1[s][st >> 1][i];
+            const uint32_t hs = hb_spread(p1, p1 << 4, hb_select(2u * (uint32_t)(st & 1) + (uint32_t)(q & 1)));
+            av = nibbles5_to_bf16_il(buf.a[s][st][i], hs, mk);
           } else {
             av = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
           }
@@ -1470,8 +1483,8 @@ __device__ __forceinline__ void dot_tile(const GemmArgs& a, int tile, uint8_t* s
         if constexpr (BITS == 4) {
           w[s] = nibbles_to_bf16_il(buf.a[s][kb], mk);
         } else if constexpr (BITS == 5) {
-          w[s] = nibbles5_to_bf16_il(buf.a[s][kb], __builtin_amdgcn_ubfe(buf.p1[s][kb >> 2], 8u * (uint32_t)(kb & 3), 8u),
-                                     mk);
+          const uint32_t p1 = buf.p1[s][kb >> 2];
+          w[s] = nibbles5_to_bf16_il(buf.a[s][kb], hb_spread(p1, p1 << 4, hb_select((uint32_t)(kb & 3))), mk);
         } else {
           w[s] = bytes_to_bf16_il(buf.a[s][2 * kb], buf.a[s][2 * kb + 1]);
         }
@@ -2101,8 +2114,8 @@ __global__ __launch_bounds__(kWideWaves * 64) void gemm_wide_kernel(WideArgs a) 
             av[st][s][i] = nibbles_to_bf16_il(buf.a[s][st][i], mk);
           } else if constexpr (BITS == 5) {
             // k-block 4 st + q is byte q of the step's 32-k high-bit word
-            const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][st][i], 8u * (uint32_t)q, 8u);
-            av[st][s][i] = nibbles5_to_bf16_il(buf.a[s][st][i], hb, mk);
+            const uint32_t p1 = buf.p1[s][st][i];
+            av[st][s][i] = nibbles5_to_bf16_il(buf.a[s][st][i], hb_spread(p1, p1 << 4, hb_select((uint32_t)q)), mk);
           } else {
             av[st][s][i] = bytes_to_bf16_il(buf.a[s][st][i], buf.a[s][st][V + i]);
           }
@@ -2324,8 +2337,8 @@ __device__ __forceinline__ void tile_group(const Buf& buf, const bf16x8 (&bfr)[4
           av[ks] = nibbles_to_bf16_il(buf.a[s][ks][i], mk);
         } else if constexpr (BITS == 5) {
           // k-block 4 ks + q is byte q of the step's 32-k high-bit word
-          const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][ks][i], 8u * (uint32_t)q, 8u);
-          av[ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb, mk);
+          const uint32_t p1 = buf.p1[s][ks][i];
+          av[ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb_spread(p1, p1 << 4, hb_select((uint32_t)q)), mk);
         } else {
           av[ks] = bytes_to_bf16_il(buf.a[s][ks][i], buf.a[s][ks][V + i]);
         }
@@ -2537,8 +2550,8 @@ __device__ __forceinline__ void tile_group_tbo(const Buf& buf, ReadB&& rb, const
           av[s][i][ks] = nibbles_to_bf16_il(buf.a[s][ks][i], mk);
         } else if constexpr (BITS == 5) {
           // k-block 4 ks + q is byte q of the step's 32-k high-bit word
-          const uint32_t hb = __builtin_amdgcn_ubfe(buf.p1[s][ks][i], 8u * (uint32_t)q, 8u);
-          av[s][i][ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb, mk);
+          const uint32_t p1 = buf.p1[s][ks][i];
+          av[s][i][ks] = nibbles5_to_bf16_il(buf.a[s][ks][i], hb_spread(p1, p1 << 4, hb_select((uint32_t)q)), mk);
         } else {
           av[s][i][ks] = bytes_to_bf16_il(buf.a[s][ks][i], buf.a[s][ks][V + i]);
         }
@@ -2715,8 +2728,8 @@ __global__ __launch_bounds__(256) void unpack_kernel(const void* wq, uint32_t p0
     v = nibbles_to_bf16_il(p0[(size_t)kb * N + n], kMasks);
   } else if constexpr (BITS == 5) {
     const uint32_t* p1 = reinterpret_cast<const uint32_t*>(static_cast<const char*>(wq) + p0_bytes);
-    v = nibbles5_to_bf16_il(p0[(size_t)kb * N + n],
-                            __builtin_amdgcn_ubfe(p1[(size_t)(kb >> 2) * N + n], 8u * (uint32_t)(kb & 3), 8u), kMasks);
+    const uint32_t hw = p1[(size_t)(kb >> 2) * N + n];
+    v = nibbles5_to_bf16_il(p0[(size_t)kb * N + n], hb_spread(hw, hw << 4, hb_select((uint32_t)(kb & 3))), kMasks);
   } else {
     v = bytes_to_bf16_il(p0[(size_t)(2 * kb) * N + n], p0[(size_t)(2 * kb + 1) * N + n]);
   }
