@@ -1071,8 +1071,18 @@ __device__ __forceinline__ uint32_t il_offset(uint32_t k) {
 // waits for it, and with it every older load, before the join)
 // NSETS = 2: the SwiGLU gate/up projection, the tile's columns of both
 // halves (gate at c, up at up_off + c) in each pair.
-template <int BITS, bool SBF16, int V, int W, int XM, int NSETS>
-__device__ __forceinline__ void stream_tile(const GemmArgs& a, int tile, uint8_t* smem) {
+// A K slice of a tile (split K): pairs pbase .. pbase + npairs - 1, ppw pair
+// slots per wave, and the slice's fp32 output block [T][Nout].
+struct StreamSlice {
+  int pbase, npairs, ppw;
+  float* partial;
+};
+
+// SLICE: the tile over one K slice, its wave blocks summed in wave order into
+// the slice's fp32 block instead of rounded into y.
+template <int BITS, bool SBF16, int V, int W, int XM, int NSETS, bool SLICE = false>
+__device__ __forceinline__ void stream_tile(const GemmArgs& a, int tile, uint8_t* smem,
+                                            const StreamSlice& sl = StreamSlice{0, 0, 0, nullptr}) {
   constexpr int WPK = BITS == 8 ? 2 : 1;
   constexpr int TILE = 16 * V;
   constexpr uint32_t XROW = Smem::XROW, XZERO = Smem::XZERO;
@@ -1132,11 +1142,16 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int tile, uint8_t
   }
 
   auto pair_of = [&](int i) { return wave + W * i; };
+  // the pairs this tile covers: all of K, or the slice's
+  const int pbase = SLICE ? sl.pbase : 0;
+  const int npairs = SLICE ? sl.npairs : a.pairs;
+  const int ppw = SLICE ? sl.ppw : a.ppw;
 
-  // the loads of pair p (p >= pairs: out of range, nothing moves); flags are
-  // combined bitwise so that no lane-divergent branch appears
-  auto issue = [&](StreamBuf<BITS, V, NSETS>& buf, int p) {
-    const bool valid = p < a.pairs;
+  // the loads of pair pbase + j (j >= npairs: out of range, nothing moves);
+  // flags are combined bitwise so that no lane-divergent branch appears
+  auto issue = [&](StreamBuf<BITS, V, NSETS>& buf, int j) {
+    const bool valid = j < npairs;
+    const int p = pbase + j;
     const uint32_t pa = valid ? (uint32_t)p * 16u * WPK * rowb : kOOB;
     const uint32_t pp1 = valid ? (uint32_t)p * 4u * rowb : kOOB;
     const uint32_t ps = valid ? (uint32_t)p * rowb : kOOB;  // two scale rows of 2-byte entries
@@ -1257,18 +1272,18 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int tile, uint8_t
   StreamBuf<BITS, V, NSETS> buf[2];
   issue(buf[0], pair_of(0));
   __builtin_amdgcn_sched_barrier(0);
-  for (int i = 0; i < a.ppw; i += 2) {
+  for (int i = 0; i < ppw; i += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     stage_x(buf[0]);
     issue(buf[1], pair_of(i + 1));
     __builtin_amdgcn_sched_barrier(0);
-    if (pair_of(i) < a.pairs) compute(buf[0]);
+    if (pair_of(i) < npairs) compute(buf[0]);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     stage_x(buf[1]);
     issue(buf[0], pair_of(i + 2));
     __builtin_amdgcn_sched_barrier(0);
-    if (pair_of(i + 1) < a.pairs) compute(buf[1]);
+    if (pair_of(i + 1) < npairs) compute(buf[1]);
     __builtin_amdgcn_sched_barrier(0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1281,8 +1296,21 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& a, int tile, uint8_t
   ln.h = h;
   store_partials<V, NSETS>(acc, ln, part + (uint32_t)wave * BLK);
   lds_barrier();
-  const ProjView pv{a.wq, a.scales, a.y, a.p0_bytes, a.p1_bytes, a.s_bytes, a.Nout, a.Ncols, a.up_off};
-  finish_outputs<V, NSETS, W>(part, pv, a.T, (int)c0);
+  if constexpr (SLICE) {
+    static_assert(NSETS == 1, "a K slice has one output set");
+    for (int idx = threadIdx.x; idx < 8 * TILE; idx += W * 64) {
+      const int tt = idx / TILE, col = idx % TILE;
+      if (tt >= a.T || (int)c0 + col >= a.Nout) continue;
+      const float* src = part + (uint32_t)tt * (uint32_t)(TILE + 4) + (uint32_t)col;
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < W; ++k) sum += src[(uint32_t)k * BLK];
+      sl.partial[(size_t)tt * a.Nout + c0 + col] = sum;
+    }
+  } else {
+    const ProjView pv{a.wq, a.scales, a.y, a.p0_bytes, a.p1_bytes, a.s_bytes, a.Nout, a.Ncols, a.up_off};
+    finish_outputs<V, NSETS, W>(part, pv, a.T, (int)c0);
+  }
 }
 
 template <int BITS, bool SBF16, int V, int W, int XM, int NSETS>
@@ -1839,100 +1867,33 @@ __global__ __launch_bounds__(kMultiStreamW * 64) void gemm_multi_stream_kernel(M
 // ---- split K: long K over few column tiles ----------------------------------
 //
 // A projection with long K and few 32-column tiles (the down projection: K =
-// 17408, 160 tiles) leaves CUs idle with one workgroup per tile, and at T = 8
-// its X does not fit in LDS.  Here K is cut into S slices of whole group pairs
-// and a unit is one column tile over one slice.  A workgroup of kSplitWaves
-// waves takes kSplitWaves tiles of slice b % S (with S = 8, each XCD works on
-// one slice and its workgroups share that slice of X through their L2); only
-// that slice of X is staged in LDS, and each wave streams its own unit's
-// pairs, kSplitNB in flight, with no pair slot left empty and no barrier after
-// the staging.  Each unit's fp32 sum goes to partial[slice][t][n] in a
-// caller's workspace, and a second kernel adds the S partials of every output
-// in slice order and rounds to bf16, so the result is deterministic.
+// 17408, 160 tiles) leaves CUs idle with one workgroup per tile.  Here K is
+// cut into S slices of whole group pairs and each workgroup streams one
+// 64-column tile over one slice on the streaming kernel's pipeline (X band
+// per pair, one pair in flight per wave), workgroup b taking tile b / S of
+// slice b % S; S is chosen so that the S x (tiles of 64 columns) workgroups
+// fill the CUs about once (down: 3 slices x 80 tiles).  Each unit's fp32 sum
+// goes to partial[slice][t][n] in a caller's workspace, and a second kernel
+// adds the S partials of every output in slice order and rounds to bf16, so
+// the result is deterministic.
 
-constexpr int kSplitWaves = 5, kSplitNB = 3;
+constexpr int kSplitWaves = 8;
+constexpr int kSplitV = 4;  // 64-column tiles
 
 struct SplitArgs {
-  const void* x;
-  const void* wq;
-  const void* scales;
+  GemmArgs g;  // the projection; g.pairs counts the pairs of the whole K
   float* partial;  // [S][T][N]
-  int T, K, N, G, pairs, ntiles, S, pps;
-  uint32_t p0_bytes, p1_bytes, s_bytes, x_bytes;
-  uint32_t mask_nib, mask_base, mask_hi;
+  int S, pps;  // slices, pairs per slice (the last may have fewer)
 };
 
-// XL chunks per thread of a K slice of X: chunk c is 16 bytes at k-chunk
-// c % (kx / 8) of row c / (kx / 8), rows of K.
-template <int XL, int W>
-__device__ __forceinline__ void x_load_slice(uint32_t (&xv)[XL][4], const void* x, uint32_t x_bytes, int T, int K,
-                                             int k0, int kx) {
-  const __amdgpu_buffer_rsrc_t rX = make_rsrc(x, x_bytes);
-  const int rowch = kx >> 3, nch = T * rowch;
-  int tt[XL], kc[XL];
-  chunk_coords<XL, W>(rowch, tt, kc);
-#pragma unroll
-  for (int j = 0; j < XL; ++j) {
-    const int c = threadIdx.x + W * 64 * j;
-    const uint32_t off = c < nch ? ((uint32_t)tt[j] * (uint32_t)K + (uint32_t)k0) * 2u + (uint32_t)kc[j] * 16u : kOOB;
-    load_words<4>(xv[j], rX, off);
-  }
-}
-
-template <int BITS, bool SBF16, int XL>
+template <int BITS, bool SBF16, int XM>
 __global__ __launch_bounds__(kSplitWaves * 64) void gemm_splitk_kernel(SplitArgs a) {
-  constexpr int W = kSplitWaves, NB = kSplitNB, V = 2, TILE = 16 * V;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int b = blockIdx.x, ks = b % a.S, j = b / a.S;
-  const int p0 = ks * a.pps, pend = min(p0 + a.pps, a.pairs), n = pend - p0;
-  const int kx = min(a.K, pend * 128) - p0 * 128;  // the slice's k (its last pair may hold one group)
-  const XresLane ln = xres_lane(a.T, kx, a.mask_nib, a.mask_base, a.mask_hi);
-  const int tile = j * W + ln.wave;  // past the last tile, the wave only helps stage X
-  const bool live = tile < a.ntiles;
-  const uint32_t c0 = (uint32_t)(tile * TILE);
-  uint32_t xv[XL][4];
-  x_load_slice<XL, W>(xv, a.x, a.x_bytes, a.T, a.K, p0 * 128, kx);
-  __builtin_amdgcn_sched_barrier(0);
-  const ProjView pv{a.wq, a.scales, nullptr, a.p0_bytes, a.p1_bytes, a.s_bytes, a.N, a.N, 0};
-  const PairLoads<BITS, V, 1> ld(pv, ln);
-  const XresShape sh{a.T, kx, a.G, a.pairs, 0, p0, pend};
-  WBuf<BITS, V, 1> buf[NB];
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    ld.issue(buf[u], c0, p0 + u, live & (u < n));
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  x_stage<XL, W>(smem, xv, a.T, kx);
-
-  f32x4 acc[1][V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) acc[0][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < n; k += NB) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      if (k + u < n) {
-        f32x4 dp[1][V];
-        pair_partials<BITS, V, 1>(buf[u], p0 + k + u, sh, ln, smem, dp);
-        scale_accumulate<V, 1>(buf[u], SBF16, dp, acc);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      ld.issue(buf[u], c0, p0 + k + u + NB, live & (k + u + NB < n));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // slots j and j + 8 hold the two group halves of token j: added here, and
-  // the lanes of the first half write the unit's sums
-  float* const out = a.partial + (size_t)ks * a.T * a.N;
-#pragma unroll
-  for (int i = 0; i < V; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int other =
-          __builtin_amdgcn_mov_dpp(__float_as_int(acc[0][i][r]), 0x128 /* row_ror:8 */, 0xF, 0xF, false);
-      const float sum = acc[0][i][r] + __int_as_float(other);
-      const int col = (int)c0 + V * (4 * ln.q + r) + i;
-      if (live & (ln.h == 0) & (ln.t < a.T) & (col < a.N)) out[(size_t)ln.t * a.N + col] = sum;
-    }
+  const int b = blockIdx.x, ks = b % a.S;
+  const int pb = ks * a.pps, np = max(0, min(a.pps, a.g.pairs - pb));
+  const StreamSlice sl{pb, np, (np + kSplitWaves - 1) / kSplitWaves,
+                       a.partial + (size_t)ks * (size_t)a.g.T * (size_t)a.g.Nout};
+  stream_tile<BITS, SBF16, kSplitV, kSplitWaves, XM, 1, true>(a.g, xcd_tile(b / a.S, a.g.ntiles), smem, sl);
 }
 
 // y[e] = bf16(partial[0][e] + partial[1][e] + ... + partial[S-1][e]), in slice
@@ -3809,47 +3770,45 @@ constexpr int kSplitMax = 8;  // slices; the workspace is sized for this many
 // at NGQ_MAX_T tokens.
 size_t splitk_workspace_bytes(int N) { return (size_t)kSplitMax * NGQ_MAX_T * (size_t)N * 4u; }
 
-// Slices for a shape: 8 (one per XCD) when X does not fit the X-resident
-// kernel's prologue (T K > 73728: the down projection at T >= 5), each slice
-// keeps at least 8 pairs and the tiles alone would leave CUs idle; 1 means no
-// split (the call runs as ngq_gemm).  Measured on MI355X for the down
-// projection (K = 17408, N = 5120): split 18.1 us against 19.1 at T = 8, but
-// no gain where X fits (17.8 against 17.7 at T = 4, 17.0 against 15.9 at
-// T = 1): with every CU busy the slices still stream at ~3 TB/s, and the
-// second launch costs ~2 us.
-int choose_splits(int T, int K, int pairs, int ntiles, int cus) {
-  if ((long)T * K <= 73728L || ntiles >= cus || pairs < kSplitMax * 8) return 1;
-  return kSplitMax;
+// Slices for a shape whose 32-column tiles leave CUs idle: as many as let
+// S x (64-column tiles) fill the CUs once, with at least 8 pairs a slice, at
+// most kSplitMax; 1 means no split.  The down projection (K = 17408, N = 5120)
+// gets 3 slices x 80 tiles.  Measured on MI355X (interleaved A/B, the split
+// and its closing kernel): 12.2, 12.7, 12.8, 13.5 us at T = 1, 2, 4, 8
+// against 14.2, 15.1, 16.1 for the unsplit streaming kernels and 16.1 for
+// the earlier 8-slice X-resident split at T = 8; with the closing rescale
+// 15.0 / 16.3 us at T = 1 / 8 against 18.3 / 19.9.  2 slices (160
+// workgroups) or 4 (320), and 32-column tiles, were slower.
+int split_count(int K, int N, int cus) {
+  const int pairs = (K / kGroup + 1) / 2, tiles64 = (N + 63) / 64;
+  if ((N + 31) / 32 >= cus || tiles64 == 0) return 1;
+  return std::max(1, std::min(kSplitMax, std::min(cus / tiles64, pairs / 8)));
 }
 
-// One split-K kernel; the flag that its LDS limit was raised is a static of
-// this instantiation, so every kernel (each XL) has its own.
-template <int BITS, bool SBF16, int XL>
-hipError_t launch_splitk_xl(const dev::SplitArgs& a, int grid, uint32_t lds, hipStream_t st) {
-  auto kern = dev::gemm_splitk_kernel<BITS, SBF16, XL>;
-  static std::atomic<uint64_t> raised{0};
-  if (lds > 64u * 1024u) {
-    const hipError_t e = raise_lds(reinterpret_cast<const void*>(kern), raised);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(dev::kSplitWaves * 64), lds, st, a);
+// The split kernel: S x (64-column tiles) workgroups.
+template <int BITS, bool SBF16>
+hipError_t launch_splitk_b(const dev::SplitArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.S * a.g.ntiles)), blk(dev::kSplitWaves * 64);
+  const uint32_t lds = dev::StreamSmem<dev::kSplitWaves>::bytes(16 * dev::kSplitV, 1);
+  if (a.g.T == 1)
+    hipLaunchKernelGGL((dev::gemm_splitk_kernel<BITS, SBF16, 1>), grid, blk, lds, st, a);
+  else if (a.g.T == 2)
+    hipLaunchKernelGGL((dev::gemm_splitk_kernel<BITS, SBF16, 2>), grid, blk, lds, st, a);
+  else if (a.g.T <= 4)
+    hipLaunchKernelGGL((dev::gemm_splitk_kernel<BITS, SBF16, 4>), grid, blk, lds, st, a);
+  else
+    hipLaunchKernelGGL((dev::gemm_splitk_kernel<BITS, SBF16, 8>), grid, blk, lds, st, a);
   return hipGetLastError();
 }
-
-template <int BITS, bool SBF16>
-hipError_t launch_splitk_b(int xl, const dev::SplitArgs& a, int grid, uint32_t lds, hipStream_t st) {
-  if (xl <= 7) return launch_splitk_xl<BITS, SBF16, 7>(a, grid, lds, st);
-  return launch_splitk_xl<BITS, SBF16, 18>(a, grid, lds, st);
-}
+static_assert(dev::StreamSmem<dev::kSplitWaves>::bytes(16 * dev::kSplitV, 1) <= 64u * 1024u,
+              "the split kernel's LDS stays under the default 64 KiB limit");
 
 // x_next == nullptr: ngq_gemm_splitk.  Otherwise ngq_gemm_rescale: the same
-// projection, then x_next = the RMS rescale of y.  Its split is taken at every
-// T where the tiles leave CUs idle: the closing kernel then also does the
-// rescale, so the split's second launch replaces the rescale's own.  With a
-// residual (ngq_gemm_residual_rescale) K is always split, into as many
-// slices (at most 8) as leave every slice at least 8 pairs, or one slice, so
-// that the residual meets the fp32 sum in the closing kernel and y is
-// rounded once.
+// projection and split, then x_next = the RMS rescale of y; where K is split
+// the closing kernel also does the rescale, so the split's second launch
+// replaces the rescale's own.  With a residual (ngq_gemm_residual_rescale) K
+// is always split (split_count's slices, or one), so that the residual meets
+// the fp32 sum in the closing kernel and y is rounded once.
 int run_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq, const void* scales, void* y,
                void* x_next, const void* residual, void* workspace, size_t workspace_bytes, void* stream) {
   Format f;
@@ -3859,10 +3818,8 @@ int run_splitk(int T, int K, int N, int bits, int group, const void* x, const vo
   if ((rc = check_kn(K, N)) != NGQ_OK) return rc;
   const bool fuse = x_next != nullptr, res = residual != nullptr;
   if (res && !fuse) return NGQ_ERR_ARG;
-  const int pairs = (K / kGroup + 1) / 2, ntiles = (N + 31) / 32, cus = cu_count();
-  const int S = res    ? std::max(1, std::min(kSplitMax, pairs / 8))
-                : fuse ? (ntiles < cus && pairs >= kSplitMax * 8 ? kSplitMax : 1)
-                       : choose_splits(T, K, pairs, ntiles, cus);
+  const int pairs = (K / kGroup + 1) / 2;
+  const int S = split_count(K, N, cu_count());
   const bool split = S > 1 || res;  // the split kernel and a closing kernel
   const size_t xb = (size_t)T * K * 2, yb = (size_t)T * N * 2;
   const size_t wb0 = p0_bytes(K, N, f.bits), wb1 = p1_bytes(K, N, f.bits), sb = (size_t)(K / kGroup) * N * 2;
@@ -3898,26 +3855,25 @@ int run_splitk(int T, int K, int N, int bits, int group, const void* x, const vo
       overlaps(workspace, pb, scales, sb) || overlaps(workspace, pb, y, yb))
     return NGQ_ERR_ARG;
   dev::SplitArgs a;
-  a.x = x; a.wq = wq; a.scales = scales; a.partial = static_cast<float*>(workspace);
-  a.T = T; a.K = K; a.N = N; a.G = K / kGroup; a.pairs = pairs; a.ntiles = ntiles; a.S = S;
+  dev::GemmArgs& g = a.g;
+  g.x = x; g.wq = wq; g.scales = scales; g.y = y;
+  g.T = T; g.K = K; g.Nout = N; g.Ncols = N; g.up_off = 0;
+  g.G = K / kGroup; g.pairs = pairs; g.ppw = 0;  // the slices set their own
+  g.ntiles = (N + 16 * dev::kSplitV - 1) / (16 * dev::kSplitV);
+  g.p0_bytes = (uint32_t)wb0; g.p1_bytes = (uint32_t)wb1; g.s_bytes = (uint32_t)sb; g.x_bytes = (uint32_t)xb;
+  g.mask_nib = dev::kMasks.nib; g.mask_base = dev::kMasks.base; g.mask_hi = dev::kMasks.hi;
+  g.tiles_q = g.tiles_r = 0;
+  a.partial = static_cast<float*>(workspace);
+  a.S = S;
   a.pps = (pairs + S - 1) / S;
-  a.p0_bytes = (uint32_t)wb0; a.p1_bytes = (uint32_t)wb1; a.s_bytes = (uint32_t)sb; a.x_bytes = (uint32_t)xb;
-  a.mask_nib = dev::kMasks.nib; a.mask_base = dev::kMasks.base; a.mask_hi = dev::kMasks.hi;
-  const int kx = a.pps * 128;  // the longest slice
-  const long xchunks = (long)T * kx / 8;
-  const int xl = (int)((xchunks + dev::kSplitWaves * 64 - 1) / (dev::kSplitWaves * 64));
-  if (xl > 18) return NGQ_ERR_UNSUPPORTED;
-  const uint32_t lds = dev::XSmem::x_end(T, kx);
-  if (lds > kMaxLds) return NGQ_ERR_UNSUPPORTED;
-  const int grid = S * ((ntiles + dev::kSplitWaves - 1) / dev::kSplitWaves);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (f.bits == 4)
-    e = f.scale_bf16 ? launch_splitk_b<4, true>(xl, a, grid, lds, st) : launch_splitk_b<4, false>(xl, a, grid, lds, st);
+    e = f.scale_bf16 ? launch_splitk_b<4, true>(a, st) : launch_splitk_b<4, false>(a, st);
   else if (f.bits == 5)
-    e = f.scale_bf16 ? launch_splitk_b<5, true>(xl, a, grid, lds, st) : launch_splitk_b<5, false>(xl, a, grid, lds, st);
+    e = f.scale_bf16 ? launch_splitk_b<5, true>(a, st) : launch_splitk_b<5, false>(a, st);
   else
-    e = f.scale_bf16 ? launch_splitk_b<8, true>(xl, a, grid, lds, st) : launch_splitk_b<8, false>(xl, a, grid, lds, st);
+    e = f.scale_bf16 ? launch_splitk_b<8, true>(a, st) : launch_splitk_b<8, false>(a, st);
   if (e != hipSuccess) return NGQ_ERR_HIP;
   if (fuse && reduce_rescale_fits(N))
     return launch_reduce_rescale(static_cast<const float*>(workspace), S, T, N, y, x_next, residual, stream);
@@ -3964,8 +3920,7 @@ int run_splitk_static(int T, int K, int N, int bits, int group, const void* x, c
   if ((rc = check_kn(K, N)) != NGQ_OK) return rc;
   if (T == 0 || N == 0) return NGQ_OK;
   // the same split as ngq_gemm_splitk; the partial sums must fit the array
-  const int pairs = (K / kGroup + 1) / 2, ntiles = (N + 31) / 32;
-  const int S = choose_splits(T, K, pairs, ntiles, cu_count());
+  const int S = split_count(K, N, cu_count());
   const size_t need = S > 1 ? (size_t)S * T * N * 4u : 0;
   if (need > dev::kStaticScratchBytes) return NGQ_ERR_UNSUPPORTED;
   void* ws = nullptr;

@@ -127,17 +127,19 @@ size_t ngq_splitk_workspace_bytes(int K, int N, int bits, int group);
 
 /* ngq_gemm for long K and few 32-column tiles (a down projection: K = 17408,
  * N = 5120), with K split into slices of whole group pairs so that every CU
- * has work and only a slice of X has to fit in LDS.  Each slice's fp32 sum
- * goes to `workspace`, and a second kernel on the same stream adds the
- * slices' sums in slice order and rounds to bf16.
+ * has work: one workgroup per 64-column tile and slice, each streaming its
+ * slice's pairs with their X bands.  Each slice's fp32 sum goes to
+ * `workspace`, and a second kernel on the same stream adds the slices' sums
+ * in slice order and rounds to bf16.
  *   workspace : device, at least ngq_splitk_workspace_bytes(K, N, bits, group)
  *               bytes, 16-byte aligned; no initial contents are needed; it
  *               must not overlap the other buffers, and calls that may run
  *               at the same time must not share it (too small: NGQ_ERR_ARG)
- * Shapes, formats and status codes as ngq_gemm.  K is split only where X
- * does not fit the single-pass kernel's LDS (T K > 73728: the down projection
- * at T >= 5), the tiles alone leave CUs idle and every slice keeps 8 pairs;
- * otherwise the call runs as ngq_gemm and the workspace is not used.
+ * Shapes, formats and status codes as ngq_gemm.  K is split, at any T, where
+ * the 32-column tiles alone leave CUs idle, into as many slices (at most 8)
+ * as let the slices' 64-column tiles fill the CUs once with at least 8 pairs
+ * each (the down projection: 3); where that leaves one slice the call runs
+ * as ngq_gemm and the workspace is not used.
  * The fp32 sums are grouped differently from ngq_gemm's, so the two can
  * differ in the last bit; each is deterministic. */
 int ngq_gemm_splitk(int T, int K, int N, int bits, int group, const void* x, const void* wq,
@@ -152,8 +154,8 @@ int ngq_gemm_splitk(int T, int K, int N, int bits, int group, const void* x, con
  * ngq_gemm_splitk.
  *  - The array's device address is looked up on a device's first call (a
  *    HIP runtime query, no allocation).
- *  - Where K is split, the partial sums take 8 * T * N * 4 bytes; beyond
- *    NGQ_STATIC_SCRATCH_BYTES (T * N > 131072) the call returns
+ *  - Where K is split into S slices, the partial sums take S * T * N * 4
+ *    bytes (S <= 8); beyond NGQ_STATIC_SCRATCH_BYTES the call returns
  *    NGQ_ERR_UNSUPPORTED before any launch.  Unsplit calls need no scratch.
  *  - Every call on one device shares that device's array: calls that may run
  *    at the same time on one device (other streams, other threads) race and
@@ -215,17 +217,16 @@ int ngq_rms_rescale(int T, int N, const void* z, void* x, void* stream);
 /* The last projection of a stacked layer with the rescale that closes it:
  *   y      = X . dequant(Wq) in bf16, as ngq_gemm_splitk computes it, and
  *   x_next = the per-token RMS rescale of y, as ngq_rms_rescale(T, N, y, x_next)
- * computes it (bit for bit, given the same y).  Where the column tiles leave
- * CUs idle (the down projection: K = 17408, N = 5120) K is split at every T,
- * and the kernel that adds the slices' fp32 sums also rescales the rows, so
- * the pair of results costs two launches; otherwise the call is ngq_gemm
- * followed by ngq_rms_rescale.
+ * computes it (bit for bit, given the same y).  K is split as
+ * ngq_gemm_splitk splits it (the down projection: K = 17408, N = 5120, 3
+ * slices at every T), and the kernel that adds the slices' fp32 sums also
+ * rescales the rows, so the pair of results costs two launches; where no
+ * split applies the call is ngq_gemm followed by ngq_rms_rescale.  y equals
+ * ngq_gemm_splitk's y bit for bit.
  *   x_next    : device bf16 [T][N], overwritten; must not overlap x, wq,
  *               scales, y or the workspace (NGQ_ERR_ARG); null: NGQ_ERR_ARG
  *   workspace : as for ngq_gemm_splitk (ngq_splitk_workspace_bytes bytes)
- * Other arguments, shapes and status codes as ngq_gemm_splitk; the grouping
- * of the fp32 sums can differ from ngq_gemm_splitk's at T <= 4 (split here,
- * not there), so y can differ from it in the last bit. */
+ * Other arguments, shapes and status codes as ngq_gemm_splitk. */
 int ngq_gemm_rescale(int T, int K, int N, int bits, int group, const void* x, const void* wq,
                      const void* scales, void* y, void* x_next, void* workspace, size_t workspace_bytes,
                      void* stream);
@@ -237,18 +238,17 @@ int ngq_gemm_rescale(int T, int K, int N, int bits, int group, const void* x, co
  *   y      = bf16( X . dequant(Wq) + residual ): the residual (bf16) is added
  *            to the projection's fp32 sum, which is rounded once
  *   x_next = the per-token RMS rescale of y, as ngq_rms_rescale(T, N, y, x_next)
- * K is always split here (S = min(8, pairs / 8) slices of whole group pairs,
- * at least one, pairs = ceil(K / 128)), and the kernel that adds the slices'
- * fp32 sums in slice order adds the residual last; the sums are therefore
- * grouped as in ngq_gemm_rescale only where both take 8 slices (K >= 8192),
- * and y can differ from ngq_gemm_rescale's y + residual in the last bit.
+ * K is always split here (ngq_gemm_splitk's slices, or one slice where it
+ * does not split), and the kernel that adds the slices' fp32 sums in slice
+ * order adds the residual last; the sums are grouped as in ngq_gemm_rescale
+ * wherever that one splits, and y can differ from ngq_gemm_rescale's y +
+ * residual in the last bit (one rounding here, two there).
  *   residual : device bf16 [T][N]; must not overlap y, x_next or the
  *              workspace (NGQ_ERR_ARG: other workgroups write those while it
  *              is read); null: NGQ_ERR_ARG
  *   workspace: device, at least ngq_splitk_workspace_bytes(K, N, bits, group)
  *              bytes, for every T (it is always used)
- * Other arguments, shapes and status codes as ngq_gemm_rescale; a K slice of
- * X that does not fit in LDS gives NGQ_ERR_UNSUPPORTED. */
+ * Other arguments, shapes and status codes as ngq_gemm_rescale. */
 int ngq_gemm_residual_rescale(int T, int K, int N, int bits, int group, const void* x, const void* wq,
                               const void* scales, const void* residual, void* y, void* x_next, void* workspace,
                               size_t workspace_bytes, void* stream);

@@ -271,7 +271,7 @@ def test_splitk_workspace_and_empty_calls(ngq):
     ((8, *DOWN, XL, WL, SL, YL, XL, WSL, 1 << 21), -1),               # x_next overlaps x
     ((8, *DOWN, XL, WL, SL, YL, WL + 4096, WSL, 1 << 21), -1),        # x_next overlaps wq
     ((8, *DOWN, XL, WL, SL, YL, WSL + 0x10000, WSL, 1 << 21), -1),    # x_next overlaps the workspace
-    ((1, *DOWN, XL, WL, SL, YL, XNL, WSL, 1 << 16), -1),              # workspace too small (split at T = 1)
+    ((1, *DOWN, XL, WL, SL, YL, XNL, WSL, 1 << 15), -1),              # workspace too small (split at T = 1)
     ((8, *DOWN, XL, WL, SL, YL, XNL, None, 1 << 21), -1),             # null workspace
 ])
 def test_gemm_rescale_rejects_bad_arguments(ngq, args, status):

@@ -67,18 +67,20 @@ def test_no_load_waits_on_a_descriptor_loop(asm):
 
 
 def test_decode_kernels_use_no_scratch(asm):
-    """The streaming, VALU-step and one-tile-per-workgroup fused kernels keep
+    """The streaming, VALU-step, split-K and one-tile-per-workgroup fused kernels keep
     everything in registers: no spills, and no private copy of the argument
     block (the fused kernels index their projection descriptors with a
     workgroup-uniform value)."""
     meta = {}
-    for m in re.finditer(r"\.name:\s+(_ZN3ngq3dev\d+(gemm_(?:multi_dot|multi_stream|stream|dot)_kernel)\S*)", asm):
+    for m in re.finditer(r"\.name:\s+(_ZN3ngq3dev\d+(gemm_(?:multi_dot|multi_stream|stream|dot|splitk)_kernel)\S*)",
+                         asm):
         start = asm.rfind("\n  - ", 0, m.start())
         end = asm.find("\n  - ", m.end())
         block = asm[start:end if end > 0 else len(asm)]
         fields = dict(re.findall(r"\.(private_segment_fixed_size|vgpr_spill_count):\s+(\d+)", block))
         meta[m.group(1)] = fields
     assert {re.match(r"_ZN3ngq3dev\d+(\w+?kernel)", k).group(1) for k in meta} == {
-        "gemm_multi_dot_kernel", "gemm_multi_stream_kernel", "gemm_stream_kernel", "gemm_dot_kernel"}
+        "gemm_multi_dot_kernel", "gemm_multi_stream_kernel", "gemm_stream_kernel", "gemm_dot_kernel",
+        "gemm_splitk_kernel"}
     bad = {k: v for k, v in meta.items() if v.get("private_segment_fixed_size") != "0" or v.get("vgpr_spill_count") != "0"}
     assert not bad, bad

@@ -1,12 +1,12 @@
 """ngq_gemm_splitk (K split over several workgroups per column tile) on the GPU.
 
-The split applies where X does not fit in LDS (T K > 73728: the down
-projection at T >= 5).  Against the oracle on the down-projection shape and
-on ragged shapes (an odd
+The split applies where the 32-column tiles leave CUs idle and every slice
+keeps 8 pairs (the down projection: 3 slices of 64-column tiles at any T).
+Against the oracle on the down-projection shape and on ragged shapes (an odd
 group count, so the last slice ends in half a pair; N not a multiple of the
-32-column tile; every bit width and both scale types); bit for bit where the
-partial sums are exact; run to run; and the shapes where a split gains
-nothing, which run as ngq_gemm.
+64-column tile; every bit width and both scale types); bit for bit where the
+partial sums are exact; run to run; and the shapes where no split applies,
+which run as ngq_gemm.
 """
 import numpy as np
 import pytest
@@ -51,12 +51,15 @@ def run(ngq, orc, bits, sbf16, T, K, N, seed, cols=None):
 
 
 @pytest.mark.parametrize("bits,sbf16,T,K,N", [
-    (4, False, 8, 12352, 100),   # 193 groups: the last slice ends in half a pair
+    (4, False, 8, 12352, 100),   # 193 groups, 8 slices of 13 pairs: the last one ends in half a pair
     (5, True, 7, 16384, 36),     # 128 pairs: sixteen per slice
     (8, False, 5, 20480, 64),
-    (4, True, 6, 12352, 260),    # 97 pairs: a short last slice
+    (4, True, 6, 12352, 260),    # 97 pairs, 5 tiles: 8 slices, a short last one
     (5, False, 7, 17408, 4),     # one narrow tile
-    (4, False, 5, 17408, 5124),  # 161 tiles: the last workgroup of a slice has one live wave
+    (4, False, 5, 17408, 5124),  # 81 tiles of 64 columns, the last one 4 wide: 3 slices
+    (4, False, 1, 17408, 5120),  # T = 1
+    (8, True, 2, 4096, 1000),    # 32 pairs: 4 slices; T = 2
+    (5, True, 3, 2176, 192),     # 17 pairs: 2 slices, the second one pair short; T = 3
 ])
 def test_splitk_small(ngq, orc, bits, sbf16, T, K, N):
     run(ngq, orc, bits, sbf16, T, K, N, seed=K + N + T)
@@ -108,10 +111,10 @@ def test_splitk_identity_scales_integer_x_bit_exact(ngq, orc, bits):
     assert np.array_equal(host_bits(y), orc.round_bf16_array(y64))
 
 
-@pytest.mark.parametrize("T,K,N", [(4, 17408, 512), (8, 4096, 64), (8, 10240, 8192), (3, 0, 8)])
+@pytest.mark.parametrize("T,K,N", [(4, 1024, 512), (8, 960, 64), (8, 10240, 8192), (1, 5120, 8192), (3, 0, 8)])
 def test_splitk_without_a_split_runs_as_gemm(ngq, T, K, N):
-    """X that fits the X-resident kernel, few pairs, enough tiles, or K = 0:
-    the call is ngq_gemm, bit for bit."""
+    """Fewer than 16 pairs (no two slices of 8), tiles that fill the CUs, or
+    K = 0: the call is ngq_gemm, bit for bit."""
     _, (codes, scales, x) = make(4, False, T, K, N, seed=5)
     packed = ngq.ngq_pack(codes, 4) if K else np.zeros(16, np.uint8)
     xd = dev_bf16(x) if K else torch.zeros((T, 0), dtype=torch.bfloat16, device="cuda")
