@@ -1833,16 +1833,18 @@ __global__ __launch_bounds__(kMultiDotW * 64) void gemm_multi_dot_kernel(MultiTi
 
 constexpr int kMultiStreamW = 4;
 
-// Columns of a plain (one output set) tile in gemm_multi_stream_kernel: 64 at
-// T >= 5, where a tile's X bands (80 KB per workgroup at T = 8) are worth
-// sharing over more columns (T = 8: 36.1 against 37.4 us; at T <= 4 no
-// gain), else 32.  SwiGLU tiles keep 32 columns of each half.
-__host__ __device__ constexpr int multi_tile_cols(int T, int nsets) { return nsets == 1 && T >= 5 ? 64 : 32; }
+// Columns of a tile (of each half, for SwiGLU) in gemm_multi_stream_kernel:
+// 64 at T >= 5, where a tile's X bands (80 KB per workgroup at T = 8) are
+// worth sharing over more columns, else 32.  Stacked layer at T = 8: 37.4 us
+// with 32-column tiles, 36.1 with 64-column plain tiles, 34.9-35.1 with
+// 64-column SwiGLU tiles too (200 VGPRs: two 4-wave workgroups a CU; 2, 3,
+// 6 or 8 waves 7-11 % slower); at T <= 4 wider tiles gain nothing.
+__host__ __device__ constexpr int multi_tile_cols(int T) { return T >= 5 ? 64 : 32; }
 
 template <int XM>
 __global__ __launch_bounds__(kMultiStreamW * 64) void gemm_multi_stream_kernel(MultiTileArgs m) {
   constexpr int W = kMultiStreamW;
-  constexpr int VP = multi_tile_cols(XM, 1) / 16;  // plain tiles; XM = 8 stands for T = 5..8
+  constexpr int VP = multi_tile_cols(XM) / 16;  // XM = 8 stands for T = 5..8
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int b = blockIdx.x;
   int p = 0;
@@ -1854,8 +1856,8 @@ __global__ __launch_bounds__(kMultiStreamW * 64) void gemm_multi_stream_kernel(M
   switch (m.kind[p]) {
     case multi_kind(4, false, 1): stream_tile<4, false, VP, W, XM, 1>(a, tile, smem); break;
     case multi_kind(4, true, 1): stream_tile<4, true, VP, W, XM, 1>(a, tile, smem); break;
-    case multi_kind(4, false, 2): stream_tile<4, false, 2, W, XM, 2>(a, tile, smem); break;
-    case multi_kind(4, true, 2): stream_tile<4, true, 2, W, XM, 2>(a, tile, smem); break;
+    case multi_kind(4, false, 2): stream_tile<4, false, VP, W, XM, 2>(a, tile, smem); break;
+    case multi_kind(4, true, 2): stream_tile<4, true, VP, W, XM, 2>(a, tile, smem); break;
     case multi_kind(5, false, 1): stream_tile<5, false, VP, W, XM, 1>(a, tile, smem); break;
     case multi_kind(5, true, 1): stream_tile<5, true, VP, W, XM, 1>(a, tile, smem); break;
     case multi_kind(8, false, 1): stream_tile<8, false, VP, W, XM, 1>(a, tile, smem); break;
@@ -3586,9 +3588,9 @@ int load_plan(int K, int nproj, const int* kind, const int* nout, int wg_max, de
 // a.proj, kinds in kind) as segments of one grid, the heaviest tiles (weight
 // and scale bytes per tile) first.  Measured against the persistent kernel
 // (QK + gate/value + gate/up): T = 1 32.7 against 37.8 us, T = 2 32.7
-// against 37.2-38.2, T = 4 33.5 against 37.4-37.9, T = 8 36.1 (37.2-37.4
-// with 32-column plain tiles) against 37.9-39.0; with 2, 3, 5, 6 or 8 waves
-// a tile at T >= 2: 2-10 % slower than 4.
+// against 37.2-38.2, T = 4 33.5 against 37.4-37.9, T = 8 34.9-35.1 (37.2-37.4
+// with 32-column tiles) against 37.9-39.0; with 2, 3, 5, 6 or 8 waves a tile
+// at T >= 2: 2-11 % slower than 4.
 constexpr int kMultiStreamMaxT = 8;
 
 int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs& a, const int* kind, int n,
@@ -3597,7 +3599,7 @@ int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs
   long tile_bytes[NGQ_MAX_PROJ];
   for (int i = 0; i < n; ++i) {
     const dev::MultiProj& mp = a.proj[i];
-    const int tc = dev::multi_tile_cols(T, mp.Ncols / mp.Nout);
+    const int tc = dev::multi_tile_cols(T);
     tile_bytes[i] = ((long)mp.p0_bytes + mp.p1_bytes + mp.s_bytes) / ((mp.Nout + tc - 1) / tc);
     order[i] = i;
   }
@@ -3615,7 +3617,7 @@ int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs
     g.T = T; g.K = K; g.Nout = mp.Nout; g.Ncols = mp.Ncols; g.up_off = mp.up_off;
     g.G = G; g.pairs = pairs;
     g.ppw = (pairs + w - 1) / w;
-    const int tc = dev::multi_tile_cols(T, mp.Ncols / mp.Nout);
+    const int tc = dev::multi_tile_cols(T);
     g.ntiles = (mp.Nout + tc - 1) / tc;
     g.p0_bytes = mp.p0_bytes; g.p1_bytes = mp.p1_bytes; g.s_bytes = mp.s_bytes; g.x_bytes = (uint32_t)xb;
     g.mask_nib = dev::kMasks.nib; g.mask_base = dev::kMasks.base; g.mask_hi = dev::kMasks.hi;
@@ -3630,8 +3632,7 @@ int run_multi_tiles(int T, int K, const void* x, size_t xb, const dev::MultiArgs
     const uint32_t lds = dev::DotSmem<dev::kMultiDotW, 1, 2>::bytes();
     hipLaunchKernelGGL(dev::gemm_multi_dot_kernel, dim3((unsigned)grid), dim3(dev::kMultiDotW * 64), lds, st, m);
   } else {
-    const uint32_t lds = std::max(dev::StreamSmem<dev::kMultiStreamW>::bytes(32, 2),
-                                  dev::StreamSmem<dev::kMultiStreamW>::bytes(64, 1));
+    const uint32_t lds = dev::StreamSmem<dev::kMultiStreamW>::bytes(64, 2);
     const dim3 g((unsigned)grid), blk(dev::kMultiStreamW * 64);
     if (T == 2)
       hipLaunchKernelGGL(dev::gemm_multi_stream_kernel<2>, g, blk, lds, st, m);
