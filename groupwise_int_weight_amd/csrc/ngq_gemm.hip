@@ -1603,8 +1603,10 @@ __global__ __launch_bounds__(W * 64) void gemm_dot_kernel(GemmArgs a) {
 // ---- several projections of one X in one launch ----------------------------
 //
 // The projections of a layer that read the same activations (QK, gate/value
-// and gate/up) run as one persistent launch: X is staged once per workgroup,
-// the launch and its ramp are paid once, and the tiles of all projections are
+// and gate/up) run as one launch.  Where every projection is int4 or plain
+// int5 / int8 that launch is one workgroup per tile (gemm_multi_dot_kernel,
+// gemm_multi_stream_kernel, below); otherwise it is this persistent kernel:
+// X is staged once per workgroup, and the tiles of all projections are
 // spread over the workgroups by cost (host-planned, longest tiles first to
 // the least loaded workgroup), which also evens out projections whose tile
 // count is not a multiple of the CU count.  Workgroup r owns a contiguous
